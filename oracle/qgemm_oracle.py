@@ -1,0 +1,380 @@
+"""CPU oracle for the quantized linear layer -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call anything in this package. The product path
+(the HIP library and its Python binding) never imports it, and this package
+imports nothing from the product path: the two share no code. Inputs come
+from the seeded generator module, which holds no quantization arithmetic.
+
+Each function is the plain definition of one step, written with numpy and
+citing the page passage it follows. Precision:
+
+* quantizers decide integer codes in float32, because the pages compute them
+  in float32 (the numpy reference in "Activation Quantization Architecture,
+  in depth", section "The integer GEMM, written out", works on float32 arrays;
+  the MXFP8 recipe of "TileLang tutorial, chapter 27", section 2.2, works on
+  float32 amax values). The GPU takes the same decisions in the same
+  precision, so codes, scales and zero points compare bit for bit;
+* integer dot products are exact (see ``int_gemm``);
+* the dequantization epilogue and the MX reference are float64.
+
+Pages cited (titles as they appear on the pages):
+
+* [D98] "100 Days of GPU -- Day 98: Quantization and sparsity"
+* [TL27] "TileLang tutorial, chapter 27: low-precision quantization"
+  (Chinese; sections numbered 1-8)
+* [SK] "Skill: Write an INT8 Quantized Kernel"
+* [AQ] "Activation Quantization Architecture, in depth"
+
+Readings where the pages are silent or disagree are listed in the header of
+each function that takes one. Every function has at least one pin in
+``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+
+INT8_QMAX = 127          # [SK] step 1, [AQ] "The quantizer itself": symmetric range +-127
+UINT8_QMAX = 255         # [SK] step 1: asymmetric range [0, 255]
+SCALE_FLOOR = F32(1e-8)  # [AQ] "The integer GEMM, written out": floor for all-zero rows
+MX_BLOCK = 32            # [TL27] 2.3(a): one shared scale per 32 elements
+E4M3_MAX = 448.0         # [TL27] 2.2 item 1: largest finite e4m3 value, 1.75 * 2^8
+MX_AMAX_FLOOR = F32(1e-4)  # [TL27] 2.2 item 3: amax.clamp_min(1e-4)
+
+# Exact-int32 limits on K (see ``k_limit``).
+INT32_MAX = 2**31 - 1
+
+
+# ----------------------------------------------------------------------------
+# Symmetric int8 quantizer
+# ----------------------------------------------------------------------------
+def quantize_sym_int8(x, per_row: bool = True):
+    """Symmetric int8 quantization, per row (token / channel) or per tensor.
+
+    [D98] "What a scale actually promises": x = q*s with s = max|x|/127, code 0
+    meaning 0. [AQ] "The integer GEMM, written out" (``quantize_per_token``):
+    s = max|x|/127 in float32, floored at 1e-8 for all-zero rows,
+    q = clip(rint(x/s), -127, 127). [D98] "Pitfalls": always clamp after
+    rounding. [TL27] 2.4 gives the same formula with a lower bound of -128;
+    the +-127 range of [SK] step 1 and [AQ] is used (with s from the same
+    data, rint(x/s) never leaves [-127, 127] anyway).
+
+    Rounding: np.rint, half to even, on the float32 quotient x/s (a correctly
+    rounded IEEE division). Returns (q int8 [R, K], s float32 [R] or [1]).
+    """
+    x = np.asarray(x, dtype=F32)
+    assert x.ndim == 2
+    if x.shape[0] == 0:
+        return np.zeros(x.shape, np.int8), np.zeros((0 if per_row else 1,), F32)
+    if per_row:
+        amax = np.max(np.abs(x), axis=1, keepdims=True)
+    else:
+        amax = np.max(np.abs(x)).reshape(1, 1)
+    s = amax / F32(INT8_QMAX)
+    s = np.maximum(s, SCALE_FLOOR).astype(F32)
+    q = np.clip(np.rint(x / s), -INT8_QMAX, INT8_QMAX).astype(np.int8)
+    return q, s.reshape(-1)
+
+
+# ----------------------------------------------------------------------------
+# Asymmetric uint8 quantizer
+# ----------------------------------------------------------------------------
+def quantize_asym_uint8(x, per_row: bool = True):
+    """Asymmetric uint8 quantization with a zero point, per row or per tensor.
+
+    [SK] step 1: s = (max(x) - min(x))/255, z = round(-min(x)/s),
+    q = clamp(round(x/s) + z, 0, 255). [AQ] "The quantizer itself":
+    q = clamp(round(x/s) + z, qmin, qmax), x_hat = s*(q - z).
+    [D98] "What a scale actually promises": x = (q - z)*s.
+
+    Readings: (1) s is floored at 1e-8 like the symmetric scale (a constant
+    row would otherwise divide by zero, [AQ] "Failure modes"); (2) z is
+    clamped to [0, 255] so it is itself a code -- the pages do not clamp it,
+    and it only matters for rows that do not contain 0 in [min, max];
+    (3) round first, then add the integer z (both pages' order).
+    Arithmetic in float32; rint half to even.
+    Returns (q uint8, s float32 [R] or [1], z int32 [R] or [1]).
+    """
+    x = np.asarray(x, dtype=F32)
+    assert x.ndim == 2
+    if x.shape[0] == 0:
+        n = 0 if per_row else 1
+        return np.zeros(x.shape, np.uint8), np.zeros((n,), F32), np.zeros((n,), np.int32)
+    if per_row:
+        mn = np.min(x, axis=1, keepdims=True)
+        mx = np.max(x, axis=1, keepdims=True)
+    else:
+        mn = np.min(x).reshape(1, 1)
+        mx = np.max(x).reshape(1, 1)
+    s = (mx - mn) / F32(UINT8_QMAX)
+    s = np.maximum(s, SCALE_FLOOR).astype(F32)
+    z = np.clip(np.rint(-mn / s), 0, UINT8_QMAX).astype(np.int32)
+    q = np.clip(np.rint(x / s).astype(np.float64) + z, 0, UINT8_QMAX).astype(np.uint8)
+    return q, s.reshape(-1), z.reshape(-1)
+
+
+# ----------------------------------------------------------------------------
+# Weight preparation
+# ----------------------------------------------------------------------------
+def prepare_weights_int8(w, per_channel: bool = True):
+    """Symmetric int8 weights with per-channel scales and column sums.
+
+    W is [N, K] (one row per output channel). [AQ] "The integer GEMM, written
+    out" (``quantize_per_channel``): one scale per output channel, the same
+    symmetric rule as the activations (the 1e-8 floor is applied here too).
+    [D98] "The program, and the gate that has to be per column": the column
+    sum sum_k q_w[k][col] depends only on the weights and is computed once,
+    when they are quantized. Returns (q_w int8 [N, K], s_w float32 [N] or [1],
+    colsum int64 [N]).
+    """
+    q, s = quantize_sym_int8(w, per_row=per_channel)
+    colsum = q.astype(np.int64).sum(axis=1)
+    return q, s, colsum
+
+
+def k_limit(asymmetric: bool) -> int:
+    """Largest K for which every int32 accumulator value is exact.
+
+    [D98] "What a scale actually promises": |acc| <= K*127*128 when one
+    operand may reach 128 in magnitude. [AQ] "The integer GEMM, written out":
+    symmetric products are at most 127*127 = 16129, so up to about 133,000
+    terms fit in int32. [SK] step 2 asks for this check. For uint8 codes with a
+    zero point the corrected sum sum (q_a - z) q_w has terms up to 255*127.
+    """
+    per_term = 255 * 127 if asymmetric else 127 * 127
+    return INT32_MAX // per_term
+
+
+# ----------------------------------------------------------------------------
+# Integer GEMM and epilogue
+# ----------------------------------------------------------------------------
+def int_gemm(q_a, z_a, q_w):
+    """C[m, n] = sum_k (q_a[m, k] - z_a[m]) * q_w[n, k], exactly.
+
+    [AQ] "The integer GEMM, written out": y = s_a*s_w*(sum qa*qw - z_a*sum qw);
+    [D98] "What a scale actually promises": integer products accumulated in
+    int32 round nothing. z_a is a scalar, a [1] array (per tensor) or an [M]
+    array (per token); pass 0 for symmetric codes.
+
+    The sum is evaluated with a float64 matrix product. That is exact here:
+    every operand is an integer of magnitude <= 255, every product and every
+    partial sum is an integer below K*255*128 < 2^53, and float64 represents
+    all such integers, so no addition in any order rounds.
+    """
+    q_a = np.asarray(q_a)
+    q_w = np.asarray(q_w)
+    M, K = q_a.shape
+    N = q_w.shape[0]
+    assert q_w.shape[1] == K
+    assert K * 255 * 128 < 2**53
+    z = np.broadcast_to(np.asarray(z_a, dtype=np.float64).reshape(-1, 1), (M, 1))
+    a = q_a.astype(np.float64) - z
+    if M == 0 or N == 0:
+        return np.zeros((M, N), np.int64)
+    C = a @ q_w.astype(np.float64).T
+    return C.astype(np.int64)
+
+
+def int_gemm_entries(q_a, z_a, q_w, rows, cols):
+    """C at the (rows[i], cols[i]) pairs only, exactly (int64 dot products)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    za = np.asarray(z_a, dtype=np.int64).reshape(-1)
+    if za.size == 1:
+        za = np.full(q_a.shape[0], za[0], np.int64)
+    a = q_a[rows].astype(np.int64) - za[rows][:, None]
+    w = q_w[cols].astype(np.int64)
+    return np.einsum("ik,ik->i", a, w)
+
+
+def epilogue(C, s_a, s_w):
+    """y[m, n] = s_a[m] * s_w[n] * C[m, n], in float64.
+
+    [D98] "The program, and the gate that has to be per column": the scales
+    multiply the corrected integer once per output element, after the loop.
+    [SK] step 4 (per-token activations, per-channel weights):
+    out[m][n] = int32_result[m][n] * scale_A[m] * scale_B[n]; [SK] "Correctness
+    requirements": zero-point correction before scaling (``int_gemm`` already
+    returns the corrected integer). s_a and s_w may be [1] (per tensor).
+    """
+    C = np.asarray(C, dtype=np.float64)
+    M, N = C.shape
+    sa = np.broadcast_to(np.asarray(s_a, dtype=np.float64).reshape(-1, 1), (M, 1))
+    sw = np.broadcast_to(np.asarray(s_w, dtype=np.float64).reshape(1, -1), (1, N))
+    return C * sa * sw
+
+
+def quantized_linear(x, w, act: str = "sym_row", wgt: str = "channel"):
+    """The whole path on the CPU: quantize A, prepare W, integer GEMM, epilogue.
+
+    act: "sym_row" (per-token int8), "sym_tensor" (one int8 scale),
+    "asym_row" (per-token uint8 + zero point). wgt: "channel" or "tensor".
+    Returns a dict with every intermediate (codes, scales, zero points, column
+    sums, the exact integer C and the float64 output).
+    """
+    if act == "sym_row":
+        qa, sa = quantize_sym_int8(x, per_row=True)
+        za = np.zeros(qa.shape[0], np.int32)
+    elif act == "sym_tensor":
+        qa, sa = quantize_sym_int8(x, per_row=False)
+        za = np.zeros(1, np.int32)
+    elif act == "asym_row":
+        qa, sa, za = quantize_asym_uint8(x, per_row=True)
+    elif act == "asym_tensor":
+        qa, sa, za = quantize_asym_uint8(x, per_row=False)
+    else:
+        raise ValueError(act)
+    qw, sw, colsum = prepare_weights_int8(w, per_channel=(wgt == "channel"))
+    C = int_gemm(qa, za, qw)
+    y = epilogue(C, sa, sw)
+    return dict(q_a=qa, s_a=sa, z_a=za, q_w=qw, s_w=sw, colsum=colsum, C=C, y=y)
+
+
+# ----------------------------------------------------------------------------
+# bf16 output rounding
+# ----------------------------------------------------------------------------
+def bf16_to_f32(bits_u16):
+    """Decode bf16 bit patterns: the upper half of a float32 ([TL27] 2.1)."""
+    b = np.asarray(bits_u16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# MX: E8M0 scales and e4m3 codes
+# ----------------------------------------------------------------------------
+def ceil_to_ue8m0(t):
+    """Biased exponent E of the smallest power of two >= |t|, as E8M0.
+
+    [TL27] 2.3(b): E8M0 is exactly a float32's biased exponent byte, values
+    2^-127 .. 2^127, code 255 reserved for NaN; rounding up to a power of two
+    adds one to the exponent when the mantissa is non-zero, then the code is
+    clamped to [1, 254] (skipping 0 and the NaN code). Returns uint8 codes;
+    the scale they stand for is 2^(E - 127).
+    """
+    t = np.abs(np.asarray(t, dtype=F32))
+    bits = t.view(np.uint32)
+    e = ((bits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int32)
+    e = e + ((bits & np.uint32(0x7FFFFF)) != 0).astype(np.int32)
+    return np.clip(e, 1, 254).astype(np.uint8)
+
+
+def e8m0_value(E):
+    """2^(E - 127) as float64 ([TL27] 2.3(b))."""
+    return np.ldexp(1.0, np.asarray(E, dtype=np.int32) - 127)
+
+
+def _e4m3_table():
+    """Values of all 256 OCP e4m3fn codes ([TL27] 2.2).
+
+    Sign bit, 4 exponent bits (bias 7), 3 mantissa bits. Exponent field 0 is
+    subnormal: m * 2^-9. No infinities; only 0x7f and 0xff are NaN, so the
+    largest finite value is 0x7e = 1.75 * 2^8 = 448. 0x80 is -0.
+    """
+    vals = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = s * m * 2.0**-9
+        else:
+            vals[c] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+E4M3_VALUES = _e4m3_table()
+_E4M3_POS = E4M3_VALUES[:127]  # codes 0x00..0x7e, strictly increasing
+
+
+def e4m3_decode(codes):
+    """float64 value of each e4m3 code (NaN for 0x7f / 0xff)."""
+    return E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode_rne(y):
+    """Nearest e4m3 code to each float32 y, ties to the even code.
+
+    Round to nearest, ties to even, over the 127 non-negative finite values,
+    sign carried separately (so -0.0 and negatives that round to zero give
+    0x80). Subnormal codes are used below 2^-6. |y| > 448 is rejected: the
+    MX scale guarantees it cannot happen ([TL27] 7, pitfall 6).
+    """
+    y = np.asarray(y, dtype=F32)
+    a = np.abs(y).astype(np.float64)
+    if np.any(~np.isfinite(a)) or np.any(a > E4M3_MAX):
+        raise ValueError("e4m3 input outside [-448, 448]")
+    hi = np.searchsorted(_E4M3_POS, a, side="left")     # first value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(y), code | np.uint8(0x80), code).astype(np.uint8)
+    return code
+
+
+def quantize_mx(x):
+    """MXFP8 quantization: e4m3 codes plus one E8M0 scale per 32 K-elements.
+
+    [TL27] 2.2 item 3 (the MXFP8 recipe): per block, amax = max|x| floored at
+    1e-4; sf = ceil_to_ue8m0(amax / 448); codes = e4m3(x * (1/sf)).
+    [TL27] 2.3(a): the block is 32 contiguous elements along K, in every row.
+    1/sf is an exact power of two, so the scaling is exact and only the e4m3
+    rounding (``e4m3_encode_rne``) loses information. Because sf >= amax/448,
+    every scaled value is <= 448 in magnitude.
+
+    x: float32 [R, K] with K % 32 == 0. Returns (codes uint8 [R, K],
+    E uint8 [R, K/32]) -- the public layout: row-major codes and row-major
+    scale bytes.
+    """
+    x = np.asarray(x, dtype=F32)
+    R, K = x.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blocks = x.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blocks), axis=2) if R else np.zeros((0, K // MX_BLOCK), F32)
+    amax = np.maximum(amax, MX_AMAX_FLOOR).astype(F32)
+    E = ceil_to_ue8m0(amax / F32(E4M3_MAX))
+    inv = np.ldexp(F32(1.0), (127 - E.astype(np.int32))).astype(F32)
+    y = (blocks * inv[:, :, None]).astype(F32)
+    codes = e4m3_encode_rne(y).reshape(R, K)
+    return codes, E
+
+
+def mx_dequantize(codes, E):
+    """float64 values codes * 2^(E - 127), E broadcast over each 32-block."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    R, K = codes.shape
+    v = e4m3_decode(codes).reshape(R, K // MX_BLOCK, MX_BLOCK)
+    v = v * e8m0_value(E)[:, :, None]
+    return v.reshape(R, K)
+
+
+def mx_gemm_ref(qa, Ea, qw, Ew):
+    """out[m, n] = sum_b 2^(Ea[m,b]-127) 2^(Ew[n,b]-127) sum_{k in b} a[m,k] w[n,k].
+
+    [TL27] 4.1: the block-scaled product is (A * scale_A)(B * scale_B) + D;
+    [TL27] 4.3: a per-K-block scale must be applied inside the K loop, to its
+    own block. Evaluated as a float64 dot product of the dequantized values.
+    Every dequantized value and every product is exact in float64 (at most 4
+    significant bits each); the sum over K rounds only at float64 precision.
+    Also returns S[m, n] = sum_k |a[m,k] w[n,k]|, the error basis of
+    [TL27] 2.5. Both [M, N] float64.
+    """
+    A = mx_dequantize(qa, Ea)
+    W = mx_dequantize(qw, Ew)
+    return A @ W.T, np.abs(A) @ np.abs(W).T
+
+
+def mx_gemm_ref_entries(qa, Ea, qw, Ew, rows, cols):
+    """``mx_gemm_ref`` at the (rows[i], cols[i]) pairs only."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    A = mx_dequantize(qa[rows], Ea[rows])
+    W = mx_dequantize(qw[cols], Ew[cols])
+    return np.einsum("ik,ik->i", A, W), np.einsum("ik,ik->i", np.abs(A), np.abs(W))

@@ -1,0 +1,457 @@
+"""Pins for the CPU oracle: each test ties one oracle function to something the
+pages or the mathematics fix, independently of the oracle's own code.
+
+Pages: [D98] "100 Days of GPU -- Day 98: Quantization and sparsity";
+[TL27] "TileLang tutorial, chapter 27: low-precision quantization";
+[SK] "Skill: Write an INT8 Quantized Kernel";
+[AQ] "Activation Quantization Architecture, in depth".
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle import metrics as MT
+from block_scaled_quantized_qgemm_amd.inputs import make_inputs, rng_for
+from conftest import GOLDEN
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# Symmetric quantizer: the worked outlier example ([AQ] "Why activations are
+# harder than weights")
+# --------------------------------------------------------------------------
+def test_outlier_row_worked_example():
+    g = _golden("aq_outlier_row.json")
+    rng = rng_for(1)
+    row = rng.uniform(-2.0, 2.0, size=64).astype(np.float32)
+    row[5] = np.float32(g["with_outlier"]["x"])
+    row[9] = np.float32(g["with_outlier"]["row_max"])
+    q, s = O.quantize_sym_int8(row[None, :], per_row=True)
+    assert abs(float(s[0]) - g["with_outlier"]["scale_approx"]) < 0.005
+    assert int(q[0, 5]) == g["with_outlier"]["code"]
+    xhat = float(q[0, 5]) * float(s[0])
+    assert abs(xhat - g["with_outlier"]["dequant_approx"]) < 0.005
+    assert abs(xhat - 0.3) / 0.3 > g["with_outlier"]["rel_error_greater_than"]
+
+    row2 = row.copy()
+    row2[9] = np.float32(1.0)
+    row2[10] = np.float32(g["without_outlier"]["row_max"])
+    row2 = np.clip(row2, -2.0, 2.0).astype(np.float32)
+    q2, s2 = O.quantize_sym_int8(row2[None, :], per_row=True)
+    assert abs(float(s2[0]) - g["without_outlier"]["scale_approx"]) < 0.001
+    xhat2 = float(q2[0, 5]) * float(s2[0])
+    assert abs(xhat2 - 0.3) / 0.3 < g["without_outlier"]["rel_error_within"]
+    # the exact value: rint(0.3 / (2/127)) = rint(19.05) = 19
+    assert int(q2[0, 5]) == 19
+
+
+# --------------------------------------------------------------------------
+# Per-tensor code starvation ([D98] opening and "What a scale actually promises")
+# --------------------------------------------------------------------------
+def test_code_starvation_per_tensor_vs_per_channel():
+    g = _golden("d98_code_starvation.json")
+    A, W = make_inputs("c1_tiny")
+    # column j of B is row j of W; row 63 carries gain 2^-6 = 1/64
+    qt, st = O.quantize_sym_int8(W, per_row=False)
+    mags = sorted(set(np.abs(qt[63].astype(int)).tolist()))
+    assert mags == g["per_tensor_code_magnitudes"]
+    qc, sc = O.quantize_sym_int8(W, per_row=True)
+    assert np.all(np.max(np.abs(qc.astype(int)), axis=1) == g["per_channel_max_code"])
+    assert len(set(qc[63].tolist())) > 100          # the quiet column keeps its range
+    assert st.shape == (1,) and sc.shape == (64,)
+
+
+# --------------------------------------------------------------------------
+# Rounding: half to even on the float32 quotient; clamp always ([D98] Pitfalls)
+# --------------------------------------------------------------------------
+def test_round_half_even_ties_and_clamp():
+    # amax = 127/8 makes s = 1/8 exactly, so x = (n + 1/2)/8 is an exact tie
+    x = np.array([[127 / 8, 2.5 / 8, 3.5 / 8, -2.5 / 8, -3.5 / 8, 0.5 / 8, -0.5 / 8, 0.0]], np.float32)
+    q, s = O.quantize_sym_int8(x)
+    assert float(s[0]) == 0.125
+    assert q[0].tolist() == [127, 2, 4, -2, -4, 0, 0, 0]
+
+
+def test_scale_floor_all_zero_row():
+    q, s = O.quantize_sym_int8(np.zeros((2, 16), np.float32))
+    assert np.all(s == np.float32(1e-8)) and np.all(q == 0)
+    q, s, z = O.quantize_asym_uint8(np.full((1, 8), 3.0, np.float32))
+    assert float(s[0]) == np.float32(1e-8)
+    assert int(z[0]) == 0 and np.all(q == 255)  # clamped, reading: z in [0, 255]
+
+
+# --------------------------------------------------------------------------
+# Storage error ([TL27] 2.4: max error s/2, RMS s/sqrt(12), u = 1/254 of absmax;
+# [SK] "Correctness requirements": round trip within 0.5 * scale)
+# --------------------------------------------------------------------------
+def test_storage_error_bounds_symmetric():
+    g = _golden("format_constants.json")
+    A, _ = make_inputs("c2_per_token", M=64, K=4096, N=8)
+    q, s = O.quantize_sym_int8(A)
+    err = np.abs(A.astype(np.float64) - q.astype(np.float64) * s[:, None])
+    half = s.astype(np.float64)[:, None] / 2
+    assert np.all(err <= half * (1 + 1e-6))
+    amax = np.max(np.abs(A), axis=1).astype(np.float64)
+    assert np.all(err.max(axis=1) / amax <= g["int8_u"] * (1 + 1e-3))
+    rms = np.sqrt(np.mean(err[1:] ** 2, axis=1)) / s[1:]
+    assert np.all(np.abs(rms - 1 / math.sqrt(12)) < 0.02)
+
+
+def test_storage_error_bounds_asymmetric():
+    A, _ = make_inputs("c2_per_token", M=32, K=2048, N=8)   # rows contain both signs
+    q, s, z = O.quantize_asym_uint8(A)
+    xhat = (q.astype(np.float64) - z[:, None]) * s[:, None]
+    err = np.abs(A - xhat)
+    assert np.all(err <= s[:, None].astype(np.float64) / 2 * (1 + 1e-5) + 1e-7)
+    assert np.all(z > 0) and np.all(z < 255)
+
+
+def test_one_sided_rows_get_zero_point_zero():
+    # reading: on |N(0,1)| rows -min/s rounds to 0, so z = 0 and x = q*s
+    A, _ = make_inputs("c3_asym_uint8", M=16, K=4096, N=8)
+    q, s, z = O.quantize_asym_uint8(A)
+    assert np.all(z == 0)
+    assert np.max(q) == 255
+
+
+# --------------------------------------------------------------------------
+# Accumulator bound ([D98] "What a scale actually promises", [AQ] "The integer
+# GEMM, written out", [SK] step 2)
+# --------------------------------------------------------------------------
+def test_accumulator_bounds_and_limits():
+    g = _golden("format_constants.json")
+    assert 127 * 127 == g["sym_product_max"]
+    ks = O.k_limit(asymmetric=False)
+    assert abs(ks - g["sym_terms_about"]) < 1000 and ks * 16129 <= 2**31 - 1 < (ks + 1) * 16129
+    ka = O.k_limit(asymmetric=True)
+    assert ka * 255 * 127 <= 2**31 - 1 < (ka + 1) * 255 * 127
+    K = 4096
+    full = np.full((1, K), 127, np.int8)
+    assert O.int_gemm(full, 0, full)[0, 0] == K * 16129
+    # uint8 code 0 with zero point 128 is -128: the K*127*128 extreme of [D98]
+    zero = np.zeros((1, K), np.uint8)
+    neg = np.full((1, K), -127, np.int8)
+    assert O.int_gemm(zero, 128, neg)[0, 0] == K * 127 * 128
+    top = np.full((1, K), 255, np.uint8)
+    assert O.int_gemm(top, 0, full)[0, 0] == K * 255 * 127
+
+
+# --------------------------------------------------------------------------
+# Integer GEMM: brute force against pure-Python integers on tiny shapes
+# --------------------------------------------------------------------------
+def test_int_gemm_every_code_pair():
+    a = np.arange(-127, 128, dtype=np.int8)
+    for qw in (-127, -1, 0, 1, 5, 127):
+        C = O.int_gemm(a[:, None], 0, np.array([[qw]], np.int8))
+        assert C[:, 0].tolist() == [int(v) * qw for v in a]
+    u = np.arange(0, 256, dtype=np.uint8)
+    for z in (0, 1, 128, 255):
+        C = O.int_gemm(u[:, None], z, np.array([[-127]], np.int8))
+        assert C[:, 0].tolist() == [(int(v) - z) * -127 for v in u]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (2, 3, 7), (7, 17, 33), (17, 5, 65), (3, 33, 127)])
+def test_int_gemm_brute_force(M, N, K):
+    rng = rng_for(M * 1000 + N * 10 + K)
+    qa = rng.integers(0, 256, (M, K)).astype(np.uint8)
+    z = rng.integers(0, 256, M).astype(np.int32)
+    qw = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    C = O.int_gemm(qa, z, qw)
+    for m in range(M):
+        for n in range(N):
+            ref = 0
+            for k in range(K):
+                ref += (int(qa[m, k]) - int(z[m])) * int(qw[n, k])
+            assert C[m, n] == ref
+    rows = np.arange(M).repeat(N)
+    cols = np.tile(np.arange(N), M)
+    assert np.array_equal(O.int_gemm_entries(qa, z, qw, rows, cols), C.reshape(-1))
+
+
+# --------------------------------------------------------------------------
+# Epilogue: scales once, against dequantize-then-multiply in float64
+# ([AQ] "The integer GEMM, written out"; [D98] section on the program)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("act", ["sym_row", "sym_tensor", "asym_row", "asym_tensor"])
+@pytest.mark.parametrize("wgt", ["channel", "tensor"])
+def test_epilogue_equals_dequantize_then_multiply(act, wgt):
+    A, W = make_inputs("c2_per_token", M=24, K=512, N=40, seed=7)
+    r = O.quantized_linear(A, W, act=act, wgt=wgt)
+    za = np.broadcast_to(r["z_a"].reshape(-1, 1), (24, 1)).astype(np.float64)
+    sa = np.broadcast_to(r["s_a"].reshape(-1, 1), (24, 1)).astype(np.float64)
+    sw = np.broadcast_to(r["s_w"].reshape(-1, 1), (40, 1)).astype(np.float64)
+    xhat = (r["q_a"].astype(np.float64) - za) * sa
+    what = r["q_w"].astype(np.float64) * sw
+    direct = xhat @ what.T
+    S = np.abs(xhat) @ np.abs(what).T
+    assert np.all(np.abs(direct - r["y"]) <= 1e-13 * S + 1e-300)
+    # integer identity: sum (qa - z) qw == sum qa qw - z * colsum(qw)
+    raw = O.int_gemm(r["q_a"], 0, r["q_w"])
+    assert np.array_equal(r["C"], raw - r["z_a"].astype(np.int64).reshape(-1, 1) * r["colsum"][None, :])
+
+
+def test_dropped_zero_point_is_a_per_column_offset():
+    # [D98] Pitfalls, [AQ] Failure modes: dropping z*colsum shifts each column by a constant
+    A, W = make_inputs("c3_asym_uint8", M=16, K=256, N=12)
+    A = A - np.float32(0.5)                      # rows with both signs, z != 0
+    qa, sa, za = O.quantize_asym_uint8(A, per_row=False)
+    qw, sw, colsum = O.prepare_weights_int8(W)
+    good = O.int_gemm(qa, za, qw)
+    planted = O.int_gemm(qa, 0, qw)              # the mistake, planted in the oracle
+    d = planted - good
+    assert int(za[0]) != 0
+    assert np.all(d == d[0:1, :])                # constant down every column
+    assert np.array_equal(d[0], int(za[0]) * colsum)
+
+
+# --------------------------------------------------------------------------
+# The per-column gate of [D98] against the float64 product of the ORIGINAL inputs
+# --------------------------------------------------------------------------
+def test_quality_gate_per_column_c1():
+    A, W = make_inputs("c1_tiny")
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    pc = O.quantized_linear(A, W, act="sym_tensor", wgt="channel")["y"]
+    pt = O.quantized_linear(A, W, act="sym_tensor", wgt="tensor")["y"]
+    kf_c, sf_c, first_c = MT.gate_fractions(pc, ref, A, W)
+    kf_t, sf_t, first_t = MT.gate_fractions(pt, ref, A, W)
+    assert first_c is None and kf_c <= 1.0           # per-column rows pass the K gate
+    assert sf_c < 1.0 < sf_t                         # the sqrt(K) diagnostic separates them
+    # the per-tensor error concentrates in the quiet columns (an axis-correlated error)
+    err_t = np.abs(pt - ref).max(axis=0)
+    err_c = np.abs(pc - ref).max(axis=0)
+    assert err_t[-8:].mean() > 4 * err_c[-8:].mean()
+
+
+def test_per_token_scales_recover_bits():
+    # [D98] Exercise and [AQ] "Why activations...": one extreme row sets a
+    # per-tensor scale and costs every other row several bits
+    A, W = make_inputs("c2_per_token", M=32, K=4096, N=64)
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    tok = O.quantized_linear(A, W, act="sym_row")["y"]
+    ten = O.quantized_linear(A, W, act="sym_tensor")["y"]
+    _, s_row = O.quantize_sym_int8(A, per_row=True)
+    _, s_ten = O.quantize_sym_int8(A, per_row=False)
+    # the step of every other row is more than 2^4 times finer per token
+    assert np.all(np.log2(s_ten[0] / s_row[1:]) > 4.0)
+    e_tok = np.sqrt(np.mean((tok[1:] - ref[1:]) ** 2))
+    e_ten = np.sqrt(np.mean((ten[1:] - ref[1:]) ** 2))
+    assert e_ten / e_tok > 4.0
+
+
+# --------------------------------------------------------------------------
+# E8M0 ([TL27] 2.3(b)) -- pinned to a definition through frexp, not the bit trick
+# --------------------------------------------------------------------------
+def _ceil_pow2_exponent(t: float) -> int:
+    m, e = math.frexp(abs(t))          # t = m * 2^e, m in [0.5, 1)
+    k = e - 1 if m == 0.5 else e       # smallest k with 2^k >= t
+    return min(max(k + 127, 1), 254)
+
+
+def test_ceil_to_ue8m0_spot_values_and_sweep():
+    g = _golden("format_constants.json")
+    spots = {1.0: 127, 1.5: 128, 0.75: 127, 2.0: 128, 0.5: 126, 448.0: 136,
+             2.0 ** -126: 1, 2.0 ** -140: 1, 1e-45: 1, 2.0 ** 127: 254, 3e38: 254}
+    for t, E in spots.items():
+        assert int(O.ceil_to_ue8m0(np.float32(t))) == E, t
+    rng = rng_for(5)
+    t = np.exp2(rng.uniform(-135, 128, 20000)).astype(np.float32)
+    t = t[np.isfinite(t) & (t > 0)]
+    E = O.ceil_to_ue8m0(t)
+    ref = np.array([_ceil_pow2_exponent(float(v)) for v in t])
+    assert np.array_equal(E.astype(int), ref)
+    assert E.min() >= 1 and E.max() <= 254 and g["e8m0_nan_code"] == 255
+    assert O.e8m0_value(np.array([1]))[0] == 2.0 ** (1 - 127)
+    assert O.e8m0_value(np.array([254]))[0] == 2.0 ** g["e8m0_max_exp"]
+
+
+# --------------------------------------------------------------------------
+# e4m3 codec ([TL27] 2.2) -- pinned to the format facts and to torch's cast
+# --------------------------------------------------------------------------
+def test_e4m3_format_facts():
+    g = _golden("format_constants.json")
+    v = O.E4M3_VALUES
+    assert v[g["e4m3_max_code"]] == g["e4m3_max"] == 1.75 * 2 ** 8
+    assert all(np.isnan(v[c]) for c in g["e4m3_nan_codes"])
+    assert np.sum(np.isnan(v)) == 2
+    assert v[0x38] == 1.0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    assert v[g["e4m3_neg_zero_code"]] == 0.0 and math.copysign(1, v[0x80]) == -1
+    assert int(O.e4m3_encode_rne(np.float32(448.0))) == 0x7E
+    assert int(O.e4m3_encode_rne(np.float32(-0.0))) == 0x80
+    assert int(O.e4m3_encode_rne(np.float32(1.0))) == 0x38
+    fin = [c for c in range(256) if not np.isnan(v[c])]
+    assert np.array_equal(O.e4m3_encode_rne(v[fin].astype(np.float32)), np.array(fin, np.uint8))
+
+
+def test_e4m3_ties_to_even_and_relative_error():
+    g = _golden("format_constants.json")
+    pos = O.E4M3_VALUES[:127]
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    codes = O.e4m3_encode_rne(mids)
+    assert np.all(codes % 2 == 0)
+    assert np.all((codes == np.arange(126)) | (codes == np.arange(1, 127)))
+    rng = rng_for(9)
+    y = rng.uniform(2.0 ** -6, 448.0, 100000).astype(np.float32)
+    rel = np.abs(O.e4m3_decode(O.e4m3_encode_rne(y)) - y) / y
+    assert rel.max() <= g["e4m3_u"] * (1 + 1e-9)         # u = 2^-p, p = 4
+    assert rel.max() > g["e4m3_u"] * 0.9                  # and the bound is tight
+
+
+def test_e4m3_matches_torch_cast():
+    torch = pytest.importorskip("torch")
+    rng = rng_for(10)
+    y = np.concatenate([
+        rng.uniform(-448, 448, 200000),
+        np.exp2(rng.uniform(-14, 8.8, 200000)) * rng.choice([-1, 1], 200000),
+        ((O.E4M3_VALUES[:126] + O.E4M3_VALUES[1:127]) / 2),
+    ]).astype(np.float32)
+    y = np.clip(y, -448, 448).astype(np.float32)
+    ours = O.e4m3_encode_rne(y)
+    theirs = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # torch turns tiny negatives into +0 or -0 consistently with the sign; compare values
+    assert np.array_equal(O.e4m3_decode(ours), O.e4m3_decode(theirs))
+
+
+# --------------------------------------------------------------------------
+# MX quantization ([TL27] 2.2 item 3, 2.3, 7 pitfall 6)
+# --------------------------------------------------------------------------
+def test_mx_quantize_scales_are_exact_and_never_overflow():
+    A, _ = make_inputs("c5_mxfp8", M=64, K=1024, N=8)
+    codes, E = O.quantize_mx(A)
+    assert codes.shape == A.shape and E.shape == (64, 32)
+    sf = O.e8m0_value(E)
+    blocks = A.reshape(64, 32, 32).astype(np.float64)
+    amax = np.maximum(np.abs(blocks).max(axis=2), 1e-4)
+    assert np.all(amax / sf <= 448.0)                         # never past e4m3's max
+    assert np.all(sf >= amax / 448.0)
+    assert np.all(sf < 2 * amax / 448.0 * (1 + 1e-7))         # the smallest such power
+    # x * 2^-k * 2^k == x (exact power-of-two scaling) in float32
+    inv = np.ldexp(np.float32(1), 127 - E.astype(np.int32)).astype(np.float32)
+    y = (blocks.astype(np.float32) * inv[:, :, None]).astype(np.float32)
+    back = (y * sf[:, :, None].astype(np.float32)).astype(np.float32)
+    assert np.array_equal(back, blocks.astype(np.float32))
+    # dequantized codes * sf are exact in float32 (<= 4 significant bits)
+    dq = O.mx_dequantize(codes, E)
+    assert np.array_equal(dq.astype(np.float32).astype(np.float64), dq)
+    # round trip: relative 2^-4 for normal scaled values, half a subnormal step below
+    err = np.abs(dq - A.astype(np.float64)).reshape(64, 32, 32)
+    yabs = np.abs(y.astype(np.float64))
+    bound = np.where(yabs >= 2.0 ** -6, yabs * 2.0 ** -4, 2.0 ** -10) * sf[:, :, None]
+    assert np.all(err <= bound * (1 + 1e-9))
+
+
+def test_mx_quantize_matches_recipe_with_torch_cast():
+    torch = pytest.importorskip("torch")
+    A, _ = make_inputs("c5_mxfp8", M=32, K=512, N=8, seed=11)
+    codes, E = O.quantize_mx(A)
+    amax = np.maximum(np.abs(A.reshape(32, 16, 32)).max(axis=2), np.float32(1e-4)).astype(np.float32)
+    t = (amax / np.float32(448.0)).astype(np.float32)
+    Eref = np.array([_ceil_pow2_exponent(float(v)) for v in t.reshape(-1)]).reshape(32, 16)
+    assert np.array_equal(E.astype(int), Eref)
+    inv = torch.from_numpy(np.exp2(127.0 - Eref).astype(np.float32))
+    y = torch.from_numpy(A.reshape(32, 16, 32)) * inv[:, :, None]
+    ref_codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(32, 512)
+    assert np.array_equal(O.e4m3_decode(codes), O.e4m3_decode(ref_codes))
+
+
+def test_mx_block_scale_on_every_block():
+    # [TL27] 4.3 and 7 pitfall 3: each K block multiplies by its own scale.
+    # Two blocks with different scales; the reference must weight each block separately.
+    qa = np.full((1, 64), 0x38, np.uint8)      # 1.0
+    qw = np.full((1, 64), 0x38, np.uint8)
+    Ea = np.array([[127, 130]], np.uint8)      # 1, 8
+    Ew = np.array([[126, 127]], np.uint8)      # 0.5, 1
+    ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew)
+    assert ref[0, 0] == 32 * 1 * 0.5 + 32 * 8 * 1
+    hoisted = 64 * 8 * 1                       # last scale applied to the whole K: wrong
+    assert ref[0, 0] != hoisted
+
+
+def test_mx_reference_against_exact_rationals():
+    A, W = make_inputs("c5_mxfp8", M=6, K=256, N=5, seed=12)
+    qa, Ea = O.quantize_mx(A)
+    qw, Ew = O.quantize_mx(W)
+    ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew)
+
+    def frac_val(code):
+        s = -1 if code & 0x80 else 1
+        e, m = (code >> 3) & 0xF, code & 7
+        if e == 0:
+            return s * Fraction(m, 512)
+        return s * (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+
+    for m in range(6):
+        for n in range(5):
+            exact = Fraction(0)
+            for b in range(256 // 32):
+                blk = sum(frac_val(int(qa[m, k])) * frac_val(int(qw[n, k])) for k in range(32 * b, 32 * b + 32))
+                exact += Fraction(2) ** (int(Ea[m, b]) + int(Ew[n, b]) - 254) * blk
+            assert abs(float(exact) - ref[m, n]) <= 256 * 2.0 ** -53 * S[m, n]
+    r2, s2 = O.mx_gemm_ref_entries(qa, Ea, qw, Ew, [1, 5, 0], [4, 0, 2])
+    assert np.allclose(r2, [ref[1, 4], ref[5, 0], ref[0, 2]], rtol=1e-15, atol=0)
+
+
+# --------------------------------------------------------------------------
+# Metrics ([TL27] 5.2) sanity on known cases
+# --------------------------------------------------------------------------
+def test_metrics_known_values():
+    ref = np.array([3.0, 4.0])
+    assert MT.rel_l2(ref, ref) == 0.0
+    assert abs(MT.rel_l2(np.zeros(2), ref) - 1.0) < 1e-15
+    assert MT.max_abs([1, 2], [1, 5]) == 3
+    assert MT.mismatch_ratio([1, 2], [1, 5], rtol=0, atol=1) == 0.5
+    assert abs(MT.sqnr_db(ref, ref * 1.1) - 20.0) < 1e-9
+    # gate: 4*K*amax*bcolmax/127
+    assert MT.column_gate_atol(2.0, [3.0], 10)[0] == 4 * 10 * 2 * 3 / 127
+
+
+# --------------------------------------------------------------------------
+# x/s is a correctly rounded float32 division (not x * (1/s)), then rint
+# ([AQ] numpy reference, [SK] step 1, [TL27] 2.4 all divide by the scale)
+# --------------------------------------------------------------------------
+def _rint_exact_quotient(x: float, s: float) -> int:
+    # float64 holds the exactly rounded quotient well enough that rounding it
+    # once more to float32 is the correctly rounded float32 quotient (53 >= 2*24+2)
+    qf = np.float32(float(Fraction(float(x)) / Fraction(float(s))))
+    return int(np.rint(qf))
+
+
+def test_quotient_is_correctly_rounded_division():
+    rng = rng_for(21)
+    x = rng.standard_normal((40, 257), dtype=np.float32)
+    x[:, 0] = rng.uniform(0.5, 9.0, 40).astype(np.float32)        # varied row maxima
+    q, s = O.quantize_sym_int8(x)
+    for m in range(40):
+        for k in range(257):
+            assert int(q[m, k]) == max(-127, min(127, _rint_exact_quotient(x[m, k], s[m])))
+    # near-tie quotients: x = (n + 1/2) * s nudged by one float32 ulp either way
+    s0 = np.float32(3.0) / np.float32(127.0)
+    n = np.arange(-120, 120, dtype=np.float64)
+    base = ((n + 0.5) * np.float64(s0)).astype(np.float32)
+    xs = np.concatenate([np.nextafter(base, np.float32(-1e9)), base, np.nextafter(base, np.float32(1e9))])
+    row = np.concatenate([[np.float32(3.0)], xs]).astype(np.float32)[None, :]
+    q, s = O.quantize_sym_int8(row)
+    assert float(s[0]) == float(s0)
+    for k in range(1, row.shape[1]):
+        assert int(q[0, k]) == max(-127, min(127, _rint_exact_quotient(row[0, k], s0)))
+
+
+def test_oracle_and_product_share_no_imports():
+    import re
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for f in glob.glob(os.path.join(root, "oracle", "*.py")):
+        src = open(f).read()
+        assert not re.search(r"^\s*(from|import)\s+block_scaled_quantized_qgemm_amd", src, re.M), f
+    for f in glob.glob(os.path.join(root, "block_scaled_quantized_qgemm_amd", "**", "*.*"), recursive=True):
+        if f.endswith((".py", ".hip", ".cpp", ".h", ".hpp")):
+            src = open(f).read()
+            assert not re.search(r"^\s*(from|import)\s+oracle|#include\s+\S*oracle", src, re.M), f
