@@ -1,0 +1,275 @@
+"""Benchmark of the quantized linear layer on one MI355X.
+
+A step is one pass of the whole hot path over one batch: quantize the float32
+activations (qgemm_quantize_rows) and run the GEMM with its fused epilogue
+(qgemm_run / qgemm_run_mx). Weights are prepared once beforehand (offline, as
+on the pages) and every input is resident in HBM before the timed region.
+Activation / weight / output buffers rotate over enough copies that the
+256 MB Infinity Cache cannot hold the working set.
+
+Prints one JSON line. Default workload: 512 tokens x K=4096 x N=4096,
+per-token int8 activations, per-channel int8 weights, float32 output.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "quantized GEMM TOPS (quant+GEMM+epilogue) and % of MFMA peak; decode-M HBM GB/s"
+
+PEAK_INT8_TOPS = 5000.0   # dense int8 MFMA, MI355X
+PEAK_FP8_TFLOPS = 5000.0  # dense fp8 / MXFP8 MFMA, MI355X
+PEAK_HBM_GBS = 8000.0     # HBM3E
+MALL_BYTES = 256 << 20
+
+# name -> (activation format, granularity, weight granularity, output type, headline unit)
+WORKLOADS = {
+    "c1_tiny": ("int8_sym", "tensor", "channel", "f32", "TOPS"),
+    "c2_per_token": ("int8_sym", "row", "channel", "f32", "TOPS"),
+    "c3_asym_uint8": ("uint8_asym", "row", "channel", "bf16", "TOPS"),
+    "c4_decode": ("int8_sym", "row", "channel", "f32", "GB/s"),
+    "c5_mxfp8": ("mxfp8", "block32", "block32", "f32", "TFLOPS"),
+}
+DESCRIPTION = {
+    "c1_tiny": "64x256x64 per-tensor int8 A, per-channel int8 W, fp32 out",
+    "c2_per_token": "512x4096x4096 per-token int8 A (outlier channels), per-channel int8 W, fp32 out",
+    "c3_asym_uint8": "2048x4096x11008 per-token asymmetric uint8 A with zero point, per-channel int8 W, bf16 out",
+    "c4_decode": "8x4096x14336 decode-shaped, per-token int8 A quantized on the fly, prepacked int8 W, fp32 out",
+    "c5_mxfp8": "8192x8192x8192 MXFP8 (e4m3 + E8M0 per 32 K) A and W, fp32 out",
+}
+
+
+def algorithmic(name, M, K, N):
+    """Ops and algorithmic bytes: whole step, and the GEMM kernel alone.
+
+    Whole step: float32 A read once, W codes + per-channel scales/column sums
+    (or E8M0 scales) read once, output written once. GEMM kernel: the same
+    with A as 1-byte codes plus its per-row scale (and zero point).
+    """
+    act, _, _, out, _ = WORKLOADS[name]
+    ob = {"f32": 4, "bf16": 2}[out]
+    ops = 2.0 * M * N * K
+    if act == "mxfp8":
+        w = N * K + N * (K // 32)
+        a_codes = M * K + M * (K // 32)
+    else:
+        w = N * K + 8 * N
+        a_codes = M * K + 8 * M
+    step_bytes = 4.0 * M * K + w + ob * M * N
+    gemm_bytes = a_codes + w + ob * M * N
+    return ops, step_bytes, gemm_bytes
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "block_scaled_quantized_qgemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, launches_per_step=1):
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, or None.
+
+    profiles/traffic_<workload>.json holds FETCH_SIZE / WRITE_SIZE per dispatch
+    (KiB), the copy-kernel calibration factor and the digest of the GEMM
+    sources they were taken with; a stale digest means the kernel changed
+    since, and the figure is not reported.
+    """
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_digest") != source_digest():
+        return None
+    return float(t["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(name, A, W, budget_s=10.0):
+    """The oracle, untuned, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    act, gran, _, _, _ = WORKLOADS[name]
+    M, K = A.shape
+    N = W.shape[0]
+    if act == "mxfp8":
+        rows = min(M, 64)
+        Wq, We = O.quantize_mx(W)                     # offline weight preparation, untimed
+        Wd = O.mx_dequantize(Wq, We)
+        sample = f"{rows} of {M} rows of A against all of W (W prepared outside the timing)"
+    else:
+        rows = min(M, 256)
+        Wq, Ws, _ = O.prepare_weights_int8(W, per_channel=True)
+        sample = f"{rows} of {M} rows of A against all of W (W prepared outside the timing)"
+    As = A[:rows]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if act == "mxfp8":
+            qa, Ea = O.quantize_mx(As)
+            _ = O.mx_dequantize(qa, Ea) @ Wd.T
+        else:
+            if act == "uint8_asym":
+                qa, sa, za = O.quantize_asym_uint8(As, per_row=(gran == "row"))
+            else:
+                qa, sa = O.quantize_sym_int8(As, per_row=(gran == "row"))
+                za = 0
+            C = O.int_gemm(qa, za, Wq)
+            _ = O.epilogue(C, sa, Ws)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    ops = 2.0 * rows * K * N * reps
+    unit = "GB/s" if WORKLOADS[name][4] == "GB/s" else WORKLOADS[name][4]
+    if unit == "GB/s":
+        _, step_bytes, _ = algorithmic(name, rows, K, N)
+        value = step_bytes * reps / el / 1e9
+    else:
+        value = ops / el / 1e12
+    return {"value": value, "unit": unit, "cores": int(cores), "kind": "oracle",
+            "sample": f"{sample}; {reps} passes in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2_per_token", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough to exceed the MALL 3x)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from block_scaled_quantized_qgemm_amd import ops
+    from block_scaled_quantized_qgemm_amd.inputs import make_inputs, WORKLOADS as SHAPES
+
+    name = args.workload
+    act, gran, wgran, out, unit = WORKLOADS[name]
+    M, K, N, _, _ = SHAPES[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    A_np, W_np = make_inputs(name)
+    fmt = {"int8_sym": ops.FMT_INT8_SYM, "uint8_asym": ops.FMT_UINT8_ASYM, "mxfp8": ops.FMT_MXFP8_E4M3}[act]
+    agr = {"tensor": ops.GRAN_TENSOR, "row": ops.GRAN_ROW, "block32": ops.GRAN_BLOCK32}[gran]
+    wgr = {"tensor": ops.GRAN_TENSOR, "channel": ops.GRAN_ROW, "block32": ops.GRAN_BLOCK32}[wgran]
+    otype = {"f32": ops.OUT_F32, "bf16": ops.OUT_BF16}[out]
+    odt = {"f32": torch.float32, "bf16": torch.bfloat16}[out]
+
+    A0 = torch.from_numpy(A_np).to(dev)
+    W0 = torch.from_numpy(W_np).to(dev)
+    w0 = ops.qgemm_prepack_weights(W0, fmt, wgr)
+    torch.cuda.synchronize()
+    ops_count, step_bytes, gemm_bytes = algorithmic(name, M, K, N)
+    set_bytes = A0.numel() * 4 + w0.packed.numel() + M * ((N + 7) // 8 * 8) * (4 if out == "f32" else 2) + M * K
+    nsets = args.rotate or max(1, min(64, math.ceil(3 * MALL_BYTES / set_bytes)))
+
+    # rotation sets: copies of A (float32), prepared W, quantized-A buffers and outputs
+    sets = []
+    for i in range(nsets):
+        Ai = A0 if i == 0 else A0.clone()
+        wi = w0 if i == 0 else ops.PackedWeights(w0.packed.clone(), w0.desc)
+        qi = ops.qgemm_quantize_rows(Ai, fmt, agr)
+        oi = torch.empty((M, (N + 7) // 8 * 8), dtype=odt, device=dev)
+        sets.append((Ai, wi, qi, oi))
+    ws = None
+    need = ops.qgemm_workspace_bytes(M, K, fmt, agr)
+    if need:
+        ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    del W0
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        Ai, wi, qi, oi = sets[i % nsets]
+        ops.qgemm_quantize_rows(Ai, fmt, agr, out=qi, workspace=ws)
+        if ev is not None:
+            ev.record()
+        if fmt == ops.FMT_MXFP8_E4M3:
+            ops.qgemm_run_mx(qi, wi, out=oi)
+        else:
+            ops.qgemm_run(qi, wi, otype, out=oi)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K_steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K_steps):
+        step(i, mids[i])
+        ends[i].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / K_steps
+    gemm_ms = sum(mids[i].elapsed_time(ends[i]) for i in range(K_steps)) / K_steps
+
+    if unit == "GB/s":
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
+        gemm_achieved = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": gemm_achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        value = ops_count / (ms_per_step * 1e-3) / 1e12
+        gemm_achieved = ops_count / (gemm_ms * 1e-3) / 1e12
+        peak = PEAK_FP8_TFLOPS if act == "mxfp8" else PEAK_INT8_TOPS
+        roof = {"bound": "mfma", "achieved": gemm_achieved, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(name)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3" if act == "mxfp8" else "i8",
+        "data": "synthetic (seeded generator with the workload's shapes and distributions)",
+        "config": {"workload": f"{name}: {DESCRIPTION[name]}", "M": M, "K": K, "N": N,
+                   "rotating_buffer_sets": nsets, "gemm_ms": gemm_ms,
+                   "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9},
+        "roofline": roof,
+    }
+    print(f"[bench] {name}: {ms_per_step * 1e3:.2f} us/step, gemm {gemm_ms * 1e3:.2f} us, "
+          f"wall {wall:.3f} s for {K_steps} steps", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(name, A_np, W_np, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,282 @@
+// C ABI of the quantized linear-layer library: argument validation, the
+// packed weight layout, device check and kernel dispatch. Every check runs
+// before anything is launched, so an error leaves all outputs untouched.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/qgemm.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int64_t kNPad = 256;   // packed rows are padded to this multiple
+constexpr int64_t kKPad = 128;   // packed columns are padded to this multiple
+constexpr int64_t kSymKMax = 133144;   // 127*127*K < 2^31
+constexpr int64_t kAsymKMax = 66311;   // 255*127*K < 2^31
+constexpr int64_t kMaxRows = 0x7fffffff;
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+std::atomic<int> g_arch_ok[64];  // per device: 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return QGEMM_E_DEVICE;
+  int c = dev < 64 ? g_arch_ok[dev].load(std::memory_order_relaxed) : 0;
+  if (c == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QGEMM_E_DEVICE;
+    c = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (dev < 64) g_arch_ok[dev].store(c, std::memory_order_relaxed);
+  }
+  return c == 1 ? QGEMM_OK : QGEMM_E_DEVICE;
+}
+
+bool is_int_fmt(int f) { return f == QGEMM_FMT_INT8_SYM || f == QGEMM_FMT_UINT8_ASYM; }
+bool is_int_gran(int g) { return g == QGEMM_GRAN_TENSOR || g == QGEMM_GRAN_ROW; }
+
+struct Layout {
+  int64_t N_pad, K_pad, codes_off, scales_off, colsum_off, bytes;
+};
+
+bool weight_layout(int64_t N, int64_t K, int fmt, int gran, Layout* L) {
+  if (N < 1 || K < 1 || N > kMaxRows || K > (int64_t)1 << 30) return false;
+  if (fmt == QGEMM_FMT_INT8_SYM) {
+    if (!is_int_gran(gran)) return false;
+  } else if (fmt == QGEMM_FMT_MXFP8_E4M3) {
+    if (gran != QGEMM_GRAN_BLOCK32 || K % 32 != 0) return false;
+  } else {
+    return false;
+  }
+  L->N_pad = round_up(N, kNPad);
+  L->K_pad = round_up(K, kKPad);
+  L->codes_off = 0;
+  L->scales_off = round_up(L->N_pad * L->K_pad, 256);
+  if (fmt == QGEMM_FMT_INT8_SYM) {
+    L->colsum_off = round_up(L->scales_off + 4 * L->N_pad, 256);
+    L->bytes = round_up(L->colsum_off + 4 * L->N_pad, 256);
+  } else {
+    L->colsum_off = -1;
+    L->bytes = round_up(L->scales_off + L->N_pad * (L->K_pad / 32), 256);
+  }
+  return true;
+}
+
+int check_desc(const qgemm_wdesc* d, int want_fmt) {
+  if (!d) return QGEMM_E_NULL;
+  if (d->magic != QGEMM_WDESC_MAGIC || d->version != QGEMM_ABI_VERSION || d->fmt != want_fmt) return QGEMM_E_DESC;
+  Layout L;
+  if (!weight_layout(d->N, d->K, d->fmt, d->gran, &L)) return QGEMM_E_DESC;
+  if (L.N_pad != d->N_pad || L.K_pad != d->K_pad || L.codes_off != d->codes_off || L.scales_off != d->scales_off ||
+      L.colsum_off != d->colsum_off || L.bytes != d->bytes)
+    return QGEMM_E_DESC;
+  return QGEMM_OK;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int launch_status() { return hipGetLastError() == hipSuccess ? QGEMM_OK : QGEMM_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int qgemm_abi_version(void) { return QGEMM_ABI_VERSION; }
+
+const char* qgemm_status_string(int s) {
+  switch (s) {
+    case QGEMM_OK: return "QGEMM_OK";
+    case QGEMM_E_NULL: return "QGEMM_E_NULL: a required pointer is NULL";
+    case QGEMM_E_SHAPE: return "QGEMM_E_SHAPE: a size or leading dimension is out of range";
+    case QGEMM_E_MODE: return "QGEMM_E_MODE: unsupported format / granularity / output combination";
+    case QGEMM_E_ALIGN: return "QGEMM_E_ALIGN: pointer or leading dimension not aligned as required";
+    case QGEMM_E_OVERFLOW: return "QGEMM_E_OVERFLOW: K too large for an exact int32 accumulator";
+    case QGEMM_E_DEVICE: return "QGEMM_E_DEVICE: the current device is not a gfx950";
+    case QGEMM_E_DESC: return "QGEMM_E_DESC: invalid weight descriptor";
+    case QGEMM_E_WORKSPACE: return "QGEMM_E_WORKSPACE: workspace missing or too small";
+    case QGEMM_E_HIP: return "QGEMM_E_HIP: a HIP call or kernel launch failed";
+    default: return "unknown qgemm status";
+  }
+}
+
+size_t qgemm_packed_weight_bytes(int64_t N, int64_t K, int fmt, int gran) {
+  Layout L;
+  return weight_layout(N, K, fmt, gran, &L) ? (size_t)L.bytes : 0;
+}
+
+size_t qgemm_workspace_bytes(int64_t rows, int64_t K, int fmt, int gran) {
+  (void)K;
+  if (rows < 0) return 0;
+  if (gran == QGEMM_GRAN_TENSOR && fmt == QGEMM_FMT_INT8_SYM) return (size_t)rows * 4;
+  if (gran == QGEMM_GRAN_TENSOR && fmt == QGEMM_FMT_UINT8_ASYM) return (size_t)rows * 8;
+  return 0;
+}
+
+int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int fmt, int gran, void* q,
+                        int64_t ldq, float* scales, int32_t* zero_points, uint8_t* mx_scales, int64_t ld_mx,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  const bool mx = fmt == QGEMM_FMT_MXFP8_E4M3;
+  if (mx) {
+    if (gran != QGEMM_GRAN_BLOCK32) return QGEMM_E_MODE;
+  } else if (!is_int_fmt(fmt) || !is_int_gran(gran)) {
+    return QGEMM_E_MODE;
+  }
+  if (M < 0 || M > kMaxRows || K < 1 || K > ((int64_t)1 << 30)) return QGEMM_E_SHAPE;
+  if (mx && K % 32 != 0) return QGEMM_E_SHAPE;
+  if (M == 0) return QGEMM_OK;
+  if (!x || !q) return QGEMM_E_NULL;
+  if (ldx < K || ldq < K) return QGEMM_E_SHAPE;
+  if (ldx % 4 != 0 || !aligned(x, 16) || ldq % 16 != 0 || !aligned(q, 16)) return QGEMM_E_ALIGN;
+  if (mx) {
+    if (!mx_scales) return QGEMM_E_NULL;
+    if (ld_mx < K / 32) return QGEMM_E_SHAPE;
+  } else {
+    if (!scales) return QGEMM_E_NULL;
+    if (fmt == QGEMM_FMT_UINT8_ASYM && !zero_points) return QGEMM_E_NULL;
+    if (!aligned(scales, 4) || (zero_points && !aligned(zero_points, 4))) return QGEMM_E_ALIGN;
+  }
+  const size_t need = qgemm_workspace_bytes(M, K, fmt, gran);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QGEMM_E_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 4)) return QGEMM_E_ALIGN;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+
+  hipStream_t st = as_stream(stream);
+  if (mx) {
+    qg::launch_quantize_mx(x, M, K, ldx, (uint8_t*)q, ldq, mx_scales, ld_mx, st);
+  } else {
+    qg::launch_quantize_int(x, M, K, ldx, fmt == QGEMM_FMT_UINT8_ASYM, gran == QGEMM_GRAN_TENSOR,
+                            (uint8_t*)q, ldq, scales, zero_points, nullptr, (float*)workspace, st);
+  }
+  return launch_status();
+}
+
+int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int fmt, int gran, void* packed,
+                          size_t packed_bytes, qgemm_wdesc* desc, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (fmt != QGEMM_FMT_INT8_SYM && fmt != QGEMM_FMT_MXFP8_E4M3) return QGEMM_E_MODE;
+  if (fmt == QGEMM_FMT_INT8_SYM && !is_int_gran(gran)) return QGEMM_E_MODE;
+  if (fmt == QGEMM_FMT_MXFP8_E4M3 && gran != QGEMM_GRAN_BLOCK32) return QGEMM_E_MODE;
+  Layout L;
+  if (!weight_layout(N, K, fmt, gran, &L)) return QGEMM_E_SHAPE;
+  if (!w || !packed || !desc) return QGEMM_E_NULL;
+  if (ldw < K) return QGEMM_E_SHAPE;
+  if (ldw % 4 != 0 || !aligned(w, 16) || !aligned(packed, 256)) return QGEMM_E_ALIGN;
+  if (packed_bytes < (size_t)L.bytes) return QGEMM_E_SHAPE;
+  const size_t need = qgemm_workspace_bytes(N, K, fmt, gran);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return QGEMM_E_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 4)) return QGEMM_E_ALIGN;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+
+  hipStream_t st = as_stream(stream);
+  uint8_t* base = (uint8_t*)packed;
+  if (hipMemsetAsync(base, 0, (size_t)L.bytes, st) != hipSuccess) return QGEMM_E_HIP;
+  if (fmt == QGEMM_FMT_INT8_SYM) {
+    qg::launch_quantize_int(w, N, K, ldw, false, gran == QGEMM_GRAN_TENSOR, base + L.codes_off, L.K_pad,
+                            (float*)(base + L.scales_off), nullptr, (int32_t*)(base + L.colsum_off),
+                            (float*)workspace, st);
+  } else {
+    if (hipMemsetAsync(base + L.scales_off, 127, (size_t)(L.N_pad * (L.K_pad / 32)), st) != hipSuccess)
+      return QGEMM_E_HIP;
+    qg::launch_quantize_mx(w, N, K, ldw, base + L.codes_off, L.K_pad, base + L.scales_off, L.K_pad / 32, st);
+  }
+  int rc = launch_status();
+  if (rc != QGEMM_OK) return rc;
+  desc->magic = QGEMM_WDESC_MAGIC;
+  desc->version = QGEMM_ABI_VERSION;
+  desc->fmt = fmt;
+  desc->gran = gran;
+  desc->N = N;
+  desc->K = K;
+  desc->N_pad = L.N_pad;
+  desc->K_pad = L.K_pad;
+  desc->codes_off = L.codes_off;
+  desc->scales_off = L.scales_off;
+  desc->colsum_off = L.colsum_off;
+  desc->bytes = L.bytes;
+  return QGEMM_OK;
+}
+
+int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t* a_zero, int a_fmt, int a_gran,
+              int64_t M, const qgemm_wdesc* w_desc, const void* w_packed, void* out, int64_t ldo, int out_type,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!is_int_fmt(a_fmt) || !is_int_gran(a_gran)) return QGEMM_E_MODE;
+  if (out_type != QGEMM_OUT_F32 && out_type != QGEMM_OUT_BF16 && out_type != QGEMM_OUT_I32) return QGEMM_E_MODE;
+  int rc = check_desc(w_desc, QGEMM_FMT_INT8_SYM);
+  if (rc != QGEMM_OK) return rc;
+  const int64_t N = w_desc->N, K = w_desc->K;
+  const bool asym = a_fmt == QGEMM_FMT_UINT8_ASYM;
+  if (K > (asym ? kAsymKMax : kSymKMax)) return QGEMM_E_OVERFLOW;
+  if (M < 0 || M > kMaxRows) return QGEMM_E_SHAPE;
+  if (M == 0) return QGEMM_OK;
+  if (!a_q || !a_scales || !w_packed || !out || (asym && !a_zero)) return QGEMM_E_NULL;
+  if (lda < K || ldo < N) return QGEMM_E_SHAPE;
+  if (lda % 16 != 0 || !aligned(a_q, 16) || ldo % 4 != 0 || !aligned(out, 16) || !aligned(w_packed, 256) ||
+      !aligned(a_scales, 4) || (a_zero && !aligned(a_zero, 4)))
+    return QGEMM_E_ALIGN;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+
+  const uint8_t* base = (const uint8_t*)w_packed;
+  qg::GemmArgs g{};
+  g.a = (const uint8_t*)a_q;
+  g.lda = lda;
+  g.sa = a_scales;
+  g.za = a_zero;
+  g.a_per_tensor = a_gran == QGEMM_GRAN_TENSOR;
+  g.w = base + w_desc->codes_off;
+  g.sw = (const float*)(base + w_desc->scales_off);
+  g.colsum = (const int32_t*)(base + w_desc->colsum_off);
+  g.w_per_tensor = w_desc->gran == QGEMM_GRAN_TENSOR;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.K_pad = w_desc->K_pad;
+  g.out = out;
+  g.ldo = ldo;
+  hipError_t e = qg::launch_gemm_i8(g, asym, out_type, as_stream(stream));
+  return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
+}
+
+int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s, int64_t M,
+                 const qgemm_wdesc* w_desc, const void* w_packed, float* out, int64_t ldo, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = check_desc(w_desc, QGEMM_FMT_MXFP8_E4M3);
+  if (rc != QGEMM_OK) return rc;
+  const int64_t N = w_desc->N, K = w_desc->K;
+  if (M < 0 || M > kMaxRows) return QGEMM_E_SHAPE;
+  if (M == 0) return QGEMM_OK;
+  if (!a_codes || !a_e8m0 || !w_packed || !out) return QGEMM_E_NULL;
+  if (lda < K || lda_s < K / 32 || ldo < N) return QGEMM_E_SHAPE;
+  if (lda % 16 != 0 || !aligned(a_codes, 16) || ldo % 4 != 0 || !aligned(out, 16) || !aligned(w_packed, 256))
+    return QGEMM_E_ALIGN;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+
+  const uint8_t* base = (const uint8_t*)w_packed;
+  qg::GemmArgs g{};
+  g.a = a_codes;
+  g.lda = lda;
+  g.ea = a_e8m0;
+  g.lda_s = lda_s;
+  g.w = base + w_desc->codes_off;
+  g.ew = base + w_desc->scales_off;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.K_pad = w_desc->K_pad;
+  g.out = out;
+  g.ldo = ldo;
+  hipError_t e = qg::launch_gemm_mx(g, as_stream(stream));
+  return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
+}
+
+}  // extern "C"

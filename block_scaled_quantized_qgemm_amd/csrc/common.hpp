@@ -1,0 +1,56 @@
+// Internal helpers shared by the gfx950 kernels of the quantized linear layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// Wave-wide reductions (64 lanes) over a value every lane holds.
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ inline float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ inline int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Round-to-nearest-even of a finite float32 to bfloat16 (the upper half of a
+// float32): add 0x7fff plus the lowest kept bit, then drop the low 16 bits.
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// E8M0 code of the smallest power of two >= t (t > 0, finite): the float32
+// biased exponent, plus one when the mantissa is non-zero, clamped to [1, 254].
+__device__ inline int ceil_to_ue8m0(float t) {
+  uint32_t b = __float_as_uint(t) & 0x7fffffffu;
+  int e = (int)(b >> 23) + ((b & 0x7fffffu) != 0u ? 1 : 0);
+  return e < 1 ? 1 : (e > 254 ? 254 : e);
+}
+
+// 2^(127 - E) as a float32 for E in [1, 254] (2^-127 is the one subnormal).
+__device__ inline float e8m0_inverse(int E) {
+  int be = 254 - E;  // biased exponent of 2^(127-E)
+  return be >= 1 ? __uint_as_float((uint32_t)be << 23) : __uint_as_float(0x00400000u);
+}
+
+}  // namespace qg

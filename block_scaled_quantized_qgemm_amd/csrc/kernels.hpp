@@ -1,0 +1,43 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+// Symmetric int8 / asymmetric uint8 row quantization (per row or per tensor).
+// `colsum` (may be null) receives the sum of each row's codes. `ws` holds
+// rows (2*rows when asym) floats for the per-tensor statistics.
+void launch_quantize_int(const float* x, int64_t rows, int64_t K, int64_t ldx, bool asym, bool per_tensor,
+                         uint8_t* q, int64_t ldq, float* scales, int32_t* zeros, int32_t* colsum, float* ws,
+                         hipStream_t st);
+
+// MXFP8 (e4m3 codes, E8M0 per 32 K-elements) row quantization; K % 32 == 0.
+void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                        uint8_t* e8, int64_t lde, hipStream_t st);
+
+struct GemmArgs {
+  const uint8_t* a;     // activation codes [M][lda]
+  int64_t lda;
+  const float* sa;      // int8: per-row or [1] scales
+  const int32_t* za;    // int8 asym: zero points
+  const uint8_t* ea;    // mx: E8M0 [M][lda_s]
+  int64_t lda_s;
+  int a_per_tensor;
+  const uint8_t* w;     // packed codes [N_pad][K_pad]
+  const float* sw;      // int8: [N_pad] or [1]
+  const int32_t* colsum;
+  const uint8_t* ew;    // mx: E8M0 [N_pad][K_pad/32]
+  int w_per_tensor;
+  int64_t M, N, K, K_pad;
+  void* out;
+  int64_t ldo;
+};
+
+// qgemm_run: int8 GEMM + epilogue. out_type: 0 f32, 1 bf16, 2 i32.
+hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_t st);
+// qgemm_run_mx: block-scaled e4m3 GEMM, float32 output.
+hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st);
+
+}  // namespace qg

@@ -1,0 +1,346 @@
+// Activation quantization and weight preparation kernels for gfx950.
+//
+// Row kernels: one 256-thread workgroup per row. Each thread keeps its share
+// of the row in registers as float4 loads (coalesced: consecutive lanes read
+// consecutive 16-byte pieces), the row statistic (amax, or min and max) is
+// reduced across the wave with lane shuffles and across the four waves
+// through LDS, and the codes are written from the registers without a second
+// read of the row. This is the "one extra reduction over data already in
+// registers" of "Activation Quantization Architecture, in depth", section
+// "Fusion: making quantization nearly free".
+//
+// MX kernel: eight lanes own one 32-element block (a float4 each), so the
+// block amax is a three-step shuffle; codes are converted two at a time with
+// the hardware e4m3 conversion (round to nearest even, OCP e4m3fn on gfx950).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qg {
+
+constexpr int kRowThreads = 256;
+
+struct RowStats {
+  float lo, hi;  // symmetric: hi = amax (lo unused); asymmetric: min and max
+};
+
+template <bool ASYM>
+__device__ inline void stats_update(RowStats& st, float v) {
+  if (ASYM) {
+    st.lo = fminf(st.lo, v);
+    st.hi = fmaxf(st.hi, v);
+  } else {
+    st.hi = fmaxf(st.hi, fabsf(v));
+  }
+}
+
+template <bool ASYM>
+__device__ inline RowStats block_reduce_stats(RowStats st, float* red) {
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  st.hi = wave_max(st.hi);
+  if (ASYM) st.lo = wave_min(st.lo);
+  if (lane == 0) {
+    red[wid] = st.hi;
+    red[8 + wid] = st.lo;
+  }
+  __syncthreads();
+  RowStats r;
+  r.hi = red[0];
+  r.lo = red[8];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / kWave; ++w) {
+    r.hi = fmaxf(r.hi, red[w]);
+    r.lo = fminf(r.lo, red[8 + w]);
+  }
+  return r;
+}
+
+__device__ inline int block_sum_int(int v, int* red) {
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+  v = wave_sum(v);
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int w = 0; w < kRowThreads / kWave; ++w) s += red[w];
+  return s;
+}
+
+// Scale (and zero point) from the row statistics, in float32 exactly as the
+// formulas read: s = max(amax / 127, 1e-8); asymmetric s = max((max - min) /
+// 255, 1e-8), z = clamp(rint(-min / s), 0, 255).
+template <bool ASYM>
+__device__ inline void scale_from_stats(const RowStats& st, float& s, int& z) {
+  if (ASYM) {
+    s = (st.hi - st.lo) / 255.0f;
+    s = fmaxf(s, 1e-8f);
+    float zf = rintf(-st.lo / s);
+    zf = fminf(fmaxf(zf, 0.0f), 255.0f);
+    z = (int)zf;
+  } else {
+    s = st.hi / 127.0f;
+    s = fmaxf(s, 1e-8f);
+    z = 0;
+  }
+}
+
+template <bool ASYM>
+__device__ inline uint32_t encode_code(float v, float s, float zf) {
+  float r = rintf(v / s);
+  if (ASYM) {
+    r = fminf(fmaxf(r + zf, 0.0f), 255.0f);
+    return (uint32_t)(int)r & 0xffu;
+  } else {
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (uint32_t)(int)r & 0xffu;
+  }
+}
+
+template <bool ASYM>
+__device__ inline int code_value(uint32_t c) {
+  return ASYM ? (int)c : (int)(int8_t)(uint8_t)c;
+}
+
+// VPT: float4 pieces per thread kept in registers (row length <= 1024 * VPT).
+// PRECOMP: scale / zero point were computed for the whole tensor and are read
+// from scales[0] / zeros[0] instead of from this row.
+template <bool ASYM, bool PRECOMP, int VPT>
+__global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
+    const float* __restrict__ x, int64_t ldx, int64_t K, uint8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ scales, int32_t* __restrict__ zeros, int32_t* __restrict__ colsum) {
+  __shared__ float red[16];
+  __shared__ int redi[8];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * ldx;
+  uint8_t* qr = q + row * ldq;
+  const int t = threadIdx.x;
+
+  float4 v[VPT];
+  RowStats st;
+  st.lo = INFINITY;
+  st.hi = ASYM ? -INFINITY : 0.0f;
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int64_t k = 4 * ((int64_t)t + (int64_t)kRowThreads * u);
+    if (k + 4 <= K) {
+      v[u] = *reinterpret_cast<const float4*>(xr + k);
+      stats_update<ASYM>(st, v[u].x);
+      stats_update<ASYM>(st, v[u].y);
+      stats_update<ASYM>(st, v[u].z);
+      stats_update<ASYM>(st, v[u].w);
+    } else {
+      float e[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < 4; ++c)
+        if (k + c < K) {
+          e[c] = xr[k + c];
+          stats_update<ASYM>(st, e[c]);
+        }
+      v[u] = make_float4(e[0], e[1], e[2], e[3]);
+    }
+  }
+
+  float s;
+  int z;
+  if (PRECOMP) {
+    s = scales[0];
+    z = ASYM ? zeros[0] : 0;
+  } else {
+    RowStats r = block_reduce_stats<ASYM>(st, red);
+    scale_from_stats<ASYM>(r, s, z);
+  }
+  const float zf = (float)z;
+
+  int csum = 0;
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int64_t k = 4 * ((int64_t)t + (int64_t)kRowThreads * u);
+    if (k + 4 <= K) {
+      uint32_t c0 = encode_code<ASYM>(v[u].x, s, zf), c1 = encode_code<ASYM>(v[u].y, s, zf);
+      uint32_t c2 = encode_code<ASYM>(v[u].z, s, zf), c3 = encode_code<ASYM>(v[u].w, s, zf);
+      *reinterpret_cast<uint32_t*>(qr + k) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+      if (colsum) csum += code_value<ASYM>(c0) + code_value<ASYM>(c1) + code_value<ASYM>(c2) + code_value<ASYM>(c3);
+    } else if (k < K) {
+      float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      for (int c = 0; c < 4; ++c)
+        if (k + c < K) {
+          uint32_t cc = encode_code<ASYM>(e[c], s, zf);
+          qr[k + c] = (uint8_t)cc;
+          if (colsum) csum += code_value<ASYM>(cc);
+        }
+    }
+  }
+  if (colsum) {
+    int tot = block_sum_int(csum, redi);
+    if (t == 0) colsum[row] = tot;
+  }
+  if (!PRECOMP && t == 0) {
+    scales[row] = s;
+    if (ASYM) zeros[row] = z;
+  }
+}
+
+// Rows longer than the register-resident kernels hold: two sweeps over the
+// row (the second one is served by the caches).
+template <bool ASYM, bool PRECOMP>
+__global__ __launch_bounds__(kRowThreads) void quant_rows_long_kernel(
+    const float* __restrict__ x, int64_t ldx, int64_t K, uint8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ scales, int32_t* __restrict__ zeros, int32_t* __restrict__ colsum) {
+  __shared__ float red[16];
+  __shared__ int redi[8];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * ldx;
+  uint8_t* qr = q + row * ldq;
+  const int t = threadIdx.x;
+  float s;
+  int z;
+  if (PRECOMP) {
+    s = scales[0];
+    z = ASYM ? zeros[0] : 0;
+  } else {
+    RowStats st;
+    st.lo = INFINITY;
+    st.hi = ASYM ? -INFINITY : 0.0f;
+    for (int64_t k = t; k < K; k += kRowThreads) stats_update<ASYM>(st, xr[k]);
+    RowStats r = block_reduce_stats<ASYM>(st, red);
+    scale_from_stats<ASYM>(r, s, z);
+  }
+  const float zf = (float)z;
+  int csum = 0;
+  for (int64_t k = t; k < K; k += kRowThreads) {
+    uint32_t c = encode_code<ASYM>(xr[k], s, zf);
+    qr[k] = (uint8_t)c;
+    csum += code_value<ASYM>(c);
+  }
+  if (colsum) {
+    int tot = block_sum_int(csum, redi);
+    if (t == 0) colsum[row] = tot;
+  }
+  if (!PRECOMP && t == 0) {
+    scales[row] = s;
+    if (ASYM) zeros[row] = z;
+  }
+}
+
+// Per-tensor granularity, pass 1: statistics of each row into the workspace.
+template <bool ASYM>
+__global__ __launch_bounds__(kRowThreads) void row_stats_kernel(const float* __restrict__ x, int64_t ldx,
+                                                                int64_t K, float* __restrict__ ws) {
+  __shared__ float red[16];
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * ldx;
+  RowStats st;
+  st.lo = INFINITY;
+  st.hi = ASYM ? -INFINITY : 0.0f;
+  for (int64_t k = threadIdx.x; k < K; k += kRowThreads) stats_update<ASYM>(st, xr[k]);
+  RowStats r = block_reduce_stats<ASYM>(st, red);
+  if (threadIdx.x == 0) {
+    if (ASYM) {
+      ws[2 * row] = r.lo;
+      ws[2 * row + 1] = r.hi;
+    } else {
+      ws[row] = r.hi;
+    }
+  }
+}
+
+// Per-tensor granularity, pass 2: one workgroup folds the row statistics and
+// writes the single scale (and zero point).
+template <bool ASYM>
+__global__ __launch_bounds__(kRowThreads) void tensor_scale_kernel(const float* __restrict__ ws, int64_t rows,
+                                                                   float* __restrict__ scales,
+                                                                   int32_t* __restrict__ zeros) {
+  __shared__ float red[16];
+  RowStats st;
+  st.lo = INFINITY;
+  st.hi = ASYM ? -INFINITY : 0.0f;
+  for (int64_t r = threadIdx.x; r < rows; r += kRowThreads) {
+    if (ASYM) {
+      st.lo = fminf(st.lo, ws[2 * r]);
+      st.hi = fmaxf(st.hi, ws[2 * r + 1]);
+    } else {
+      st.hi = fmaxf(st.hi, ws[r]);
+    }
+  }
+  RowStats r = block_reduce_stats<ASYM>(st, red);
+  if (threadIdx.x == 0) {
+    float s;
+    int z;
+    scale_from_stats<ASYM>(r, s, z);
+    scales[0] = s;
+    if (ASYM) zeros[0] = z;
+  }
+}
+
+// MXFP8: grid (rows, ceil(K / 1024)); each thread one float4, eight threads
+// per 32-element block.
+__global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __restrict__ x, int64_t ldx,
+                                                               int64_t K, uint8_t* __restrict__ q, int64_t ldq,
+                                                               uint8_t* __restrict__ e8, int64_t lde) {
+  const int64_t row = blockIdx.x;
+  const int64_t k = (int64_t)blockIdx.y * (4 * kRowThreads) + 4 * threadIdx.x;
+  const bool valid = k < K;  // K % 32 == 0: a block's eight lanes agree
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (valid) v = *reinterpret_cast<const float4*>(x + row * ldx + k);
+  float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  a = fmaxf(a, __shfl_xor(a, 1, kWave));
+  a = fmaxf(a, __shfl_xor(a, 2, kWave));
+  a = fmaxf(a, __shfl_xor(a, 4, kWave));
+  a = fmaxf(a, 1e-4f);
+  const int E = ceil_to_ue8m0(a / 448.0f);
+  const float inv = e8m0_inverse(E);
+  if (!valid) return;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v.x * inv, v.y * inv, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(v.z * inv, v.w * inv, w, true);
+  *reinterpret_cast<uint32_t*>(q + row * ldq + k) = (uint32_t)w;
+  if ((threadIdx.x & 7) == 0) e8[row * lde + (k >> 5)] = (uint8_t)E;
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+template <bool ASYM, bool PRECOMP>
+static void launch_rows(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                        float* scales, int32_t* zeros, int32_t* colsum, hipStream_t st) {
+  dim3 grid((unsigned)rows), block(kRowThreads);
+  if (K <= 1024)
+    quant_rows_kernel<ASYM, PRECOMP, 1><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+  else if (K <= 2048)
+    quant_rows_kernel<ASYM, PRECOMP, 2><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+  else if (K <= 4096)
+    quant_rows_kernel<ASYM, PRECOMP, 4><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+  else if (K <= 8192)
+    quant_rows_kernel<ASYM, PRECOMP, 8><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+  else
+    quant_rows_long_kernel<ASYM, PRECOMP><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+}
+
+void launch_quantize_int(const float* x, int64_t rows, int64_t K, int64_t ldx, bool asym, bool per_tensor,
+                         uint8_t* q, int64_t ldq, float* scales, int32_t* zeros, int32_t* colsum, float* ws,
+                         hipStream_t st) {
+  if (rows == 0) return;
+  if (!per_tensor) {
+    if (asym)
+      launch_rows<true, false>(x, rows, K, ldx, q, ldq, scales, zeros, colsum, st);
+    else
+      launch_rows<false, false>(x, rows, K, ldx, q, ldq, scales, zeros, colsum, st);
+    return;
+  }
+  dim3 grid((unsigned)rows), block(kRowThreads);
+  if (asym) {
+    row_stats_kernel<true><<<grid, block, 0, st>>>(x, ldx, K, ws);
+    tensor_scale_kernel<true><<<1, block, 0, st>>>(ws, rows, scales, zeros);
+    launch_rows<true, true>(x, rows, K, ldx, q, ldq, scales, zeros, colsum, st);
+  } else {
+    row_stats_kernel<false><<<grid, block, 0, st>>>(x, ldx, K, ws);
+    tensor_scale_kernel<false><<<1, block, 0, st>>>(ws, rows, scales, zeros);
+    launch_rows<false, true>(x, rows, K, ldx, q, ldq, scales, zeros, colsum, st);
+  }
+}
+
+void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                        uint8_t* e8, int64_t lde, hipStream_t st) {
+  if (rows == 0) return;
+  dim3 grid((unsigned)rows, (unsigned)((K + 4 * kRowThreads - 1) / (4 * kRowThreads))), block(kRowThreads);
+  quant_mx_kernel<<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+}
+
+}  // namespace qg

@@ -1,0 +1,192 @@
+"""Python binding of the C ABI: the same four calls, on torch tensors.
+
+Marshalling only -- shapes, dtypes, strides, allocation of outputs and the
+current HIP stream are turned into the plain pointers and sizes of
+include/qgemm.h; every step of the computation runs in the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+FMT_INT8_SYM, FMT_UINT8_ASYM, FMT_MXFP8_E4M3 = 0, 1, 2
+GRAN_TENSOR, GRAN_ROW, GRAN_BLOCK32 = 0, 1, 2
+OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
+
+_OUT_DTYPES = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_I32: torch.int32}
+
+
+class QgemmError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = L.load().qgemm_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise QgemmError(fn, status)
+
+
+def _round_up(v: int, m: int) -> int:
+    return (v + m - 1) // m * m
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class QuantizedRows:
+    """Codes [M, ld] (first K columns valid) plus scales / zero points / E8M0 scales."""
+    q: torch.Tensor
+    K: int
+    fmt: int
+    gran: int
+    scales: Optional[torch.Tensor] = None
+    zero_points: Optional[torch.Tensor] = None
+    mx_scales: Optional[torch.Tensor] = None
+
+    @property
+    def M(self) -> int:
+        return self.q.shape[0]
+
+    def codes(self) -> torch.Tensor:
+        return self.q[:, : self.K]
+
+
+@dataclass
+class PackedWeights:
+    """A prepared weight buffer and its host descriptor."""
+    packed: torch.Tensor
+    desc: L.WDesc
+
+    @property
+    def N(self) -> int:
+        return int(self.desc.N)
+
+    @property
+    def K(self) -> int:
+        return int(self.desc.K)
+
+    def codes(self) -> torch.Tensor:
+        d = self.desc
+        c = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad].view(d.N_pad, d.K_pad)
+        return c.view(torch.int8) if d.fmt == FMT_INT8_SYM else c
+
+    def scales(self) -> torch.Tensor:
+        d = self.desc
+        if d.fmt == FMT_INT8_SYM:
+            n = 1 if d.gran == GRAN_TENSOR else d.N_pad
+            return self.packed[d.scales_off: d.scales_off + 4 * n].view(torch.float32)
+        return self.packed[d.scales_off: d.scales_off + d.N_pad * (d.K_pad // 32)].view(d.N_pad, d.K_pad // 32)
+
+    def colsum(self) -> torch.Tensor:
+        d = self.desc
+        return self.packed[d.colsum_off: d.colsum_off + 4 * d.N_pad].view(torch.int32)
+
+
+def qgemm_workspace_bytes(rows: int, K: int, fmt: int, gran: int) -> int:
+    return int(L.load().qgemm_workspace_bytes(rows, K, fmt, gran))
+
+
+def qgemm_packed_weight_bytes(N: int, K: int, fmt: int, gran: int) -> int:
+    return int(L.load().qgemm_packed_weight_bytes(N, K, fmt, gran))
+
+
+def qgemm_quantize_rows(x: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = GRAN_ROW,
+                        out: Optional[QuantizedRows] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> QuantizedRows:
+    """Quantize the rows of a float32 [M, K] device matrix (see qgemm.h)."""
+    lib = L.load()
+    assert x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    dev = x.device
+    if out is None:
+        ld = _round_up(max(K, 1), 16)
+        q = torch.empty((M, ld), dtype=torch.int8 if fmt == FMT_INT8_SYM else torch.uint8, device=dev)
+        scales = zeros = mx = None
+        if fmt == FMT_MXFP8_E4M3:
+            mx = torch.empty((M, max(K // 32, 1)), dtype=torch.uint8, device=dev)
+        else:
+            scales = torch.empty((1 if gran == GRAN_TENSOR else M,), dtype=torch.float32, device=dev)
+            if fmt == FMT_UINT8_ASYM:
+                zeros = torch.empty_like(scales, dtype=torch.int32)
+        out = QuantizedRows(q, K, fmt, gran, scales, zeros, mx)
+    need = qgemm_workspace_bytes(M, K, fmt, gran)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.qgemm_quantize_rows(
+        _ptr(x), M, K, x.stride(0), fmt, gran, _ptr(out.q), out.q.stride(0),
+        _ptr(out.scales), _ptr(out.zero_points), _ptr(out.mx_scales),
+        0 if out.mx_scales is None else out.mx_scales.stride(0),
+        _ptr(workspace), ws_bytes, ctypes.c_void_p(_stream(dev, stream)))
+    _check("qgemm_quantize_rows", st)
+    return out
+
+
+def qgemm_prepack_weights(w: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = GRAN_ROW,
+                          stream=None) -> PackedWeights:
+    """Prepare a float32 [N, K] weight (per-channel / per-tensor int8, or MXFP8)."""
+    lib = L.load()
+    assert w.dtype == torch.float32 and w.dim() == 2 and w.stride(1) == 1
+    N, K = w.shape
+    dev = w.device
+    nbytes = qgemm_packed_weight_bytes(N, K, fmt, gran)
+    if nbytes == 0:
+        raise QgemmError("qgemm_prepack_weights", -2)
+    packed = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    need = qgemm_workspace_bytes(N, K, fmt, gran)
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
+    desc = L.WDesc()
+    st = lib.qgemm_prepack_weights(_ptr(w), N, K, w.stride(0), fmt, gran, _ptr(packed), nbytes,
+                                   ctypes.byref(desc), _ptr(ws), need, ctypes.c_void_p(_stream(dev, stream)))
+    _check("qgemm_prepack_weights", st)
+    return PackedWeights(packed, desc)
+
+
+def _alloc_out(M: int, N: int, dtype, dev):
+    buf = torch.empty((M, _round_up(N, 8)), dtype=dtype, device=dev)
+    return buf
+
+
+def qgemm_run(a: QuantizedRows, w: PackedWeights, out_type: int = OUT_F32,
+              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """int8 GEMM with the fused dequantization epilogue; returns out[:, :N]."""
+    lib = L.load()
+    dev = a.q.device
+    N = w.N
+    if out is None:
+        out = _alloc_out(a.M, N, _OUT_DTYPES[out_type], dev)
+    st = lib.qgemm_run(_ptr(a.q), a.q.stride(0), _ptr(a.scales), _ptr(a.zero_points), a.fmt, a.gran, a.M,
+                       ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0), out_type,
+                       None, 0, ctypes.c_void_p(_stream(dev, stream)))
+    _check("qgemm_run", st)
+    return out[:, :N]
+
+
+def qgemm_run_mx(a: QuantizedRows, w: PackedWeights, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """Block-scaled e4m3 GEMM (float32 out); returns out[:, :N]."""
+    lib = L.load()
+    dev = a.q.device
+    N = w.N
+    if out is None:
+        out = _alloc_out(a.M, N, torch.float32, dev)
+    st = lib.qgemm_run_mx(_ptr(a.q), a.q.stride(0), _ptr(a.mx_scales), a.mx_scales.stride(0), a.M,
+                          ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0),
+                          None, 0, ctypes.c_void_p(_stream(dev, stream)))
+    _check("qgemm_run_mx", st)
+    return out[:, :N]

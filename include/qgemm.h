@@ -1,0 +1,264 @@
+/*
+ * qgemm.h -- C ABI of the MI355X (gfx950) quantized linear-layer library.
+ *
+ * One hot path: dynamic per-token activation quantization, an int8 x int8
+ * GEMM accumulated exactly in int32, and a dequantization epilogue that
+ * applies s_a * s_w once per output and subtracts z_a * colsum(W_q) for
+ * asymmetric activations; plus the MX variant (e4m3 data, one E8M0 scale per
+ * 32 K-elements) on the block-scaled fp8 matrix cores.
+ *
+ * Pages the operations follow (titles as they appear on the pages):
+ *   [D98]  "100 Days of GPU -- Day 98: Quantization and sparsity"
+ *   [TL27] "TileLang tutorial, chapter 27: low-precision quantization"
+ *   [SK]   "Skill: Write an INT8 Quantized Kernel"
+ *   [AQ]   "Activation Quantization Architecture, in depth"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named "device" are HIP device allocations on the current
+ *   device; the caller allocates and owns every buffer, including the
+ *   workspace. The library allocates no device memory and keeps no state
+ *   beyond a per-device cache of "is this a gfx950".
+ * - Matrices are row-major with an explicit leading dimension in ELEMENTS.
+ *   Activations are [M, K] (one row per token); weights are [N, K] (one row
+ *   per output channel, K contiguous); outputs are [M, N].
+ * - `stream` is a hipStream_t (NULL = the null stream), borrowed for the call.
+ *   Every call is asynchronous: a return of QGEMM_OK means the arguments were
+ *   valid and the kernels were launched; device faults surface at the
+ *   caller's next synchronization.
+ * - Every argument is validated before anything is launched, so an error
+ *   return leaves every output untouched. Nothing aborts or throws.
+ * - M == 0 is a valid empty call (nothing is launched). N and K must be >= 1.
+ * - Unsupported devices are an error (QGEMM_E_DEVICE): there is no fallback
+ *   path, and a block-scaled call is never served by a kernel that would
+ *   drop its scales ([TL27] 4.2(d)).
+ * - Non-finite inputs (NaN, Inf) are not supported; outputs are then
+ *   unspecified.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QGEMM_ABI_VERSION 1
+#define QGEMM_WDESC_MAGIC 0x51474d57u /* "WMGQ" */
+
+/* Status codes. Every entry point returns one of these. */
+typedef enum {
+  QGEMM_OK = 0,
+  QGEMM_E_NULL = -1,      /* a required pointer is NULL                                    */
+  QGEMM_E_SHAPE = -2,     /* a size or leading dimension is out of range                   */
+  QGEMM_E_MODE = -3,      /* unsupported format / granularity / output combination         */
+  QGEMM_E_ALIGN = -4,     /* a pointer or leading dimension is not aligned as documented   */
+  QGEMM_E_OVERFLOW = -5,  /* K too large for an exact int32 accumulator                    */
+  QGEMM_E_DEVICE = -6,    /* the current device is not a gfx950                            */
+  QGEMM_E_DESC = -7,      /* the weight descriptor is invalid or does not fit the call     */
+  QGEMM_E_WORKSPACE = -8, /* workspace missing or smaller than qgemm_workspace_bytes()     */
+  QGEMM_E_HIP = -9        /* a HIP runtime call or a kernel launch failed                  */
+} qgemm_status;
+
+/* Quantized formats. */
+typedef enum {
+  /* Symmetric int8, codes in [-127, 127], x = q * s.
+   * [D98] "What a scale actually promises"; [AQ] "The quantizer itself". */
+  QGEMM_FMT_INT8_SYM = 0,
+  /* Asymmetric uint8 with zero point, codes in [0, 255], x = (q - z) * s.
+   * [SK] "Required reasoning process" step 1; [AQ] "The quantizer itself". */
+  QGEMM_FMT_UINT8_ASYM = 1,
+  /* OCP e4m3fn data with one E8M0 power-of-two scale per 32 K-elements.
+   * [TL27] sections 2.2 and 2.3. */
+  QGEMM_FMT_MXFP8_E4M3 = 2
+} qgemm_format;
+
+/* Scale granularity. */
+typedef enum {
+  QGEMM_GRAN_TENSOR = 0,  /* one scale (and zero point) for the whole matrix          */
+  QGEMM_GRAN_ROW = 1,     /* one per row: per token for A, per output channel for W   */
+  QGEMM_GRAN_BLOCK32 = 2  /* one per 32 contiguous K-elements of a row (MX only)      */
+} qgemm_granularity;
+
+/* Output element type of qgemm_run. */
+typedef enum {
+  QGEMM_OUT_F32 = 0,   /* float32                                                    */
+  QGEMM_OUT_BF16 = 1,  /* bfloat16, round to nearest even of the float32 result       */
+  QGEMM_OUT_I32 = 2    /* int32: the corrected sum C = sum_k (q_a - z_a) * q_w,
+                          before scaling (for exact checks)                          */
+} qgemm_out_type;
+
+/*
+ * Host-side descriptor of a prepared weight buffer ("checkpoint metadata":
+ * [TL27] section 7, pitfall 10 -- record the granularity with the weights).
+ * Filled by qgemm_prepack_weights; read by qgemm_run / qgemm_run_mx.
+ *
+ * Layout of the packed device buffer (all offsets in bytes, 256-aligned):
+ *   codes   at codes_off:  [N_pad][K_pad] bytes, row-major. int8 codes for
+ *           QGEMM_FMT_INT8_SYM, e4m3 codes for QGEMM_FMT_MXFP8_E4M3. Rows >= N
+ *           and columns >= K are zero.
+ *   scales  at scales_off: INT8: float32 [N_pad] (GRAN_ROW; rows >= N are 0)
+ *           or float32 [1] (GRAN_TENSOR). MX: E8M0 bytes [N_pad][K_pad/32]
+ *           row-major, padding blocks hold 127 (scale 1.0).
+ *   colsum  at colsum_off: INT8 only: int32 [N_pad], colsum[n] = sum_k q_w[n,k]
+ *           ([D98] "The program, and the gate that has to be per column":
+ *           computed once, when the weights are quantized). -1 for MX.
+ */
+typedef struct qgemm_wdesc {
+  uint32_t magic;      /* QGEMM_WDESC_MAGIC                        */
+  uint32_t version;    /* QGEMM_ABI_VERSION                        */
+  int32_t fmt;         /* qgemm_format                             */
+  int32_t gran;        /* qgemm_granularity                        */
+  int64_t N, K;        /* logical sizes                            */
+  int64_t N_pad;       /* N rounded up to a multiple of 256        */
+  int64_t K_pad;       /* K rounded up to a multiple of 128        */
+  int64_t codes_off;
+  int64_t scales_off;
+  int64_t colsum_off;
+  int64_t bytes;       /* bytes of the packed buffer that are used */
+} qgemm_wdesc;
+
+/* ABI version of the loaded library (QGEMM_ABI_VERSION it was built with). */
+int qgemm_abi_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char* qgemm_status_string(int status);
+
+/*
+ * Size in bytes of the packed weight buffer qgemm_prepack_weights needs for
+ * an [N, K] weight in format `fmt` with granularity `gran`. Returns 0 for an
+ * invalid combination or size.
+ */
+size_t qgemm_packed_weight_bytes(int64_t N, int64_t K, int fmt, int gran);
+
+/*
+ * Workspace bytes the quantize / prepack calls need for these arguments.
+ * Per-tensor quantization needs M (or N) float partial results (2x for the
+ * asymmetric min/max); per-row and MX quantization need none (0 returned).
+ * `rows` is M for activations, N for weights.
+ */
+size_t qgemm_workspace_bytes(int64_t rows, int64_t K, int fmt, int gran);
+
+/*
+ * qgemm_quantize_rows -- dynamic activation quantization (steps Q1-Q3 and MXQ).
+ *
+ *   INT8_SYM   ([AQ] "The integer GEMM, written out", quantize_per_token;
+ *               [D98] "What a scale actually promises" and "Pitfalls"):
+ *     amax = max_k |x[m,k]| (per row) or over the whole matrix (TENSOR);
+ *     s = max(amax / 127, 1e-8)                         (float32)
+ *     q = clamp(rint(x / s), -127, 127)                 (int8)
+ *   UINT8_ASYM ([SK] step 1; [AQ] "The quantizer itself"):
+ *     s = max((max - min) / 255, 1e-8); z = clamp(rint(-min / s), 0, 255)
+ *     q = clamp(rint(x / s) + z, 0, 255)                (uint8)
+ *   MXFP8_E4M3 ([TL27] 2.2 item 3 and 2.3; GRAN_BLOCK32 only; K % 32 == 0):
+ *     per row and 32-block b: amax = max(max|x|, 1e-4);
+ *     E = ceil_to_ue8m0(amax / 448) in [1, 254]  (scale 2^(E-127));
+ *     q = e4m3(x * 2^(127-E)), round to nearest even.
+ *   Division is the correctly rounded float32 x / s (no reciprocal), rint is
+ *   round-half-to-even, so codes, scales and zero points are bit-exact
+ *   against a float32 evaluation of the same formulas.
+ *
+ * Arguments:
+ *   x            device, float32 [M][ldx], ldx >= K, ldx % 4 == 0, 16-byte aligned.
+ *   M, K         M >= 0, K >= 1.
+ *   fmt, gran    INT8_SYM or UINT8_ASYM with TENSOR or ROW; MXFP8_E4M3 with BLOCK32.
+ *   q            device, codes [M][ldq] bytes, ldq >= K, ldq % 16 == 0, 16-byte aligned.
+ *                Columns >= K are not written.
+ *   scales       device float32 [M] (ROW) or [1] (TENSOR); NULL for MX.
+ *   zero_points  device int32 [M] or [1] for UINT8_ASYM; NULL otherwise.
+ *   mx_scales    device E8M0 bytes [M][ld_mx] for MX (ld_mx >= K/32); NULL otherwise.
+ *   workspace    device, >= qgemm_workspace_bytes(M, K, fmt, gran) bytes
+ *                (may be NULL when that is 0). Contents need no initialization.
+ */
+int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx,
+                        int fmt, int gran,
+                        void* q, int64_t ldq,
+                        float* scales, int32_t* zero_points,
+                        uint8_t* mx_scales, int64_t ld_mx,
+                        void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * qgemm_prepack_weights -- offline weight preparation (step "W prepack").
+ *
+ *   INT8_SYM, ROW or TENSOR: per output channel n (or once for the matrix),
+ *     s_w = max(amax / 127, 1e-8); q_w = clamp(rint(w / s_w), -127, 127);
+ *     colsum[n] = sum_k q_w[n,k]  ([AQ] "The integer GEMM, written out",
+ *     quantize_per_channel; [D98] the column sums of the zero-point row).
+ *   MXFP8_E4M3, BLOCK32: the MX rule of qgemm_quantize_rows on each row of W.
+ *   Writes the packed layout described at qgemm_wdesc (including zero padding)
+ *   and fills *desc on the host.
+ *
+ *   w        device float32 [N][ldw], ldw >= K, ldw % 4 == 0, 16-byte aligned.
+ *   packed   device, >= qgemm_packed_weight_bytes(N, K, fmt, gran) bytes, 256-byte aligned.
+ *   desc     host, written on success only.
+ *   workspace as for qgemm_quantize_rows with rows = N.
+ *   The packed buffer is immutable afterwards and may be used on any stream.
+ */
+int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw,
+                          int fmt, int gran,
+                          void* packed, size_t packed_bytes, qgemm_wdesc* desc,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * qgemm_run -- int8 GEMM with the fused dequantization epilogue (steps G, E).
+ *
+ *   C[m,n]   = sum_k (q_a[m,k] - z_a[m]) * q_w[n,k]        exact int32
+ *              ([AQ] "The integer GEMM, written out": the integer dot product
+ *              minus z_a * colsum(q_w); [D98] "What a scale actually
+ *              promises": int32 accumulation rounds nothing)
+ *   out[m,n] = float(C[m,n]) * (s_a[m] * s_w[n])            float32 arithmetic
+ *              ([D98] "The program, and the gate that has to be per column":
+ *              the scales multiply once per output, after the loop;
+ *              [SK] "Correctness requirements": zero point before scaling)
+ *   cast to float32, to bfloat16 (round to nearest even), or C itself (I32).
+ *
+ *   a_q      device codes [M][lda] (int8 for INT8_SYM, uint8 for UINT8_ASYM),
+ *            lda >= K, lda % 16 == 0, 16-byte aligned.
+ *   a_scales device float32 [M] (ROW) or [1] (TENSOR).
+ *   a_zero   device int32 [M] or [1] (UINT8_ASYM, values 0..255); NULL for INT8_SYM.
+ *   w_desc   host descriptor from qgemm_prepack_weights (INT8_SYM weights).
+ *   w_packed device packed buffer of that descriptor.
+ *   out      device [M][ldo] of out_type, ldo >= N, 16-byte aligned, ldo % 4 == 0.
+ *   K limit  (QGEMM_E_OVERFLOW): K <= 133144 for INT8_SYM activations
+ *            (127*127*K < 2^31), K <= 66311 for UINT8_ASYM (255*127*K < 2^31)
+ *            ([SK] step 2 and "Correctness requirements"; [AQ] about 133,000 terms).
+ *   workspace unused by this version (pass NULL, 0).
+ */
+int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t* a_zero,
+              int a_fmt, int a_gran, int64_t M,
+              const qgemm_wdesc* w_desc, const void* w_packed,
+              void* out, int64_t ldo, int out_type,
+              void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/*
+ * qgemm_run_mx -- block-scaled fp8 GEMM (step MXG).
+ *
+ *   out[m,n] = sum_b 2^(Ea[m,b]-127) * 2^(Ew[n,b]-127) *
+ *              sum_{k in block b} e4m3(a[m,k]) * e4m3(w[n,k])
+ *   Each 32-element K block is multiplied by its own pair of scales inside
+ *   the K loop ([TL27] 4.1: (A*scale_A)(B*scale_B); 4.3: a per-K-block scale
+ *   cannot be moved out of the sum). Products are exact; the sum is
+ *   accumulated in float32 by the matrix cores. float32 output.
+ *
+ *   a_codes  device e4m3 [M][lda], lda >= K, lda % 16 == 0, 16-byte aligned.
+ *   a_e8m0   device E8M0 [M][lda_s], lda_s >= K/32.
+ *   w_desc   descriptor of MXFP8_E4M3 weights with the same K (K % 32 == 0).
+ *   out      device float32 [M][ldo], ldo >= N, ldo % 4 == 0, 16-byte aligned.
+ *   workspace unused by this version (pass NULL, 0).
+ */
+int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s,
+                 int64_t M, const qgemm_wdesc* w_desc, const void* w_packed,
+                 float* out, int64_t ldo,
+                 void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

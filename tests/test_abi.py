@@ -1,0 +1,173 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+torch = pytest.importorskip("torch")
+
+from block_scaled_quantized_qgemm_amd import _lib as L  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+
+OK, E_NULL, E_SHAPE, E_MODE, E_ALIGN, E_OVERFLOW, E_DEVICE, E_DESC, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+INT8, UINT8, MX = 0, 1, 2
+TENSOR, ROW, BLK = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libqgemm.so is not built (run __graft_entry__.build())")
+    return L.load()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(qgemm_\w+)\s*\(", src, flags=re.M))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert names == set(L.SIGNATURES), names ^ set(L.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.qgemm_abi_version() == 1
+    for s in range(-9, 1):
+        assert lib.qgemm_status_string(s).startswith(b"QGEMM_")
+    assert lib.qgemm_status_string(-100) == b"unknown qgemm status"
+
+
+def test_sizes(lib):
+    # int8: codes [256][128] + scales 4*256 + colsum 4*256
+    assert lib.qgemm_packed_weight_bytes(1, 1, INT8, ROW) == 256 * 128 + 1024 + 1024
+    assert lib.qgemm_packed_weight_bytes(4096, 4096, INT8, ROW) == 4096 * 4096 + 4 * 4096 * 2
+    assert lib.qgemm_packed_weight_bytes(8192, 8192, MX, BLK) == 8192 * 8192 + 8192 * 256
+    assert lib.qgemm_packed_weight_bytes(64, 100, MX, BLK) == 0       # K % 32
+    assert lib.qgemm_packed_weight_bytes(64, 96, UINT8, ROW) == 0     # weights are symmetric
+    assert lib.qgemm_packed_weight_bytes(0, 96, INT8, ROW) == 0
+    assert lib.qgemm_workspace_bytes(64, 256, INT8, TENSOR) == 256
+    assert lib.qgemm_workspace_bytes(64, 256, UINT8, TENSOR) == 512
+    assert lib.qgemm_workspace_bytes(64, 256, INT8, ROW) == 0
+    assert lib.qgemm_workspace_bytes(64, 256, MX, BLK) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _q(lib, x=FAKE, M=4, K=64, ldx=64, fmt=INT8, gran=ROW, q=FAKE, ldq=64, s=FAKE, z=None, mx=None,
+       ldmx=0, ws=None, wsb=0):
+    return lib.qgemm_quantize_rows(x, M, K, ldx, fmt, gran, q, ldq, s, z, mx, ldmx, ws, wsb, None)
+
+
+def test_quantize_rows_validation(lib):
+    assert _q(lib, fmt=7) == E_MODE
+    assert _q(lib, fmt=MX, gran=ROW) == E_MODE
+    assert _q(lib, fmt=INT8, gran=BLK) == E_MODE
+    assert _q(lib, K=0) == E_SHAPE
+    assert _q(lib, M=-1) == E_SHAPE
+    assert _q(lib, M=0, x=None, q=None, s=None) == OK           # empty call
+    assert _q(lib, x=None) == E_NULL
+    assert _q(lib, s=None) == E_NULL
+    assert _q(lib, fmt=UINT8, z=None) == E_NULL
+    assert _q(lib, ldx=32) == E_SHAPE
+    assert _q(lib, ldq=63) == E_SHAPE
+    assert _q(lib, ldx=66) == E_ALIGN
+    assert _q(lib, ldq=80 + 8) == E_ALIGN
+    assert _q(lib, x=FAKE + 4) == E_ALIGN
+    assert _q(lib, fmt=MX, gran=BLK, K=48, ldx=48, ldq=48, s=None, mx=FAKE, ldmx=2) == E_SHAPE
+    assert _q(lib, fmt=MX, gran=BLK, s=None, mx=None) == E_NULL
+    assert _q(lib, fmt=MX, gran=BLK, s=None, mx=FAKE, ldmx=1) == E_SHAPE
+    assert _q(lib, gran=TENSOR) == E_WS
+    assert _q(lib, gran=TENSOR, ws=FAKE, wsb=15) == E_WS
+
+
+def _wdesc(**kw):
+    d = L.WDesc(magic=0x51474D57, version=1, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=384,
+                codes_off=0, scales_off=256 * 384, colsum_off=256 * 384 + 1024, bytes=256 * 384 + 2048)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _run(lib, d, a=FAKE, lda=304, s=FAKE, z=None, fmt=INT8, gran=ROW, M=8, w=FAKE, out=FAKE, ldo=100,
+         ot=0):
+    return lib.qgemm_run(a, lda, s, z, fmt, gran, M, ctypes.byref(d), w, out, ldo, ot, None, 0, None)
+
+
+def test_run_validation(lib):
+    good = _wdesc()
+    assert lib.qgemm_packed_weight_bytes(100, 300, INT8, ROW) == good.bytes
+    assert _run(lib, _wdesc(magic=1)) == E_DESC
+    assert _run(lib, _wdesc(version=2)) == E_DESC
+    assert _run(lib, _wdesc(fmt=MX)) == E_DESC
+    assert _run(lib, _wdesc(K_pad=512)) == E_DESC
+    assert _run(lib, _wdesc(bytes=5)) == E_DESC
+    assert lib.qgemm_run(FAKE, 304, FAKE, None, INT8, ROW, 8, None, FAKE, FAKE, 100, 0, None, 0, None) == E_NULL
+    assert _run(lib, good, fmt=MX) == E_MODE
+    assert _run(lib, good, ot=3) == E_MODE
+    assert _run(lib, good, M=-1) == E_SHAPE
+    assert _run(lib, good, M=0, a=None, s=None, w=None, out=None) == OK
+    assert _run(lib, good, a=None) == E_NULL
+    assert _run(lib, good, fmt=UINT8) == E_NULL            # missing zero points
+    assert _run(lib, good, lda=288) == E_SHAPE
+    assert _run(lib, good, lda=312) == E_ALIGN
+    assert _run(lib, good, ldo=99) == E_SHAPE
+    assert _run(lib, good, ldo=102) == E_ALIGN
+    assert _run(lib, good, w=FAKE + 16) == E_ALIGN
+    # exact-int32 limits on K
+    nb = lib.qgemm_packed_weight_bytes(8, 133145, INT8, ROW)
+    big = _wdesc(N=8, K=133145, K_pad=133248, scales_off=256 * 133248, colsum_off=256 * 133248 + 1024,
+                 bytes=nb)
+    assert _run(lib, big, lda=133152) == E_OVERFLOW
+    nb = lib.qgemm_packed_weight_bytes(8, 66312, INT8, ROW)
+    mid = _wdesc(N=8, K=66312, K_pad=66432, scales_off=256 * 66432, colsum_off=256 * 66432 + 1024, bytes=nb)
+    assert _run(lib, mid, lda=66320, fmt=UINT8, z=FAKE) == E_OVERFLOW
+
+
+def test_run_mx_validation(lib):
+    nb = lib.qgemm_packed_weight_bytes(100, 320, MX, BLK)
+    d = L.WDesc(magic=0x51474D57, version=1, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=384,
+                codes_off=0, scales_off=256 * 384, colsum_off=-1, bytes=nb)
+    call = lambda **kw: lib.qgemm_run_mx(kw.get("a", FAKE), kw.get("lda", 320), kw.get("e", FAKE),
+                                         kw.get("ldas", 10), kw.get("M", 4), ctypes.byref(kw.get("d", d)),
+                                         FAKE, kw.get("out", FAKE), kw.get("ldo", 100), None, 0, None)
+    assert call(d=_wdesc()) == E_DESC                     # an int8 descriptor
+    assert call(e=None) == E_NULL
+    assert call(ldas=9) == E_SHAPE
+    assert call(lda=304) == E_SHAPE
+    assert call(lda=328) == E_ALIGN
+    assert call(M=0, a=None, e=None, out=None) == OK
+
+
+def test_prepack_validation(lib):
+    d = L.WDesc()
+    f = lambda **kw: lib.qgemm_prepack_weights(kw.get("w", FAKE), kw.get("N", 64), kw.get("K", 64),
+                                               kw.get("ldw", 64), kw.get("fmt", INT8), kw.get("gran", ROW),
+                                               kw.get("p", 0x100000), kw.get("pb", 1 << 20), ctypes.byref(d),
+                                               kw.get("ws", None), kw.get("wsb", 0), None)
+    assert f(fmt=UINT8) == E_MODE
+    assert f(fmt=MX, gran=ROW) == E_MODE
+    assert f(fmt=MX, gran=BLK, K=40, ldw=40) == E_SHAPE
+    assert f(N=0) == E_SHAPE
+    assert f(w=None) == E_NULL
+    assert f(ldw=32) == E_SHAPE
+    assert f(p=0x100000 + 128) == E_ALIGN
+    assert f(pb=100) == E_SHAPE
+    assert f(gran=TENSOR) == E_WS
+    assert d.magic == 0                                   # untouched on error
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_no_device_is_an_error_not_a_fallback(lib):
+    # fully valid arguments: the only thing missing is a gfx950
+    assert _q(lib) == E_DEVICE
+    assert _run(lib, _wdesc()) == E_DEVICE

@@ -1,0 +1,251 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer results (codes, zero points, column sums, int32 sums) and float32
+scales must be bit-exact; float32 outputs within 1e-6 relative of the
+oracle's float64 epilogue; bfloat16 outputs within half a bf16 ulp (plus
+float32 slack); MX outputs within 1e-5 * sum_k |a_k w_k| of the float64
+reference over the dequantized e4m3 values.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from block_scaled_quantized_qgemm_amd.inputs import make_inputs, rng_for
+from conftest import print_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+F32_RTOL = 1e-6
+BF16_RTOL = 2.0 ** -8 + 2.0 ** -20
+MX_STOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def ops():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_scaled_quantized_qgemm_amd import ops as _ops
+    _ops.L.load()
+    return _ops
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+ACT = {  # name -> (fmt, gran, oracle act)
+    "sym_row": (0, 1, "sym_row"), "sym_tensor": (0, 0, "sym_tensor"),
+    "asym_row": (1, 1, "asym_row"), "asym_tensor": (1, 0, "asym_tensor"),
+}
+
+
+def _edge_rows(K, rng):
+    rows = [np.zeros(K), np.full(K, 3.25), np.full(K, -2.0), np.linspace(-10, -9, K),
+            np.linspace(4, 5, K), rng.standard_normal(K) * 1e-30]
+    spike = np.zeros(K)
+    spike[K // 2] = -7.0
+    rows.append(spike)
+    big = rng.standard_normal(K)
+    big[0] = 6.0e4
+    rows.append(big)
+    return np.stack(rows).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Q1-Q3: row quantization, bit-exact
+# ---------------------------------------------------------------------------
+QSHAPES = [(1, 1), (3, 5), (7, 17), (64, 256), (33, 1000), (5, 4095), (4, 4097), (9, 8192), (2, 9000), (512, 4096)]
+
+
+@pytest.mark.parametrize("act", list(ACT))
+@pytest.mark.parametrize("M,K", QSHAPES)
+def test_quantize_rows_bit_exact(ops, act, M, K):
+    print_case("quantize_rows", act, M, K)
+    fmt, gran, oact = ACT[act]
+    A, _ = make_inputs("c3_asym_uint8" if act.startswith("asym") and M % 2 else "c2_per_token", M=M, K=K, N=1,
+                       seed=M * 7919 + K)
+    r = ops.qgemm_quantize_rows(dev(A), fmt, gran)
+    codes = host(r.codes())
+    if fmt == 0:
+        q, s = O.quantize_sym_int8(A, per_row=(gran == 1))
+    else:
+        q, s, z = O.quantize_asym_uint8(A, per_row=(gran == 1))
+        assert np.array_equal(host(r.zero_points), z)
+    assert np.array_equal(codes.view(np.uint8), q.view(np.uint8))
+    assert np.array_equal(host(r.scales).view(np.uint32), s.view(np.uint32))
+
+
+@pytest.mark.parametrize("act", list(ACT))
+@pytest.mark.parametrize("K", [7, 256, 4096, 8200])
+def test_quantize_rows_edge_rows(ops, act, K):
+    print_case("quantize_rows edge rows", act, K)
+    fmt, gran, _ = ACT[act]
+    A = _edge_rows(K, rng_for(K))
+    r = ops.qgemm_quantize_rows(dev(A), fmt, gran)
+    if fmt == 0:
+        q, s = O.quantize_sym_int8(A, per_row=(gran == 1))
+    else:
+        q, s, z = O.quantize_asym_uint8(A, per_row=(gran == 1))
+        assert np.array_equal(host(r.zero_points), z)
+    assert np.array_equal(host(r.codes()).view(np.uint8), q.view(np.uint8))
+    assert np.array_equal(host(r.scales).view(np.uint32), s.view(np.uint32))
+
+
+def test_quantize_rows_empty(ops):
+    r = ops.qgemm_quantize_rows(torch.empty((0, 64), device="cuda"), 0, 1)
+    assert r.codes().shape == (0, 64)
+
+
+# ---------------------------------------------------------------------------
+# MXQ: MX quantization, bit-exact (the two zero codes 0x00 / 0x80 are one value)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 64), (17, 96), (64, 1024), (130, 4192), (8, 8192)])
+def test_quantize_mx_bit_exact(ops, M, K):
+    print_case("quantize_mx", M, K)
+    A, _ = make_inputs("c5_mxfp8", M=M, K=K, N=1, seed=M * 31 + K)
+    if M >= 8:
+        A[-8:] = _edge_rows(K, rng_for(K))
+    r = ops.qgemm_quantize_rows(dev(A), 2, 2)
+    codes, E = O.quantize_mx(A)
+    got = host(r.codes())
+    assert np.array_equal(host(r.mx_scales)[:, : K // 32], E)
+    same = (got == codes) | (((got | 0x80) == 0x80) & ((codes | 0x80) == 0x80))
+    assert same.all()
+
+
+# ---------------------------------------------------------------------------
+# Weight preparation, bit-exact, padding zero
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("per_channel", [True, False])
+@pytest.mark.parametrize("N,K", [(1, 1), (5, 7), (64, 256), (300, 1000), (257, 4097)])
+def test_prepack_int8_bit_exact(ops, N, K, per_channel):
+    print_case("prepack int8", N, K, per_channel)
+    _, W = make_inputs("c2_per_token", M=1, K=K, N=N, seed=N * 101 + K)
+    pw = ops.qgemm_prepack_weights(dev(W), 0, 1 if per_channel else 0)
+    q, s, colsum = O.prepare_weights_int8(W, per_channel=per_channel)
+    codes = host(pw.codes())
+    assert np.array_equal(codes[:N, :K], q)
+    assert not codes[N:].any() and not codes[:, K:].any()
+    sc = host(pw.scales())
+    assert np.array_equal(sc[: s.size].view(np.uint32), s.view(np.uint32))
+    cs = host(pw.colsum())
+    assert np.array_equal(cs[:N], colsum) and not cs[N:].any()
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (70, 96), (300, 1024)])
+def test_prepack_mx_bit_exact(ops, N, K):
+    print_case("prepack mx", N, K)
+    _, W = make_inputs("c5_mxfp8", M=1, K=K, N=N, seed=N + K)
+    pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
+    codes, E = O.quantize_mx(W)
+    got = host(pw.codes())
+    assert np.array_equal(O.e4m3_decode(got[:N, :K]), O.e4m3_decode(codes))
+    assert not got[N:].any() and not got[:, K:].any()
+    e = host(pw.scales())
+    assert np.array_equal(e[:N, : K // 32], E)
+    assert (e[N:] == 127).all() and (e[:, K // 32:] == 127).all()
+
+
+# ---------------------------------------------------------------------------
+# G + E: int8 GEMM and epilogue, end to end from float32 inputs
+# ---------------------------------------------------------------------------
+GSHAPES = [(1, 1, 1), (3, 5, 7), (33, 65, 129), (64, 64, 256), (130, 260, 300), (257, 513, 1000),
+           (300, 300, 4112), (17, 1030, 64)]
+
+
+def _run_int(ops, A, W, act, wgt, out_type):
+    fmt, gran, _ = ACT[act]
+    a = ops.qgemm_quantize_rows(dev(A), fmt, gran)
+    pw = ops.qgemm_prepack_weights(dev(W), 0, 1 if wgt == "channel" else 0)
+    return host(ops.qgemm_run(a, pw, out_type))
+
+
+def _check_out(got, y, out_type, C=None):
+    if out_type == 2:
+        assert np.array_equal(got, C)
+    elif out_type == 0:
+        err = np.abs(got.astype(np.float64) - y)
+        bad = err > F32_RTOL * np.abs(y)
+        assert not bad.any(), (np.argwhere(bad)[:5], err.max())
+    else:
+        g = O.bf16_to_f32(got.view(np.uint16)).astype(np.float64)
+        err = np.abs(g - y)
+        bad = err > BF16_RTOL * np.abs(y)
+        assert not bad.any(), (np.argwhere(bad)[:5], err.max())
+
+
+@pytest.mark.parametrize("act", list(ACT))
+@pytest.mark.parametrize("wgt", ["channel", "tensor"])
+@pytest.mark.parametrize("M,N,K", GSHAPES)
+def test_gemm_int32_exact(ops, M, N, K, act, wgt):
+    print_case("gemm i32", M, N, K, act, wgt)
+    recipe = "c3_asym_uint8" if act.startswith("asym") else "c2_per_token"
+    A, W = make_inputs(recipe, M=M, K=K, N=N, seed=M + 3 * N + 7 * K)
+    if act.startswith("asym"):
+        A = A - np.float32(0.3)     # both signs: zero points strictly inside (0, 255)
+    ref = O.quantized_linear(A, W, act=ACT[act][2], wgt=wgt)
+    got = _run_int(ops, A, W, act, wgt, 2)
+    _check_out(got, None, 2, ref["C"])
+
+
+@pytest.mark.parametrize("out_type", [0, 1])
+@pytest.mark.parametrize("act", list(ACT))
+@pytest.mark.parametrize("M,N,K", [(3, 5, 7), (64, 64, 256), (257, 513, 1000), (300, 300, 4112)])
+def test_gemm_epilogue_float(ops, M, N, K, act, out_type):
+    print_case("gemm epilogue", M, N, K, act, out_type)
+    A, W = make_inputs("c2_per_token", M=M, K=K, N=N, seed=5 * M + N + K)
+    ref = O.quantized_linear(A, W, act=ACT[act][2], wgt="channel")
+    got = _run_int(ops, A, W, act, "channel", out_type)
+    _check_out(got, ref["y"], out_type)
+
+
+def test_gemm_c1_both_weight_granularities_and_gate(ops):
+    print_case("gemm c1 gate")
+    A, W = make_inputs("c1_tiny")
+    ref64 = A.astype(np.float64) @ W.astype(np.float64).T
+    fr = {}
+    for wgt in ("tensor", "channel"):
+        ref = O.quantized_linear(A, W, act="sym_tensor", wgt=wgt)
+        got = _run_int(ops, A, W, "sym_tensor", wgt, 0)
+        _check_out(got, ref["y"], 0)
+        fr[wgt] = O.metrics.gate_fractions(got, ref64, A, W)
+    assert fr["channel"][2] is None and fr["channel"][1] < 1.0 < fr["tensor"][1]
+
+
+def test_gemm_deterministic(ops):
+    A, W = make_inputs("c3_asym_uint8", M=200, K=1000, N=300)
+    a = ops.qgemm_quantize_rows(dev(A), 1, 1)
+    pw = ops.qgemm_prepack_weights(dev(W), 0, 1)
+    o1 = host(ops.qgemm_run(a, pw, 1))
+    o2 = host(ops.qgemm_run(a, pw, 1))
+    assert np.array_equal(o1.view(np.uint16), o2.view(np.uint16))
+
+
+def test_gemm_empty_m(ops):
+    pw = ops.qgemm_prepack_weights(dev(np.ones((8, 64), np.float32)), 0, 1)
+    a = ops.qgemm_quantize_rows(torch.empty((0, 64), device="cuda"), 0, 1)
+    assert ops.qgemm_run(a, pw, 0).shape == (0, 8)
+
+
+# ---------------------------------------------------------------------------
+# MXG: block-scaled GEMM
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (33, 65, 96), (130, 260, 320), (64, 64, 1024),
+                                   (300, 200, 2080), (257, 300, 4096)])
+def test_gemm_mx_parity(ops, M, N, K):
+    print_case("gemm mx", M, N, K)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=M * 13 + N + K)
+    a = ops.qgemm_quantize_rows(dev(A), 2, 2)
+    pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
+    got = host(ops.qgemm_run_mx(a, pw)).astype(np.float64)
+    qa, Ea = O.quantize_mx(A)
+    qw, Ew = O.quantize_mx(W)
+    ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew)
+    err = np.abs(got - ref)
+    assert (err <= MX_STOL * S).all(), (err / np.maximum(S, 1e-300)).max()
