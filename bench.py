@@ -28,6 +28,7 @@ METRIC = "quantized GEMM TOPS (quant+GEMM+epilogue) and % of MFMA peak; decode-M
 
 PEAK_INT8_TOPS = 5000.0   # dense int8 MFMA, MI355X
 PEAK_FP8_TFLOPS = 5000.0  # dense fp8 / MXFP8 MFMA, MI355X
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X (the exact MX mode runs on these)
 PEAK_HBM_GBS = 8000.0     # HBM3E
 MALL_BYTES = 256 << 20
 
@@ -154,6 +155,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough to exceed the MALL 3x)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--mx-mode", default="exact", choices=["exact", "scaled-mfma"],
+                    help="MX workload: exact products (bf16 matrix cores) or block-scaled fp8 matrix cores")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -179,9 +182,11 @@ def main():
     otype = {"f32": ops.OUT_F32, "bf16": ops.OUT_BF16}[out]
     odt = {"f32": torch.float32, "bf16": torch.bfloat16}[out]
 
+    mx_mode = ops.MX_EXACT if args.mx_mode == "exact" else ops.MX_SCALED_MFMA
     A0 = torch.from_numpy(A_np).to(dev)
     W0 = torch.from_numpy(W_np).to(dev)
-    w0 = ops.qgemm_prepack_weights(W0, fmt, wgr)
+    wfmt = ops.FMT_MXFP8_E4M3 if act == "mxfp8" else ops.FMT_INT8_SYM   # weights are symmetric
+    w0 = ops.qgemm_prepack_weights(W0, wfmt, wgr)
     torch.cuda.synchronize()
     ops_count, step_bytes, gemm_bytes = algorithmic(name, M, K, N)
     set_bytes = A0.numel() * 4 + w0.packed.numel() + M * ((N + 7) // 8 * 8) * (4 if out == "f32" else 2) + M * K
@@ -208,7 +213,7 @@ def main():
         if ev is not None:
             ev.record()
         if fmt == ops.FMT_MXFP8_E4M3:
-            ops.qgemm_run_mx(qi, wi, out=oi)
+            ops.qgemm_run_mx(qi, wi, out=oi, mode=mx_mode)
         else:
             ops.qgemm_run(qi, wi, otype, out=oi)
 
@@ -241,7 +246,10 @@ def main():
     else:
         value = ops_count / (ms_per_step * 1e-3) / 1e12
         gemm_achieved = ops_count / (gemm_ms * 1e-3) / 1e12
-        peak = PEAK_FP8_TFLOPS if act == "mxfp8" else PEAK_INT8_TOPS
+        if act == "mxfp8":
+            peak = PEAK_BF16_TFLOPS if mx_mode == ops.MX_EXACT else PEAK_FP8_TFLOPS
+        else:
+            peak = PEAK_INT8_TOPS
         roof = {"bound": "mfma", "achieved": gemm_achieved, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(name)
@@ -259,7 +267,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8-e4m3" if act == "mxfp8" else "i8",
         "data": "synthetic (seeded generator with the workload's shapes and distributions)",
-        "config": {"workload": f"{name}: {DESCRIPTION[name]}", "M": M, "K": K, "N": N,
+        "config": {"workload": f"{name}: {DESCRIPTION[name]}"
+                   + (f" ({args.mx_mode} mode)" if act == "mxfp8" else ""), "M": M, "K": K, "N": N,
                    "rotating_buffer_sets": nsets, "gemm_ms": gemm_ms,
                    "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9},
         "roofline": roof,

@@ -12,7 +12,7 @@
 namespace {
 
 constexpr int64_t kNPad = 256;   // packed rows are padded to this multiple
-constexpr int64_t kKPad = 128;   // packed columns are padded to this multiple
+constexpr int64_t kKPad = 256;   // packed columns are padded to this multiple (an even number of 128-deep steps)
 constexpr int64_t kSymKMax = 133144;   // 127*127*K < 2^31
 constexpr int64_t kAsymKMax = 66311;   // 255*127*K < 2^31
 constexpr int64_t kMaxRows = 0x7fffffff;
@@ -129,7 +129,7 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int f
   if (M == 0) return QGEMM_OK;
   if (!x || !q) return QGEMM_E_NULL;
   if (ldx < K || ldq < K) return QGEMM_E_SHAPE;
-  if (ldx % 4 != 0 || !aligned(x, 16) || ldq % 16 != 0 || !aligned(q, 16)) return QGEMM_E_ALIGN;
+  if (!aligned(x, 4) || ldq % 16 != 0 || !aligned(q, 16)) return QGEMM_E_ALIGN;
   if (mx) {
     if (!mx_scales) return QGEMM_E_NULL;
     if (ld_mx < K / 32) return QGEMM_E_SHAPE;
@@ -164,7 +164,7 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int
   if (!weight_layout(N, K, fmt, gran, &L)) return QGEMM_E_SHAPE;
   if (!w || !packed || !desc) return QGEMM_E_NULL;
   if (ldw < K) return QGEMM_E_SHAPE;
-  if (ldw % 4 != 0 || !aligned(w, 16) || !aligned(packed, 256)) return QGEMM_E_ALIGN;
+  if (!aligned(w, 4) || !aligned(packed, 256)) return QGEMM_E_ALIGN;
   if (packed_bytes < (size_t)L.bytes) return QGEMM_E_SHAPE;
   const size_t need = qgemm_workspace_bytes(N, K, fmt, gran);
   if (need > 0 && (!workspace || workspace_bytes < need)) return QGEMM_E_WORKSPACE;
@@ -245,10 +245,11 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
 }
 
 int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s, int64_t M,
-                 const qgemm_wdesc* w_desc, const void* w_packed, float* out, int64_t ldo, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 const qgemm_wdesc* w_desc, const void* w_packed, float* out, int64_t ldo, int mode,
+                 void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
+  if (mode != QGEMM_MX_EXACT && mode != QGEMM_MX_SCALED_MFMA) return QGEMM_E_MODE;
   int rc = check_desc(w_desc, QGEMM_FMT_MXFP8_E4M3);
   if (rc != QGEMM_OK) return rc;
   const int64_t N = w_desc->N, K = w_desc->K;
@@ -275,7 +276,7 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
   g.K_pad = w_desc->K_pad;
   g.out = out;
   g.ldo = ldo;
-  hipError_t e = qg::launch_gemm_mx(g, as_stream(stream));
+  hipError_t e = qg::launch_gemm_mx(g, mode, as_stream(stream));
   return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
 }
 

@@ -1,17 +1,27 @@
-// Matrix-core GEMMs for gfx950: the int8 path (v_mfma_i32_32x32x32_i8, exact
-// int32 accumulation, fused dequantization epilogue) and the MX path
-// (v_mfma_scale_f32_32x32x64_f8f6f4, e4m3 operands with one E8M0 scale per
-// 32 K-elements fed per lane, float32 accumulation).
+// Matrix-core GEMMs for gfx950.
 //
-// Structure (one template for both):
-//  * a workgroup owns a BM x BN output tile and walks K in BK-byte steps;
-//  * the A and W tiles of the next step are fetched from global memory into
-//    registers (16-byte loads, consecutive lanes on consecutive bytes of a
-//    row) while the matrix cores work on the current step out of LDS;
-//  * LDS holds two stages; rows are stored with their 16-byte chunks XOR-
-//    swizzled by row so that the 16-byte fragment reads of 32 consecutive rows
-//    spread over all banks;
-//  * each wave owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA blocks.
+// Three modes share one tiled kernel template:
+//  * I8   -- int8 x int8 on v_mfma_i32_32x32x32_i8: exact int32 sums and the
+//            fused dequantization epilogue.
+//  * MXB  -- MX (e4m3 + E8M0 per 32 K) with exact products: each e4m3 value is
+//            multiplied by its block's power-of-two scale while the tile is
+//            moved into LDS (v_cvt_scalef32_pk_bf16_fp8; e4m3 times a power of
+//            two is exactly representable in bf16), then v_mfma_f32_32x32x16_bf16
+//            forms exact products and float32 sums.
+//  * MXF  -- MX on the block-scaled fp8 matrix cores
+//            (v_mfma_scale_f32_32x32x64_f8f6f4), one E8M0 byte per lane and block.
+//            Inside each group of 8 consecutive K the hardware aligns the
+//            products to the largest one and drops bits more than 13 binades
+//            below it, so sums are not float32-exact.
+//
+// Tiling: a workgroup owns a BM x BN tile and walks K in BK-deep steps; the
+// next step's A and W tiles are fetched from global memory into registers
+// (16-byte loads, consecutive lanes on consecutive bytes of a row) while the
+// matrix cores consume the current step out of LDS; LDS holds two stages whose
+// rows store 16-byte chunks XOR-swizzled by row, so the 16-byte fragment reads
+// of 32 consecutive rows spread over all banks. Each wave owns a
+// (BM/WM) x (BN/WN) sub-tile of 32x32 matrix-core blocks. The epilogue goes
+// through LDS so that every lane stores 16 contiguous bytes of a row.
 //
 // Semantics followed:
 //  * int8: C = sum_k (q_a - z_a) q_w exactly in int32 ("Activation
@@ -21,8 +31,8 @@
 //    column"). uint8 codes enter the signed matrix cores as q - 128 (a byte
 //    XOR with 0x80) and the epilogue subtracts (z - 128) * colsum instead of
 //    z * colsum, which yields the same exact C.
-//  * MX: each 32-element K block is scaled by its own pair of E8M0 factors
-//    inside the K loop ("TileLang tutorial, chapter 27", sections 4.1 and 4.3).
+//  * MX: every 32-element K block carries its own pair of E8M0 factors inside
+//    the K loop ("TileLang tutorial, chapter 27", sections 4.1 and 4.3).
 #include <type_traits>
 
 #include "common.hpp"
@@ -30,29 +40,63 @@
 
 namespace qg {
 
-template <int BK>
-__device__ inline int swz(int row) {
-  constexpr int CPR = BK / 16;            // 16-byte chunks per row
-  constexpr int RPL = 128 / BK > 0 ? 128 / BK : 1;  // rows sharing one 128-byte line
-  return (row / RPL) % CPR;
-}
+enum GemmMode { I8 = 0, MXB = 1, MXF = 2 };
 
-template <int BK>
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// LDS row of RB bytes made of 16-byte chunks. gfx950 serves a 16-byte-per-lane
+// LDS access 16 lanes at a time over 64 four-byte banks (256 bytes), so the 16
+// rows that 16 lanes read at the same logical chunk must land in 16 distinct
+// 16-byte slots of a 256-byte bank line: the chunk index is XOR-ed with the
+// row's position among the rows that share a bank line.
+template <int RB>
 __device__ inline int lds_off(int row, int chunk) {
-  return row * BK + ((chunk ^ swz<BK>(row)) << 4);
+  constexpr int CPR = RB / 16;
+  constexpr int RPL = RB >= 256 ? 1 : 256 / RB;  // rows sharing one 256-byte bank line
+  return row * RB + ((chunk ^ ((row / RPL) % CPR)) << 4);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool MX, bool ASYM, int OUT>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
-  constexpr int FM = TM / 32, FN = TN / 32;  // 32x32 blocks per wave
-  constexpr int CPR = BK / 16;
-  constexpr int A_CH = BM * CPR / NT;        // 16-byte chunks per thread per stage
-  constexpr int B_CH = BN * CPR / NT;
+__device__ inline float e8m0_to_f32(int E) { return __uint_as_float((uint32_t)E << 23); }
+
+// Sixteen e4m3 codes times 2^(E-127) as sixteen bf16 (exact for E in [3, 240]).
+__device__ inline void fp8x16_to_bf16(const v4i& q, float scale, v4i& lo, v4i& hi) {
+  v2bf t[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    t[2 * d] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)q[d], scale, false);
+    t[2 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)q[d], scale, true);
+  }
+  int w[8];
+  __builtin_memcpy(w, t, 32);
+  lo = v4i{w[0], w[1], w[2], w[3]};
+  hi = v4i{w[4], w[5], w[6], w[7]};
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int MODE, bool ASYM, int OUT>
+struct GemmCfg {
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int CPR = BK / 16;                    // 16-byte global chunks per row and K step
+  static constexpr int RB = MODE == MXB ? 2 * BK : BK;   // LDS bytes per row
+  static constexpr int A_CH = BM * CPR / NT, B_CH = BN * CPR / NT;
+  static constexpr int STAGE = (BM + BN) * RB;
+  static constexpr int RS = TN + 8;  // epilogue staging row stride in words: rows r and r+4
+                                     // (the two half-waves) start 32 banks apart
+  static constexpr int EPI = WM * WN * 32 * RS * 4;      // per-wave 32 x TN float/int staging
+  static constexpr int LDS = 2 * STAGE > EPI ? 2 * STAGE : EPI;
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile / thread mismatch");
-  static_assert(!MX || BK % 64 == 0, "MX steps are 64 deep");
-  constexpr int STAGE = (BM + BN) * BK;
+  static_assert(MODE != MXF || BK % 64 == 0, "scaled fp8 steps are 64 deep");
+  static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int MODE, bool ASYM, int OUT>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
+  using C = GemmCfg<BM, BN, BK, WM, WN, MODE, ASYM, OUT>;
+  constexpr int NT = C::NT, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RB = C::RB;
+  constexpr int A_CH = C::A_CH, B_CH = C::B_CH, STAGE = C::STAGE;
+  constexpr bool MX = MODE != I8;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -61,8 +105,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   const int wm = wid / WN, wn = wid % WN;
 
   // Tile order: workgroups are dealt round-robin over the 8 XCDs; give each
-  // XCD a contiguous run of tiles, walked column-block-major within groups of
-  // 8 tile-rows so that neighbours share A rows and W columns in that L2.
+  // XCD a contiguous run of tiles, walked in groups of 8 tile-rows so that
+  // neighbours share A rows and W columns in that XCD's L2.
   const int tiles_m = (int)((p.M + BM - 1) / BM);
   const int tiles_n = (int)((p.N + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
@@ -79,62 +123,94 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   const int tile_m = first_m + (pid % group_tiles) % gsize;
   const int tile_n = (pid % group_tiles) / gsize;
   const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
-
   const int nkt = (int)(p.K_pad / BK);
-
-  // ---- global -> register staging, register -> LDS stores
-  v4i ra[A_CH], rb[B_CH];
-#define QG_LOAD_STAGE(KT)                                                                     \
-  {                                                                                           \
-    const int64_t k0_ = (int64_t)(KT) * BK;                                                   \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                        \
-      const int id = tid + i * NT;                                                            \
-      const int r = id / CPR, c = id % CPR;                                                   \
-      const int64_t m = m0 + r, k = k0_ + c * 16;                                             \
-      ra[i] = (m < p.M && k < p.K) ? *reinterpret_cast<const v4i*>(p.a + m * p.lda + k)       \
-                                   : v4i{0, 0, 0, 0};                                         \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                        \
-      const int id = tid + i * NT;                                                            \
-      const int r = id / CPR, c = id % CPR;                                                   \
-      rb[i] = *reinterpret_cast<const v4i*>(p.w + (n0 + r) * p.K_pad + k0_ + c * 16);         \
-    }                                                                                         \
-  }
-#define QG_STORE_STAGE(S)                                                                     \
-  {                                                                                           \
-    uint8_t* sa_ = smem + (S) * STAGE;                                                        \
-    uint8_t* sb_ = sa_ + BM * BK;                                                             \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                        \
-      const int id = tid + i * NT;                                                            \
-      const int r = id / CPR, c = id % CPR;                                                   \
-      v4i v = ra[i];                                                                          \
-      if (ASYM) v ^= (int)0x80808080u;                                                        \
-      *reinterpret_cast<v4i*>(sa_ + lds_off<BK>(r, c)) = v;                                   \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                        \
-      const int id = tid + i * NT;                                                            \
-      const int r = id / CPR, c = id % CPR;                                                   \
-      *reinterpret_cast<v4i*>(sb_ + lds_off<BK>(r, c)) = rb[i];                               \
-    }                                                                                         \
-  }
-
-  // ---- MX scales: per lane, one E8M0 byte per (fragment, 64-deep step)
-  constexpr int KS = MX ? BK / 64 : 1;
-  int esa[MX ? FM * KS : 1], esb[MX ? FN * KS : 1];
   const int64_t kblocks = p.K / 32;
-#define QG_LOAD_SCALES(KT)                                                                    \
-  if constexpr (MX) {                                                                         \
-    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                       \
-      const int64_t blk = ((int64_t)(KT) * BK + ks * 64) / 32 + (lane >> 5);                  \
-      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                        \
-        const int64_t m = m0 + wm * TM + i * 32 + (lane & 31);                                \
-        esa[ks * FM + i] = (m < p.M && blk < kblocks) ? (int)p.ea[m * p.lda_s + blk] : 127;   \
-      }                                                                                       \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                        \
-        const int64_t n = n0 + wn * TN + j * 32 + (lane & 31);                                \
-        esb[ks * FN + j] = (int)p.ew[n * (p.K_pad / 32) + blk];                               \
-      }                                                                                       \
-    }                                                                                         \
+  const int64_t wblocks = p.K_pad / 32;
+
+  // ---- global -> register staging (and, for MXB, the scale of each chunk).
+  // Two register sets: while the matrix cores consume stage kt from LDS, set
+  // (kt+1)&1 already holds stage kt+1 and stage kt+2 is in flight into the
+  // other set, so global latency is covered by two stages of matrix work.
+  v4i ra0[A_CH], rb0[B_CH], ra1[A_CH], rb1[B_CH];
+  int ea0[MODE == MXB ? A_CH : 1], eb0[MODE == MXB ? B_CH : 1];
+  int ea1[MODE == MXB ? A_CH : 1], eb1[MODE == MXB ? B_CH : 1];
+#define QG_LOAD_STAGE(KT, RA, RB_, EA, EB)                                                      \
+  {                                                                                             \
+    const int64_t k0_ = (int64_t)(KT) * BK;                                                     \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                          \
+      const int id = tid + i * NT;                                                              \
+      const int r = id / CPR, c = id % CPR;                                                     \
+      /* Unconditional load from a clamped address: no branch and no use of the */             \
+      /* value before the LDS store, so the loads stay in flight. Rows >= M only */             \
+      /* feed outputs that are never stored; columns >= K meet zero weights (and */             \
+      /* are zeroed at the store for MX, where a stray code could be NaN). */                   \
+      const int64_t m = min(m0 + r, p.M - 1), k = k0_ + c * 16;                                  \
+      const int64_t kc = k < p.K ? k : 0;                                                       \
+      RA[i] = *reinterpret_cast<const v4i*>(p.a + m * p.lda + kc);                              \
+      if constexpr (MODE == MXB) EA[i] = (int)p.ea[m * p.lda_s + (kc >> 5)];                    \
+    }                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                          \
+      const int id = tid + i * NT;                                                              \
+      const int r = id / CPR, c = id % CPR;                                                     \
+      const int64_t n = n0 + r, k = k0_ + c * 16;                                               \
+      RB_[i] = *reinterpret_cast<const v4i*>(p.w + n * p.K_pad + k);                            \
+      if constexpr (MODE == MXB) EB[i] = (int)p.ew[n * wblocks + (k >> 5)];                     \
+    }                                                                                           \
+  }
+#define QG_STORE_STAGE(KT, S, RA, RB_, EA, EB)                                                  \
+  {                                                                                             \
+    uint8_t* sa_ = smem + (S) * STAGE;                                                          \
+    uint8_t* sb_ = sa_ + BM * RB;                                                               \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                          \
+      const int id = tid + i * NT;                                                              \
+      const int r = id / CPR, c = id % CPR;                                                     \
+      if constexpr (MX) {                                                                       \
+        if ((int64_t)(KT) * BK + c * 16 >= p.K) RA[i] = v4i{0, 0, 0, 0};                        \
+      }                                                                                         \
+      if constexpr (MODE == MXB) {                                                              \
+        v4i lo, hi;                                                                             \
+        fp8x16_to_bf16(RA[i], e8m0_to_f32(EA[i]), lo, hi);                                      \
+        *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, 2 * c)) = lo;                              \
+        *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, 2 * c + 1)) = hi;                          \
+      } else {                                                                                  \
+        v4i v = RA[i];                                                                          \
+        if (ASYM) v ^= (int)0x80808080u;                                                        \
+        *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, c)) = v;                                   \
+      }                                                                                         \
+    }                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                          \
+      const int id = tid + i * NT;                                                              \
+      const int r = id / CPR, c = id % CPR;                                                     \
+      if constexpr (MODE == MXB) {                                                              \
+        v4i lo, hi;                                                                             \
+        fp8x16_to_bf16(RB_[i], e8m0_to_f32(EB[i]), lo, hi);                                     \
+        *reinterpret_cast<v4i*>(sb_ + lds_off<RB>(r, 2 * c)) = lo;                              \
+        *reinterpret_cast<v4i*>(sb_ + lds_off<RB>(r, 2 * c + 1)) = hi;                          \
+      } else {                                                                                  \
+        *reinterpret_cast<v4i*>(sb_ + lds_off<RB>(r, c)) = RB_[i];                              \
+      }                                                                                         \
+    }                                                                                           \
+  }
+
+  // ---- MXF: per lane one E8M0 byte per (fragment, 64-deep step), loaded a stage ahead
+  constexpr int KS = MODE == MXF ? BK / 64 : 1;
+  int esa[MODE == MXF ? FM * KS : 1], esb[MODE == MXF ? FN * KS : 1];
+  int nsa[MODE == MXF ? FM * KS : 1], nsb[MODE == MXF ? FN * KS : 1];
+#define QG_LOAD_SCALES(KT, DA, DB)                                                              \
+  if constexpr (MODE == MXF) {                                                                  \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                         \
+      const int64_t blk = ((int64_t)(KT) * BK + ks * 64) / 32 + (lane >> 5);                    \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                          \
+        /* clamped row and block: a valid E8M0 byte; rows >= M are never stored */            \
+        /* and the data of blocks >= K/32 are zeroed */                                        \
+        const int64_t m = min(m0 + wm * TM + i * 32 + (lane & 31), p.M - 1);                    \
+        DA[ks * FM + i] = (int)p.ea[m * p.lda_s + min(blk, kblocks - 1)];                       \
+      }                                                                                         \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                          \
+        const int64_t n = n0 + wn * TN + j * 32 + (lane & 31);                                  \
+        DB[ks * FN + j] = (int)p.ew[n * wblocks + blk];                                         \
+      }                                                                                         \
+    }                                                                                           \
   }
 
   typedef typename std::conditional<MX, v16f, v16i>::type acc_t;
@@ -146,165 +222,233 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-  QG_LOAD_STAGE(0)
-  QG_STORE_STAGE(0)
+#define QG_COMPUTE(S)                                                                           \
+  {                                                                                             \
+    const uint8_t* sa = smem + (S) * STAGE;                                                     \
+    const uint8_t* sb = sa + BM * RB;                                                           \
+    if constexpr (MODE == I8) {                                                                 \
+      _Pragma("unroll") for (int kk = 0; kk < BK / 32; ++kk) {                                  \
+        const int ch = kk * 2 + (lane >> 5);                                                    \
+        v4i af[FM], bf[FN];                                                                     \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] =                                  \
+            *reinterpret_cast<const v4i*>(sa + lds_off<RB>(wm * TM + i * 32 + (lane & 31), ch)); \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) bf[j] =                                  \
+            *reinterpret_cast<const v4i*>(sb + lds_off<RB>(wn * TN + j * 32 + (lane & 31), ch)); \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
+          _Pragma("unroll") for (int j = 0; j < FN; ++j)                                        \
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0); \
+        __builtin_amdgcn_sched_barrier(0); /* keep one sub-step of fragments live */            \
+      }                                                                                         \
+    } else if constexpr (MODE == MXB) {                                                         \
+      /* 16-deep bf16 steps: lane 32h + r holds K 8h..8h+7 of the step */                      \
+      _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                                  \
+        const int ch = kk * 2 + (lane >> 5);                                                    \
+        v8bf af[FM], bf[FN];                                                                    \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] =                                  \
+            *reinterpret_cast<const v8bf*>(sa + lds_off<RB>(wm * TM + i * 32 + (lane & 31), ch)); \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) bf[j] =                                  \
+            *reinterpret_cast<const v8bf*>(sb + lds_off<RB>(wn * TN + j * 32 + (lane & 31), ch)); \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
+          _Pragma("unroll") for (int j = 0; j < FN; ++j)                                        \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0); \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+      }                                                                                         \
+    } else {                                                                                    \
+      /* 64-deep scaled fp8 steps: lane 32h + r holds K 16h.. and 32+16h.. */                   \
+      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                       \
+        const int c0 = ks * 4 + (lane >> 5), c1 = c0 + 2;                                       \
+        v8i af[FM], bf[FN];                                                                     \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                        \
+          const int r = wm * TM + i * 32 + (lane & 31);                                         \
+          const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<RB>(r, c0));                \
+          const v4i hi = *reinterpret_cast<const v4i*>(sa + lds_off<RB>(r, c1));                \
+          af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                  \
+        }                                                                                       \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                        \
+          const int r = wn * TN + j * 32 + (lane & 31);                                         \
+          const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<RB>(r, c0));                \
+          const v4i hi = *reinterpret_cast<const v4i*>(sb + lds_off<RB>(r, c1));                \
+          bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                  \
+        }                                                                                       \
+        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
+          _Pragma("unroll") for (int j = 0; j < FN; ++j)                                        \
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                        \
+                af[i], bf[j], acc[i][j], 0, 0, 0, esa[ks * FM + i], 0, esb[ks * FN + j]);       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+      }                                                                                         \
+    }                                                                                           \
+  }
+#define QG_NEXT_SCALES()                                                                        \
+  if constexpr (MODE == MXF) {                                                                  \
+    _Pragma("unroll") for (int t = 0; t < FM * KS; ++t) esa[t] = nsa[t];                        \
+    _Pragma("unroll") for (int t = 0; t < FN * KS; ++t) esb[t] = nsb[t];                        \
+  }
+
+  QG_LOAD_SCALES(0, esa, esb)
+  QG_LOAD_STAGE(0, ra0, rb0, ea0, eb0)
+  QG_STORE_STAGE(0, 0, ra0, rb0, ea0, eb0)
+  QG_LOAD_STAGE(1, ra1, rb1, ea1, eb1)
   __syncthreads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    QG_LOAD_SCALES(kt)
-    if (kt + 1 < nkt) QG_LOAD_STAGE(kt + 1)
-    const uint8_t* sa = smem + cur * STAGE;
-    const uint8_t* sb = sa + BM * BK;
-    if constexpr (!MX) {
-#pragma unroll
-      for (int kk = 0; kk < BK / 32; ++kk) {
-        const int ch = kk * 2 + (lane >> 5);
-        v4i af[FM], bf[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[i] = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(wm * TM + i * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bf[j] = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(wn * TN + j * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        // lane 32h + r: bytes 0..15 = K 16h.., bytes 16..31 = K 32+16h.. of this 64-deep step
-        const int c0 = ks * 4 + (lane >> 5), c1 = c0 + 2;
-        v8i af[FM], bf[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * TM + i * 32 + (lane & 31);
-          v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, c0));
-          v4i hi = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, c1));
-          af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int r = wn * TN + j * 32 + (lane & 31);
-          v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, c0));
-          v4i hi = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, c1));
-          bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[i], bf[j], acc[i][j], 0, 0, 0, esa[ks * FM + i], 0, esb[ks * FN + j]);
-      }
-    }
-    if (kt + 1 < nkt) QG_STORE_STAGE(cur ^ 1)
+  // nkt is even: the packed K is a multiple of 256 and BK divides 128. The
+  // body is branch-free (the last stage is simply fetched again at the end),
+  // so the compiler can wait for exactly the older register set.
+  for (int kt = 0; kt < nkt; kt += 2) {
+    // even stage kt: LDS buffer 0; set 1 holds stage kt+1; stage kt+2 goes into set 0
+    QG_LOAD_STAGE(min(kt + 2, nkt - 1), ra0, rb0, ea0, eb0)
+    QG_LOAD_SCALES(kt + 1, nsa, nsb)
+    QG_COMPUTE(0)
+    QG_STORE_STAGE(kt + 1, 1, ra1, rb1, ea1, eb1)
+    QG_NEXT_SCALES()
+    __syncthreads();
+    // odd stage kt+1: LDS buffer 1; set 0 holds stage kt+2; stage kt+3 goes into set 1
+    QG_LOAD_STAGE(min(kt + 3, nkt - 1), ra1, rb1, ea1, eb1)
+    QG_LOAD_SCALES(min(kt + 2, nkt - 1), nsa, nsb)
+    QG_COMPUTE(1)
+    QG_STORE_STAGE(kt + 2, 0, ra0, rb0, ea0, eb0)
+    QG_NEXT_SCALES()
     __syncthreads();
   }
 #undef QG_LOAD_STAGE
 #undef QG_STORE_STAGE
 #undef QG_LOAD_SCALES
+#undef QG_COMPUTE
+#undef QG_NEXT_SCALES
 
-  // ---- epilogue: lane l of a 32x32 block holds column l%32 and rows
-  // 8*(e/4) + 4*(l/32) + e%4 for its 16 values e. The tile's per-row scale
-  // and zero point are staged in LDS (free after the last barrier).
-  float* s_sa = reinterpret_cast<float*>(smem);
-  int* s_z = reinterpret_cast<int*>(smem + BM * 4);
-  if constexpr (!MX && OUT != 2) {
-    for (int r = tid; r < BM; r += NT) {
-      const int64_t m = m0 + r;
-      s_sa[r] = m < p.M ? (p.a_per_tensor ? p.sa[0] : p.sa[m]) : 0.f;
-    }
-  }
-  if constexpr (!MX && ASYM) {
-    for (int r = tid; r < BM; r += NT) {
-      const int64_t m = m0 + r;
-      s_z[r] = m < p.M ? (p.a_per_tensor ? p.za[0] : p.za[m]) : 0;
-    }
-  }
-  if constexpr (!MX && (ASYM || OUT != 2)) __syncthreads();
-
+  // ---- epilogue through LDS. Lane l of a 32x32 block holds column l%32 and
+  // rows 8*(e/4) + 4*(l/32) + e%4 of its 16 values e. Each wave writes one
+  // 32-row slab of its sub-tile to its own LDS region, then reads it back row
+  // by row so that every lane finishes 4 consecutive columns of one row.
+  constexpr int LPR = TN / 4;        // lanes per row on the way out
+  constexpr int RPI = 64 / LPR;      // rows per read-back pass
+  constexpr int RS = C::RS;
+  uint8_t* wreg = smem + wid * (32 * RS * 4);
+  const int cq = (lane % LPR) * 4;   // this lane's first column inside the wave tile
+  const int64_t nq = n0 + wn * TN + cq;
+  float sw4[4] = {0.f, 0.f, 0.f, 0.f};
+  int cs4[4] = {0, 0, 0, 0};
+  if constexpr (!MX) {
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int64_t n = n0 + wn * TN + j * 32 + (lane & 31);
-    const bool n_ok = n < p.N;
-    float sw = 0.f;
-    int cs = 0;
-    if constexpr (!MX) {
-      if (n_ok) {
-        sw = p.w_per_tensor ? p.sw[0] : p.sw[n];
-        if (ASYM) cs = p.colsum[n];
+    for (int t = 0; t < 4; ++t) {
+      if (nq + t < p.N) {
+        sw4[t] = p.w_per_tensor ? p.sw[0] : p.sw[nq + t];
+        if (ASYM) cs4[t] = p.colsum[nq + t];
       }
     }
+  }
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int r = wm * TM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int64_t m = m0 + r;
-        if (!(n_ok && m < p.M)) continue;
+        const int r = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        int bits;
+        if constexpr (MX)
+          bits = __float_as_int(acc[i][j][e]);
+        else
+          bits = acc[i][j][e];
+        reinterpret_cast<int*>(wreg)[r * RS + j * 32 + (lane & 31)] = bits;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPI; ++pass) {
+      const int r = pass * RPI + lane / LPR;
+      const int64_t m = m0 + wm * TM + i * 32 + r;
+      const v4i raw = *reinterpret_cast<const v4i*>(wreg + (r * RS + cq) * 4);
+      if (m < p.M && nq < p.N) {
+        float y[4];
+        int ci[4];
         if constexpr (MX) {
-          reinterpret_cast<float*>(p.out)[m * p.ldo + n] = acc[i][j][e];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) y[t] = __int_as_float(raw[t]);
         } else {
-          int c = acc[i][j][e];
-          if (ASYM) {
+          const float sam = p.a_per_tensor ? p.sa[0] : p.sa[m];
+          const int zm = ASYM ? (p.a_per_tensor ? p.za[0] : p.za[m]) : 0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            int c = raw[t];
             // wrap-around int32 arithmetic: the true C fits, so the result is exact
-            c = (int)((uint32_t)c - (uint32_t)(s_z[r] - 128) * (uint32_t)cs);
+            if (ASYM) c = (int)((uint32_t)c - (uint32_t)(zm - 128) * (uint32_t)cs4[t]);
+            ci[t] = c;
+            y[t] = (float)c * (sam * sw4[t]);
           }
-          if constexpr (OUT == 2) {
-            reinterpret_cast<int32_t*>(p.out)[m * p.ldo + n] = c;
+        }
+        const bool full = nq + 3 < p.N;
+        if constexpr (OUT == 2) {
+          int32_t* o = reinterpret_cast<int32_t*>(p.out) + m * p.ldo + nq;
+          if (full)
+            *reinterpret_cast<v4i*>(o) = v4i{ci[0], ci[1], ci[2], ci[3]};
+          else
+            for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = ci[t];
+        } else if constexpr (OUT == 0) {
+          float* o = reinterpret_cast<float*>(p.out) + m * p.ldo + nq;
+          if (full)
+            *reinterpret_cast<v4f*>(o) = v4f{y[0], y[1], y[2], y[3]};
+          else
+            for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = y[t];
+        } else {
+          uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + m * p.ldo + nq;
+          uint16_t h[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) h[t] = f32_to_bf16_rne(y[t]);
+          if (full) {
+            uint2 v;
+            v.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+            v.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+            *reinterpret_cast<uint2*>(o) = v;
           } else {
-            const float y = (float)c * (s_sa[r] * sw);
-            if constexpr (OUT == 0)
-              reinterpret_cast<float*>(p.out)[m * p.ldo + n] = y;
-            else
-              reinterpret_cast<uint16_t*>(p.out)[m * p.ldo + n] = f32_to_bf16_rne(y);
+            for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = h[t];
           }
         }
       }
     }
+    __syncthreads();
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool MX, bool ASYM, int OUT>
+template <int BM, int BN, int BK, int WM, int WN, int MODE, bool ASYM, int OUT>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
-  auto kern = gemm_kernel<BM, BN, BK, WM, WN, MX, ASYM, OUT>;
-  const size_t lds = (size_t)2 * (BM + BN) * BK;
+  using C = GemmCfg<BM, BN, BK, WM, WN, MODE, ASYM, OUT>;
+  auto kern = gemm_kernel<BM, BN, BK, WM, WN, MODE, ASYM, OUT>;
+  const size_t lds = C::LDS;
   if (lds > 65536) {  // above the default dynamic-LDS limit (gfx950 has 160 KiB)
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(WM * WN * 64), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::NT), lds, st, a);
   return hipGetLastError();
 }
 
-template <bool MX, bool ASYM, int OUT>
+template <int MODE, bool ASYM, int OUT>
 static hipError_t launch_pick(const GemmArgs& a, hipStream_t st) {
-  // Large problems: 256x256 tiles (4 waves of 128x128); otherwise 128x128.
+  // Large problems: 256x256 tiles (8 waves of 128x64); otherwise 128x128 (4 waves of 64x64).
+  // K steps of 128 bytes for the 1-byte operands; the bf16 staging of the
+  // exact MX mode doubles the LDS row, so it steps 64 deep.
+  constexpr int BK = MODE == MXB ? 64 : 128;
+  constexpr int BK_BIG = MODE == I8 ? 128 : 64;  // the scaled-fp8 scales need registers too
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big_tiles >= 256) return launch_cfg<256, 256, 64, 2, 2, MX, ASYM, OUT>(a, st);
-  return launch_cfg<128, 128, 64, 2, 2, MX, ASYM, OUT>(a, st);
+  if (big_tiles >= 256) return launch_cfg<256, 256, BK_BIG, 2, 4, MODE, ASYM, OUT>(a, st);
+  return launch_cfg<128, 128, BK, 2, 2, MODE, ASYM, OUT>(a, st);
 }
 
 hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   if (asym) {
-    if (out_type == 0) return launch_pick<false, true, 0>(a, st);
-    if (out_type == 1) return launch_pick<false, true, 1>(a, st);
-    return launch_pick<false, true, 2>(a, st);
+    if (out_type == 0) return launch_pick<I8, true, 0>(a, st);
+    if (out_type == 1) return launch_pick<I8, true, 1>(a, st);
+    return launch_pick<I8, true, 2>(a, st);
   }
-  if (out_type == 0) return launch_pick<false, false, 0>(a, st);
-  if (out_type == 1) return launch_pick<false, false, 1>(a, st);
-  return launch_pick<false, false, 2>(a, st);
+  if (out_type == 0) return launch_pick<I8, false, 0>(a, st);
+  if (out_type == 1) return launch_pick<I8, false, 1>(a, st);
+  return launch_pick<I8, false, 2>(a, st);
 }
 
-hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  return launch_pick<true, false, 0>(a, st);
+  if (mode == 1) return launch_pick<MXF, false, 0>(a, st);
+  return launch_pick<MXB, false, 0>(a, st);
 }
 
 }  // namespace qg

@@ -37,7 +37,8 @@ struct GemmArgs {
 
 // qgemm_run: int8 GEMM + epilogue. out_type: 0 f32, 1 bf16, 2 i32.
 hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_t st);
-// qgemm_run_mx: block-scaled e4m3 GEMM, float32 output.
-hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t st);
+// qgemm_run_mx: block-scaled e4m3 GEMM, float32 output. mode 0: exact products
+// (bf16 matrix cores on dequantized values), mode 1: block-scaled fp8 matrix cores.
+hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st);
 
 }  // namespace qg

@@ -118,11 +118,17 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
   RowStats st;
   st.lo = INFINITY;
   st.hi = ASYM ? -INFINITY : 0.0f;
+  // All of this thread's loads are issued before any is used (clamped
+  // addresses, no branches), so their latencies overlap.
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int64_t k = 4 * ((int64_t)t + (int64_t)kRowThreads * u);
+    v[u] = *reinterpret_cast<const float4*>(xr + (k + 4 <= K ? k : 0));
+  }
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int64_t k = 4 * ((int64_t)t + (int64_t)kRowThreads * u);
     if (k + 4 <= K) {
-      v[u] = *reinterpret_cast<const float4*>(xr + k);
       stats_update<ASYM>(st, v[u].x);
       stats_update<ASYM>(st, v[u].y);
       stats_update<ASYM>(st, v[u].z);
@@ -272,14 +278,20 @@ __global__ __launch_bounds__(kRowThreads) void tensor_scale_kernel(const float* 
 
 // MXFP8: grid (rows, ceil(K / 1024)); each thread one float4, eight threads
 // per 32-element block.
+template <bool VEC>
 __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __restrict__ x, int64_t ldx,
                                                                int64_t K, uint8_t* __restrict__ q, int64_t ldq,
                                                                uint8_t* __restrict__ e8, int64_t lde) {
   const int64_t row = blockIdx.x;
   const int64_t k = (int64_t)blockIdx.y * (4 * kRowThreads) + 4 * threadIdx.x;
   const bool valid = k < K;  // K % 32 == 0: a block's eight lanes agree
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (valid) v = *reinterpret_cast<const float4*>(x + row * ldx + k);
+  const float* xr = x + row * ldx + (valid ? k : 0);
+  float4 v;
+  if (VEC)
+    v = *reinterpret_cast<const float4*>(xr);
+  else
+    v = make_float4(xr[0], xr[1], xr[2], xr[3]);
+  if (!valid) v = make_float4(0.f, 0.f, 0.f, 0.f);
   float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   a = fmaxf(a, __shfl_xor(a, 1, kWave));
   a = fmaxf(a, __shfl_xor(a, 2, kWave));
@@ -290,7 +302,15 @@ __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __re
   if (!valid) return;
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(v.x * inv, v.y * inv, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(v.z * inv, v.w * inv, w, true);
-  *reinterpret_cast<uint32_t*>(q + row * ldq + k) = (uint32_t)w;
+  uint8_t* qr = q + row * ldq + k;
+  if (VEC) {
+    *reinterpret_cast<uint32_t*>(qr) = (uint32_t)w;
+  } else {
+    qr[0] = (uint8_t)w;
+    qr[1] = (uint8_t)(w >> 8);
+    qr[2] = (uint8_t)(w >> 16);
+    qr[3] = (uint8_t)(w >> 24);
+  }
   if ((threadIdx.x & 7) == 0) e8[row * lde + (k >> 5)] = (uint8_t)E;
 }
 
@@ -301,7 +321,10 @@ template <bool ASYM, bool PRECOMP>
 static void launch_rows(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
                         float* scales, int32_t* zeros, int32_t* colsum, hipStream_t st) {
   dim3 grid((unsigned)rows), block(kRowThreads);
-  if (K <= 1024)
+  const bool vec = ldx % 4 == 0 && ((uintptr_t)x % 16) == 0 && ldq % 4 == 0 && ((uintptr_t)q % 4) == 0;
+  if (!vec)
+    quant_rows_long_kernel<ASYM, PRECOMP><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+  else if (K <= 1024)
     quant_rows_kernel<ASYM, PRECOMP, 1><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
   else if (K <= 2048)
     quant_rows_kernel<ASYM, PRECOMP, 2><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
@@ -340,7 +363,11 @@ void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, ui
                         uint8_t* e8, int64_t lde, hipStream_t st) {
   if (rows == 0) return;
   dim3 grid((unsigned)rows, (unsigned)((K + 4 * kRowThreads - 1) / (4 * kRowThreads))), block(kRowThreads);
-  quant_mx_kernel<<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+  const bool vec = ldx % 4 == 0 && ((uintptr_t)x % 16) == 0 && ldq % 4 == 0 && ((uintptr_t)q % 4) == 0;
+  if (vec)
+    quant_mx_kernel<true><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+  else
+    quant_mx_kernel<false><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
 }
 
 }  // namespace qg

@@ -17,6 +17,7 @@ from . import _lib as L
 FMT_INT8_SYM, FMT_UINT8_ASYM, FMT_MXFP8_E4M3 = 0, 1, 2
 GRAN_TENSOR, GRAN_ROW, GRAN_BLOCK32 = 0, 1, 2
 OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
+MX_EXACT, MX_SCALED_MFMA = 0, 1
 
 _OUT_DTYPES = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_I32: torch.int32}
 
@@ -178,7 +179,7 @@ def qgemm_run(a: QuantizedRows, w: PackedWeights, out_type: int = OUT_F32,
 
 
 def qgemm_run_mx(a: QuantizedRows, w: PackedWeights, out: Optional[torch.Tensor] = None,
-                 stream=None) -> torch.Tensor:
+                 mode: int = MX_EXACT, stream=None) -> torch.Tensor:
     """Block-scaled e4m3 GEMM (float32 out); returns out[:, :N]."""
     lib = L.load()
     dev = a.q.device
@@ -186,7 +187,7 @@ def qgemm_run_mx(a: QuantizedRows, w: PackedWeights, out: Optional[torch.Tensor]
     if out is None:
         out = _alloc_out(a.M, N, torch.float32, dev)
     st = lib.qgemm_run_mx(_ptr(a.q), a.q.stride(0), _ptr(a.mx_scales), a.mx_scales.stride(0), a.M,
-                          ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0),
+                          ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0), mode,
                           None, 0, ctypes.c_void_p(_stream(dev, stream)))
     _check("qgemm_run_mx", st)
     return out[:, :N]

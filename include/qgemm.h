@@ -91,6 +91,25 @@ typedef enum {
 } qgemm_out_type;
 
 /*
+ * How qgemm_run_mx evaluates the block-scaled product (both apply every
+ * 32-element block's own pair of scales inside the K loop).
+ */
+typedef enum {
+  /* Exact products: each e4m3 value is multiplied by its block's power-of-two
+   * scale on the way into on-chip memory -- an exact operation whose result a
+   * bfloat16 holds exactly -- and the bf16 matrix cores form every product
+   * exactly and sum in float32. Error: float32 summation only. */
+  QGEMM_MX_EXACT = 0,
+  /* gfx950 block-scaled fp8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4),
+   * fed the e4m3 codes and one E8M0 byte per lane and block. Twice the peak
+   * rate of QGEMM_MX_EXACT, but inside each group of 8 consecutive K the
+   * hardware aligns the products to the largest one and drops the bits more
+   * than 13 binades below it (measured), so
+   * |out - exact| <= 2^-10 * sum_k |a_k w_k| plus float32 summation. */
+  QGEMM_MX_SCALED_MFMA = 1
+} qgemm_mx_mode;
+
+/*
  * Host-side descriptor of a prepared weight buffer ("checkpoint metadata":
  * [TL27] section 7, pitfall 10 -- record the granularity with the weights).
  * Filled by qgemm_prepack_weights; read by qgemm_run / qgemm_run_mx.
@@ -113,7 +132,7 @@ typedef struct qgemm_wdesc {
   int32_t gran;        /* qgemm_granularity                        */
   int64_t N, K;        /* logical sizes                            */
   int64_t N_pad;       /* N rounded up to a multiple of 256        */
-  int64_t K_pad;       /* K rounded up to a multiple of 128        */
+  int64_t K_pad;       /* K rounded up to a multiple of 256        */
   int64_t codes_off;
   int64_t scales_off;
   int64_t colsum_off;
@@ -161,7 +180,8 @@ size_t qgemm_workspace_bytes(int64_t rows, int64_t K, int fmt, int gran);
  *   against a float32 evaluation of the same formulas.
  *
  * Arguments:
- *   x            device, float32 [M][ldx], ldx >= K, ldx % 4 == 0, 16-byte aligned.
+ *   x            device, float32 [M][ldx], ldx >= K, 4-byte aligned (rows that start on
+ *                16-byte boundaries, ldx % 4 == 0, are read with 16-byte loads).
  *   M, K         M >= 0, K >= 1.
  *   fmt, gran    INT8_SYM or UINT8_ASYM with TENSOR or ROW; MXFP8_E4M3 with BLOCK32.
  *   q            device, codes [M][ldq] bytes, ldq >= K, ldq % 16 == 0, 16-byte aligned.
@@ -191,7 +211,7 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx,
  *   Writes the packed layout described at qgemm_wdesc (including zero padding)
  *   and fills *desc on the host.
  *
- *   w        device float32 [N][ldw], ldw >= K, ldw % 4 == 0, 16-byte aligned.
+ *   w        device float32 [N][ldw], ldw >= K, 4-byte aligned.
  *   packed   device, >= qgemm_packed_weight_bytes(N, K, fmt, gran) bytes, 256-byte aligned.
  *   desc     host, written on success only.
  *   workspace as for qgemm_quantize_rows with rows = N.
@@ -242,18 +262,22 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
  *              sum_{k in block b} e4m3(a[m,k]) * e4m3(w[n,k])
  *   Each 32-element K block is multiplied by its own pair of scales inside
  *   the K loop ([TL27] 4.1: (A*scale_A)(B*scale_B); 4.3: a per-K-block scale
- *   cannot be moved out of the sum). Products are exact; the sum is
- *   accumulated in float32 by the matrix cores. float32 output.
+ *   cannot be moved out of the sum). float32 accumulation and output; how
+ *   exactly the products and sums are formed depends on `mode`.
  *
  *   a_codes  device e4m3 [M][lda], lda >= K, lda % 16 == 0, 16-byte aligned.
  *   a_e8m0   device E8M0 [M][lda_s], lda_s >= K/32.
  *   w_desc   descriptor of MXFP8_E4M3 weights with the same K (K % 32 == 0).
  *   out      device float32 [M][ldo], ldo >= N, ldo % 4 == 0, 16-byte aligned.
+ *   mode     qgemm_mx_mode: QGEMM_MX_EXACT (products exact, float32 sums) or
+ *            QGEMM_MX_SCALED_MFMA (block-scaled fp8 matrix cores; see the enum).
+ *            Both need E8M0 codes in [3, 240] for exactness of the scaled values,
+ *            which qgemm_quantize_rows always produces for inputs below 2^120.
  *   workspace unused by this version (pass NULL, 0).
  */
 int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s,
                  int64_t M, const qgemm_wdesc* w_desc, const void* w_packed,
-                 float* out, int64_t ldo,
+                 float* out, int64_t ldo, int mode,
                  void* workspace, size_t workspace_bytes,
                  void* stream);
 

@@ -48,7 +48,7 @@ def test_version_and_status_strings(lib):
 
 def test_sizes(lib):
     # int8: codes [256][128] + scales 4*256 + colsum 4*256
-    assert lib.qgemm_packed_weight_bytes(1, 1, INT8, ROW) == 256 * 128 + 1024 + 1024
+    assert lib.qgemm_packed_weight_bytes(1, 1, INT8, ROW) == 256 * 256 + 1024 + 1024
     assert lib.qgemm_packed_weight_bytes(4096, 4096, INT8, ROW) == 4096 * 4096 + 4 * 4096 * 2
     assert lib.qgemm_packed_weight_bytes(8192, 8192, MX, BLK) == 8192 * 8192 + 8192 * 256
     assert lib.qgemm_packed_weight_bytes(64, 100, MX, BLK) == 0       # K % 32
@@ -80,9 +80,9 @@ def test_quantize_rows_validation(lib):
     assert _q(lib, fmt=UINT8, z=None) == E_NULL
     assert _q(lib, ldx=32) == E_SHAPE
     assert _q(lib, ldq=63) == E_SHAPE
-    assert _q(lib, ldx=66) == E_ALIGN
     assert _q(lib, ldq=80 + 8) == E_ALIGN
-    assert _q(lib, x=FAKE + 4) == E_ALIGN
+    assert _q(lib, x=FAKE + 2) == E_ALIGN
+    assert _q(lib, q=FAKE + 4) == E_ALIGN
     assert _q(lib, fmt=MX, gran=BLK, K=48, ldx=48, ldq=48, s=None, mx=FAKE, ldmx=2) == E_SHAPE
     assert _q(lib, fmt=MX, gran=BLK, s=None, mx=None) == E_NULL
     assert _q(lib, fmt=MX, gran=BLK, s=None, mx=FAKE, ldmx=1) == E_SHAPE
@@ -91,8 +91,8 @@ def test_quantize_rows_validation(lib):
 
 
 def _wdesc(**kw):
-    d = L.WDesc(magic=0x51474D57, version=1, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=384,
-                codes_off=0, scales_off=256 * 384, colsum_off=256 * 384 + 1024, bytes=256 * 384 + 2048)
+    d = L.WDesc(magic=0x51474D57, version=1, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
+                codes_off=0, scales_off=256 * 512, colsum_off=256 * 512 + 1024, bytes=256 * 512 + 2048)
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -109,7 +109,7 @@ def test_run_validation(lib):
     assert _run(lib, _wdesc(magic=1)) == E_DESC
     assert _run(lib, _wdesc(version=2)) == E_DESC
     assert _run(lib, _wdesc(fmt=MX)) == E_DESC
-    assert _run(lib, _wdesc(K_pad=512)) == E_DESC
+    assert _run(lib, _wdesc(K_pad=384)) == E_DESC
     assert _run(lib, _wdesc(bytes=5)) == E_DESC
     assert lib.qgemm_run(FAKE, 304, FAKE, None, INT8, ROW, 8, None, FAKE, FAKE, 100, 0, None, 0, None) == E_NULL
     assert _run(lib, good, fmt=MX) == E_MODE
@@ -125,27 +125,29 @@ def test_run_validation(lib):
     assert _run(lib, good, w=FAKE + 16) == E_ALIGN
     # exact-int32 limits on K
     nb = lib.qgemm_packed_weight_bytes(8, 133145, INT8, ROW)
-    big = _wdesc(N=8, K=133145, K_pad=133248, scales_off=256 * 133248, colsum_off=256 * 133248 + 1024,
+    big = _wdesc(N=8, K=133145, K_pad=133376, scales_off=256 * 133376, colsum_off=256 * 133376 + 1024,
                  bytes=nb)
     assert _run(lib, big, lda=133152) == E_OVERFLOW
     nb = lib.qgemm_packed_weight_bytes(8, 66312, INT8, ROW)
-    mid = _wdesc(N=8, K=66312, K_pad=66432, scales_off=256 * 66432, colsum_off=256 * 66432 + 1024, bytes=nb)
+    mid = _wdesc(N=8, K=66312, K_pad=66560, scales_off=256 * 66560, colsum_off=256 * 66560 + 1024, bytes=nb)
     assert _run(lib, mid, lda=66320, fmt=UINT8, z=FAKE) == E_OVERFLOW
 
 
 def test_run_mx_validation(lib):
     nb = lib.qgemm_packed_weight_bytes(100, 320, MX, BLK)
-    d = L.WDesc(magic=0x51474D57, version=1, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=384,
-                codes_off=0, scales_off=256 * 384, colsum_off=-1, bytes=nb)
+    d = L.WDesc(magic=0x51474D57, version=1, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
+                codes_off=0, scales_off=256 * 512, colsum_off=-1, bytes=nb)
     call = lambda **kw: lib.qgemm_run_mx(kw.get("a", FAKE), kw.get("lda", 320), kw.get("e", FAKE),
                                          kw.get("ldas", 10), kw.get("M", 4), ctypes.byref(kw.get("d", d)),
-                                         FAKE, kw.get("out", FAKE), kw.get("ldo", 100), None, 0, None)
+                                         FAKE, kw.get("out", FAKE), kw.get("ldo", 100), kw.get("mode", 0),
+                                         None, 0, None)
     assert call(d=_wdesc()) == E_DESC                     # an int8 descriptor
     assert call(e=None) == E_NULL
     assert call(ldas=9) == E_SHAPE
     assert call(lda=304) == E_SHAPE
     assert call(lda=328) == E_ALIGN
     assert call(M=0, a=None, e=None, out=None) == OK
+    assert call(mode=2) == E_MODE
 
 
 def test_prepack_validation(lib):

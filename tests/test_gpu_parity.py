@@ -36,6 +36,8 @@ def dev(a):
 
 def host(t):
     torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy()
 
 
@@ -236,16 +238,41 @@ def test_gemm_empty_m(ops):
 # ---------------------------------------------------------------------------
 # MXG: block-scaled GEMM
 # ---------------------------------------------------------------------------
+MX_SCALED_STOL = 2.0 ** -10   # derived in qgemm.h from the measured 13-binade window per 8-K group
+
+
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (33, 65, 96), (130, 260, 320), (64, 64, 1024),
-                                   (300, 200, 2080), (257, 300, 4096)])
-def test_gemm_mx_parity(ops, M, N, K):
-    print_case("gemm mx", M, N, K)
+                                   (300, 200, 2080), (257, 300, 4096), (520, 530, 1024)])
+def test_gemm_mx_parity(ops, M, N, K, mode):
+    print_case("gemm mx", M, N, K, "mode", mode)
     A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=M * 13 + N + K)
     a = ops.qgemm_quantize_rows(dev(A), 2, 2)
     pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
-    got = host(ops.qgemm_run_mx(a, pw)).astype(np.float64)
+    got = host(ops.qgemm_run_mx(a, pw, mode=mode)).astype(np.float64)
     qa, Ea = O.quantize_mx(A)
     qw, Ew = O.quantize_mx(W)
     ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew)
     err = np.abs(got - ref)
-    assert (err <= MX_STOL * S).all(), (err / np.maximum(S, 1e-300)).max()
+    tol = MX_STOL if mode == 0 else MX_SCALED_STOL
+    assert (err <= tol * S).all(), (err / np.maximum(S, 1e-300)).max()
+    if mode == 0:
+        assert O.metrics.rel_l2(got, ref) < 1e-6
+
+
+def test_gemm_mx_modes_on_an_8_group_with_a_wide_exponent_spread(ops):
+    """448 and 2^-6 in one group of 8 K: exact mode keeps the small product;
+    the block-scaled fp8 matrix cores drop it (the behaviour qgemm.h documents)."""
+    A = np.zeros((1, 32), np.float32)
+    A[0, 0], A[0, 1] = 448.0, 2.0 ** -6
+    W = np.ones((1, 32), np.float32)
+    a = ops.qgemm_quantize_rows(dev(A), 2, 2)
+    pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
+    qa, Ea = O.quantize_mx(A)
+    qw, Ew = O.quantize_mx(W)
+    ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew)
+    assert ref[0, 0] == 448.0 + 2.0 ** -6
+    exact = host(ops.qgemm_run_mx(a, pw, mode=0))[0, 0]
+    mfma = host(ops.qgemm_run_mx(a, pw, mode=1))[0, 0]
+    assert exact == ref[0, 0]
+    assert mfma == 448.0 and abs(mfma - ref[0, 0]) <= MX_SCALED_STOL * S[0, 0]
