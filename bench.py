@@ -155,6 +155,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough to exceed the MALL 3x)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="after the timed region, copy MIB MiB device-to-device: a plain copy of known size "
+                         "whose FETCH_SIZE / WRITE_SIZE counters calibrate the GEMM's traffic")
     ap.add_argument("--mx-mode", default="exact", choices=["exact", "scaled-mfma"],
                     help="MX workload: exact products (bf16 matrix cores) or block-scaled fp8 matrix cores")
     args = ap.parse_args()
@@ -273,6 +276,14 @@ def main():
                    "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9},
         "roofline": roof,
     }
+    if args.calibration_copy:
+        nb = args.calibration_copy << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] {name}: {ms_per_step * 1e3:.2f} us/step, gemm {gemm_ms * 1e3:.2f} us, "
           f"wall {wall:.3f} s for {K_steps} steps", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:

@@ -407,6 +407,252 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Deep pipeline for the 1-byte operand path (int8): the tiles travel from
+// global memory straight into an NS-stage LDS ring (global_load_lds_dwordx4:
+// each lane's 16 bytes land at the wave's LDS block + 16 * lane), so no
+// registers hold staged data and NS - 1 stages are in flight. One explicit
+// vmcnt wait and one barrier per K step; the fragments of sub-step kk + 1 are
+// read while the matrix cores work on sub-step kk.
+// ---------------------------------------------------------------------------
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+#define QG_LDSP(x) ((__attribute__((address_space(3))) void*)(x))
+
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool ASYM, int OUT>
+struct DmaCfg {
+  static constexpr int NT = WM * WN * 64, NW = WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int RB = BK;                       // one byte per element
+  static constexpr int STAGE = (BM + BN) * RB;
+  static constexpr int IPS = STAGE / 1024;            // 1 KB wave loads per stage
+  static constexpr int IPW = IPS / NW;                // ... per wave
+  static constexpr int RS = TN + 8;
+  static constexpr int EPI = NW * 32 * RS * 4;
+  static constexpr int EPI_ALL = EPI + BM * 8;        // + per-row scale and zero point
+  static constexpr int LDS = NS * STAGE > EPI_ALL ? NS * STAGE : EPI_ALL;
+  static_assert(STAGE % 1024 == 0 && IPS % NW == 0 && (BM * RB) % 1024 == 0, "stage / wave-load mismatch");
+  static_assert(NS >= 2 && (NS - 2) * IPW < 64, "vmcnt range");
+  static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool ASYM, int OUT>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
+  using C = DmaCfg<BM, BN, BK, WM, WN, NS, ASYM, OUT>;
+  constexpr int NT = C::NT, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, RB = C::RB;
+  constexpr int STAGE = C::STAGE, IPW = C::IPW;
+  (void)NT;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
+  const int ntiles = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  {
+    const int per = ntiles / 8;
+    if (per > 0 && pid < per * 8) pid = (pid % 8) * per + pid / 8;
+  }
+  constexpr int GROUP = 8;
+  const int group_tiles = GROUP * tiles_n;
+  const int g = pid / group_tiles;
+  const int first_m = g * GROUP;
+  const int gsize = min(tiles_m - first_m, GROUP);
+  const int tile_m = first_m + (pid % group_tiles) % gsize;
+  const int tile_n = (pid % group_tiles) / gsize;
+  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+  const int nkt = (int)(p.K_pad / BK);
+
+  // Per-lane global source of each of this wave's 1 KB loads, relative to the
+  // stage's K offset. A rows >= M are clamped (their outputs are never stored);
+  // A columns >= K are redirected to column 0 (they meet zero weights).
+#define QG_DMA_STAGE(KT, S)                                                                       \
+  {                                                                                               \
+    const int64_t k0_ = (int64_t)(KT) * BK;                                                       \
+    _Pragma("unroll") for (int i = 0; i < IPW; ++i) {                                             \
+      const int b = wid * IPW + i;                                                                \
+      const int P = b * 1024 + lane * 16;                                                         \
+      const uint8_t* src;                                                                         \
+      if (b * 1024 < BM * RB) {                                                                   \
+        const int r = P / RB, c = ((P % RB) >> 4) ^ ((r / (RB >= 256 ? 1 : 256 / RB)) % (RB / 16)); \
+        const int64_t m = min(m0 + r, p.M - 1), k = k0_ + c * 16;                                 \
+        src = p.a + m * p.lda + (k < p.K ? k : 0);                                                \
+      } else {                                                                                    \
+        const int P2 = P - BM * RB;                                                               \
+        const int r = P2 / RB, c = ((P2 % RB) >> 4) ^ ((r / (RB >= 256 ? 1 : 256 / RB)) % (RB / 16)); \
+        src = p.w + (n0 + r) * p.K_pad + k0_ + c * 16;                                            \
+      }                                                                                           \
+      __builtin_amdgcn_global_load_lds(src, QG_LDSP(smem + (S) * STAGE + b * 1024), 16, 0, 0);   \
+    }                                                                                             \
+  }
+
+  v16i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+#define QG_LOAD_FRAGS(BUF, KK, FA, FB)                                                            \
+  {                                                                                               \
+    const uint8_t* sa_ = smem + (BUF) * STAGE;                                                    \
+    const int ch_ = (KK) * 2 + (lane >> 5);                                                       \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) FA[i] =                                        \
+        *reinterpret_cast<const v4i*>(sa_ + lds_off<RB>(wm * TM + i * 32 + (lane & 31), ch_));    \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) FB[j] = *reinterpret_cast<const v4i*>(         \
+        sa_ + BM * RB + lds_off<RB>(wn * TN + j * 32 + (lane & 31), ch_));                        \
+  }
+  constexpr int NKK = BK / 32;
+  static_assert(NKK % 2 == 0, "fragment double buffer parity");
+  v4i fa[2][FM], fb[2][FN];
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) QG_DMA_STAGE(min(s, nkt - 1), s)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW));
+  __builtin_amdgcn_s_barrier();
+  QG_LOAD_FRAGS(0, 0, fa[0], fb[0])
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    // refill the buffer every wave finished reading before the last barrier
+    QG_DMA_STAGE(min(kt + NS - 1, nkt - 1), (kt + NS - 1) % NS)
+    const int cur = kt % NS, nxt = (kt + 1) % NS;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int pb = kk & 1, qb = pb ^ 1;
+      if (kk + 1 < NKK) {
+        QG_LOAD_FRAGS(cur, kk + 1, fa[qb], fb[qb])
+      } else {
+        // next stage: this wave's loads landed, its reads of this stage are
+        // done; after the barrier everyone's are, so the stage can be refilled
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW) & ~(15 << 8));  // vmcnt and lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        QG_LOAD_FRAGS(nxt, 0, fa[qb], fb[qb])
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (ASYM) {  // uint8 codes enter the signed matrix cores as q - 128
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[pb][i] ^= (int)0x80808080u;
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[pb][i], fb[pb][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#undef QG_LOAD_FRAGS
+#undef QG_DMA_STAGE
+  // trailing (clamped) stage loads may still be writing LDS
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  // ---- epilogue through LDS (same scheme as gemm_kernel); the tile's row
+  // scales and zero points are fetched once into LDS after the staging area
+  constexpr int LPR = TN / 4;
+  constexpr int RPI = 64 / LPR;
+  constexpr int RS = C::RS;
+  uint8_t* wreg = smem + wid * (32 * RS * 4);
+  float* rsa = reinterpret_cast<float*>(smem + C::EPI);
+  int* rza = reinterpret_cast<int*>(smem + C::EPI + BM * 4);
+  for (int r = tid; r < BM; r += C::NT) {
+    const int64_t m = min(m0 + r, p.M - 1);
+    rsa[r] = p.a_per_tensor ? p.sa[0] : p.sa[m];
+    if (ASYM) rza[r] = p.a_per_tensor ? p.za[0] : p.za[m];
+  }
+  const int cq = (lane % LPR) * 4;
+  const int64_t nq = n0 + wn * TN + cq;
+  float sw4[4] = {0.f, 0.f, 0.f, 0.f};
+  int cs4[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (nq + t < p.N) {
+      sw4[t] = p.w_per_tensor ? p.sw[0] : p.sw[nq + t];
+      if (ASYM) cs4[t] = p.colsum[nq + t];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        reinterpret_cast<int*>(wreg)[r * RS + j * 32 + (lane & 31)] = acc[i][j][e];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPI; ++pass) {
+      const int r = pass * RPI + lane / LPR;
+      const int64_t m = m0 + wm * TM + i * 32 + r;
+      const v4i raw = *reinterpret_cast<const v4i*>(wreg + (r * RS + cq) * 4);
+      if (m < p.M && nq < p.N) {
+        float y[4];
+        int ci[4];
+        const float sam = rsa[wm * TM + i * 32 + r];
+        const int zm = ASYM ? rza[wm * TM + i * 32 + r] : 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          int c = raw[t];
+          // wrap-around int32 arithmetic: the true C fits, so the result is exact
+          if (ASYM) c = (int)((uint32_t)c - (uint32_t)(zm - 128) * (uint32_t)cs4[t]);
+          ci[t] = c;
+          y[t] = (float)c * (sam * sw4[t]);
+        }
+        const bool full = nq + 3 < p.N;
+        if constexpr (OUT == 2) {
+          int32_t* o = reinterpret_cast<int32_t*>(p.out) + m * p.ldo + nq;
+          if (full)
+            *reinterpret_cast<v4i*>(o) = v4i{ci[0], ci[1], ci[2], ci[3]};
+          else
+            for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = ci[t];
+        } else if constexpr (OUT == 0) {
+          float* o = reinterpret_cast<float*>(p.out) + m * p.ldo + nq;
+          if (full)
+            *reinterpret_cast<v4f*>(o) = v4f{y[0], y[1], y[2], y[3]};
+          else
+            for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = y[t];
+        } else {
+          uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + m * p.ldo + nq;
+          uint16_t h[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) h[t] = f32_to_bf16_rne(y[t]);
+          if (full) {
+            uint2 v;
+            v.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+            v.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+            *reinterpret_cast<uint2*>(o) = v;
+          } else {
+            for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = h[t];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool ASYM, int OUT>
+static hipError_t launch_dma(const GemmArgs& a, hipStream_t st) {
+  using C = DmaCfg<BM, BN, BK, WM, WN, NS, ASYM, OUT>;
+  auto kern = gemm_i8_dma_kernel<BM, BN, BK, WM, WN, NS, ASYM, OUT>;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::NT), 0, st, a);
+  return hipGetLastError();
+}
+
+template <bool ASYM, int OUT>
+static hipError_t launch_i8(const GemmArgs& a, hipStream_t st) {
+  const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  if (big_tiles >= 256) return launch_dma<256, 256, 64, 2, 4, 4, ASYM, OUT>(a, st);
+  return launch_dma<128, 128, 128, 2, 2, 4, ASYM, OUT>(a, st);
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int MODE, bool ASYM, int OUT>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   using C = GemmCfg<BM, BN, BK, WM, WN, MODE, ASYM, OUT>;
@@ -436,13 +682,13 @@ static hipError_t launch_pick(const GemmArgs& a, hipStream_t st) {
 hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   if (asym) {
-    if (out_type == 0) return launch_pick<I8, true, 0>(a, st);
-    if (out_type == 1) return launch_pick<I8, true, 1>(a, st);
-    return launch_pick<I8, true, 2>(a, st);
+    if (out_type == 0) return launch_i8<true, 0>(a, st);
+    if (out_type == 1) return launch_i8<true, 1>(a, st);
+    return launch_i8<true, 2>(a, st);
   }
-  if (out_type == 0) return launch_pick<I8, false, 0>(a, st);
-  if (out_type == 1) return launch_pick<I8, false, 1>(a, st);
-  return launch_pick<I8, false, 2>(a, st);
+  if (out_type == 0) return launch_i8<false, 0>(a, st);
+  if (out_type == 1) return launch_i8<false, 1>(a, st);
+  return launch_i8<false, 2>(a, st);
 }
 
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st) {
