@@ -415,6 +415,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
 // vmcnt wait and one barrier per K step; the fragments of sub-step kk + 1 are
 // read while the matrix cores work on sub-step kk.
 // ---------------------------------------------------------------------------
+// dword 3 of a raw buffer descriptor: 32-bit data format, no swizzle
+constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
 #define QG_LDSP(x) ((__attribute__((address_space(3))) void*)(x))
@@ -428,25 +430,30 @@ struct DmaCfg {
   static constexpr int STAGE = (BM + BN) * RB;
   static constexpr int IPS = STAGE / 1024;            // 1 KB wave loads per stage
   static constexpr int IPW = IPS / NW;                // ... per wave
+  static constexpr int IA = BM * RB / 1024;           // the first IA loads of a stage carry A
+  static constexpr int NKK = BK / 32;                 // matrix-core sub-steps per stage
+  static constexpr int SLOTS = (NKK - 1) * FM * FN;   // MFMAs the stage's loads are spread over
   static constexpr int RS = TN + 8;
   static constexpr int EPI = NW * 32 * RS * 4;
   static constexpr int EPI_ALL = EPI + BM * 8;        // + per-row scale and zero point
   static constexpr int LDS = NS * STAGE > EPI_ALL ? NS * STAGE : EPI_ALL;
   static_assert(STAGE % 1024 == 0 && IPS % NW == 0 && (BM * RB) % 1024 == 0, "stage / wave-load mismatch");
-  static_assert(NS >= 2 && (NS - 2) * IPW < 64, "vmcnt range");
+  static_assert(IA % IPW == 0, "every wave loads from one operand only");
+  static_assert(NKK >= 2 && NKK % 2 == 0 && SLOTS >= IPW, "load slots");
+  static_assert(NS >= 3 && (NS - 2) * IPW < 64, "vmcnt range");
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
 
 template <int BM, int BN, int BK, int WM, int WN, int NS, bool ASYM, int OUT>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
   using C = DmaCfg<BM, BN, BK, WM, WN, NS, ASYM, OUT>;
-  constexpr int NT = C::NT, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, RB = C::RB;
-  constexpr int STAGE = C::STAGE, IPW = C::IPW;
-  (void)NT;
+  constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, RB = C::RB;
+  constexpr int STAGE = C::STAGE, IPW = C::IPW, NKK = C::NKK, SLOTS = C::SLOTS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wid / WN, wn = wid % WN;
 
   const int tiles_m = (int)((p.M + BM - 1) / BM);
@@ -467,28 +474,36 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
   const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
   const int nkt = (int)(p.K_pad / BK);
 
-  // Per-lane global source of each of this wave's 1 KB loads, relative to the
-  // stage's K offset. A rows >= M are clamped (their outputs are never stored);
-  // A columns >= K are redirected to column 0 (they meet zero weights).
-#define QG_DMA_STAGE(KT, S)                                                                       \
-  {                                                                                               \
-    const int64_t k0_ = (int64_t)(KT) * BK;                                                       \
-    _Pragma("unroll") for (int i = 0; i < IPW; ++i) {                                             \
-      const int b = wid * IPW + i;                                                                \
-      const int P = b * 1024 + lane * 16;                                                         \
-      const uint8_t* src;                                                                         \
-      if (b * 1024 < BM * RB) {                                                                   \
-        const int r = P / RB, c = ((P % RB) >> 4) ^ ((r / (RB >= 256 ? 1 : 256 / RB)) % (RB / 16)); \
-        const int64_t m = min(m0 + r, p.M - 1), k = k0_ + c * 16;                                 \
-        src = p.a + m * p.lda + (k < p.K ? k : 0);                                                \
-      } else {                                                                                    \
-        const int P2 = P - BM * RB;                                                               \
-        const int r = P2 / RB, c = ((P2 % RB) >> 4) ^ ((r / (RB >= 256 ? 1 : 256 / RB)) % (RB / 16)); \
-        src = p.w + (n0 + r) * p.K_pad + k0_ + c * 16;                                            \
-      }                                                                                           \
-      __builtin_amdgcn_global_load_lds(src, QG_LDSP(smem + (S) * STAGE + b * 1024), 16, 0, 0);   \
-    }                                                                                             \
+  // Stage loads (buffer_load ... lds, 16 bytes per lane). Wave wid issues the
+  // stage's 1 KB loads wid*IPW .. wid*IPW+IPW-1, all from one operand. The
+  // lane offsets (row * stride + swizzled chunk) do not change along K: they
+  // are computed once, and the stage's K offset goes in the scalar offset.
+  // A rows >= M are clamped to row M - 1 (their outputs are never stored). The
+  // buffer's byte range ends at the 16-byte chunk holding A column K - 1 of
+  // the last row, so nothing past it is read: the hardware returns zeros for
+  // every dword outside the range (the weights are zero there). A stage past
+  // the last one gets an empty range, so its loads move no data and still
+  // count in vmcnt.
+  const bool wave_a = wid * IPW < C::IA;
+  const int64_t stride = wave_a ? p.lda : p.K_pad;
+  const uint8_t* const obase = wave_a ? p.a + m0 * p.lda : p.w + n0 * p.K_pad;
+  const int64_t last_a_row = min((int64_t)BM - 1, p.M - 1 - m0);
+  const uint32_t nrec = (uint32_t)(wave_a ? last_a_row * p.lda + ((p.K + 15) & ~(int64_t)15) : (int64_t)BN * p.K_pad);
+  uint32_t voff[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int P = (wid * IPW + i) * 1024 + lane * 16 - (wave_a ? 0 : BM * RB);
+    const int r = P / RB;
+    const int c = ((P % RB) >> 4) ^ ((r / (RB >= 256 ? 1 : 256 / RB)) % (RB / 16));
+    const int64_t rr = wave_a ? min((int64_t)r, last_a_row) : (int64_t)r;
+    voff[i] = (uint32_t)(rr * stride) + (uint32_t)(c * 16);
   }
+  auto dma = [&](int kt, int s, int i, bool live) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)obase, (short)0, live ? (int)nrec : 0, kRawBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, QG_LDSP(smem + s * STAGE + (wid * IPW + i) * 1024), 16, (int)voff[i],
+                                             kt * BK, 0, 0);
+  };
 
   v16i acc[FM][FN];
 #pragma unroll
@@ -507,29 +522,34 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
     _Pragma("unroll") for (int j = 0; j < FN; ++j) FB[j] = *reinterpret_cast<const v4i*>(         \
         sa_ + BM * RB + lds_off<RB>(wn * TN + j * 32 + (lane & 31), ch_));                        \
   }
-  constexpr int NKK = BK / 32;
-  static_assert(NKK % 2 == 0, "fragment double buffer parity");
   v4i fa[2][FM], fb[2][FN];
 
+  // prologue: stages 0 .. NS-2 in flight
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) QG_DMA_STAGE(min(s, nkt - 1), s)
+  for (int s = 0; s < NS - 1; ++s)
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) dma(s, s, i, s < nkt);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW));
   __builtin_amdgcn_s_barrier();
   QG_LOAD_FRAGS(0, 0, fa[0], fb[0])
 
   for (int kt = 0; kt < nkt; ++kt) {
-    // refill the buffer every wave finished reading before the last barrier
-    QG_DMA_STAGE(min(kt + NS - 1, nkt - 1), (kt + NS - 1) % NS)
-    const int cur = kt % NS, nxt = (kt + 1) % NS;
+    // Stage kt + NS - 1 refills the slot every wave finished reading before the
+    // last barrier; its loads are spread between the matrix-core instructions
+    // of the first NKK - 1 sub-steps.
+    const int ks = kt + NS - 1;
+    const bool live = ks < nkt;
+    const int cur = kt % NS, nxt = (kt + 1) % NS, sl = ks % NS;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int pb = kk & 1, qb = pb ^ 1;
       if (kk + 1 < NKK) {
         QG_LOAD_FRAGS(cur, kk + 1, fa[qb], fb[qb])
       } else {
-        // next stage: this wave's loads landed, its reads of this stage are
-        // done; after the barrier everyone's are, so the stage can be refilled
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW) & ~(15 << 8));  // vmcnt and lgkmcnt(0)
+        // next stage: its loads landed (vmcnt counts the loads issued after
+        // it), this wave's reads of the current stage are done (lgkmcnt 0);
+        // after the barrier everyone's are
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW) & ~(15 << 8));
         __builtin_amdgcn_s_barrier();
         QG_LOAD_FRAGS(nxt, 0, fa[qb], fb[qb])
       }
@@ -541,14 +561,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[pb][i], fb[pb][j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+          if (kk + 1 < NKK) {
+            const int slot = kk * FM * FN + i * FN + j;
+#pragma unroll
+            for (int d = 0; d < IPW; ++d)
+              if ((d * SLOTS) / IPW == slot) dma(ks, sl, d, live);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
     }
   }
 #undef QG_LOAD_FRAGS
-#undef QG_DMA_STAGE
-  // trailing (clamped) stage loads may still be writing LDS
+  // the empty loads past the last stage may still be in flight
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 

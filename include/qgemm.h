@@ -237,7 +237,9 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw,
  *   cast to float32, to bfloat16 (round to nearest even), or C itself (I32).
  *
  *   a_q      device codes [M][lda] (int8 for INT8_SYM, uint8 for UINT8_ASYM),
- *            lda >= K, lda % 16 == 0, 16-byte aligned.
+ *            lda >= K, lda % 16 == 0, 16-byte aligned. Row m is read from byte
+ *            0 up to the end of the 16-byte chunk holding column K - 1, never
+ *            further; (min(M, 256) - 1) * lda + K_pad < 2^32 (QGEMM_E_SHAPE).
  *   a_scales device float32 [M] (ROW) or [1] (TENSOR).
  *   a_zero   device int32 [M] or [1] (UINT8_ASYM, values 0..255); NULL for INT8_SYM.
  *   w_desc   host descriptor from qgemm_prepack_weights (INT8_SYM weights).
