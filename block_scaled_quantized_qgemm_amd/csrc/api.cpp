@@ -150,7 +150,7 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int f
     qg::launch_quantize_mx(x, M, K, ldx, (uint8_t*)q, ldq, mx_scales, ld_mx, st);
   } else {
     qg::launch_quantize_int(x, M, K, ldx, fmt == QGEMM_FMT_UINT8_ASYM, gran == QGEMM_GRAN_TENSOR,
-                            (uint8_t*)q, ldq, scales, zero_points, nullptr, (float*)workspace, st);
+                            (uint8_t*)q, ldq, 0, scales, zero_points, nullptr, (float*)workspace, st);
   }
   return launch_status();
 }
@@ -178,7 +178,7 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int
   if (hipMemsetAsync(base, 0, (size_t)L.bytes, st) != hipSuccess) return QGEMM_E_HIP;
   if (fmt == QGEMM_FMT_INT8_SYM) {
     qg::launch_quantize_int(w, N, K, ldw, false, gran == QGEMM_GRAN_TENSOR, base + L.codes_off, L.K_pad,
-                            (float*)(base + L.scales_off), nullptr, (int32_t*)(base + L.colsum_off),
+                            L.K_pad / 64, (float*)(base + L.scales_off), nullptr, (int32_t*)(base + L.colsum_off),
                             (float*)workspace, st);
   } else {
     if (hipMemsetAsync(base + L.scales_off, 127, (size_t)(L.N_pad * (L.K_pad / 32)), st) != hipSuccess)

@@ -57,6 +57,16 @@ __device__ inline int lds_off(int row, int chunk) {
   return row * RB + ((chunk ^ ((row / RPL) % CPR)) << 4);
 }
 
+// LDS offset of the 16-byte chunk `chunk` (K bytes [16 chunk, 16 chunk + 16)
+// of the stage) of W tile row `row` when the stage holds the packed weight
+// blocks of 16 rows x 64 K in order (row block major, BK / 64 blocks per row
+// block). The 16 lanes that read one chunk of 16 consecutive rows cover 256
+// contiguous bytes, i.e. every bank once.
+template <int BK>
+__device__ inline int w_blk_off(int row, int chunk) {
+  return (((row >> 4) * (BK / 64) + (chunk >> 2)) << 10) + ((chunk & 3) << 8) + ((row & 15) << 4);
+}
+
 __device__ inline float e8m0_to_f32(int E) { return __uint_as_float((uint32_t)E << 23); }
 
 // Sixteen e4m3 codes times 2^(E-127) as sixteen bf16 (exact for E in [3, 240]).
@@ -440,7 +450,7 @@ struct DmaCfg {
   static_assert(STAGE % 1024 == 0 && IPS % NW == 0 && (BM * RB) % 1024 == 0, "stage / wave-load mismatch");
   static_assert(IA % IPW == 0, "every wave loads from one operand only");
   static_assert(NKK >= 2 && NKK % 2 == 0 && SLOTS >= IPW, "load slots");
-  static_assert(NS >= 3 && (NS - 2) * IPW < 64, "vmcnt range");
+  static_assert(NS >= 2 && (NS - 2) * IPW < 64, "vmcnt range");
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
 
@@ -475,9 +485,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
   const int nkt = (int)(p.K_pad / BK);
 
   // Stage loads (buffer_load ... lds, 16 bytes per lane). Wave wid issues the
-  // stage's 1 KB loads wid*IPW .. wid*IPW+IPW-1, all from one operand. The
-  // lane offsets (row * stride + swizzled chunk) do not change along K: they
-  // are computed once, and the stage's K offset goes in the scalar offset.
+  // stage's 1 KB loads wid*IPW .. wid*IPW+IPW-1, all from one operand. For A,
+  // lane l fetches the 16-byte chunk that belongs at LDS slot l of the
+  // swizzled row-major tile (row * lda + chunk); for W, one load copies one
+  // packed 16 x 64 weight block (1 KB contiguous) as it is. The lane offsets
+  // do not change along K: they are computed once, and the stage's K offset
+  // goes in the scalar offset.
   // A rows >= M are clamped to row M - 1 (their outputs are never stored). The
   // buffer's byte range ends at the 16-byte chunk holding A column K - 1 of
   // the last row, so nothing past it is read: the hardware returns zeros for
@@ -485,24 +498,29 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
   // the last one gets an empty range, so its loads move no data and still
   // count in vmcnt.
   const bool wave_a = wid * IPW < C::IA;
-  const int64_t stride = wave_a ? p.lda : p.K_pad;
+  const int64_t stride = p.lda;  // A rows
   const uint8_t* const obase = wave_a ? p.a + m0 * p.lda : p.w + n0 * p.K_pad;
   const int64_t last_a_row = min((int64_t)BM - 1, p.M - 1 - m0);
   const uint32_t nrec = (uint32_t)(wave_a ? last_a_row * p.lda + ((p.K + 15) & ~(int64_t)15) : (int64_t)BN * p.K_pad);
   uint32_t voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int P = (wid * IPW + i) * 1024 + lane * 16 - (wave_a ? 0 : BM * RB);
-    const int r = P / RB;
-    const int c = ((P % RB) >> 4) ^ ((r / (RB >= 256 ? 1 : 256 / RB)) % (RB / 16));
-    const int64_t rr = wave_a ? min((int64_t)r, last_a_row) : (int64_t)r;
-    voff[i] = (uint32_t)(rr * stride) + (uint32_t)(c * 16);
+    if (wave_a) {  // swizzled row-major A tile: slot P holds chunk c of row r
+      const int P = (wid * IPW + i) * 1024 + lane * 16;
+      const int r = P / RB;
+      const int c = ((P % RB) >> 4) ^ ((r / (RB >= 256 ? 1 : 256 / RB)) % (RB / 16));
+      voff[i] = (uint32_t)(min((int64_t)r, last_a_row) * stride) + (uint32_t)(c * 16);
+    } else {  // W tile: the weight blocks (16 rows x 64 K, 1 KB) copied whole, in order
+      const int j = wid * IPW + i - C::IA;
+      voff[i] = (uint32_t)(((j / (BK / 64)) * (p.K_pad >> 6) + j % (BK / 64)) << 10) + (uint32_t)(lane * 16);
+    }
   }
+  const int kstride = wave_a ? BK : BK * 16;  // bytes per stage along the operand's K order
   auto dma = [&](int kt, int s, int i, bool live) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)obase, (short)0, live ? (int)nrec : 0, kRawBufferWord3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, QG_LDSP(smem + s * STAGE + (wid * IPW + i) * 1024), 16, (int)voff[i],
-                                             kt * BK, 0, 0);
+                                             kt * kstride, 0, 0);
   };
 
   v16i acc[FM][FN];
@@ -520,7 +538,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
     _Pragma("unroll") for (int i = 0; i < FM; ++i) FA[i] =                                        \
         *reinterpret_cast<const v4i*>(sa_ + lds_off<RB>(wm * TM + i * 32 + (lane & 31), ch_));    \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) FB[j] = *reinterpret_cast<const v4i*>(         \
-        sa_ + BM * RB + lds_off<RB>(wn * TN + j * 32 + (lane & 31), ch_));                        \
+        sa_ + BM * RB + w_blk_off<BK>(wn * TN + j * 32 + (lane & 31), ch_));                      \
   }
   v4i fa[2][FM], fb[2][FN];
 
@@ -672,8 +690,116 @@ static hipError_t launch_dma(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Decode-shaped GEMM (M <= 16 rows): the time is the stream of W out of HBM,
+// so every byte of W is read once, straight into registers, and the matrix
+// cores only need to keep up. A workgroup owns NB blocks of 16 weight rows
+// (v_mfma_i32_16x16x64_i8 column blocks) over all of K; its four waves take
+// one quarter of K each and issue eight 1 KB loads of W per block and batch,
+// each one contiguous 16 x 64 weight block already in the operand's lane
+// order. The activation rows ride in the other operand (rows >= M and columns
+// past the last 16-byte chunk holding column K - 1 come back as zeros from the
+// range-checked buffer loads). The four partial int32 tiles are summed through
+// LDS before the epilogue, so the result is exact.
+// ---------------------------------------------------------------------------
+template <int OUT>
+__device__ inline void store_one(void* out, int64_t idx, int c, float y) {
+  if constexpr (OUT == 2) {
+    reinterpret_cast<int32_t*>(out)[idx] = c;
+  } else if constexpr (OUT == 0) {
+    reinterpret_cast<float*>(out)[idx] = y;
+  } else {
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(y);
+  }
+}
+
+template <bool ASYM, int OUT, int NB>
+__global__ __launch_bounds__(256) void gemm_i8_decode_kernel(GemmArgs p) {
+  constexpr int NR = 16 * NB;  // weight rows per workgroup: NB column blocks of 16
+  constexpr int U = 8;         // 64-deep K steps per load batch
+  __shared__ v4i red[4][NB][64];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * NR;
+  const int steps = (int)(p.K_pad / 256);  // 64-deep steps per wave (K_pad is a multiple of 256)
+  const int64_t kbeg = (int64_t)wid * steps * 64;
+
+  // operand lanes: lane l carries row l % 16 and the 16-byte K chunk l / 16 of
+  // every 64-deep step. Steps past this wave's range (the last batch) read as
+  // zeros through an offset beyond both buffers' ranges.
+  const int row = lane & 15;
+  const int chunk = (lane >> 4) * 16;
+  constexpr uint32_t kOff = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.w + n0 * p.K_pad), (short)0, (int)(NR * p.K_pad), kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.a, (short)0, (int)((p.M - 1) * p.lda + ((p.K + 15) & ~(int64_t)15)), kRawBufferWord3);
+  const uint32_t woff = (uint32_t)((kbeg >> 6) << 10) + (uint32_t)(lane * 16);  // 16 x 64 blocks, lane order
+  const uint32_t aoff = row < p.M ? (uint32_t)(row * p.lda + kbeg + chunk) : kOff;  // rows >= M: zeros
+
+  v4i acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = v4i{0, 0, 0, 0};
+  for (int s0 = 0; s0 < steps; s0 += U) {
+    v4i wv[U][NB], av[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const bool live = s0 + u < steps;
+        const uint32_t o = woff + (uint32_t)(b * 16 * p.K_pad) + (uint32_t)((s0 + u) * 1024);
+        wv[u][b] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)(live ? o : kOff), 0, 0));
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = s0 + u < steps;
+      av[u] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)(live ? aoff + (uint32_t)((s0 + u) * 64) : kOff), 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v4i a = av[u];
+      if (ASYM) a ^= (int)0x80808080u;  // uint8 codes enter as q - 128 (a dead step still meets zero weights)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wv[u][b], acc[b], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) red[wid][b][lane] = acc[b];
+  __syncthreads();
+
+  // thread t finishes item t / 64 of lane t % 64 in each block: row 4 * (l / 16) + item, column l % 16
+  const int t = threadIdx.x;
+  const int l = t & 63, item = t >> 6;
+  const int m = 4 * (l >> 4) + item;
+  if (m >= p.M) return;
+  const float sa = p.a_per_tensor ? p.sa[0] : p.sa[m];
+  const int z = ASYM ? (p.a_per_tensor ? p.za[0] : p.za[m]) : 0;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int64_t n = n0 + b * 16 + (l & 15);
+    if (n < p.N) {
+      int c = red[0][b][l][item] + red[1][b][l][item] + red[2][b][l][item] + red[3][b][l][item];
+      if (ASYM) c = (int)((uint32_t)c - (uint32_t)(z - 128) * (uint32_t)p.colsum[n]);
+      const float sw = p.w_per_tensor ? p.sw[0] : p.sw[n];
+      store_one<OUT>(p.out, m * p.ldo + n, c, (float)c * (sa * sw));
+    }
+  }
+}
+
+template <bool ASYM, int OUT>
+static hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
+  // one 16-row block per workgroup: with the weights streamed from HBM, wider
+  // workgroups (fewer activation re-reads) measured no faster
+  constexpr int NB = 1;
+  const int64_t groups = (a.N + 16 * NB - 1) / (16 * NB);
+  hipLaunchKernelGGL((gemm_i8_decode_kernel<ASYM, OUT, NB>), dim3((unsigned)groups), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <bool ASYM, int OUT>
 static hipError_t launch_i8(const GemmArgs& a, hipStream_t st) {
+  if (a.M <= 16) return launch_decode<ASYM, OUT>(a, st);
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   if (big_tiles >= 256) return launch_dma<256, 256, 64, 2, 4, 4, ASYM, OUT>(a, st);
   return launch_dma<128, 128, 128, 2, 2, 4, ASYM, OUT>(a, st);

@@ -7,11 +7,13 @@
 namespace qg {
 
 // Symmetric int8 / asymmetric uint8 row quantization (per row or per tensor).
-// `colsum` (may be null) receives the sum of each row's codes. `ws` holds
-// rows (2*rows when asym) floats for the per-tensor statistics.
+// Codes go row-major with stride ldq (kblocks == 0) or, for packed weights,
+// into 1 KB blocks of 16 rows x 64 K with kblocks blocks along K (see
+// GemmArgs::w). `colsum` (may be null) receives the sum of each row's codes.
+// `ws` holds rows (2*rows when asym) floats for the per-tensor statistics.
 void launch_quantize_int(const float* x, int64_t rows, int64_t K, int64_t ldx, bool asym, bool per_tensor,
-                         uint8_t* q, int64_t ldq, float* scales, int32_t* zeros, int32_t* colsum, float* ws,
-                         hipStream_t st);
+                         uint8_t* q, int64_t ldq, int64_t kblocks, float* scales, int32_t* zeros, int32_t* colsum,
+                         float* ws, hipStream_t st);
 
 // MXFP8 (e4m3 codes, E8M0 per 32 K-elements) row quantization; K % 32 == 0.
 void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
@@ -25,7 +27,11 @@ struct GemmArgs {
   const uint8_t* ea;    // mx: E8M0 [M][lda_s]
   int64_t lda_s;
   int a_per_tensor;
-  const uint8_t* w;     // packed codes [N_pad][K_pad]
+  // packed codes, N_pad x K_pad. int8: 1 KB blocks of 16 rows x 64 K, block
+  // (n / 16, k / 64) at byte ((n / 16) * (K_pad / 64) + k / 64) * 1024, and in
+  // it the 16 bytes k % 64 in [16c, 16c + 16) of row n % 16 at 256 c + 16 (n % 16)
+  // (one v_mfma_i32_16x16x64_i8 B operand in lane order). MX: row-major.
+  const uint8_t* w;
   const float* sw;      // int8: [N_pad] or [1]
   const int32_t* colsum;
   const uint8_t* ew;    // mx: E8M0 [N_pad][K_pad/32]

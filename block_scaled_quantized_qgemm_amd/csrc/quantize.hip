@@ -95,6 +95,24 @@ __device__ inline uint32_t encode_code(float v, float s, float zf) {
   }
 }
 
+// Where code (row, k) is stored: row-major with stride ldq, or (kblocks > 0,
+// the packed int8 weight layout) in 1 KB blocks of 16 rows x 64 K, block
+// (row / 16, k / 64) at ((row / 16) * kblocks + k / 64) KB, and inside a block
+// the 16-byte chunk (k / 16) % 4 of row row % 16 at 256 * ((k / 16) % 4) +
+// 16 * (row % 16). Four consecutive codes k .. k + 3 (k % 4 == 0) stay
+// contiguous in both layouts.
+struct CodeDst {
+  uint8_t* q;
+  int64_t ldq;
+  int64_t kblocks;
+};
+
+__device__ inline uint8_t* code_ptr(const CodeDst& d, int64_t row, int64_t k) {
+  if (d.kblocks)
+    return d.q + (((row >> 4) * d.kblocks + (k >> 6)) << 10) + (((k >> 4) & 3) << 8) + ((row & 15) << 4) + (k & 15);
+  return d.q + row * d.ldq + k;
+}
+
 template <bool ASYM>
 __device__ inline int code_value(uint32_t c) {
   return ASYM ? (int)c : (int)(int8_t)(uint8_t)c;
@@ -105,13 +123,12 @@ __device__ inline int code_value(uint32_t c) {
 // from scales[0] / zeros[0] instead of from this row.
 template <bool ASYM, bool PRECOMP, int VPT>
 __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
-    const float* __restrict__ x, int64_t ldx, int64_t K, uint8_t* __restrict__ q, int64_t ldq,
+    const float* __restrict__ x, int64_t ldx, int64_t K, CodeDst qd,
     float* __restrict__ scales, int32_t* __restrict__ zeros, int32_t* __restrict__ colsum) {
   __shared__ float red[16];
   __shared__ int redi[8];
   const int64_t row = blockIdx.x;
   const float* xr = x + row * ldx;
-  uint8_t* qr = q + row * ldq;
   const int t = threadIdx.x;
 
   float4 v[VPT];
@@ -162,14 +179,14 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     if (k + 4 <= K) {
       uint32_t c0 = encode_code<ASYM>(v[u].x, s, zf), c1 = encode_code<ASYM>(v[u].y, s, zf);
       uint32_t c2 = encode_code<ASYM>(v[u].z, s, zf), c3 = encode_code<ASYM>(v[u].w, s, zf);
-      *reinterpret_cast<uint32_t*>(qr + k) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+      *reinterpret_cast<uint32_t*>(code_ptr(qd, row, k)) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
       if (colsum) csum += code_value<ASYM>(c0) + code_value<ASYM>(c1) + code_value<ASYM>(c2) + code_value<ASYM>(c3);
     } else if (k < K) {
       float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       for (int c = 0; c < 4; ++c)
         if (k + c < K) {
           uint32_t cc = encode_code<ASYM>(e[c], s, zf);
-          qr[k + c] = (uint8_t)cc;
+          *code_ptr(qd, row, k + c) = (uint8_t)cc;
           if (colsum) csum += code_value<ASYM>(cc);
         }
     }
@@ -188,13 +205,12 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
 // row (the second one is served by the caches).
 template <bool ASYM, bool PRECOMP>
 __global__ __launch_bounds__(kRowThreads) void quant_rows_long_kernel(
-    const float* __restrict__ x, int64_t ldx, int64_t K, uint8_t* __restrict__ q, int64_t ldq,
+    const float* __restrict__ x, int64_t ldx, int64_t K, CodeDst qd,
     float* __restrict__ scales, int32_t* __restrict__ zeros, int32_t* __restrict__ colsum) {
   __shared__ float red[16];
   __shared__ int redi[8];
   const int64_t row = blockIdx.x;
   const float* xr = x + row * ldx;
-  uint8_t* qr = q + row * ldq;
   const int t = threadIdx.x;
   float s;
   int z;
@@ -213,7 +229,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_long_kernel(
   int csum = 0;
   for (int64_t k = t; k < K; k += kRowThreads) {
     uint32_t c = encode_code<ASYM>(xr[k], s, zf);
-    qr[k] = (uint8_t)c;
+    *code_ptr(qd, row, k) = (uint8_t)c;
     csum += code_value<ASYM>(c);
   }
   if (colsum) {
@@ -318,44 +334,45 @@ __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __re
 // Host launchers
 // ---------------------------------------------------------------------------
 template <bool ASYM, bool PRECOMP>
-static void launch_rows(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
-                        float* scales, int32_t* zeros, int32_t* colsum, hipStream_t st) {
+static void launch_rows(const float* x, int64_t rows, int64_t K, int64_t ldx, CodeDst qd, float* scales,
+                        int32_t* zeros, int32_t* colsum, hipStream_t st) {
   dim3 grid((unsigned)rows), block(kRowThreads);
-  const bool vec = ldx % 4 == 0 && ((uintptr_t)x % 16) == 0 && ldq % 4 == 0 && ((uintptr_t)q % 4) == 0;
+  const bool vec = ldx % 4 == 0 && ((uintptr_t)x % 16) == 0 && qd.ldq % 4 == 0 && ((uintptr_t)qd.q % 4) == 0;
   if (!vec)
-    quant_rows_long_kernel<ASYM, PRECOMP><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+    quant_rows_long_kernel<ASYM, PRECOMP><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
   else if (K <= 1024)
-    quant_rows_kernel<ASYM, PRECOMP, 1><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+    quant_rows_kernel<ASYM, PRECOMP, 1><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
   else if (K <= 2048)
-    quant_rows_kernel<ASYM, PRECOMP, 2><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+    quant_rows_kernel<ASYM, PRECOMP, 2><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
   else if (K <= 4096)
-    quant_rows_kernel<ASYM, PRECOMP, 4><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+    quant_rows_kernel<ASYM, PRECOMP, 4><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
   else if (K <= 8192)
-    quant_rows_kernel<ASYM, PRECOMP, 8><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+    quant_rows_kernel<ASYM, PRECOMP, 8><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
   else
-    quant_rows_long_kernel<ASYM, PRECOMP><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, scales, zeros, colsum);
+    quant_rows_long_kernel<ASYM, PRECOMP><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
 }
 
 void launch_quantize_int(const float* x, int64_t rows, int64_t K, int64_t ldx, bool asym, bool per_tensor,
-                         uint8_t* q, int64_t ldq, float* scales, int32_t* zeros, int32_t* colsum, float* ws,
-                         hipStream_t st) {
+                         uint8_t* q, int64_t ldq, int64_t kblocks, float* scales, int32_t* zeros, int32_t* colsum,
+                         float* ws, hipStream_t st) {
   if (rows == 0) return;
+  const CodeDst qd{q, kblocks ? 16 : ldq, kblocks};
   if (!per_tensor) {
     if (asym)
-      launch_rows<true, false>(x, rows, K, ldx, q, ldq, scales, zeros, colsum, st);
+      launch_rows<true, false>(x, rows, K, ldx, qd, scales, zeros, colsum, st);
     else
-      launch_rows<false, false>(x, rows, K, ldx, q, ldq, scales, zeros, colsum, st);
+      launch_rows<false, false>(x, rows, K, ldx, qd, scales, zeros, colsum, st);
     return;
   }
   dim3 grid((unsigned)rows), block(kRowThreads);
   if (asym) {
     row_stats_kernel<true><<<grid, block, 0, st>>>(x, ldx, K, ws);
     tensor_scale_kernel<true><<<1, block, 0, st>>>(ws, rows, scales, zeros);
-    launch_rows<true, true>(x, rows, K, ldx, q, ldq, scales, zeros, colsum, st);
+    launch_rows<true, true>(x, rows, K, ldx, qd, scales, zeros, colsum, st);
   } else {
     row_stats_kernel<false><<<grid, block, 0, st>>>(x, ldx, K, ws);
     tensor_scale_kernel<false><<<1, block, 0, st>>>(ws, rows, scales, zeros);
-    launch_rows<false, true>(x, rows, K, ldx, q, ldq, scales, zeros, colsum, st);
+    launch_rows<false, true>(x, rows, K, ldx, qd, scales, zeros, colsum, st);
   }
 }
 

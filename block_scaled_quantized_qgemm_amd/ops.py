@@ -67,6 +67,14 @@ class QuantizedRows:
         return self.q[:, : self.K]
 
 
+def unblock_int8_codes(raw: torch.Tensor, n_pad: int, k_pad: int) -> torch.Tensor:
+    """Row-major [n_pad, k_pad] copy of packed int8 codes stored as 1 KB blocks:
+    block (n // 16, k // 64) in block-row-major order, and inside it the 16 bytes
+    of row n % 16 with k % 64 in [16c, 16c + 16) at 256 c + 16 (n % 16)."""
+    b = raw.reshape(n_pad // 16, k_pad // 64, 4, 16, 16)      # [rb, kb, c, r, j]
+    return b.permute(0, 3, 1, 2, 4).reshape(n_pad, k_pad)     # [rb, r, kb, c, j]
+
+
 @dataclass
 class PackedWeights:
     """A prepared weight buffer and its host descriptor."""
@@ -82,9 +90,13 @@ class PackedWeights:
         return int(self.desc.K)
 
     def codes(self) -> torch.Tensor:
+        """Codes as [N_pad, K_pad], row-major. The int8 buffer stores 1 KB blocks
+        of 16 rows x 64 K (see qgemm_wdesc); those come back as a row-major copy."""
         d = self.desc
-        c = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad].view(d.N_pad, d.K_pad)
-        return c.view(torch.int8) if d.fmt == FMT_INT8_SYM else c
+        raw = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad]
+        if d.fmt != FMT_INT8_SYM:
+            return raw.view(d.N_pad, d.K_pad)
+        return unblock_int8_codes(raw, d.N_pad, d.K_pad).view(torch.int8)
 
     def scales(self) -> torch.Tensor:
         d = self.desc

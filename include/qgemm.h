@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define QGEMM_ABI_VERSION 1
+#define QGEMM_ABI_VERSION 2
 #define QGEMM_WDESC_MAGIC 0x51474d57u /* "WMGQ" */
 
 /* Status codes. Every entry point returns one of these. */
@@ -115,9 +115,13 @@ typedef enum {
  * Filled by qgemm_prepack_weights; read by qgemm_run / qgemm_run_mx.
  *
  * Layout of the packed device buffer (all offsets in bytes, 256-aligned):
- *   codes   at codes_off:  [N_pad][K_pad] bytes, row-major. int8 codes for
- *           QGEMM_FMT_INT8_SYM, e4m3 codes for QGEMM_FMT_MXFP8_E4M3. Rows >= N
- *           and columns >= K are zero.
+ *   codes   at codes_off:  N_pad x K_pad bytes; rows >= N and columns >= K
+ *           are zero. QGEMM_FMT_INT8_SYM: 1 KB blocks of 16 rows x 64 K; block
+ *           (n/16, k/64) starts at byte ((n/16)*(K_pad/64) + k/64) * 1024 and
+ *           holds, at 256*c + 16*(n%16), the 16 codes of row n with k%64 in
+ *           [16c, 16c+16) (so each block is one 16x16x64 int8 matrix-core
+ *           operand in lane order and a streamed 1 KB load).
+ *           QGEMM_FMT_MXFP8_E4M3: e4m3 codes [N_pad][K_pad], row-major.
  *   scales  at scales_off: INT8: float32 [N_pad] (GRAN_ROW; rows >= N are 0)
  *           or float32 [1] (GRAN_TENSOR). MX: E8M0 bytes [N_pad][K_pad/32]
  *           row-major, padding blocks hold 127 (scale 1.0).

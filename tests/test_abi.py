@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.qgemm_abi_version() == 1
+    assert lib.qgemm_abi_version() == 2
     for s in range(-9, 1):
         assert lib.qgemm_status_string(s).startswith(b"QGEMM_")
     assert lib.qgemm_status_string(-100) == b"unknown qgemm status"
@@ -91,7 +91,7 @@ def test_quantize_rows_validation(lib):
 
 
 def _wdesc(**kw):
-    d = L.WDesc(magic=0x51474D57, version=1, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=2, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 512, colsum_off=256 * 512 + 1024, bytes=256 * 512 + 2048)
     for k, v in kw.items():
         setattr(d, k, v)
@@ -107,7 +107,7 @@ def test_run_validation(lib):
     good = _wdesc()
     assert lib.qgemm_packed_weight_bytes(100, 300, INT8, ROW) == good.bytes
     assert _run(lib, _wdesc(magic=1)) == E_DESC
-    assert _run(lib, _wdesc(version=2)) == E_DESC
+    assert _run(lib, _wdesc(version=1)) == E_DESC
     assert _run(lib, _wdesc(fmt=MX)) == E_DESC
     assert _run(lib, _wdesc(K_pad=384)) == E_DESC
     assert _run(lib, _wdesc(bytes=5)) == E_DESC
@@ -135,7 +135,7 @@ def test_run_validation(lib):
 
 def test_run_mx_validation(lib):
     nb = lib.qgemm_packed_weight_bytes(100, 320, MX, BLK)
-    d = L.WDesc(magic=0x51474D57, version=1, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=2, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 512, colsum_off=-1, bytes=nb)
     call = lambda **kw: lib.qgemm_run_mx(kw.get("a", FAKE), kw.get("lda", 320), kw.get("e", FAKE),
                                          kw.get("ldas", 10), kw.get("M", 4), ctypes.byref(kw.get("d", d)),
@@ -173,3 +173,20 @@ def test_no_device_is_an_error_not_a_fallback(lib):
     # fully valid arguments: the only thing missing is a gfx950
     assert _q(lib) == E_DEVICE
     assert _run(lib, _wdesc()) == E_DEVICE
+
+
+def test_packed_int8_block_layout_round_trip():
+    """The Python view of packed int8 codes inverts the documented block layout:
+    block (n // 16, k // 64) at ((n // 16) * (K_pad // 64) + k // 64) KB, code (n, k)
+    at 256 * ((k % 64) // 16) + 16 * (n % 16) + k % 16 inside it."""
+    import torch
+    from block_scaled_quantized_qgemm_amd.ops import unblock_int8_codes
+    n_pad, k_pad = 32, 256
+    ref = torch.randint(0, 256, (n_pad, k_pad), dtype=torch.int32).to(torch.uint8)
+    raw = torch.zeros(n_pad * k_pad, dtype=torch.uint8)
+    kb = k_pad // 64
+    for n in range(n_pad):
+        for k in range(k_pad):
+            off = ((n // 16) * kb + k // 64) * 1024 + 256 * ((k % 64) // 16) + 16 * (n % 16) + k % 16
+            raw[off] = ref[n, k]
+    assert torch.equal(unblock_int8_codes(raw, n_pad, k_pad), ref)

@@ -158,7 +158,9 @@ def test_prepack_mx_bit_exact(ops, N, K):
 # G + E: int8 GEMM and epilogue, end to end from float32 inputs
 # ---------------------------------------------------------------------------
 GSHAPES = [(1, 1, 1), (3, 5, 7), (33, 65, 129), (64, 64, 256), (130, 260, 300), (257, 513, 1000),
-           (300, 300, 4112), (17, 1030, 64)]
+           (300, 300, 4112), (17, 1030, 64),
+           # decode-shaped (M <= 16): ragged weight-row groups, K tails inside and past a load batch
+           (8, 300, 4112), (16, 1030, 1000), (5, 77, 9000), (12, 2000, 600), (1, 16, 8192)]
 
 
 def _run_int(ops, A, W, act, wgt, out_type):
@@ -198,7 +200,7 @@ def test_gemm_int32_exact(ops, M, N, K, act, wgt):
 
 @pytest.mark.parametrize("out_type", [0, 1])
 @pytest.mark.parametrize("act", list(ACT))
-@pytest.mark.parametrize("M,N,K", [(3, 5, 7), (64, 64, 256), (257, 513, 1000), (300, 300, 4112)])
+@pytest.mark.parametrize("M,N,K", [(3, 5, 7), (64, 64, 256), (257, 513, 1000), (300, 300, 4112), (8, 700, 4096)])
 def test_gemm_epilogue_float(ops, M, N, K, act, out_type):
     print_case("gemm epilogue", M, N, K, act, out_type)
     A, W = make_inputs("c2_per_token", M=M, K=K, N=N, seed=5 * M + N + K)
