@@ -218,8 +218,9 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
   if (M == 0) return QGEMM_OK;
   if (!a_q || !a_scales || !w_packed || !out || (asym && !a_zero)) return QGEMM_E_NULL;
   if (lda < K || ldo < N) return QGEMM_E_SHAPE;
-  // the GEMM addresses one 256-row band of A with 32-bit byte offsets
-  if ((std::min<int64_t>(M, 256) - 1) * lda + w_desc->K_pad >= (int64_t(1) << 32)) return QGEMM_E_SHAPE;
+  // the GEMM addresses one 256-row band of A with 32-bit byte offsets (the
+  // decode kernel's last wave may read up to 32 KB past K_pad)
+  if ((std::min<int64_t>(M, 256) - 1) * lda + w_desc->K_pad + 65536 >= (int64_t(1) << 32)) return QGEMM_E_SHAPE;
   if (lda % 16 != 0 || !aligned(a_q, 16) || ldo % 4 != 0 || !aligned(out, 16) || !aligned(w_packed, 256) ||
       !aligned(a_scales, 4) || (a_zero && !aligned(a_zero, 4)))
     return QGEMM_E_ALIGN;

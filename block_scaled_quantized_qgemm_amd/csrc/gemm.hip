@@ -693,14 +693,17 @@ static hipError_t launch_dma(const GemmArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Decode-shaped GEMM (M <= 16 rows): the time is the stream of W out of HBM,
 // so every byte of W is read once, straight into registers, and the matrix
-// cores only need to keep up. A workgroup owns NB blocks of 16 weight rows
-// (v_mfma_i32_16x16x64_i8 column blocks) over all of K; its four waves take
-// one quarter of K each and issue eight 1 KB loads of W per block and batch,
-// each one contiguous 16 x 64 weight block already in the operand's lane
-// order. The activation rows ride in the other operand (rows >= M and columns
-// past the last 16-byte chunk holding column K - 1 come back as zeros from the
-// range-checked buffer loads). The four partial int32 tiles are summed through
-// LDS before the epilogue, so the result is exact.
+// cores only need to keep up. A workgroup owns one block of 16 weight rows
+// (a v_mfma_i32_16x16x64_i8 column block) over all of K; its eight waves
+// take contiguous ranges of K. A wave works through its range in batches of
+// eight 64-deep steps: each step is one contiguous 1 KB load of W (a 16 x 64
+// weight block already in the operand's lane order) and one 16-byte load per
+// lane of the activation rows. Every load of a batch is issued before any is
+// used (16 loads in flight per wave, three workgroups per CU). The activation
+// rows ride in the other operand. Rows >= M, steps at or past K_pad and
+// columns past the last 16-byte chunk holding column K - 1 come back as zeros
+// from the range-checked buffer loads. The eight partial int32 tiles are
+// summed through LDS before the epilogue, so the result is exact.
 // ---------------------------------------------------------------------------
 template <int OUT>
 __device__ inline void store_one(void* out, int64_t idx, int c, float y) {
@@ -713,73 +716,79 @@ __device__ inline void store_one(void* out, int64_t idx, int c, float y) {
   }
 }
 
-template <bool ASYM, int OUT, int NB>
-__global__ __launch_bounds__(256) void gemm_i8_decode_kernel(GemmArgs p) {
-  constexpr int NR = 16 * NB;  // weight rows per workgroup: NB column blocks of 16
-  constexpr int U = 8;         // 64-deep K steps per load batch
-  __shared__ v4i red[4][NB][64];
+constexpr int kDecWaves = 8;  // waves per workgroup, each on its own K range
+constexpr int kDecBatch = 8;  // 64-deep steps per load batch
+
+template <bool ASYM>
+__device__ inline void decode_batch_mfma(const v4i (&av)[kDecBatch], const v4i (&wv)[kDecBatch], v4i& acc) {
+#pragma unroll
+  for (int u = 0; u < kDecBatch; ++u) {
+    v4i a = av[u];
+    if (ASYM) a ^= (int)0x80808080u;  // uint8 codes enter as q - 128 (a dead step still meets zero weights)
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wv[u], acc, 0, 0, 0);
+  }
+}
+
+// ONE: K_pad <= 512 * kDecWaves, one batch per wave (no loop)
+template <bool ASYM, int OUT, bool ONE>
+__global__ __launch_bounds__(kDecWaves * 64) void gemm_i8_decode_kernel(GemmArgs p) {
+  constexpr int U = kDecBatch;
+  __shared__ v4i red[kDecWaves][64];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = (int64_t)blockIdx.x * NR;
-  const int steps = (int)(p.K_pad / 256);  // 64-deep steps per wave (K_pad is a multiple of 256)
-  const int64_t kbeg = (int64_t)wid * steps * 64;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int steps = (int)(p.K_pad / 64);
+  // steps of each wave: a whole number of batches. Steps at or past K_pad
+  // fall outside the block's W range and read as zeros, so no load is tested;
+  // the A bytes they meet (the next row's, or zeros past A's end) are
+  // multiplied by those zeros.
+  const int per = ONE ? U : (steps + kDecWaves * U - 1) / (kDecWaves * U) * U;
+  const int sbeg = wid * per;
 
-  // operand lanes: lane l carries row l % 16 and the 16-byte K chunk l / 16 of
-  // every 64-deep step. Steps past this wave's range (the last batch) read as
-  // zeros through an offset beyond both buffers' ranges.
+  // operand lanes: lane l carries row l % 16 and the 16-byte K chunk l / 16
+  // of every 64-deep step. Rows >= M read A as zeros through an offset beyond
+  // its range.
   const int row = lane & 15;
   const int chunk = (lane >> 4) * 16;
   constexpr uint32_t kOff = 0x80000000u;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.w + n0 * p.K_pad), (short)0, (int)(NR * p.K_pad), kRawBufferWord3);
+      (void*)(p.w + n0 * p.K_pad), (short)0, (int)(16 * p.K_pad), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.a, (short)0, (int)((p.M - 1) * p.lda + ((p.K + 15) & ~(int64_t)15)), kRawBufferWord3);
-  const uint32_t woff = (uint32_t)((kbeg >> 6) << 10) + (uint32_t)(lane * 16);  // 16 x 64 blocks, lane order
-  const uint32_t aoff = row < p.M ? (uint32_t)(row * p.lda + kbeg + chunk) : kOff;  // rows >= M: zeros
+  const uint32_t woff = (uint32_t)sbeg * 1024u + (uint32_t)(lane * 16);  // 16 x 64 blocks, lane order
+  const uint32_t aoff = row < p.M ? (uint32_t)(row * p.lda + sbeg * 64 + chunk) : kOff;
 
-  v4i acc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = v4i{0, 0, 0, 0};
-  for (int s0 = 0; s0 < steps; s0 += U) {
-    v4i wv[U][NB], av[U];
+  // one batch at a time: the data of a batch takes 64 VGPRs, which leaves
+  // room for three workgroups per CU; their loads overlap each other's waits
+  v4i acc = {0, 0, 0, 0};
+  for (int b = 0; b < (ONE ? U : per); b += U) {
+    v4i av[U], wv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
+      wv[u] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)(woff + (uint32_t)((b + u) * 1024)), 0, 0));
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const bool live = s0 + u < steps;
-        const uint32_t o = woff + (uint32_t)(b * 16 * p.K_pad) + (uint32_t)((s0 + u) * 1024);
-        wv[u][b] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)(live ? o : kOff), 0, 0));
-      }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool live = s0 + u < steps;
+    for (int u = 0; u < U; ++u)
       av[u] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)(live ? aoff + (uint32_t)((s0 + u) * 64) : kOff), 0, 0));
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v4i a = av[u];
-      if (ASYM) a ^= (int)0x80808080u;  // uint8 codes enter as q - 128 (a dead step still meets zero weights)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wv[u][b], acc[b], 0, 0, 0);
-    }
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)(aoff + (uint32_t)((b + u) * 64)), 0, 0));
+    __builtin_amdgcn_sched_barrier(0);
+    decode_batch_mfma<ASYM>(av, wv, acc);
+    __builtin_amdgcn_sched_barrier(0);
   }
-#pragma unroll
-  for (int b = 0; b < NB; ++b) red[wid][b][lane] = acc[b];
+  red[wid][lane] = acc;
   __syncthreads();
 
-  // thread t finishes item t / 64 of lane t % 64 in each block: row 4 * (l / 16) + item, column l % 16
-  const int t = threadIdx.x;
-  const int l = t & 63, item = t >> 6;
-  const int m = 4 * (l >> 4) + item;
-  if (m >= p.M) return;
-  const float sa = p.a_per_tensor ? p.sa[0] : p.sa[m];
-  const int z = ASYM ? (p.a_per_tensor ? p.za[0] : p.za[m]) : 0;
+  // thread t < 256 finishes item t / 64 of lane t % 64: row 4 * (l / 16) + item, column l % 16
+  for (int t = threadIdx.x; t < 256; t += kDecWaves * 64) {
+    const int l = t & 63, item = t >> 6;
+    const int m = 4 * (l >> 4) + item;
+    const int64_t n = n0 + (l & 15);
+    if (m < p.M && n < p.N) {
+      int c = 0;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int64_t n = n0 + b * 16 + (l & 15);
-    if (n < p.N) {
-      int c = red[0][b][l][item] + red[1][b][l][item] + red[2][b][l][item] + red[3][b][l][item];
+      for (int w = 0; w < kDecWaves; ++w) c += red[w][l][item];
+      const float sa = p.a_per_tensor ? p.sa[0] : p.sa[m];
+      const int z = ASYM ? (p.a_per_tensor ? p.za[0] : p.za[m]) : 0;
       if (ASYM) c = (int)((uint32_t)c - (uint32_t)(z - 128) * (uint32_t)p.colsum[n]);
       const float sw = p.w_per_tensor ? p.sw[0] : p.sw[n];
       store_one<OUT>(p.out, m * p.ldo + n, c, (float)c * (sa * sw));
@@ -789,11 +798,11 @@ __global__ __launch_bounds__(256) void gemm_i8_decode_kernel(GemmArgs p) {
 
 template <bool ASYM, int OUT>
 static hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
-  // one 16-row block per workgroup: with the weights streamed from HBM, wider
-  // workgroups (fewer activation re-reads) measured no faster
-  constexpr int NB = 1;
-  const int64_t groups = (a.N + 16 * NB - 1) / (16 * NB);
-  hipLaunchKernelGGL((gemm_i8_decode_kernel<ASYM, OUT, NB>), dim3((unsigned)groups), dim3(256), 0, st, a);
+  const int64_t groups = (a.N + 15) / 16;
+  if (a.K_pad <= 64 * kDecBatch * kDecWaves)
+    hipLaunchKernelGGL((gemm_i8_decode_kernel<ASYM, OUT, true>), dim3((unsigned)groups), dim3(kDecWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_i8_decode_kernel<ASYM, OUT, false>), dim3((unsigned)groups), dim3(kDecWaves * 64), 0, st, a);
   return hipGetLastError();
 }
 
