@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB device-to-device: a plain copy of known size "
                          "whose FETCH_SIZE / WRITE_SIZE counters calibrate the GEMM's traffic")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from Python instead of replaying a captured HIP graph")
     ap.add_argument("--mx-mode", default="exact", choices=["exact", "scaled-mfma"],
                     help="MX workload: exact products (bf16 matrix cores) or block-scaled fp8 matrix cores")
     args = ap.parse_args()
@@ -229,35 +231,40 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region 1: K whole steps (quantize + GEMM + epilogue) back to back.
-    # No events between the kernels: a recorded event costs the stream a few
-    # microseconds, which would be charged to the step.
+    # The timed launches are captured once into HIP graphs (K whole steps, and
+    # K GEMM launches) and replayed, so the host's per-call overhead (Python,
+    # ctypes) is not charged to the GPU: the library launches onto the current
+    # stream, the step allocates nothing and records no memset. --eager
+    # launches every step from Python instead.
     K_steps = args.steps
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(K_steps):
-        step(i)
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / K_steps
 
+    def timed(fn):
+        """Milliseconds per call of fn(i), i = 0 .. K-1, on the current stream."""
+        if args.eager:
+            run = lambda: [fn(i) for i in range(K_steps)]  # noqa: E731
+        else:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(K_steps):
+                    fn(i)
+            run = graph.replay
+            run()  # one untimed replay
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        run()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / K_steps, time.perf_counter() - t0
+
+    # Timed region 1: K whole steps (quantize + GEMM + epilogue) back to back.
+    ms_per_step, wall = timed(step)
     # Timed region 2: the GEMM kernel alone, K launches over the same rotating
     # buffer sets, bracketed by events on the stream it runs on; the average
     # launch duration feeds the roofline.
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    g0.record()
-    for i in range(K_steps):
-        gemm(i)
-    g1.record()
-    torch.cuda.synchronize()
-    gemm_ms = g0.elapsed_time(g1) / K_steps
+    gemm_ms, _ = timed(gemm)
 
     if unit == "GB/s":
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -290,6 +297,7 @@ def main():
         "config": {"workload": f"{name}: {DESCRIPTION[name]}"
                    + (f" ({args.mx_mode} mode)" if act == "mxfp8" else ""), "M": M, "K": K, "N": N,
                    "rotating_buffer_sets": nsets, "gemm_ms": gemm_ms,
+                   "launch": "eager" if args.eager else "hip graph (K steps captured, replayed once)",
                    "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9},
         "roofline": roof,
     }

@@ -33,6 +33,7 @@
 //    z * colsum, which yields the same exact C.
 //  * MX: every 32-element K block carries its own pair of E8M0 factors inside
 //    the K loop ("TileLang tutorial, chapter 27", sections 4.1 and 4.3).
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -448,7 +449,6 @@ struct DmaCfg {
   static constexpr int EPI_ALL = EPI + BM * 8;        // + per-row scale and zero point
   static constexpr int LDS = NS * STAGE > EPI_ALL ? NS * STAGE : EPI_ALL;
   static_assert(STAGE % 1024 == 0 && IPS % NW == 0 && (BM * RB) % 1024 == 0, "stage / wave-load mismatch");
-  static_assert(IA % IPW == 0, "every wave loads from one operand only");
   static_assert(NKK >= 2 && NKK % 2 == 0 && SLOTS >= IPW, "load slots");
   static_assert(NS >= 2 && (NS - 2) * IPW < 64, "vmcnt range");
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
   const int nkt = (int)(p.K_pad / BK);
 
   // Stage loads (buffer_load ... lds, 16 bytes per lane). Wave wid issues the
-  // stage's 1 KB loads wid*IPW .. wid*IPW+IPW-1, all from one operand. For A,
+  // stage's 1 KB loads wid*IPW .. wid*IPW+IPW-1. For A,
   // lane l fetches the 16-byte chunk that belongs at LDS slot l of the
   // swizzled row-major tile (row * lda + chunk); for W, one load copies one
   // packed 16 x 64 weight block (1 KB contiguous) as it is. The lane offsets
@@ -496,31 +496,37 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
   // the last row, so nothing past it is read: the hardware returns zeros for
   // every dword outside the range (the weights are zero there). A stage past
   // the last one gets an empty range, so its loads move no data and still
-  // count in vmcnt.
-  const bool wave_a = wid * IPW < C::IA;
-  const int64_t stride = p.lda;  // A rows
-  const uint8_t* const obase = wave_a ? p.a + m0 * p.lda : p.w + n0 * p.K_pad;
+  // count in vmcnt. Load j = wid * IPW + i of a stage carries A when j < IA,
+  // else W (the test is uniform over the wave).
+  const uint8_t* const abase = p.a + m0 * p.lda;
+  const uint8_t* const wbase = p.w + n0 * p.K_pad;
   const int64_t last_a_row = min((int64_t)BM - 1, p.M - 1 - m0);
-  const uint32_t nrec = (uint32_t)(wave_a ? last_a_row * p.lda + ((p.K + 15) & ~(int64_t)15) : (int64_t)BN * p.K_pad);
+  const uint32_t nrec_a = (uint32_t)(last_a_row * p.lda + ((p.K + 15) & ~(int64_t)15));
+  // W rows end at N_pad (N rounded up to 256): a tile width that does not
+  // divide 256 must not read past the packed codes
+  const int64_t n_pad = (p.N + 255) / 256 * 256;
+  const uint32_t nrec_w = (uint32_t)(min((int64_t)BN, n_pad - n0) * p.K_pad);
   uint32_t voff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    if (wave_a) {  // swizzled row-major A tile: slot P holds chunk c of row r
-      const int P = (wid * IPW + i) * 1024 + lane * 16;
+    const int j = wid * IPW + i;
+    if (j < C::IA) {  // swizzled row-major A tile: slot P holds chunk c of row r
+      const int P = j * 1024 + lane * 16;
       const int r = P / RB;
       const int c = ((P % RB) >> 4) ^ ((r / (RB >= 256 ? 1 : 256 / RB)) % (RB / 16));
-      voff[i] = (uint32_t)(min((int64_t)r, last_a_row) * stride) + (uint32_t)(c * 16);
+      voff[i] = (uint32_t)(min((int64_t)r, last_a_row) * p.lda) + (uint32_t)(c * 16);
     } else {  // W tile: the weight blocks (16 rows x 64 K, 1 KB) copied whole, in order
-      const int j = wid * IPW + i - C::IA;
-      voff[i] = (uint32_t)(((j / (BK / 64)) * (p.K_pad >> 6) + j % (BK / 64)) << 10) + (uint32_t)(lane * 16);
+      const int jw = j - C::IA;
+      voff[i] = (uint32_t)(((jw / (BK / 64)) * (p.K_pad >> 6) + jw % (BK / 64)) << 10) + (uint32_t)(lane * 16);
     }
   }
-  const int kstride = wave_a ? BK : BK * 16;  // bytes per stage along the operand's K order
   auto dma = [&](int kt, int s, int i, bool live) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)obase, (short)0, live ? (int)nrec : 0, kRawBufferWord3);
+    const bool ja = wid * IPW + i < C::IA;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ja ? abase : wbase), (short)0, live ? (int)(ja ? nrec_a : nrec_w) : 0, kRawBufferWord3);
+    // bytes per stage along the operand's K order: A rows are plain, W blocks hold 16 rows
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, QG_LDSP(smem + s * STAGE + (wid * IPW + i) * 1024), 16, (int)voff[i],
-                                             kt * kstride, 0, 0);
+                                             kt * (ja ? BK : BK * 16), 0, 0);
   };
 
   v16i acc[FM][FN];
@@ -681,6 +687,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
   }
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int NS, bool ASYM, int OUT>
 static hipError_t launch_dma(const GemmArgs& a, hipStream_t st) {
   using C = DmaCfg<BM, BN, BK, WM, WN, NS, ASYM, OUT>;
@@ -809,9 +828,14 @@ static hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
 template <bool ASYM, int OUT>
 static hipError_t launch_i8(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 16) return launch_decode<ASYM, OUT>(a, st);
-  const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big_tiles >= 256) return launch_dma<256, 256, 64, 2, 4, 4, ASYM, OUT>(a, st);
-  return launch_dma<128, 128, 128, 2, 2, 4, ASYM, OUT>(a, st);
+  // The largest tile whose count still fills every CU once: bigger tiles
+  // reuse each loaded byte more, but a round of tiles that leaves CUs idle
+  // costs a whole tile time.
+  const int64_t cus = cu_count();
+  auto tiles = [&](int64_t bm, int64_t bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+  if (tiles(256, 256) >= cus) return launch_dma<256, 256, 64, 2, 4, 5, ASYM, OUT>(a, st);
+  if (tiles(128, 128) >= cus) return launch_dma<128, 128, 128, 2, 4, 4, ASYM, OUT>(a, st);
+  return launch_dma<64, 128, 128, 2, 4, 6, ASYM, OUT>(a, st);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int MODE, bool ASYM, int OUT>

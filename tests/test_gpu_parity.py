@@ -231,6 +231,24 @@ def test_gemm_deterministic(ops):
     assert np.array_equal(o1.view(np.uint16), o2.view(np.uint16))
 
 
+@pytest.mark.parametrize("act", ["sym_row", "asym_row"])
+@pytest.mark.parametrize("M,N,K", [(1100, 3900, 700), (4100, 4100, 320)])
+def test_gemm_large_tile_configs(ops, M, N, K, act):
+    """Shapes whose tile count selects the 128x128 and 256x256 tile kernels
+    on a 256-CU device (ragged in M, N and K); int32 sums exact, float32
+    epilogue in tolerance."""
+    print_case("gemm tile config", M, N, K, act)
+    A, W = make_inputs("c2_per_token", M=M, K=K, N=N, seed=3 * M + N + 5 * K)
+    if act == "asym_row":
+        A = A - np.float32(0.3)
+    ref = O.quantized_linear(A, W, act=ACT[act][2], wgt="channel")
+    fmt, gran, _ = ACT[act]
+    a = ops.qgemm_quantize_rows(dev(A), fmt, gran)
+    pw = ops.qgemm_prepack_weights(dev(W), 0, 1)
+    _check_out(host(ops.qgemm_run(a, pw, 2)), None, 2, ref["C"])
+    _check_out(host(ops.qgemm_run(a, pw, 0)), ref["y"], 0)
+
+
 def test_gemm_empty_m(ops):
     pw = ops.qgemm_prepack_weights(dev(np.ones((8, 64), np.float32)), 0, 1)
     a = ops.qgemm_quantize_rows(torch.empty((0, 64), device="cuda"), 0, 1)
