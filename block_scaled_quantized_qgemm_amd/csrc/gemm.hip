@@ -830,35 +830,18 @@ static hipError_t launch_i8(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 16) return launch_decode<ASYM, OUT>(a, st);
   // The largest tile whose count still fills every CU once: bigger tiles
   // reuse each loaded byte more, but a round of tiles that leaves CUs idle
-  // costs a whole tile time.
+  // costs a whole tile time. 256 x 256 tiles (one 160 KB workgroup per CU)
+  // when they come in whole rounds; when they would end in a partial round,
+  // 128 x 256 tiles with a 72 KB ring, two workgroups per CU, whose finer
+  // grain fills the last round and whose barriers overlap each other's
+  // matrix-core work.
   const int64_t cus = cu_count();
-  auto tiles = [&](int64_t m, int64_t n, int64_t bm, int64_t bn) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
-  if (tiles(a.M, a.N, 256, 256) >= cus) {
-    // When the 256 x 256 tiles end in a partial round over the CUs, the
-    // leading columns take the whole rounds and the remaining columns follow
-    // as 128 x 256 tiles, which fill the last round with about twice as many
-    // workgroups of half the work each. The column split is a multiple of
-    // 256, so the packed weights, their scales and column sums and the output
-    // are simply offset.
-    const int64_t tm = (a.M + 255) / 256;
-    const int64_t whole = tiles(a.M, a.N, 256, 256) / cus * cus;
-    const int64_t n_split = whole / tm * 256;
-    if (whole != tiles(a.M, a.N, 256, 256) && n_split > 0 && n_split < a.N &&
-        tiles(a.M, a.N - n_split, 128, 256) <= cus) {
-      GemmArgs lead = a, rest = a;
-      lead.N = n_split;
-      rest.N = a.N - n_split;
-      rest.w = a.w + n_split * a.K_pad;
-      if (!a.w_per_tensor) rest.sw = a.sw + n_split;
-      rest.colsum = a.colsum + n_split;
-      rest.out = reinterpret_cast<uint8_t*>(a.out) + n_split * (OUT == 1 ? 2 : 4);
-      hipError_t e = launch_dma<256, 256, 64, 2, 4, 5, ASYM, OUT>(lead, st);
-      if (e != hipSuccess) return e;
-      return launch_dma<128, 256, 64, 2, 4, 6, ASYM, OUT>(rest, st);
-    }
-    return launch_dma<256, 256, 64, 2, 4, 5, ASYM, OUT>(a, st);
+  auto tiles = [&](int64_t bm, int64_t bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+  if (tiles(256, 256) >= cus) {
+    if (tiles(256, 256) % cus == 0) return launch_dma<256, 256, 64, 2, 4, 5, ASYM, OUT>(a, st);
+    return launch_dma<128, 256, 64, 2, 4, 3, ASYM, OUT>(a, st);
   }
-  if (tiles(a.M, a.N, 128, 128) >= cus) return launch_dma<128, 128, 128, 2, 4, 4, ASYM, OUT>(a, st);
+  if (tiles(128, 128) >= cus) return launch_dma<128, 128, 128, 2, 4, 4, ASYM, OUT>(a, st);
   return launch_dma<64, 128, 128, 2, 4, 6, ASYM, OUT>(a, st);
 }
 

@@ -232,11 +232,13 @@ def test_gemm_deterministic(ops):
 
 
 @pytest.mark.parametrize("act", ["sym_row", "asym_row"])
-@pytest.mark.parametrize("M,N,K", [(1100, 3900, 700), (4100, 4100, 320)])
+@pytest.mark.parametrize("M,N,K", [(1100, 3900, 700), (4100, 4100, 320), (4000, 4090, 300)])
 def test_gemm_large_tile_configs(ops, M, N, K, act):
-    """Shapes whose tile count selects the 128x128 and 256x256 tile kernels
-    on a 256-CU device (ragged in M, N and K); int32 sums exact, float32
-    epilogue in tolerance."""
+    """Shapes whose tile count selects, on a 256-CU device, the 128x128 tiles
+    (1100 x 3900), the 128x256 tiles two per CU (4100 x 4100: 289 tiles of
+    256 x 256, a partial round) and the 256x256 tiles (4000 x 4090: exactly
+    256 of them), ragged in M, N and K; int32 sums exact, float32 epilogue in
+    tolerance."""
     print_case("gemm tile config", M, N, K, act)
     A, W = make_inputs("c2_per_token", M=M, K=K, N=N, seed=3 * M + N + 5 * K)
     if act == "asym_row":
