@@ -1,27 +1,30 @@
 // Matrix-core GEMMs for gfx950.
 //
-// Three modes share one tiled kernel template:
-//  * I8   -- int8 x int8 on v_mfma_i32_32x32x32_i8: exact int32 sums and the
-//            fused dequantization epilogue.
-//  * MXB  -- MX (e4m3 + E8M0 per 32 K) with exact products: each e4m3 value is
-//            multiplied by its block's power-of-two scale while the tile is
-//            moved into LDS (v_cvt_scalef32_pk_bf16_fp8; e4m3 times a power of
-//            two is exactly representable in bf16), then v_mfma_f32_32x32x16_bf16
-//            forms exact products and float32 sums.
-//  * MXF  -- MX on the block-scaled fp8 matrix cores
-//            (v_mfma_scale_f32_32x32x64_f8f6f4), one E8M0 byte per lane and block.
-//            Inside each group of 8 consecutive K the hardware aligns the
-//            products to the largest one and drops bits more than 13 binades
-//            below it, so sums are not float32-exact.
+// int8 x int8 (exact int32 sums, fused dequantization epilogue):
+//  * gemm_i8_dma_kernel -- tiled, v_mfma_i32_32x32x32_i8, tiles fetched from
+//    global memory straight into an LDS ring; for M > 16.
+//  * gemm_i8_decode_kernel -- M <= 16: a stream over the weights with
+//    v_mfma_i32_16x16x64_i8, every weight byte read once into registers.
 //
-// Tiling: a workgroup owns a BM x BN tile and walks K in BK-deep steps; the
-// next step's A and W tiles are fetched from global memory into registers
-// (16-byte loads, consecutive lanes on consecutive bytes of a row) while the
-// matrix cores consume the current step out of LDS; LDS holds two stages whose
-// rows store 16-byte chunks XOR-swizzled by row, so the 16-byte fragment reads
-// of 32 consecutive rows spread over all banks. Each wave owns a
-// (BM/WM) x (BN/WN) sub-tile of 32x32 matrix-core blocks. The epilogue goes
-// through LDS so that every lane stores 16 contiguous bytes of a row.
+// MX (e4m3 + E8M0 per 32 K), float32 output, gemm_mx_kernel in two modes:
+//  * MXB -- exact products: each e4m3 value is multiplied by its block's
+//           power-of-two scale while the tile is moved into LDS
+//           (v_cvt_scalef32_pk_bf16_fp8; e4m3 times a power of two is exactly
+//           representable in bf16), then v_mfma_f32_32x32x16_bf16 forms exact
+//           products and float32 sums.
+//  * MXF -- the block-scaled fp8 matrix cores
+//           (v_mfma_scale_f32_32x32x64_f8f6f4), one E8M0 byte per lane and
+//           block. Inside each group of 8 consecutive K the hardware aligns the
+//           products to the largest one and drops bits more than 13 binades
+//           below it, so sums are not float32-exact.
+//  The MX tiling: a workgroup owns a BM x BN tile and walks K in BK-deep
+//  steps; the next step's A and W tiles are fetched from global memory into
+//  registers (16-byte loads, consecutive lanes on consecutive bytes of a row)
+//  while the matrix cores consume the current step out of LDS; LDS holds two
+//  stages whose rows store 16-byte chunks XOR-swizzled by row, so the 16-byte
+//  fragment reads of 32 consecutive rows spread over all banks. Each wave owns
+//  a (BM/WM) x (BN/WN) sub-tile of 32x32 matrix-core blocks. The epilogue goes
+//  through LDS so that every lane stores 16 contiguous bytes of a row.
 //
 // Semantics followed:
 //  * int8: C = sum_k (q_a - z_a) q_w exactly in int32 ("Activation
@@ -34,14 +37,13 @@
 //  * MX: every 32-element K block carries its own pair of E8M0 factors inside
 //    the K loop ("TileLang tutorial, chapter 27", sections 4.1 and 4.3).
 #include <atomic>
-#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace qg {
 
-enum GemmMode { I8 = 0, MXB = 1, MXF = 2 };
+enum MxMode { MXB = 1, MXF = 2 };
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -84,8 +86,8 @@ __device__ inline void fp8x16_to_bf16(const v4i& q, float scale, v4i& lo, v4i& h
   hi = v4i{w[4], w[5], w[6], w[7]};
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int MODE, bool ASYM, int OUT>
-struct GemmCfg {
+template <int BM, int BN, int BK, int WM, int WN, int MODE>
+struct MxCfg {
   static constexpr int NT = WM * WN * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
@@ -95,19 +97,18 @@ struct GemmCfg {
   static constexpr int STAGE = (BM + BN) * RB;
   static constexpr int RS = TN + 8;  // epilogue staging row stride in words: rows r and r+4
                                      // (the two half-waves) start 32 banks apart
-  static constexpr int EPI = WM * WN * 32 * RS * 4;      // per-wave 32 x TN float/int staging
+  static constexpr int EPI = WM * WN * 32 * RS * 4;      // per-wave 32 x TN float staging
   static constexpr int LDS = 2 * STAGE > EPI ? 2 * STAGE : EPI;
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile / thread mismatch");
   static_assert(MODE != MXF || BK % 64 == 0, "scaled fp8 steps are 64 deep");
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int MODE, bool ASYM, int OUT>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
-  using C = GemmCfg<BM, BN, BK, WM, WN, MODE, ASYM, OUT>;
+template <int BM, int BN, int BK, int WM, int WN, int MODE>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
+  using C = MxCfg<BM, BN, BK, WM, WN, MODE>;
   constexpr int NT = C::NT, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RB = C::RB;
   constexpr int A_CH = C::A_CH, B_CH = C::B_CH, STAGE = C::STAGE;
-  constexpr bool MX = MODE != I8;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -175,18 +176,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                          \
       const int id = tid + i * NT;                                                              \
       const int r = id / CPR, c = id % CPR;                                                     \
-      if constexpr (MX) {                                                                       \
-        if ((int64_t)(KT) * BK + c * 16 >= p.K) RA[i] = v4i{0, 0, 0, 0};                        \
-      }                                                                                         \
+      if ((int64_t)(KT) * BK + c * 16 >= p.K) RA[i] = v4i{0, 0, 0, 0};                          \
       if constexpr (MODE == MXB) {                                                              \
         v4i lo, hi;                                                                             \
         fp8x16_to_bf16(RA[i], e8m0_to_f32(EA[i]), lo, hi);                                      \
         *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, 2 * c)) = lo;                              \
         *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, 2 * c + 1)) = hi;                          \
       } else {                                                                                  \
-        v4i v = RA[i];                                                                          \
-        if (ASYM) v ^= (int)0x80808080u;                                                        \
-        *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, c)) = v;                                   \
+        *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, c)) = RA[i];                               \
       }                                                                                         \
     }                                                                                           \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                          \
@@ -224,8 +221,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
     }                                                                                           \
   }
 
-  typedef typename std::conditional<MX, v16f, v16i>::type acc_t;
-  acc_t acc[FM][FN];
+  v16f acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -237,20 +233,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   {                                                                                             \
     const uint8_t* sa = smem + (S) * STAGE;                                                     \
     const uint8_t* sb = sa + BM * RB;                                                           \
-    if constexpr (MODE == I8) {                                                                 \
-      _Pragma("unroll") for (int kk = 0; kk < BK / 32; ++kk) {                                  \
-        const int ch = kk * 2 + (lane >> 5);                                                    \
-        v4i af[FM], bf[FN];                                                                     \
-        _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] =                                  \
-            *reinterpret_cast<const v4i*>(sa + lds_off<RB>(wm * TM + i * 32 + (lane & 31), ch)); \
-        _Pragma("unroll") for (int j = 0; j < FN; ++j) bf[j] =                                  \
-            *reinterpret_cast<const v4i*>(sb + lds_off<RB>(wn * TN + j * 32 + (lane & 31), ch)); \
-        _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
-          _Pragma("unroll") for (int j = 0; j < FN; ++j)                                        \
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0); \
-        __builtin_amdgcn_sched_barrier(0); /* keep one sub-step of fragments live */            \
-      }                                                                                         \
-    } else if constexpr (MODE == MXB) {                                                         \
+    if constexpr (MODE == MXB) {                                                                \
       /* 16-deep bf16 steps: lane 32h + r holds K 8h..8h+7 of the step */                      \
       _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                                  \
         const int ch = kk * 2 + (lane >> 5);                                                    \
@@ -336,17 +319,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
   uint8_t* wreg = smem + wid * (32 * RS * 4);
   const int cq = (lane % LPR) * 4;   // this lane's first column inside the wave tile
   const int64_t nq = n0 + wn * TN + cq;
-  float sw4[4] = {0.f, 0.f, 0.f, 0.f};
-  int cs4[4] = {0, 0, 0, 0};
-  if constexpr (!MX) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (nq + t < p.N) {
-        sw4[t] = p.w_per_tensor ? p.sw[0] : p.sw[nq + t];
-        if (ASYM) cs4[t] = p.colsum[nq + t];
-      }
-    }
-  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -354,64 +326,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        int bits;
-        if constexpr (MX)
-          bits = __float_as_int(acc[i][j][e]);
-        else
-          bits = acc[i][j][e];
-        reinterpret_cast<int*>(wreg)[r * RS + j * 32 + (lane & 31)] = bits;
+        reinterpret_cast<float*>(wreg)[r * RS + j * 32 + (lane & 31)] = acc[i][j][e];
       }
     __syncthreads();
 #pragma unroll
     for (int pass = 0; pass < 32 / RPI; ++pass) {
       const int r = pass * RPI + lane / LPR;
       const int64_t m = m0 + wm * TM + i * 32 + r;
-      const v4i raw = *reinterpret_cast<const v4i*>(wreg + (r * RS + cq) * 4);
+      const v4f y = *reinterpret_cast<const v4f*>(wreg + (r * RS + cq) * 4);
       if (m < p.M && nq < p.N) {
-        float y[4];
-        int ci[4];
-        if constexpr (MX) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) y[t] = __int_as_float(raw[t]);
-        } else {
-          const float sam = p.a_per_tensor ? p.sa[0] : p.sa[m];
-          const int zm = ASYM ? (p.a_per_tensor ? p.za[0] : p.za[m]) : 0;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            int c = raw[t];
-            // wrap-around int32 arithmetic: the true C fits, so the result is exact
-            if (ASYM) c = (int)((uint32_t)c - (uint32_t)(zm - 128) * (uint32_t)cs4[t]);
-            ci[t] = c;
-            y[t] = (float)c * (sam * sw4[t]);
-          }
-        }
-        const bool full = nq + 3 < p.N;
-        if constexpr (OUT == 2) {
-          int32_t* o = reinterpret_cast<int32_t*>(p.out) + m * p.ldo + nq;
-          if (full)
-            *reinterpret_cast<v4i*>(o) = v4i{ci[0], ci[1], ci[2], ci[3]};
-          else
-            for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = ci[t];
-        } else if constexpr (OUT == 0) {
-          float* o = reinterpret_cast<float*>(p.out) + m * p.ldo + nq;
-          if (full)
-            *reinterpret_cast<v4f*>(o) = v4f{y[0], y[1], y[2], y[3]};
-          else
-            for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = y[t];
-        } else {
-          uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + m * p.ldo + nq;
-          uint16_t h[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) h[t] = f32_to_bf16_rne(y[t]);
-          if (full) {
-            uint2 v;
-            v.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-            v.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-            *reinterpret_cast<uint2*>(o) = v;
-          } else {
-            for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = h[t];
-          }
-        }
+        float* o = reinterpret_cast<float*>(p.out) + m * p.ldo + nq;
+        if (nq + 3 < p.N)
+          *reinterpret_cast<v4f*>(o) = y;
+        else
+          for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = y[t];
       }
     }
     __syncthreads();
@@ -602,7 +530,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  // ---- epilogue through LDS (same scheme as gemm_kernel); the tile's row
+  // ---- epilogue through LDS (the scheme of gemm_mx_kernel); the tile's row
   // scales and zero points are fetched once into LDS after the staging area
   constexpr int LPR = TN / 4;
   constexpr int RPI = 64 / LPR;
@@ -845,10 +773,10 @@ static hipError_t launch_i8(const GemmArgs& a, hipStream_t st) {
   return launch_dma<64, 128, 128, 2, 4, 6, ASYM, OUT>(a, st);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int MODE, bool ASYM, int OUT>
-static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
-  using C = GemmCfg<BM, BN, BK, WM, WN, MODE, ASYM, OUT>;
-  auto kern = gemm_kernel<BM, BN, BK, WM, WN, MODE, ASYM, OUT>;
+template <int BM, int BN, int BK, int WM, int WN, int MODE>
+static hipError_t launch_mx_cfg(const GemmArgs& a, hipStream_t st) {
+  using C = MxCfg<BM, BN, BK, WM, WN, MODE>;
+  auto kern = gemm_mx_kernel<BM, BN, BK, WM, WN, MODE>;
   const size_t lds = C::LDS;
   if (lds > 65536) {  // above the default dynamic-LDS limit (gfx950 has 160 KiB)
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -859,16 +787,16 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int MODE, bool ASYM, int OUT>
-static hipError_t launch_pick(const GemmArgs& a, hipStream_t st) {
-  // Large problems: 256x256 tiles (8 waves of 128x64); otherwise 128x128 (4 waves of 64x64).
-  // K steps of 128 bytes for the 1-byte operands; the bf16 staging of the
-  // exact MX mode doubles the LDS row, so it steps 64 deep.
+template <int MODE>
+static hipError_t launch_mx(const GemmArgs& a, hipStream_t st) {
+  // Large problems: 256x256 tiles (8 waves of 128x64); otherwise 128x128 (4
+  // waves of 64x64). The bf16 staging of the exact mode doubles the LDS row,
+  // so it steps 64 deep; the scaled-fp8 mode steps 128 deep on small tiles
+  // and 64 deep on large ones (its scales need registers too).
   constexpr int BK = MODE == MXB ? 64 : 128;
-  constexpr int BK_BIG = MODE == I8 ? 128 : 64;  // the scaled-fp8 scales need registers too
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big_tiles >= 256) return launch_cfg<256, 256, BK_BIG, 2, 4, MODE, ASYM, OUT>(a, st);
-  return launch_cfg<128, 128, BK, 2, 2, MODE, ASYM, OUT>(a, st);
+  if (big_tiles >= 256) return launch_mx_cfg<256, 256, 64, 2, 4, MODE>(a, st);
+  return launch_mx_cfg<128, 128, BK, 2, 2, MODE>(a, st);
 }
 
 hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_t st) {
@@ -885,8 +813,8 @@ hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_
 
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  if (mode == 1) return launch_pick<MXF, false, 0>(a, st);
-  return launch_pick<MXB, false, 0>(a, st);
+  if (mode == 1) return launch_mx<MXF>(a, st);
+  return launch_mx<MXB>(a, st);
 }
 
 }  // namespace qg
