@@ -83,9 +83,22 @@ __device__ inline void scale_from_stats(const RowStats& st, float& s, int& z) {
   }
 }
 
+// The correctly rounded quotient v / s from y = RN(1 / s), taken once per
+// row: q0 = RN(v * y) is within an ulp of v / s, the FMA forms the remainder
+// v - q0 * s exactly, and RN(q0 + remainder * y) is RN(v / s) (Markstein's
+// correction step; it needs normal intermediates, which hold whenever
+// |v / s| is above 2^-100, and below that both quotients give the code 0).
+// The identity is checked on the CPU against the IEEE division near every
+// code boundary (n + 1/2) s over the significands of s.
+__device__ inline float div_rn(float v, float s, float y) {
+  const float q0 = v * y;
+  const float e = __builtin_fmaf(-q0, s, v);
+  return __builtin_fmaf(e, y, q0);
+}
+
 template <bool ASYM>
-__device__ inline uint32_t encode_code(float v, float s, float zf) {
-  float r = rintf(v / s);
+__device__ inline uint32_t encode_code(float v, float s, float y, float zf) {
+  float r = rintf(div_rn(v, s, y));
   if (ASYM) {
     r = fminf(fmaxf(r + zf, 0.0f), 255.0f);
     return (uint32_t)(int)r & 0xffu;
@@ -171,21 +184,22 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     scale_from_stats<ASYM>(r, s, z);
   }
   const float zf = (float)z;
+  const float y = 1.0f / s;  // correctly rounded
 
   int csum = 0;
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int64_t k = 4 * ((int64_t)t + (int64_t)kRowThreads * u);
     if (k + 4 <= K) {
-      uint32_t c0 = encode_code<ASYM>(v[u].x, s, zf), c1 = encode_code<ASYM>(v[u].y, s, zf);
-      uint32_t c2 = encode_code<ASYM>(v[u].z, s, zf), c3 = encode_code<ASYM>(v[u].w, s, zf);
+      uint32_t c0 = encode_code<ASYM>(v[u].x, s, y, zf), c1 = encode_code<ASYM>(v[u].y, s, y, zf);
+      uint32_t c2 = encode_code<ASYM>(v[u].z, s, y, zf), c3 = encode_code<ASYM>(v[u].w, s, y, zf);
       *reinterpret_cast<uint32_t*>(code_ptr(qd, row, k)) = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
       if (colsum) csum += code_value<ASYM>(c0) + code_value<ASYM>(c1) + code_value<ASYM>(c2) + code_value<ASYM>(c3);
     } else if (k < K) {
       float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       for (int c = 0; c < 4; ++c)
         if (k + c < K) {
-          uint32_t cc = encode_code<ASYM>(e[c], s, zf);
+          uint32_t cc = encode_code<ASYM>(e[c], s, y, zf);
           *code_ptr(qd, row, k + c) = (uint8_t)cc;
           if (colsum) csum += code_value<ASYM>(cc);
         }
@@ -226,9 +240,10 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_long_kernel(
     scale_from_stats<ASYM>(r, s, z);
   }
   const float zf = (float)z;
+  const float y = 1.0f / s;  // correctly rounded
   int csum = 0;
   for (int64_t k = t; k < K; k += kRowThreads) {
-    uint32_t c = encode_code<ASYM>(xr[k], s, zf);
+    uint32_t c = encode_code<ASYM>(xr[k], s, y, zf);
     *code_ptr(qd, row, k) = (uint8_t)c;
     csum += code_value<ASYM>(c);
   }
