@@ -96,8 +96,9 @@ def measured_traffic(name, launches_per_step=1):
     return float(t["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(name, A, W, budget_s=10.0):
-    """The oracle, untuned, on a bounded sample of the same workload."""
+def cpu_baseline(name, A, W, budget_s=10.0, fused=None):
+    """The oracle, untuned, on a bounded sample of the same workload.
+    fused: (gamma, eps, bias) to time the RMSNorm-fused step with a bias."""
     import numpy as np
     import oracle as O
     try:
@@ -124,13 +125,16 @@ def cpu_baseline(name, A, W, budget_s=10.0):
             qa, Ea = O.quantize_mx(As)
             _ = O.mx_dequantize(qa, Ea) @ Wd.T
         else:
-            if act == "uint8_asym":
+            if fused is not None:
+                r = O.rmsnorm_quantize(As, fused[0], fused[1], act="asym_row" if act == "uint8_asym" else "sym_row")
+                qa, sa, za = r[0], r[1], (r[2] if act == "uint8_asym" else 0)
+            elif act == "uint8_asym":
                 qa, sa, za = O.quantize_asym_uint8(As, per_row=(gran == "row"))
             else:
                 qa, sa = O.quantize_sym_int8(As, per_row=(gran == "row"))
                 za = 0
             C = O.int_gemm(qa, za, Wq)
-            _ = O.epilogue(C, sa, Ws)
+            _ = O.add_bias(O.epilogue(C, sa, Ws), None if fused is None else fused[2])
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 1000:
@@ -158,6 +162,9 @@ def main():
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB device-to-device: a plain copy of known size "
                          "whose FETCH_SIZE / WRITE_SIZE counters calibrate the GEMM's traffic")
+    ap.add_argument("--fused", action="store_true",
+                    help="int8 per-token workloads: RMSNorm fused with the quantizer "
+                         "(qgemm_rmsnorm_quantize_rows) and a float32 bias in the GEMM epilogue")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying a captured HIP graph")
     ap.add_argument("--mx-mode", default="exact", choices=["exact", "scaled-mfma"],
@@ -176,6 +183,9 @@ def main():
 
     name = args.workload
     act, gran, wgran, out, unit = WORKLOADS[name]
+    if args.fused and (act == "mxfp8" or gran != "row"):
+        print("bench.py: --fused applies to the per-token int8 / uint8 workloads", file=sys.stderr)
+        sys.exit(2)
     M, K, N, _, _ = SHAPES[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -194,6 +204,9 @@ def main():
     w0 = ops.qgemm_prepack_weights(W0, wfmt, wgr)
     torch.cuda.synchronize()
     ops_count, step_bytes, gemm_bytes = algorithmic(name, M, K, N)
+    if args.fused:  # the norm weight and the bias are read once more
+        step_bytes += 4 * K + 4 * N
+        gemm_bytes += 4 * N
     set_bytes = A0.numel() * 4 + w0.packed.numel() + M * ((N + 7) // 8 * 8) * (4 if out == "f32" else 2) + M * K
     nsets = args.rotate or max(1, min(64, math.ceil(3 * MALL_BYTES / set_bytes)))
 
@@ -205,6 +218,10 @@ def main():
         qi = ops.qgemm_quantize_rows(Ai, fmt, agr)
         oi = torch.empty((M, (N + 7) // 8 * 8), dtype=odt, device=dev)
         sets.append((Ai, wi, qi, oi))
+    rng = np.random.default_rng(1234)
+    gamma = torch.from_numpy(rng.normal(1.0, 0.1, size=K).astype(np.float32)).to(dev)
+    bias = torch.from_numpy(rng.normal(0.0, 0.5, size=N).astype(np.float32)).to(dev)
+    eps = 1e-6
     ws = None
     need = ops.qgemm_workspace_bytes(M, K, fmt, agr)
     if need:
@@ -214,14 +231,17 @@ def main():
 
     def quantize(i):
         Ai, wi, qi, oi = sets[i % nsets]
-        ops.qgemm_quantize_rows(Ai, fmt, agr, out=qi, workspace=ws)
+        if args.fused:
+            ops.qgemm_rmsnorm_quantize_rows(Ai, gamma, eps, fmt, out=qi)
+        else:
+            ops.qgemm_quantize_rows(Ai, fmt, agr, out=qi, workspace=ws)
 
     def gemm(i):
         Ai, wi, qi, oi = sets[i % nsets]
         if fmt == ops.FMT_MXFP8_E4M3:
             ops.qgemm_run_mx(qi, wi, out=oi, mode=mx_mode)
         else:
-            ops.qgemm_run(qi, wi, otype, out=oi)
+            ops.qgemm_run(qi, wi, otype, out=oi, bias=bias if args.fused else None)
 
     def step(i):
         quantize(i)
@@ -295,7 +315,9 @@ def main():
         "dtype": "fp8-e4m3" if act == "mxfp8" else "i8",
         "data": "synthetic (seeded generator with the workload's shapes and distributions)",
         "config": {"workload": f"{name}: {DESCRIPTION[name]}"
-                   + (f" ({args.mx_mode} mode)" if act == "mxfp8" else ""), "M": M, "K": K, "N": N,
+                   + (f" ({args.mx_mode} mode)" if act == "mxfp8" else "")
+                   + (" with RMSNorm fused into the quantizer and a float32 bias" if args.fused else ""),
+                   "M": M, "K": K, "N": N,
                    "rotating_buffer_sets": nsets, "gemm_ms": gemm_ms,
                    "launch": "eager" if args.eager else "hip graph (K steps captured, replayed once)",
                    "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9},
@@ -312,7 +334,8 @@ def main():
     print(f"[bench] {name}: {ms_per_step * 1e3:.2f} us/step, gemm {gemm_ms * 1e3:.2f} us, "
           f"wall {wall:.3f} s for {K_steps} steps", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(name, A_np, W_np, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(name, A_np, W_np, args.cpu_budget,
+                                            (gamma.cpu().numpy(), eps, bias.cpu().numpy()) if args.fused else None)
     print(json.dumps(line), flush=True)
 
 

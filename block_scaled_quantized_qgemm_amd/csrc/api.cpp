@@ -155,6 +155,25 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int f
   return launch_status();
 }
 
+int qgemm_rmsnorm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, const float* gamma, float eps,
+                                int fmt, int gran, void* q, int64_t ldq, float* scales, int32_t* zero_points,
+                                void* stream) {
+  if (!is_int_fmt(fmt) || gran != QGEMM_GRAN_ROW) return QGEMM_E_MODE;
+  if (!(eps >= 0.0f) || !(eps <= 3.0e38f)) return QGEMM_E_MODE;  // also rejects NaN
+  if (M < 0 || M > kMaxRows || K < 1 || K > ((int64_t)1 << 30)) return QGEMM_E_SHAPE;
+  if (M == 0) return QGEMM_OK;
+  if (!x || !gamma || !q || !scales || (fmt == QGEMM_FMT_UINT8_ASYM && !zero_points)) return QGEMM_E_NULL;
+  if (ldx < K || ldq < K) return QGEMM_E_SHAPE;
+  if (!aligned(x, 4) || !aligned(gamma, 4) || ldq % 16 != 0 || !aligned(q, 16) || !aligned(scales, 4) ||
+      (zero_points && !aligned(zero_points, 4)))
+    return QGEMM_E_ALIGN;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+  qg::launch_rmsnorm_quantize(x, M, K, ldx, gamma, eps, fmt == QGEMM_FMT_UINT8_ASYM, (uint8_t*)q, ldq, scales,
+                              zero_points, as_stream(stream));
+  return launch_status();
+}
+
 int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int fmt, int gran, void* packed,
                           size_t packed_bytes, qgemm_wdesc* desc, void* workspace, size_t workspace_bytes,
                           void* stream) {
@@ -204,11 +223,12 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int
 
 int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t* a_zero, int a_fmt, int a_gran,
               int64_t M, const qgemm_wdesc* w_desc, const void* w_packed, void* out, int64_t ldo, int out_type,
-              void* workspace, size_t workspace_bytes, void* stream) {
+              const float* bias, void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   if (!is_int_fmt(a_fmt) || !is_int_gran(a_gran)) return QGEMM_E_MODE;
   if (out_type != QGEMM_OUT_F32 && out_type != QGEMM_OUT_BF16 && out_type != QGEMM_OUT_I32) return QGEMM_E_MODE;
+  if (bias && out_type == QGEMM_OUT_I32) return QGEMM_E_MODE;  // the int32 export is the exact sum C
   int rc = check_desc(w_desc, QGEMM_FMT_INT8_SYM);
   if (rc != QGEMM_OK) return rc;
   const int64_t N = w_desc->N, K = w_desc->K;
@@ -222,7 +242,7 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
   // decode kernel's last wave may read up to 32 KB past K_pad)
   if ((std::min<int64_t>(M, 256) - 1) * lda + w_desc->K_pad + 65536 >= (int64_t(1) << 32)) return QGEMM_E_SHAPE;
   if (lda % 16 != 0 || !aligned(a_q, 16) || ldo % 4 != 0 || !aligned(out, 16) || !aligned(w_packed, 256) ||
-      !aligned(a_scales, 4) || (a_zero && !aligned(a_zero, 4)))
+      !aligned(a_scales, 4) || (a_zero && !aligned(a_zero, 4)) || (bias && !aligned(bias, 4)))
     return QGEMM_E_ALIGN;
   int dc = check_device();
   if (dc != QGEMM_OK) return dc;
@@ -244,13 +264,14 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
   g.K_pad = w_desc->K_pad;
   g.out = out;
   g.ldo = ldo;
+  g.bias = bias;
   hipError_t e = qg::launch_gemm_i8(g, asym, out_type, as_stream(stream));
   return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
 }
 
 int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s, int64_t M,
                  const qgemm_wdesc* w_desc, const void* w_packed, float* out, int64_t ldo, int mode,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+                 const float* bias, void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   if (mode != QGEMM_MX_EXACT && mode != QGEMM_MX_SCALED_MFMA) return QGEMM_E_MODE;
@@ -261,7 +282,8 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
   if (M == 0) return QGEMM_OK;
   if (!a_codes || !a_e8m0 || !w_packed || !out) return QGEMM_E_NULL;
   if (lda < K || lda_s < K / 32 || ldo < N) return QGEMM_E_SHAPE;
-  if (lda % 16 != 0 || !aligned(a_codes, 16) || ldo % 4 != 0 || !aligned(out, 16) || !aligned(w_packed, 256))
+  if (lda % 16 != 0 || !aligned(a_codes, 16) || ldo % 4 != 0 || !aligned(out, 16) || !aligned(w_packed, 256) ||
+      (bias && !aligned(bias, 4)))
     return QGEMM_E_ALIGN;
   int dc = check_device();
   if (dc != QGEMM_OK) return dc;
@@ -280,6 +302,7 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
   g.K_pad = w_desc->K_pad;
   g.out = out;
   g.ldo = ldo;
+  g.bias = bias;
   hipError_t e = qg::launch_gemm_mx(g, mode, as_stream(stream));
   return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
 }

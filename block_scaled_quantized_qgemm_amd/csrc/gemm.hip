@@ -333,8 +333,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
     for (int pass = 0; pass < 32 / RPI; ++pass) {
       const int r = pass * RPI + lane / LPR;
       const int64_t m = m0 + wm * TM + i * 32 + r;
-      const v4f y = *reinterpret_cast<const v4f*>(wreg + (r * RS + cq) * 4);
+      v4f y = *reinterpret_cast<const v4f*>(wreg + (r * RS + cq) * 4);
       if (m < p.M && nq < p.N) {
+        if (p.bias) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (nq + t < p.N) y[t] = y[t] + p.bias[nq + t];
+        }
         float* o = reinterpret_cast<float*>(p.out) + m * p.ldo + nq;
         if (nq + 3 < p.N)
           *reinterpret_cast<v4f*>(o) = y;
@@ -545,13 +550,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
   }
   const int cq = (lane % LPR) * 4;
   const int64_t nq = n0 + wn * TN + cq;
-  float sw4[4] = {0.f, 0.f, 0.f, 0.f};
+  float sw4[4] = {0.f, 0.f, 0.f, 0.f}, bs4[4] = {0.f, 0.f, 0.f, 0.f};
   int cs4[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     if (nq + t < p.N) {
       sw4[t] = p.w_per_tensor ? p.sw[0] : p.sw[nq + t];
       if (ASYM) cs4[t] = p.colsum[nq + t];
+      if (p.bias) bs4[t] = p.bias[nq + t];
     }
   }
 #pragma unroll
@@ -581,6 +587,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
           if (ASYM) c = (int)((uint32_t)c - (uint32_t)(zm - 128) * (uint32_t)cs4[t]);
           ci[t] = c;
           y[t] = (float)c * (sam * sw4[t]);
+          if (p.bias) y[t] = y[t] + bs4[t];  // the bias after the scales, in float32
         }
         const bool full = nq + 3 < p.N;
         if constexpr (OUT == 2) {
@@ -738,7 +745,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_i8_decode_kernel(GemmArgs
       const int z = ASYM ? (p.a_per_tensor ? p.za[0] : p.za[m]) : 0;
       if (ASYM) c = (int)((uint32_t)c - (uint32_t)(z - 128) * (uint32_t)p.colsum[n]);
       const float sw = p.w_per_tensor ? p.sw[0] : p.sw[n];
-      store_one<OUT>(p.out, m * p.ldo + n, c, (float)c * (sa * sw));
+      float yv = (float)c * (sa * sw);
+      if (p.bias) yv = yv + p.bias[n];  // the bias after the scales, in float32
+      store_one<OUT>(p.out, m * p.ldo + n, c, yv);
     }
   }
 }

@@ -15,6 +15,11 @@ void launch_quantize_int(const float* x, int64_t rows, int64_t K, int64_t ldx, b
                          uint8_t* q, int64_t ldq, int64_t kblocks, float* scales, int32_t* zeros, int32_t* colsum,
                          float* ws, hipStream_t st);
 
+// RMSNorm (float64 sum of squares, float32 normalized row (x * r) * gamma)
+// fused with per-row symmetric int8 / asymmetric uint8 quantization.
+void launch_rmsnorm_quantize(const float* x, int64_t rows, int64_t K, int64_t ldx, const float* gamma, float eps,
+                             bool asym, uint8_t* q, int64_t ldq, float* scales, int32_t* zeros, hipStream_t st);
+
 // MXFP8 (e4m3 codes, E8M0 per 32 K-elements) row quantization; K % 32 == 0.
 void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
                         uint8_t* e8, int64_t lde, hipStream_t st);
@@ -39,9 +44,10 @@ struct GemmArgs {
   int64_t M, N, K, K_pad;
   void* out;
   int64_t ldo;
+  const float* bias;    // [N] added to each output row after the scales (float32), or null
 };
 
-// qgemm_run: int8 GEMM + epilogue. out_type: 0 f32, 1 bf16, 2 i32.
+// qgemm_run: int8 GEMM + epilogue. out_type: 0 f32, 1 bf16, 2 i32 (no bias).
 hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_t st);
 // qgemm_run_mx: block-scaled e4m3 GEMM, float32 output. mode 0: exact products
 // (bf16 matrix cores on dequantized values), mode 1: block-scaled fp8 matrix cores.

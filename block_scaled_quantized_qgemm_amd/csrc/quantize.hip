@@ -65,6 +65,33 @@ __device__ inline int block_sum_int(int v, int* red) {
   return s;
 }
 
+__device__ inline double block_sum_double(double v, double* red) {
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < kRowThreads / kWave; ++w) s += red[w];
+  return s;
+}
+
+// RMSNorm in front of the quantizer ("Activation Quantization Architecture,
+// in depth", section "Fusion: making quantization nearly free": the norm
+// kernel already holds the row, so it also finds the amax and writes codes
+// and the scale). The normalized row is y_k = (x_k * r) * gamma_k in float32
+// with r = 1 / sqrt(sum_k x_k^2 / K + eps) taken in float64 (every square is
+// exact there) and rounded once to float32.
+struct RowNorm {
+  const float* gamma;  // [K]; null: no normalization
+  float eps;
+};
+
+__device__ inline float rms_factor(double sumsq, int64_t K, float eps) {
+  return (float)(1.0 / sqrt(sumsq / (double)K + (double)eps));
+}
+
 // Scale (and zero point) from the row statistics, in float32 exactly as the
 // formulas read: s = max(amax / 127, 1e-8); asymmetric s = max((max - min) /
 // 255, 1e-8), z = clamp(rint(-min / s), 0, 255).
@@ -133,13 +160,15 @@ __device__ inline int code_value(uint32_t c) {
 
 // VPT: float4 pieces per thread kept in registers (row length <= 1024 * VPT).
 // PRECOMP: scale / zero point were computed for the whole tensor and are read
-// from scales[0] / zeros[0] instead of from this row.
-template <bool ASYM, bool PRECOMP, int VPT>
+// from scales[0] / zeros[0] instead of from this row. NORM: the row is
+// RMS-normalized (see RowNorm) before it is quantized.
+template <bool ASYM, bool PRECOMP, int VPT, bool NORM = false>
 __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     const float* __restrict__ x, int64_t ldx, int64_t K, CodeDst qd,
-    float* __restrict__ scales, int32_t* __restrict__ zeros, int32_t* __restrict__ colsum) {
+    float* __restrict__ scales, int32_t* __restrict__ zeros, int32_t* __restrict__ colsum, RowNorm nm) {
   __shared__ float red[16];
   __shared__ int redi[8];
+  __shared__ double redd[8];
   const int64_t row = blockIdx.x;
   const float* xr = x + row * ldx;
   const int t = threadIdx.x;
@@ -155,6 +184,43 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     const int64_t k = 4 * ((int64_t)t + (int64_t)kRowThreads * u);
     v[u] = *reinterpret_cast<const float4*>(xr + (k + 4 <= K ? k : 0));
   }
+  float4 g[NORM ? VPT : 1];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int64_t k = 4 * ((int64_t)t + (int64_t)kRowThreads * u);
+      g[u] = *reinterpret_cast<const float4*>(nm.gamma + (k + 4 <= K ? k : 0));
+    }
+  }
+  // the piece holding column K - 1 is re-read element by element; past K: zeros
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int64_t k = 4 * ((int64_t)t + (int64_t)kRowThreads * u);
+    if (k + 4 > K) {
+      float e[4] = {0.f, 0.f, 0.f, 0.f}, ge[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < 4; ++c)
+        if (k + c < K) {
+          e[c] = xr[k + c];
+          if (NORM) ge[c] = nm.gamma[k + c];
+        }
+      v[u] = make_float4(e[0], e[1], e[2], e[3]);
+      if constexpr (NORM) g[u] = make_float4(ge[0], ge[1], ge[2], ge[3]);
+    }
+  }
+  if constexpr (NORM) {
+    double ss = 0.0;
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      ss = fma((double)v[u].x, (double)v[u].x, ss);
+      ss = fma((double)v[u].y, (double)v[u].y, ss);
+      ss = fma((double)v[u].z, (double)v[u].z, ss);
+      ss = fma((double)v[u].w, (double)v[u].w, ss);
+    }
+    const float r = rms_factor(block_sum_double(ss, redd), K, nm.eps);
+#pragma unroll
+    for (int u = 0; u < VPT; ++u)
+      v[u] = make_float4((v[u].x * r) * g[u].x, (v[u].y * r) * g[u].y, (v[u].z * r) * g[u].z, (v[u].w * r) * g[u].w);
+  }
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int64_t k = 4 * ((int64_t)t + (int64_t)kRowThreads * u);
@@ -164,13 +230,9 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
       stats_update<ASYM>(st, v[u].z);
       stats_update<ASYM>(st, v[u].w);
     } else {
-      float e[4] = {0.f, 0.f, 0.f, 0.f};
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
       for (int c = 0; c < 4; ++c)
-        if (k + c < K) {
-          e[c] = xr[k + c];
-          stats_update<ASYM>(st, e[c]);
-        }
-      v[u] = make_float4(e[0], e[1], e[2], e[3]);
+        if (k + c < K) stats_update<ASYM>(st, e[c]);
     }
   }
 
@@ -217,15 +279,24 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
 
 // Rows longer than the register-resident kernels hold: two sweeps over the
 // row (the second one is served by the caches).
-template <bool ASYM, bool PRECOMP>
+template <bool ASYM, bool PRECOMP, bool NORM = false>
 __global__ __launch_bounds__(kRowThreads) void quant_rows_long_kernel(
     const float* __restrict__ x, int64_t ldx, int64_t K, CodeDst qd,
-    float* __restrict__ scales, int32_t* __restrict__ zeros, int32_t* __restrict__ colsum) {
+    float* __restrict__ scales, int32_t* __restrict__ zeros, int32_t* __restrict__ colsum, RowNorm nm) {
   __shared__ float red[16];
   __shared__ int redi[8];
+  __shared__ double redd[8];
   const int64_t row = blockIdx.x;
   const float* xr = x + row * ldx;
   const int t = threadIdx.x;
+  float r = 1.0f;
+  if constexpr (NORM) {
+    double ss = 0.0;
+    for (int64_t k = t; k < K; k += kRowThreads) ss = fma((double)xr[k], (double)xr[k], ss);
+    r = rms_factor(block_sum_double(ss, redd), K, nm.eps);
+  }
+  // element k of the row as quantized: x, or the normalized (x * r) * gamma
+  auto val = [&](int64_t k) { return NORM ? (xr[k] * r) * nm.gamma[k] : xr[k]; };
   float s;
   int z;
   if (PRECOMP) {
@@ -235,15 +306,15 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_long_kernel(
     RowStats st;
     st.lo = INFINITY;
     st.hi = ASYM ? -INFINITY : 0.0f;
-    for (int64_t k = t; k < K; k += kRowThreads) stats_update<ASYM>(st, xr[k]);
-    RowStats r = block_reduce_stats<ASYM>(st, red);
-    scale_from_stats<ASYM>(r, s, z);
+    for (int64_t k = t; k < K; k += kRowThreads) stats_update<ASYM>(st, val(k));
+    RowStats rs = block_reduce_stats<ASYM>(st, red);
+    scale_from_stats<ASYM>(rs, s, z);
   }
   const float zf = (float)z;
   const float y = 1.0f / s;  // correctly rounded
   int csum = 0;
   for (int64_t k = t; k < K; k += kRowThreads) {
-    uint32_t c = encode_code<ASYM>(xr[k], s, y, zf);
+    uint32_t c = encode_code<ASYM>(val(k), s, y, zf);
     *code_ptr(qd, row, k) = (uint8_t)c;
     csum += code_value<ASYM>(c);
   }
@@ -348,23 +419,25 @@ __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __re
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <bool ASYM, bool PRECOMP>
+template <bool ASYM, bool PRECOMP, bool NORM>
 static void launch_rows(const float* x, int64_t rows, int64_t K, int64_t ldx, CodeDst qd, float* scales,
-                        int32_t* zeros, int32_t* colsum, hipStream_t st) {
+                        int32_t* zeros, int32_t* colsum, RowNorm nm, hipStream_t st) {
   dim3 grid((unsigned)rows), block(kRowThreads);
-  const bool vec = ldx % 4 == 0 && ((uintptr_t)x % 16) == 0 && qd.ldq % 4 == 0 && ((uintptr_t)qd.q % 4) == 0;
+  // the register kernels read 16 bytes at a row's start even when K < 4
+  const bool vec = K >= 4 && ldx % 4 == 0 && ((uintptr_t)x % 16) == 0 && qd.ldq % 4 == 0 &&
+                   ((uintptr_t)qd.q % 4) == 0 && (!NORM || ((uintptr_t)nm.gamma % 16) == 0);
   if (!vec)
-    quant_rows_long_kernel<ASYM, PRECOMP><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
+    quant_rows_long_kernel<ASYM, PRECOMP, NORM><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum, nm);
   else if (K <= 1024)
-    quant_rows_kernel<ASYM, PRECOMP, 1><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
+    quant_rows_kernel<ASYM, PRECOMP, 1, NORM><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum, nm);
   else if (K <= 2048)
-    quant_rows_kernel<ASYM, PRECOMP, 2><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
+    quant_rows_kernel<ASYM, PRECOMP, 2, NORM><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum, nm);
   else if (K <= 4096)
-    quant_rows_kernel<ASYM, PRECOMP, 4><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
+    quant_rows_kernel<ASYM, PRECOMP, 4, NORM><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum, nm);
   else if (K <= 8192)
-    quant_rows_kernel<ASYM, PRECOMP, 8><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
+    quant_rows_kernel<ASYM, PRECOMP, 8, NORM><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum, nm);
   else
-    quant_rows_long_kernel<ASYM, PRECOMP><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum);
+    quant_rows_long_kernel<ASYM, PRECOMP, NORM><<<grid, block, 0, st>>>(x, ldx, K, qd, scales, zeros, colsum, nm);
 }
 
 void launch_quantize_int(const float* x, int64_t rows, int64_t K, int64_t ldx, bool asym, bool per_tensor,
@@ -374,21 +447,32 @@ void launch_quantize_int(const float* x, int64_t rows, int64_t K, int64_t ldx, b
   const CodeDst qd{q, kblocks ? 16 : ldq, kblocks};
   if (!per_tensor) {
     if (asym)
-      launch_rows<true, false>(x, rows, K, ldx, qd, scales, zeros, colsum, st);
+      launch_rows<true, false, false>(x, rows, K, ldx, qd, scales, zeros, colsum, RowNorm{}, st);
     else
-      launch_rows<false, false>(x, rows, K, ldx, qd, scales, zeros, colsum, st);
+      launch_rows<false, false, false>(x, rows, K, ldx, qd, scales, zeros, colsum, RowNorm{}, st);
     return;
   }
   dim3 grid((unsigned)rows), block(kRowThreads);
   if (asym) {
     row_stats_kernel<true><<<grid, block, 0, st>>>(x, ldx, K, ws);
     tensor_scale_kernel<true><<<1, block, 0, st>>>(ws, rows, scales, zeros);
-    launch_rows<true, true>(x, rows, K, ldx, qd, scales, zeros, colsum, st);
+    launch_rows<true, true, false>(x, rows, K, ldx, qd, scales, zeros, colsum, RowNorm{}, st);
   } else {
     row_stats_kernel<false><<<grid, block, 0, st>>>(x, ldx, K, ws);
     tensor_scale_kernel<false><<<1, block, 0, st>>>(ws, rows, scales, zeros);
-    launch_rows<false, true>(x, rows, K, ldx, qd, scales, zeros, colsum, st);
+    launch_rows<false, true, false>(x, rows, K, ldx, qd, scales, zeros, colsum, RowNorm{}, st);
   }
+}
+
+void launch_rmsnorm_quantize(const float* x, int64_t rows, int64_t K, int64_t ldx, const float* gamma, float eps,
+                             bool asym, uint8_t* q, int64_t ldq, float* scales, int32_t* zeros, hipStream_t st) {
+  if (rows == 0) return;
+  const CodeDst qd{q, ldq, 0};
+  const RowNorm nm{gamma, eps};
+  if (asym)
+    launch_rows<true, false, true>(x, rows, K, ldx, qd, scales, zeros, nullptr, nm, st);
+  else
+    launch_rows<false, false, true>(x, rows, K, ldx, qd, scales, zeros, nullptr, nm, st);
 }
 
 void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,

@@ -150,6 +150,28 @@ def qgemm_quantize_rows(x: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = GR
     return out
 
 
+def qgemm_rmsnorm_quantize_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float, fmt: int = FMT_INT8_SYM,
+                                out: Optional[QuantizedRows] = None, stream=None) -> QuantizedRows:
+    """RMSNorm of the float32 [M, K] rows with weight gamma [K], then per-row quantization (see qgemm.h)."""
+    lib = L.load()
+    assert x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
+    assert gamma.dtype == torch.float32 and gamma.dim() == 1 and gamma.is_contiguous()
+    M, K = x.shape
+    assert gamma.shape[0] == K
+    dev = x.device
+    if out is None:
+        ld = _round_up(max(K, 1), 16)
+        q = torch.empty((M, ld), dtype=torch.int8 if fmt == FMT_INT8_SYM else torch.uint8, device=dev)
+        scales = torch.empty((M,), dtype=torch.float32, device=dev)
+        zeros = torch.empty_like(scales, dtype=torch.int32) if fmt == FMT_UINT8_ASYM else None
+        out = QuantizedRows(q, K, fmt, GRAN_ROW, scales, zeros, None)
+    st = lib.qgemm_rmsnorm_quantize_rows(
+        _ptr(x), M, K, x.stride(0), _ptr(gamma), ctypes.c_float(eps), fmt, GRAN_ROW, _ptr(out.q), out.q.stride(0),
+        _ptr(out.scales), _ptr(out.zero_points), ctypes.c_void_p(_stream(dev, stream)))
+    _check("qgemm_rmsnorm_quantize_rows", st)
+    return out
+
+
 def qgemm_prepack_weights(w: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = GRAN_ROW,
                           stream=None) -> PackedWeights:
     """Prepare a float32 [N, K] weight (per-channel / per-tensor int8, or MXFP8)."""
@@ -175,9 +197,18 @@ def _alloc_out(M: int, N: int, dtype, dev):
     return buf
 
 
+def _bias_ptr(bias: Optional[torch.Tensor], N: int):
+    if bias is None:
+        return None
+    assert bias.dtype == torch.float32 and bias.dim() == 1 and bias.shape[0] == N and bias.is_contiguous()
+    return _ptr(bias)
+
+
 def qgemm_run(a: QuantizedRows, w: PackedWeights, out_type: int = OUT_F32,
-              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """int8 GEMM with the fused dequantization epilogue; returns out[:, :N]."""
+              out: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """int8 GEMM with the fused dequantization epilogue (plus an optional
+    float32 bias [N]); returns out[:, :N]."""
     lib = L.load()
     dev = a.q.device
     N = w.N
@@ -185,14 +216,14 @@ def qgemm_run(a: QuantizedRows, w: PackedWeights, out_type: int = OUT_F32,
         out = _alloc_out(a.M, N, _OUT_DTYPES[out_type], dev)
     st = lib.qgemm_run(_ptr(a.q), a.q.stride(0), _ptr(a.scales), _ptr(a.zero_points), a.fmt, a.gran, a.M,
                        ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0), out_type,
-                       None, 0, ctypes.c_void_p(_stream(dev, stream)))
+                       _bias_ptr(bias, N), None, 0, ctypes.c_void_p(_stream(dev, stream)))
     _check("qgemm_run", st)
     return out[:, :N]
 
 
 def qgemm_run_mx(a: QuantizedRows, w: PackedWeights, out: Optional[torch.Tensor] = None,
-                 mode: int = MX_EXACT, stream=None) -> torch.Tensor:
-    """Block-scaled e4m3 GEMM (float32 out); returns out[:, :N]."""
+                 mode: int = MX_EXACT, bias: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Block-scaled e4m3 GEMM (float32 out, plus an optional float32 bias [N]); returns out[:, :N]."""
     lib = L.load()
     dev = a.q.device
     N = w.N
@@ -200,6 +231,6 @@ def qgemm_run_mx(a: QuantizedRows, w: PackedWeights, out: Optional[torch.Tensor]
         out = _alloc_out(a.M, N, torch.float32, dev)
     st = lib.qgemm_run_mx(_ptr(a.q), a.q.stride(0), _ptr(a.mx_scales), a.mx_scales.stride(0), a.M,
                           ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0), mode,
-                          None, 0, ctypes.c_void_p(_stream(dev, stream)))
+                          _bias_ptr(bias, N), None, 0, ctypes.c_void_p(_stream(dev, stream)))
     _check("qgemm_run_mx", st)
     return out[:, :N]

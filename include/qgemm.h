@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define QGEMM_ABI_VERSION 2
+#define QGEMM_ABI_VERSION 3
 #define QGEMM_WDESC_MAGIC 0x51474d57u /* "WMGQ" */
 
 /* Status codes. Every entry point returns one of these. */
@@ -205,6 +205,36 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx,
                         void* stream);
 
 /*
+ * qgemm_rmsnorm_quantize_rows -- RMSNorm and per-row quantization in one pass
+ * over the rows ([AQ] "Fusion: making quantization nearly free": the norm
+ * kernel already holds each row, so it finds the row's amax and writes the
+ * codes and one scale per token without another read of the activations).
+ *
+ *   r      = 1 / sqrt(sum_k x[m,k]^2 / K + eps)   float64 (every square is
+ *            exact there), rounded once to float32
+ *   y[m,k] = (x[m,k] * r) * gamma[k]              two float32 multiplies
+ *   then exactly qgemm_quantize_rows on y with gran = ROW: INT8_SYM
+ *   (s = max(amax / 127, 1e-8), q = clamp(rint(y / s), -127, 127)) or
+ *   UINT8_ASYM (s, z from the row's min and max).
+ *
+ *   x        device float32 [M][ldx], ldx >= K.
+ *   gamma    device float32 [K] (the norm's per-column weight).
+ *   eps      finite, >= 0 (else QGEMM_E_MODE).
+ *   fmt      QGEMM_FMT_INT8_SYM or QGEMM_FMT_UINT8_ASYM; gran QGEMM_GRAN_ROW
+ *            (any other combination: QGEMM_E_MODE).
+ *   q, ldq, scales, zero_points as in qgemm_quantize_rows (ROW granularity).
+ *   The order of the float64 sum of squares is the kernel's; it can move r
+ *   by one float32 ulp only when the float64 value lies within about
+ *   K * 2^-53 (relative) of a float32 rounding boundary.
+ */
+int qgemm_rmsnorm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx,
+                                const float* gamma, float eps,
+                                int fmt, int gran,
+                                void* q, int64_t ldq,
+                                float* scales, int32_t* zero_points,
+                                void* stream);
+
+/*
  * qgemm_prepack_weights -- offline weight preparation (step "W prepack").
  *
  *   INT8_SYM, ROW or TENSOR: per output channel n (or once for the matrix),
@@ -238,6 +268,9 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw,
  *              ([D98] "The program, and the gate that has to be per column":
  *              the scales multiply once per output, after the loop;
  *              [SK] "Correctness requirements": zero point before scaling)
+ *   out[m,n] = out[m,n] + bias[n]                           if bias != NULL,
+ *              float32 ([AQ] int8_linear: y + bias after the scales; [SK]
+ *              step 5: apply the bias in fp32 in the epilogue)
  *   cast to float32, to bfloat16 (round to nearest even), or C itself (I32).
  *
  *   a_q      device codes [M][lda] (int8 for INT8_SYM, uint8 for UINT8_ASYM),
@@ -249,6 +282,7 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw,
  *   w_desc   host descriptor from qgemm_prepack_weights (INT8_SYM weights).
  *   w_packed device packed buffer of that descriptor.
  *   out      device [M][ldo] of out_type, ldo >= N, 16-byte aligned, ldo % 4 == 0.
+ *   bias     device float32 [N] or NULL; NULL with out_type I32 (else QGEMM_E_MODE).
  *   K limit  (QGEMM_E_OVERFLOW): K <= 133144 for INT8_SYM activations
  *            (127*127*K < 2^31), K <= 66311 for UINT8_ASYM (255*127*K < 2^31)
  *            ([SK] step 2 and "Correctness requirements"; [AQ] about 133,000 terms).
@@ -257,7 +291,7 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw,
 int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t* a_zero,
               int a_fmt, int a_gran, int64_t M,
               const qgemm_wdesc* w_desc, const void* w_packed,
-              void* out, int64_t ldo, int out_type,
+              void* out, int64_t ldo, int out_type, const float* bias,
               void* workspace, size_t workspace_bytes,
               void* stream);
 
@@ -269,7 +303,9 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
  *   Each 32-element K block is multiplied by its own pair of scales inside
  *   the K loop ([TL27] 4.1: (A*scale_A)(B*scale_B); 4.3: a per-K-block scale
  *   cannot be moved out of the sum). float32 accumulation and output; how
- *   exactly the products and sums are formed depends on `mode`.
+ *   exactly the products and sums are formed depends on `mode`. With a bias,
+ *   out[m,n] + bias[n] in float32 (the bias term of the MX formula
+ *   C = (scale_A x A)(scale_B x B) + bias on the [TL27] pages).
  *
  *   a_codes  device e4m3 [M][lda], lda >= K, lda % 16 == 0, 16-byte aligned.
  *   a_e8m0   device E8M0 [M][lda_s], lda_s >= K/32.
@@ -279,11 +315,12 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
  *            QGEMM_MX_SCALED_MFMA (block-scaled fp8 matrix cores; see the enum).
  *            Both need E8M0 codes in [3, 240] for exactness of the scaled values,
  *            which qgemm_quantize_rows always produces for inputs below 2^120.
+ *   bias     device float32 [N] or NULL.
  *   workspace unused by this version (pass NULL, 0).
  */
 int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s,
                  int64_t M, const qgemm_wdesc* w_desc, const void* w_packed,
-                 float* out, int64_t ldo, int mode,
+                 float* out, int64_t ldo, int mode, const float* bias,
                  void* workspace, size_t workspace_bytes,
                  void* stream);
 

@@ -206,11 +206,21 @@ def epilogue(C, s_a, s_w):
     return C * sa * sw
 
 
-def quantized_linear(x, w, act: str = "sym_row", wgt: str = "channel"):
+def add_bias(y, bias):
+    """y[m, n] + bias[n] in float64: the bias after the scales ([AQ] "The
+    integer GEMM, written out", int8_linear returns y + bias; [SK] step 5,
+    "optionally apply bias (in fp32)" in the epilogue)."""
+    if bias is None:
+        return y
+    return np.asarray(y, np.float64) + np.asarray(bias, np.float32).astype(np.float64)[None, :]
+
+
+def quantized_linear(x, w, act: str = "sym_row", wgt: str = "channel", bias=None):
     """The whole path on the CPU: quantize A, prepare W, integer GEMM, epilogue.
 
     act: "sym_row" (per-token int8), "sym_tensor" (one int8 scale),
     "asym_row" (per-token uint8 + zero point). wgt: "channel" or "tensor".
+    bias: optional float32 [N] added after the scales (``add_bias``).
     Returns a dict with every intermediate (codes, scales, zero points, column
     sums, the exact integer C and the float64 output).
     """
@@ -228,8 +238,63 @@ def quantized_linear(x, w, act: str = "sym_row", wgt: str = "channel"):
         raise ValueError(act)
     qw, sw, colsum = prepare_weights_int8(w, per_channel=(wgt == "channel"))
     C = int_gemm(qa, za, qw)
-    y = epilogue(C, sa, sw)
+    y = add_bias(epilogue(C, sa, sw), bias)
     return dict(q_a=qa, s_a=sa, z_a=za, q_w=qw, s_w=sw, colsum=colsum, C=C, y=y)
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm in front of the per-token quantizer
+# ----------------------------------------------------------------------------
+def rms_factor(x, eps):
+    """r[m] = 1 / sqrt(mean_k x[m, k]^2 + eps) per row, as float32.
+
+    [AQ] "Fusion: making quantization nearly free" (the fused norm-and-quantize
+    pseudocode: rms = sqrt(mean(x * x) + eps)). Readings: every square is
+    exact in float64 and the sum of a row is rounded once (math.fsum); the
+    mean, the square root and the reciprocal are float64; the factor is
+    rounded once to float32.
+    """
+    import math
+    x = np.asarray(x, np.float32)
+    K = x.shape[1]
+    r = np.empty(x.shape[0], np.float32)
+    for m in range(x.shape[0]):
+        row = x[m].astype(np.float64)
+        ss = math.fsum((row * row).tolist())
+        r[m] = np.float32(1.0 / math.sqrt(ss / K + float(np.float32(eps))))
+    return r
+
+
+def rmsnorm(x, gamma, eps, r=None):
+    """y[m, k] = x[m, k] / rms[m] * gamma[k] ([AQ] "Fusion: making
+    quantization nearly free", the RMSNorm line of the pseudocode).
+
+    Reading: the division by rms is a multiplication by the float32 factor
+    ``rms_factor`` (the usual reciprocal form of the norm), and the two
+    products are float32 roundings in the pseudocode's order: (x * r) * gamma.
+    ``r`` may be passed in (a per-row float32 factor) to evaluate the same
+    formula with a neighbouring factor.
+    """
+    x = np.asarray(x, np.float32)
+    g = np.asarray(gamma, np.float32)
+    r = rms_factor(x, eps) if r is None else np.asarray(r, np.float32)
+    return ((x * r[:, None]).astype(np.float32) * g[None, :]).astype(np.float32)
+
+
+def rmsnorm_quantize(x, gamma, eps, act: str = "sym_row", r=None):
+    """The fused norm-and-quantize step: ``rmsnorm`` then the per-token
+    quantizer on its float32 output ([AQ] "Fusion: making quantization nearly
+    free": amax of the normalized row, s = amax / 127, codes and one scale per
+    token). Reading: the quantizer is exactly ``quantize_sym_int8`` /
+    ``quantize_asym_uint8`` per row (s floored at 1e-8 after the division, as
+    everywhere else), so the fused step equals the two steps composed.
+    Returns (q, s) or (q, s, z)."""
+    y = rmsnorm(x, gamma, eps, r)
+    if act == "sym_row":
+        return quantize_sym_int8(y, per_row=True)
+    if act == "asym_row":
+        return quantize_asym_uint8(y, per_row=True)
+    raise ValueError(act)
 
 
 # ----------------------------------------------------------------------------

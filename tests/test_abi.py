@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.qgemm_abi_version() == 2
+    assert lib.qgemm_abi_version() == 3
     for s in range(-9, 1):
         assert lib.qgemm_status_string(s).startswith(b"QGEMM_")
     assert lib.qgemm_status_string(-100) == b"unknown qgemm status"
@@ -91,7 +91,7 @@ def test_quantize_rows_validation(lib):
 
 
 def _wdesc(**kw):
-    d = L.WDesc(magic=0x51474D57, version=2, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=3, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 512, colsum_off=256 * 512 + 1024, bytes=256 * 512 + 2048)
     for k, v in kw.items():
         setattr(d, k, v)
@@ -99,21 +99,23 @@ def _wdesc(**kw):
 
 
 def _run(lib, d, a=FAKE, lda=304, s=FAKE, z=None, fmt=INT8, gran=ROW, M=8, w=FAKE, out=FAKE, ldo=100,
-         ot=0):
-    return lib.qgemm_run(a, lda, s, z, fmt, gran, M, ctypes.byref(d), w, out, ldo, ot, None, 0, None)
+         ot=0, bias=None):
+    return lib.qgemm_run(a, lda, s, z, fmt, gran, M, ctypes.byref(d), w, out, ldo, ot, bias, None, 0, None)
 
 
 def test_run_validation(lib):
     good = _wdesc()
     assert lib.qgemm_packed_weight_bytes(100, 300, INT8, ROW) == good.bytes
     assert _run(lib, _wdesc(magic=1)) == E_DESC
-    assert _run(lib, _wdesc(version=1)) == E_DESC
+    assert _run(lib, _wdesc(version=2)) == E_DESC
     assert _run(lib, _wdesc(fmt=MX)) == E_DESC
     assert _run(lib, _wdesc(K_pad=384)) == E_DESC
     assert _run(lib, _wdesc(bytes=5)) == E_DESC
-    assert lib.qgemm_run(FAKE, 304, FAKE, None, INT8, ROW, 8, None, FAKE, FAKE, 100, 0, None, 0, None) == E_NULL
+    assert lib.qgemm_run(FAKE, 304, FAKE, None, INT8, ROW, 8, None, FAKE, FAKE, 100, 0, None, None, 0, None) == E_NULL
     assert _run(lib, good, fmt=MX) == E_MODE
     assert _run(lib, good, ot=3) == E_MODE
+    assert _run(lib, good, ot=2, bias=FAKE) == E_MODE     # the int32 export takes no bias
+    assert _run(lib, good, bias=FAKE + 2) == E_ALIGN
     assert _run(lib, good, M=-1) == E_SHAPE
     assert _run(lib, good, M=0, a=None, s=None, w=None, out=None) == OK
     assert _run(lib, good, a=None) == E_NULL
@@ -135,12 +137,12 @@ def test_run_validation(lib):
 
 def test_run_mx_validation(lib):
     nb = lib.qgemm_packed_weight_bytes(100, 320, MX, BLK)
-    d = L.WDesc(magic=0x51474D57, version=2, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=3, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 512, colsum_off=-1, bytes=nb)
     call = lambda **kw: lib.qgemm_run_mx(kw.get("a", FAKE), kw.get("lda", 320), kw.get("e", FAKE),
                                          kw.get("ldas", 10), kw.get("M", 4), ctypes.byref(kw.get("d", d)),
                                          FAKE, kw.get("out", FAKE), kw.get("ldo", 100), kw.get("mode", 0),
-                                         None, 0, None)
+                                         kw.get("bias", None), None, 0, None)
     assert call(d=_wdesc()) == E_DESC                     # an int8 descriptor
     assert call(e=None) == E_NULL
     assert call(ldas=9) == E_SHAPE
@@ -148,6 +150,26 @@ def test_run_mx_validation(lib):
     assert call(lda=328) == E_ALIGN
     assert call(M=0, a=None, e=None, out=None) == OK
     assert call(mode=2) == E_MODE
+    assert call(bias=FAKE + 1) == E_ALIGN
+
+
+def test_rmsnorm_quantize_validation(lib):
+    f = lambda **kw: lib.qgemm_rmsnorm_quantize_rows(
+        kw.get("x", FAKE), kw.get("M", 4), kw.get("K", 64), kw.get("ldx", 64), kw.get("g", FAKE),
+        kw.get("eps", 1e-6), kw.get("fmt", INT8), kw.get("gran", ROW), kw.get("q", FAKE), kw.get("ldq", 64),
+        kw.get("s", FAKE), kw.get("z", None), None)
+    assert f(fmt=MX, gran=BLK) == E_MODE
+    assert f(gran=TENSOR) == E_MODE
+    assert f(eps=-1.0) == E_MODE
+    assert f(eps=float("nan")) == E_MODE
+    assert f(eps=float("inf")) == E_MODE
+    assert f(K=0) == E_SHAPE
+    assert f(M=0, x=None, g=None, q=None, s=None) == OK
+    assert f(g=None) == E_NULL
+    assert f(fmt=UINT8) == E_NULL                         # missing zero points
+    assert f(ldx=32) == E_SHAPE
+    assert f(ldq=72) == E_ALIGN
+    assert f(g=FAKE + 2) == E_ALIGN
 
 
 def test_prepack_validation(lib):
@@ -173,6 +195,8 @@ def test_no_device_is_an_error_not_a_fallback(lib):
     # fully valid arguments: the only thing missing is a gfx950
     assert _q(lib) == E_DEVICE
     assert _run(lib, _wdesc()) == E_DEVICE
+    assert lib.qgemm_rmsnorm_quantize_rows(FAKE, 4, 64, 64, FAKE, 1e-6, INT8, ROW, FAKE, 64, FAKE, None,
+                                           None) == E_DEVICE
 
 
 def test_packed_int8_block_layout_round_trip():

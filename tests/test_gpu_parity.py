@@ -6,6 +6,8 @@ oracle's float64 epilogue; bfloat16 outputs within half a bf16 ulp (plus
 float32 slack); MX outputs within 1e-5 * sum_k |a_k w_k| of the float64
 reference over the dequantized e4m3 values.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -298,3 +300,98 @@ def test_gemm_mx_modes_on_an_8_group_with_a_wide_exponent_spread(ops):
     mfma = host(ops.qgemm_run_mx(a, pw, mode=1))[0, 0]
     assert exact == ref[0, 0]
     assert mfma == 448.0 and abs(mfma - ref[0, 0]) <= MX_SCALED_STOL * S[0, 0]
+
+
+# ---------------------------------------------------------------------------
+# Bias after the scales (int8 and MX) and the fused RMSNorm + quantize step
+# ---------------------------------------------------------------------------
+def _bias_bar(ref, b, out_type):
+    """float32: two roundings (the scaled product, then + bias) on top of the
+    epilogue's; bf16 adds half a bf16 ulp of the result."""
+    y0 = np.abs(ref - b.astype(np.float64)[None, :])
+    bar = F32_RTOL * (y0 + np.abs(ref))
+    return bar + (BF16_RTOL * np.abs(ref) if out_type == 1 else 0.0)
+
+
+@pytest.mark.parametrize("out_type", [0, 1])
+@pytest.mark.parametrize("act", ["sym_row", "asym_row", "sym_tensor"])
+@pytest.mark.parametrize("M,N,K", [(8, 300, 4112), (64, 64, 256), (257, 513, 1000), (1100, 3900, 700)])
+def test_gemm_bias(ops, M, N, K, act, out_type):
+    print_case("gemm bias", M, N, K, act, out_type)
+    A, W = make_inputs("c2_per_token", M=M, K=K, N=N, seed=2 * M + 3 * N + K)
+    if act == "asym_row":
+        A = A - np.float32(0.3)
+    b = rng_for(N + K).normal(0.0, 2.0, size=N).astype(np.float32)
+    ref = O.quantized_linear(A, W, act=ACT[act][2], wgt="channel", bias=b)["y"]
+    fmt, gran, _ = ACT[act]
+    a = ops.qgemm_quantize_rows(dev(A), fmt, gran)
+    pw = ops.qgemm_prepack_weights(dev(W), 0, 1)
+    got = host(ops.qgemm_run(a, pw, out_type, bias=dev(b)))
+    g = got.astype(np.float64) if out_type == 0 else O.bf16_to_f32(got.view(np.uint16)).astype(np.float64)
+    err = np.abs(g - ref)
+    bad = err > _bias_bar(ref, b, out_type)
+    assert not bad.any(), (np.argwhere(bad)[:5], err.max())
+
+
+@pytest.mark.parametrize("M,N,K", [(33, 65, 96), (300, 200, 2080)])
+def test_gemm_mx_bias(ops, M, N, K):
+    print_case("gemm mx bias", M, N, K)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=M + 5 * N + K)
+    b = rng_for(K).normal(0.0, 10.0, size=N).astype(np.float32)
+    a = ops.qgemm_quantize_rows(dev(A), 2, 2)
+    pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
+    got = host(ops.qgemm_run_mx(a, pw, mode=0, bias=dev(b))).astype(np.float64)
+    qa, Ea = O.quantize_mx(A)
+    qw, Ew = O.quantize_mx(W)
+    ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew)
+    ref = O.add_bias(ref, b)
+    assert (np.abs(got - ref) <= MX_STOL * S + F32_RTOL * np.abs(ref)).all()
+
+
+def _rms_candidates(x, eps):
+    """Per row: the oracle's float32 factor, its float32 neighbour on the
+    side of the float64 value, and whether that value lies so close to the
+    rounding boundary between them (relative 1e-11, above the float64 sum's
+    order-dependent error for these K) that either is a valid result."""
+    r = O.rms_factor(x, eps)
+    r64 = np.array([1.0 / math.sqrt(math.fsum((row.astype(np.float64) ** 2).tolist()) / x.shape[1]
+                                    + float(np.float32(eps))) for row in x])
+    up = r64 > r.astype(np.float64)
+    alt = np.where(up, np.nextafter(r, np.float32(np.inf)), np.nextafter(r, np.float32(-np.inf))).astype(np.float32)
+    boundary = (r.astype(np.float64) + alt.astype(np.float64)) / 2.0
+    ambiguous = np.abs(r64 - boundary) <= 1e-11 * np.abs(r64)
+    return r, alt, ambiguous
+
+
+@pytest.mark.parametrize("act", ["sym_row", "asym_row"])
+@pytest.mark.parametrize("M,K,misaligned", [(1, 1, False), (3, 5, False), (7, 17, False), (64, 256, False),
+                                            (33, 1000, False), (5, 4097, False), (512, 4096, False),
+                                            (9, 8192, False), (2, 9000, False), (6, 260, True)])
+def test_rmsnorm_quantize_parity(ops, act, M, K, misaligned):
+    """Codes, scales and zero points of the fused step equal the oracle's bit
+    for bit, except on rows whose float64 norm factor sits at a float32
+    rounding boundary, where the neighbouring factor is accepted too."""
+    print_case("rmsnorm quantize", act, M, K, misaligned)
+    A, _ = make_inputs("c2_per_token", M=M, K=K, N=1, seed=M * 17 + K)
+    if M >= 8:
+        A[-8:] = _edge_rows(K, rng_for(K))
+    g = rng_for(K + 1).normal(1.0, 0.3, size=K).astype(np.float32)
+    g[:: max(K // 7, 1)] = 0.0
+    g[1:: max(K // 5, 1)] *= -1.0
+    eps = 1e-6
+    fmt = ACT[act][0]
+    gd = dev(np.concatenate([np.zeros(1, np.float32), g]))[1:] if misaligned else dev(g)
+    r = ops.qgemm_rmsnorm_quantize_rows(dev(A), gd, eps, fmt)
+    q_gpu = host(r.codes()).view(np.uint8)
+    s_gpu = host(r.scales).view(np.uint32)
+    z_gpu = host(r.zero_points) if fmt == 1 else None
+    r32, alt, amb = _rms_candidates(A, eps)
+    assert amb.sum() <= max(1, M // 64)
+    for cand in (r32, np.where(amb, alt, r32)):
+        out = O.rmsnorm_quantize(A, g, eps, act=act, r=cand)
+        ok = (q_gpu == out[0].view(np.uint8)).all(axis=1) & (s_gpu == out[1].view(np.uint32))
+        if fmt == 1:
+            ok &= z_gpu == out[2]
+        if cand is r32:
+            first = ok
+    assert (first | (amb & ok)).all(), np.argwhere(~(first | (amb & ok)))[:5]

@@ -455,3 +455,84 @@ def test_oracle_and_product_share_no_imports():
         if f.endswith((".py", ".hip", ".cpp", ".h", ".hpp")):
             src = open(f).read()
             assert not re.search(r"^\s*(from|import)\s+oracle|#include\s+\S*oracle", src, re.M), f
+
+
+# --------------------------------------------------------------------------
+# Bias after the scales ([AQ] int8_linear: y + bias; [SK] step 5)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("act", ["sym_row", "asym_row"])
+def test_bias_is_added_after_dequantize_then_multiply(act):
+    """With a bias, the output is the float64 product of the dequantized
+    operands plus the bias per output channel: a route through dequantized
+    values instead of the integer GEMM."""
+    A, W = make_inputs("c2_per_token", M=9, K=70, N=13, seed=41)
+    if act == "asym_row":
+        A = A - np.float32(0.3)
+    b = rng_for(42).normal(0.0, 3.0, size=13).astype(np.float32)
+    r = O.quantized_linear(A, W, act=act, wgt="channel", bias=b)
+    xa = (r["q_a"].astype(np.float64) - r["z_a"].astype(np.float64)[:, None]) * r["s_a"].astype(np.float64)[:, None]
+    xw = r["q_w"].astype(np.float64) * r["s_w"].astype(np.float64)[:, None]
+    ref = xa @ xw.T + b.astype(np.float64)[None, :]
+    assert np.allclose(r["y"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    r0 = O.quantized_linear(A, W, act=act, wgt="channel")
+    assert np.array_equal(r0["C"], r["C"])          # the bias never enters the integer sum
+    d = r["y"] - r0["y"]
+    assert np.allclose(d, np.broadcast_to(b.astype(np.float64), d.shape), rtol=0, atol=1e-12 * np.abs(r["y"]).max())
+
+
+# --------------------------------------------------------------------------
+# RMSNorm in front of the per-token quantizer ([AQ] "Fusion: making
+# quantization nearly free")
+# --------------------------------------------------------------------------
+def test_rmsnorm_hand_example():
+    """x = [3, 4]: mean(x^2) = 12.5, so y = x / sqrt(12.5 + eps) * gamma."""
+    x = np.array([[3.0, 4.0]], np.float32)
+    g = np.array([1.0, 2.0], np.float32)
+    for eps in (0.0, 1.0):
+        y = O.rmsnorm(x, g, eps).astype(np.float64)
+        rms = math.sqrt(12.5 + eps)
+        want = np.array([3.0 / rms, 2.0 * 4.0 / rms])
+        assert np.allclose(y[0], want, rtol=2.0 ** -22, atol=0)
+
+
+def test_rmsnorm_constant_rows():
+    """A constant row c normalizes to sign(c) * gamma (eps = 0); for c a power
+    of two every step is exact."""
+    g = np.array([1.0, -0.5, 3.0, 0.0], np.float32)
+    for c in (1.0, -8.0, 2.0 ** -20, 2.0 ** 30):
+        y = O.rmsnorm(np.full((1, 4), c, np.float32), g, 0.0)
+        assert np.array_equal(y[0], np.sign(c) * g)
+    y = O.rmsnorm(np.full((1, 4), 3.0, np.float32), np.ones(4, np.float32), 0.0)
+    assert np.all(y == 1.0)                          # 3 * RN(1/3) rounds back to 1
+
+
+def test_rmsnorm_power_of_two_scale_invariance():
+    """RMSNorm(2^j x) == RMSNorm(x) bit for bit with eps = 0: scaling by a
+    power of two commutes with every rounding step (in range)."""
+    x = make_inputs("c2_per_token", M=6, K=300, N=1, seed=7)[0]
+    g = rng_for(8).normal(1.0, 0.3, size=300).astype(np.float32)
+    base = O.rmsnorm(x, g, 0.0)
+    for j in (-20, -3, 5, 40):
+        assert np.array_equal(O.rmsnorm(x * np.float32(2.0 ** j), g, 0.0), base)
+
+
+def test_rmsnorm_output_has_unit_rms():
+    x = make_inputs("c2_per_token", M=8, K=4096, N=1, seed=9)[0]
+    y = O.rmsnorm(x, np.ones(4096, np.float32), 0.0).astype(np.float64)
+    assert np.allclose(np.sqrt((y * y).mean(axis=1)), 1.0, rtol=0, atol=1e-6)
+    # eps > 0 only shrinks the output
+    y_eps = O.rmsnorm(x, np.ones(4096, np.float32), 10.0).astype(np.float64)
+    assert np.all(np.abs(y_eps) <= np.abs(y))
+
+
+def test_rmsnorm_quantize_edge_rows():
+    """An all-zero row normalizes to zeros (rms = sqrt(eps)) and takes the
+    1e-8 scale floor and code 0; a one-hot row puts its spike on code 127."""
+    x = np.zeros((2, 64), np.float32)
+    x[1, 17] = -5.0
+    q, s = O.rmsnorm_quantize(x, np.ones(64, np.float32), 1e-6)
+    assert not q[0].any() and s[0] == np.float32(1e-8)
+    assert q[1, 17] == -127 and np.count_nonzero(q[1]) == 1
+    q, s, z = O.rmsnorm_quantize(x, np.ones(64, np.float32), 1e-6, act="asym_row")
+    assert not q[0].any() and z[0] == 0
+    assert q[1, 17] == 0 and np.all(q[1, np.arange(64) != 17] == z[1]) and z[1] == 255
