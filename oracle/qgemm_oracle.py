@@ -43,6 +43,9 @@ MX_BLOCK = 32            # [TL27] 2.3(a): one shared scale per 32 elements
 E4M3_MAX = 448.0         # [TL27] 2.2 item 1: largest finite e4m3 value, 1.75 * 2^8
 MX_AMAX_FLOOR = F32(1e-4)  # [TL27] 2.2 item 3: amax.clamp_min(1e-4)
 
+INT4_QMAX = 7            # [TL27] 2.4: int4 takes qmax = 7, codes clipped to [-qmax - 1, qmax]
+W4_GROUP = 64            # [TL27] 5.1: the W4A8 check uses int8 X and int4 W per group of 64
+
 # Exact-int32 limits on K (see ``k_limit``).
 INT32_MAX = 2**31 - 1
 
@@ -132,6 +135,58 @@ def prepare_weights_int8(w, per_channel: bool = True):
     q, s = quantize_sym_int8(w, per_row=per_channel)
     colsum = q.astype(np.int64).sum(axis=1)
     return q, s, colsum
+
+
+def quantize_int4_groups(w, group: int = W4_GROUP):
+    """Symmetric int4 weights with one scale per ``group`` consecutive K of a row.
+
+    [TL27] 2.4: s = absmax / qmax with qmax = 7, q = clip(round(x / s),
+    -qmax - 1, qmax), x_hat = q * s; its error is at most s / 2, i.e.
+    1 / (2 * 7) = 7.143e-2 of the absmax. [TL27] 2.4 and 5.1: int4 needs a
+    fine granularity, per group of 64 along K in the W4A8 measurement.
+    Readings: float32 arithmetic and rint (half to even) as for int8; s
+    floored at 1e-8 for all-zero groups; a last, partial group takes the
+    amax of its own elements. Returns (q int8 [N, K] with values in [-8, 7],
+    s float32 [N, ceil(K / group)]).
+    """
+    w = np.asarray(w, dtype=F32)
+    N, K = w.shape
+    ng = -(-K // group)
+    wp = np.zeros((N, ng * group), F32)
+    wp[:, :K] = w
+    g = wp.reshape(N, ng, group)
+    s = np.maximum(np.max(np.abs(g), axis=2) / F32(INT4_QMAX), SCALE_FLOOR).astype(F32)
+    q = np.clip(np.rint(g / s[:, :, None]), -INT4_QMAX - 1, INT4_QMAX).astype(np.int8)
+    return q.reshape(N, ng * group)[:, :K], s
+
+
+def w4a8_gemm(q_a, s_a, q_w, s_w, group: int = W4_GROUP):
+    """out[m, n] = s_a[m] * sum_g s_w[n, g] * P_g[m, n] with the exact integer
+    partial sums P_g[m, n] = sum_{k in group g} q_a[m, k] * q_w[n, k].
+
+    [TL27] 4.3: a scale that changes along K must multiply its own block's
+    partial sum inside the K loop (multiplying once after the integer sum
+    only works for scales that do not depend on K). [TL27] 5.1: the
+    quantization-aware float64 reference. The partials are exact (int64);
+    scaling and the sum over groups are float64. s_a is [M] or [1] (per
+    token or per tensor, symmetric int8). Returns (out float64 [M, N],
+    S float64 [M, N] = sum_g |s_a s_w P_g|, the basis of the float32 error).
+    """
+    qa = np.asarray(q_a, np.int64)
+    qw = np.asarray(q_w, np.int64)
+    M, K = qa.shape
+    N = qw.shape[0]
+    sa = np.broadcast_to(np.asarray(s_a, F32).astype(np.float64).reshape(-1), (M,))
+    sw = np.asarray(s_w, F32).astype(np.float64)
+    out = np.zeros((M, N))
+    S = np.zeros((M, N))
+    for gi in range(sw.shape[1]):
+        k0, k1 = gi * group, min(K, (gi + 1) * group)
+        P = (qa[:, k0:k1] @ qw[:, k0:k1].T).astype(np.float64)
+        term = sa[:, None] * sw[None, :, gi] * P
+        out += term
+        S += np.abs(term)
+    return out, S
 
 
 def k_limit(asymmetric: bool) -> int:

@@ -536,3 +536,78 @@ def test_rmsnorm_quantize_edge_rows():
     q, s, z = O.rmsnorm_quantize(x, np.ones(64, np.float32), 1e-6, act="asym_row")
     assert not q[0].any() and z[0] == 0
     assert q[1, 17] == 0 and np.all(q[1, np.arange(64) != 17] == z[1]) and z[1] == 255
+
+
+# --------------------------------------------------------------------------
+# int4 weights per group of 64 and the W4A8 GEMM ([TL27] 2.4, 4.3, 5.1)
+# --------------------------------------------------------------------------
+def test_int4_group_error_bound_is_the_pages_u():
+    """[TL27] 2.4: the int4 error is at most s / 2 = absmax / 14, printed as
+    u = 7.143e-2 of the absmax; codes stay in [-7, 7] with scales from the
+    same data (the -8 bound of the clip never bites)."""
+    W = make_inputs("c4_decode", M=1, K=1000, N=37, seed=5)[1]
+    q, s = O.quantize_int4_groups(W)
+    assert q.min() >= -7 and q.max() <= 7 and q.dtype == np.int8
+    Wp = np.zeros((37, 1024), np.float32)
+    Wp[:, :1000] = W
+    qp = np.zeros((37, 1024), np.int8)
+    qp[:, :1000] = q
+    err = np.abs(Wp.reshape(37, 16, 64) - qp.reshape(37, 16, 64) * s[:, :, None].astype(np.float64))
+    amax = np.abs(Wp.reshape(37, 16, 64)).max(axis=2)
+    ratio = err.max(axis=2) / amax
+    assert ratio.max() <= 1.0 / 14 * (1 + 1e-6)
+    assert abs(1.0 / 14 - 7.143e-2) < 5e-6 and ratio.max() > 0.06     # the bound is nearly reached
+
+
+def test_int4_granularity_beats_per_channel():
+    """[TL27] 2.4: precision is set by how many elements share a scale; with
+    outliers along K, per-group-64 int4 beats one int4 scale per row."""
+    W = make_inputs("c4_decode", M=1, K=4096, N=16, seed=6)[1].copy()
+    W[:, ::700] *= 50.0
+    q, s = O.quantize_int4_groups(W)
+    deq_g = (q.reshape(16, 64, 64) * s[:, :, None]).reshape(16, 4096)
+    q1, s1 = O.quantize_int4_groups(W, group=4096)
+    deq_c = q1 * s1[:, :1]
+    e_g = np.linalg.norm(deq_g - W) / np.linalg.norm(W)
+    e_c = np.linalg.norm(deq_c - W) / np.linalg.norm(W)
+    assert e_g < 0.5 * e_c
+
+
+def test_w4a8_gemm_equals_dequantize_then_multiply_and_catches_scale_mistakes():
+    """The per-group reference equals the float64 product of the dequantized
+    operands; [TL27] 5.1's two planted mistakes -- only the last group's
+    scale, or no weight scale at all -- are far from it."""
+    A, W = make_inputs("c4_decode", M=5, K=700, N=23, seed=11)
+    qa, sa = O.quantize_sym_int8(A, per_row=True)
+    qw, sw = O.quantize_int4_groups(W)
+    out, S = O.w4a8_gemm(qa, sa, qw, sw)
+    swk = np.repeat(sw.astype(np.float64), 64, axis=1)[:, :700]
+    xhat = qa.astype(np.float64) * sa.astype(np.float64)[:, None]
+    what = qw.astype(np.float64) * swk
+    ref = xhat @ what.T
+    assert np.all(np.abs(out - ref) <= 1e-13 * S)
+    last = xhat @ (qw.astype(np.float64) * sw[:, -1:].astype(np.float64)).T
+    none = xhat @ qw.astype(np.float64).T
+    for bad in (last, none):
+        assert np.linalg.norm(bad - ref) / np.linalg.norm(ref) > 0.05
+
+
+def test_w4a8_gemm_integer_partials_brute_force():
+    """Tiny shapes against pure-Python integers and exact rationals."""
+    rng = rng_for(12)
+    for M, N, K in [(1, 1, 1), (2, 3, 65), (3, 2, 130)]:
+        qa = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+        qw = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+        sa = rng.uniform(0.01, 1, size=M).astype(np.float32)
+        ng = -(-K // 64)
+        sw = rng.uniform(0.01, 1, size=(N, ng)).astype(np.float32)
+        out, S = O.w4a8_gemm(qa, sa, qw, sw)
+        for m in range(M):
+            for n in range(N):
+                tot = Fraction(0)
+                for g in range(ng):
+                    P = sum(int(qa[m, k]) * int(qw[n, k]) for k in range(g * 64, min(K, g * 64 + 64)))
+                    tot += Fraction(float(sw[n, g])) * P
+                exact = Fraction(float(sa[m])) * tot
+                # float64 scaling and group sum: a few ulps of S (sum of |terms|)
+                assert abs(Fraction(out[m, n]) - exact) <= Fraction(S[m, n]) * Fraction(4 * ng, 2 ** 53) + Fraction(1, 2 ** 100)
