@@ -160,6 +160,33 @@ def quantize_int4_groups(w, group: int = W4_GROUP):
     return q.reshape(N, ng * group)[:, :K], s
 
 
+def pack_int4_pairs(q):
+    """Two int4 codes per byte along the last axis: element 2i in the low
+    nibble and 2i + 1 in the high nibble, each as its low four two's-complement
+    bits ([TL27] 3.3(b) and pitfall 9: (a & 0x0F) | ((b & 0x0F) << 4)). An odd
+    length is padded with a zero code. Returns uint8 [..., ceil(K / 2)]."""
+    q = np.asarray(q, np.int16)
+    if q.shape[-1] % 2:
+        q = np.concatenate([q, np.zeros(q.shape[:-1] + (1,), np.int16)], axis=-1)
+    lo = q[..., 0::2] & 0x0F
+    hi = q[..., 1::2] & 0x0F
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4_pairs(b, K: int):
+    """Inverse of pack_int4_pairs: each nibble moved to the top of a signed
+    byte, then shifted right arithmetically by four, which restores the sign
+    ([TL27] 3.3(c) and pitfall 9: a logical shift would turn -1 into 15).
+    Returns int8 [..., K]."""
+    b = np.asarray(b, np.uint8)
+    lo = ((b << 4).astype(np.uint8).view(np.int8) >> 4).astype(np.int8)
+    hi = (b.view(np.int8) >> 4).astype(np.int8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out[..., :K]
+
+
 def w4a8_gemm(q_a, s_a, q_w, s_w, group: int = W4_GROUP):
     """out[m, n] = s_a[m] * sum_g s_w[n, g] * P_g[m, n] with the exact integer
     partial sums P_g[m, n] = sum_{k in group g} q_a[m, k] * q_w[n, k].

@@ -611,3 +611,42 @@ def test_w4a8_gemm_integer_partials_brute_force():
                 exact = Fraction(float(sa[m])) * tot
                 # float64 scaling and group sum: a few ulps of S (sum of |terms|)
                 assert abs(Fraction(out[m, n]) - exact) <= Fraction(S[m, n]) * Fraction(4 * ng, 2 ** 53) + Fraction(1, 2 ** 100)
+
+
+def test_w4a8_reference_table_rows_b_and_d():
+    """[TL27] 5.1's table: with int4 per-group-64 weights, a product that takes
+    only the last group's scale sits ~0.21 from the quantization-aware
+    reference, and the unquantized product ~0.108 (the int4 error)."""
+    g = _golden("tl27_w4a8_reference_table.json")
+    rng = rng_for(13)
+    A = rng.standard_normal((96, 2048)).astype(np.float32)
+    W = rng.standard_normal((192, 2048)).astype(np.float32)
+    qa, sa = O.quantize_sym_int8(A, per_row=True)
+    qw, sw = O.quantize_int4_groups(W, group=g["group"])
+    out, _ = O.w4a8_gemm(qa, sa, qw, sw, group=g["group"])
+    xhat = qa.astype(np.float64) * sa.astype(np.float64)[:, None]
+    row_b = xhat @ (qw.astype(np.float64) * sw[:, -1:].astype(np.float64)).T
+    row_d = A.astype(np.float64) @ W.astype(np.float64).T
+    rel = lambda x: np.linalg.norm(x - out) / np.linalg.norm(out)
+    for got, want in ((rel(row_b), g["row_B_only_last_group_scale_rel_l2"]),
+                      (rel(row_d), g["row_D_unquantized_weights_rel_l2"])):
+        assert abs(got - want) <= g["tolerance_rel"] * want, (got, want)
+
+
+def test_int4_pair_packing_bytes_and_sign_restoration():
+    """[TL27] 3.3(b)/(c) and pitfall 9: low nibble first, two's complement,
+    arithmetic shift on the way back. Every one of the 256 code pairs
+    round-trips; -1 packs to 0xF (not 15 on the way back)."""
+    codes = np.array([(a, b) for a in range(-8, 8) for b in range(-8, 8)], np.int8).reshape(1, -1)
+    packed = O.pack_int4_pairs(codes)
+    assert packed.shape == (1, 256)
+    for i in range(256):
+        a, b = int(codes[0, 2 * i]), int(codes[0, 2 * i + 1])
+        assert int(packed[0, i]) == (a % 16) + 16 * (b % 16)
+    assert sorted(set(packed[0].tolist())) == list(range(256))
+    assert np.array_equal(O.unpack_int4_pairs(packed, 512), codes)
+    assert O.pack_int4_pairs(np.array([[-1, 0]], np.int8))[0, 0] == 0x0F
+    assert O.unpack_int4_pairs(np.array([[0x0F]], np.uint8), 2).tolist() == [[-1, 0]]
+    # odd K pads one zero code
+    assert O.pack_int4_pairs(np.array([[3, -2, -8]], np.int8)).tolist() == [[0xE3, 0x08]]
+    assert O.unpack_int4_pairs(np.array([[0xE3, 0x08]], np.uint8), 3).tolist() == [[3, -2, -8]]
