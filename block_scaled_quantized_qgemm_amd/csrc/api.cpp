@@ -17,6 +17,8 @@ constexpr int64_t kKPad = 256;   // packed columns are padded to this multiple (
 constexpr int64_t kSymKMax = 133144;   // 127*127*K < 2^31
 constexpr int64_t kAsymKMax = 66311;   // 255*127*K < 2^31
 constexpr int64_t kMaxRows = 0x7fffffff;
+constexpr int64_t kW4MaxRows = 16 * 65535;  // 16-row bands along the grid's second dimension
+constexpr int64_t kW4MaxK = int64_t(1) << 27;  // a 16-row block's codes (8 K_pad bytes) in one 32-bit range
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -49,12 +51,20 @@ bool weight_layout(int64_t N, int64_t K, int fmt, int gran, Layout* L) {
     if (!is_int_gran(gran)) return false;
   } else if (fmt == QGEMM_FMT_MXFP8_E4M3) {
     if (gran != QGEMM_GRAN_BLOCK32 || K % 32 != 0) return false;
+  } else if (fmt == QGEMM_FMT_INT4_SYM) {
+    if (gran != QGEMM_GRAN_GROUP64) return false;
   } else {
     return false;
   }
   L->N_pad = round_up(N, kNPad);
   L->K_pad = round_up(K, kKPad);
   L->codes_off = 0;
+  if (fmt == QGEMM_FMT_INT4_SYM) {  // two codes per byte, one float32 scale per 64 K
+    L->scales_off = round_up(L->N_pad * L->K_pad / 2, 256);
+    L->colsum_off = -1;
+    L->bytes = round_up(L->scales_off + 4 * L->N_pad * (L->K_pad / 64), 256);
+    return true;
+  }
   L->scales_off = round_up(L->N_pad * L->K_pad, 256);
   if (fmt == QGEMM_FMT_INT8_SYM) {
     L->colsum_off = round_up(L->scales_off + 4 * L->N_pad, 256);
@@ -177,9 +187,10 @@ int qgemm_rmsnorm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ld
 int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int fmt, int gran, void* packed,
                           size_t packed_bytes, qgemm_wdesc* desc, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  if (fmt != QGEMM_FMT_INT8_SYM && fmt != QGEMM_FMT_MXFP8_E4M3) return QGEMM_E_MODE;
+  if (fmt != QGEMM_FMT_INT8_SYM && fmt != QGEMM_FMT_MXFP8_E4M3 && fmt != QGEMM_FMT_INT4_SYM) return QGEMM_E_MODE;
   if (fmt == QGEMM_FMT_INT8_SYM && !is_int_gran(gran)) return QGEMM_E_MODE;
   if (fmt == QGEMM_FMT_MXFP8_E4M3 && gran != QGEMM_GRAN_BLOCK32) return QGEMM_E_MODE;
+  if (fmt == QGEMM_FMT_INT4_SYM && gran != QGEMM_GRAN_GROUP64) return QGEMM_E_MODE;
   Layout L;
   if (!weight_layout(N, K, fmt, gran, &L)) return QGEMM_E_SHAPE;
   if (!w || !packed || !desc) return QGEMM_E_NULL;
@@ -199,6 +210,8 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int
     qg::launch_quantize_int(w, N, K, ldw, false, gran == QGEMM_GRAN_TENSOR, base + L.codes_off, L.K_pad,
                             L.K_pad / 64, (float*)(base + L.scales_off), nullptr, (int32_t*)(base + L.colsum_off),
                             (float*)workspace, st);
+  } else if (fmt == QGEMM_FMT_INT4_SYM) {
+    qg::launch_quantize_int4(w, N, K, ldw, L.K_pad, base + L.codes_off, (float*)(base + L.scales_off), st);
   } else {
     if (hipMemsetAsync(base + L.scales_off, 127, (size_t)(L.N_pad * (L.K_pad / 32)), st) != hipSuccess)
       return QGEMM_E_HIP;
@@ -304,6 +317,49 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
   g.ldo = ldo;
   g.bias = bias;
   hipError_t e = qg::launch_gemm_mx(g, mode, as_stream(stream));
+  return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
+}
+
+int qgemm_run_w4a8(const int8_t* a_q, int64_t lda, const float* a_scales, int a_gran, int64_t M,
+                   const qgemm_wdesc* w_desc, const void* w_packed, void* out, int64_t ldo, int out_type,
+                   const float* bias, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!is_int_gran(a_gran)) return QGEMM_E_MODE;
+  if (out_type != QGEMM_OUT_F32 && out_type != QGEMM_OUT_BF16) return QGEMM_E_MODE;
+  int rc = check_desc(w_desc, QGEMM_FMT_INT4_SYM);
+  if (rc != QGEMM_OK) return rc;
+  const int64_t N = w_desc->N, K = w_desc->K;
+  if (K > kW4MaxK) return QGEMM_E_SHAPE;
+  if (M < 0 || M > kW4MaxRows) return QGEMM_E_SHAPE;
+  if (M == 0) return QGEMM_OK;
+  if (!a_q || !a_scales || !w_packed || !out) return QGEMM_E_NULL;
+  if (lda < K || ldo < N) return QGEMM_E_SHAPE;
+  // one 16-row band of A is addressed with 32-bit byte offsets (a wave may
+  // read up to 4 KB past K_pad)
+  if ((std::min<int64_t>(M, 16) - 1) * lda + w_desc->K_pad + 65536 >= (int64_t(1) << 32)) return QGEMM_E_SHAPE;
+  if (lda % 16 != 0 || !aligned(a_q, 16) || ldo % 4 != 0 || !aligned(out, 16) || !aligned(w_packed, 256) ||
+      !aligned(a_scales, 4) || (bias && !aligned(bias, 4)))
+    return QGEMM_E_ALIGN;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+
+  const uint8_t* base = (const uint8_t*)w_packed;
+  qg::GemmArgs g{};
+  g.a = (const uint8_t*)a_q;
+  g.lda = lda;
+  g.sa = a_scales;
+  g.a_per_tensor = a_gran == QGEMM_GRAN_TENSOR;
+  g.w = base + w_desc->codes_off;
+  g.sw = (const float*)(base + w_desc->scales_off);
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.K_pad = w_desc->K_pad;
+  g.out = out;
+  g.ldo = ldo;
+  g.bias = bias;
+  hipError_t e = qg::launch_gemm_w4a8(g, out_type, as_stream(stream));
   return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
 }
 

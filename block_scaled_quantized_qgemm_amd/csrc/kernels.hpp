@@ -24,6 +24,11 @@ void launch_rmsnorm_quantize(const float* x, int64_t rows, int64_t K, int64_t ld
 void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
                         uint8_t* e8, int64_t lde, hipStream_t st);
 
+// int4 weights, symmetric, one scale per group of 64 K of each row, into the
+// packed layout of GemmArgs::w (INT4). The buffer must be zero beforehand.
+void launch_quantize_int4(const float* w, int64_t rows, int64_t K, int64_t ldw, int64_t K_pad, uint8_t* codes,
+                          float* scales, hipStream_t st);
+
 struct GemmArgs {
   const uint8_t* a;     // activation codes [M][lda]
   int64_t lda;
@@ -36,8 +41,14 @@ struct GemmArgs {
   // (n / 16, k / 64) at byte ((n / 16) * (K_pad / 64) + k / 64) * 1024, and in
   // it the 16 bytes k % 64 in [16c, 16c + 16) of row n % 16 at 256 c + 16 (n % 16)
   // (one v_mfma_i32_16x16x64_i8 B operand in lane order). MX: row-major.
+  // INT4: N_pad x K_pad / 2 bytes in 1 KB blocks of 16 rows x 128 K, block
+  // (n / 16, k / 128) at ((n / 16) * (K_pad / 128) + k / 128) * 1024; lane
+  // l = 16 c + n % 16 owns the 16 bytes at 16 l: bytes 0-7 hold k % 128 in
+  // [16c, 16c + 16), bytes 8-15 the same chunk of the next group; in each
+  // 8 bytes, dword d holds kk = k % 16 in [8d, 8d + 8), kk % 4 in its byte,
+  // the low nibble for kk % 8 < 4 and the high one otherwise.
   const uint8_t* w;
-  const float* sw;      // int8: [N_pad] or [1]
+  const float* sw;      // int8: [N_pad] or [1]; INT4: 32 per code block, 2 (n % 16) + g % 2
   const int32_t* colsum;
   const uint8_t* ew;    // mx: E8M0 [N_pad][K_pad/32]
   int w_per_tensor;
@@ -52,5 +63,8 @@ hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_
 // qgemm_run_mx: block-scaled e4m3 GEMM, float32 output. mode 0: exact products
 // (bf16 matrix cores on dequantized values), mode 1: block-scaled fp8 matrix cores.
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st);
+// qgemm_run_w4a8: int8 activations x int4 weights, per-group scales inside
+// the K loop, float32 sums. out_type: 0 f32, 1 bf16.
+hipError_t launch_gemm_w4a8(const GemmArgs& a, int out_type, hipStream_t st);
 
 }  // namespace qg

@@ -416,6 +416,35 @@ __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __re
   if ((threadIdx.x & 7) == 0) e8[row * lde + (k >> 5)] = (uint8_t)E;
 }
 
+// int4 weights: one wave per group of 64 K of a row, a lane per element.
+// s = max(amax / 7, 1e-8), q = clamp(rint(w / s), -8, 7) ("TileLang
+// tutorial, chapter 27", section 2.4, with the groups of 64 of its section
+// 5.1). The lane of the lower K of each (k, k + 4) pair takes its partner's
+// code and writes the byte holding both (low nibble first); lane 0 writes the
+// scale. Groups wholly past K exit (their codes and scales stay zero).
+__global__ __launch_bounds__(kRowThreads) void quant_int4_groups_kernel(const float* __restrict__ w, int64_t ldw,
+                                                                        int64_t K, int64_t K_pad,
+                                                                        uint8_t* __restrict__ codes,
+                                                                        float* __restrict__ scales) {
+  const int64_t n = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t g = (int64_t)blockIdx.y * (kRowThreads / kWave) + (threadIdx.x / kWave);
+  if (g * 64 >= K) return;  // the whole wave
+  const int64_t k = g * 64 + lane;
+  const float v = k < K ? w[n * ldw + k] : 0.0f;
+  const float amax = wave_max(fabsf(v));
+  const float s = fmaxf(amax / 7.0f, 1e-8f);
+  const float y = 1.0f / s;  // correctly rounded
+  const float r = fminf(fmaxf(rintf(div_rn(v, s, y)), -8.0f), 7.0f);
+  const uint32_t nib = (uint32_t)(int)r & 0xfu;
+  const uint32_t up = (uint32_t)__shfl_xor((int)nib, 4, kWave);
+  const int64_t blk = (n >> 4) * (K_pad >> 7) + (g >> 1);
+  const int kk = lane & 15, c = lane >> 4;
+  if ((lane & 4) == 0)
+    codes[(blk << 10) + ((16 * c + (n & 15)) << 4) + 8 * (g & 1) + 4 * (kk >> 3) + (kk & 3)] = (uint8_t)(nib | (up << 4));
+  if (lane == 0) scales[blk * 32 + 2 * (n & 15) + (g & 1)] = s;
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
@@ -473,6 +502,14 @@ void launch_rmsnorm_quantize(const float* x, int64_t rows, int64_t K, int64_t ld
     launch_rows<true, false, true>(x, rows, K, ldx, qd, scales, zeros, nullptr, nm, st);
   else
     launch_rows<false, false, true>(x, rows, K, ldx, qd, scales, zeros, nullptr, nm, st);
+}
+
+void launch_quantize_int4(const float* w, int64_t rows, int64_t K, int64_t ldw, int64_t K_pad, uint8_t* codes,
+                          float* scales, hipStream_t st) {
+  if (rows == 0) return;
+  constexpr int gpb = kRowThreads / kWave;  // groups per workgroup
+  dim3 grid((unsigned)rows, (unsigned)((K_pad / 64 + gpb - 1) / gpb)), block(kRowThreads);
+  quant_int4_groups_kernel<<<grid, block, 0, st>>>(w, ldw, K, K_pad, codes, scales);
 }
 
 void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,

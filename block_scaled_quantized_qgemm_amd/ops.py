@@ -14,8 +14,8 @@ import torch
 
 from . import _lib as L
 
-FMT_INT8_SYM, FMT_UINT8_ASYM, FMT_MXFP8_E4M3 = 0, 1, 2
-GRAN_TENSOR, GRAN_ROW, GRAN_BLOCK32 = 0, 1, 2
+FMT_INT8_SYM, FMT_UINT8_ASYM, FMT_MXFP8_E4M3, FMT_INT4_SYM = 0, 1, 2, 3
+GRAN_TENSOR, GRAN_ROW, GRAN_BLOCK32, GRAN_GROUP64 = 0, 1, 2, 3
 OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
 MX_EXACT, MX_SCALED_MFMA = 0, 1
 
@@ -75,6 +75,21 @@ def unblock_int8_codes(raw: torch.Tensor, n_pad: int, k_pad: int) -> torch.Tenso
     return b.permute(0, 3, 1, 2, 4).reshape(n_pad, k_pad)     # [rb, r, kb, c, j]
 
 
+def unblock_int4_codes(raw: torch.Tensor, n_pad: int, k_pad: int) -> torch.Tensor:
+    """Row-major int8 [n_pad, k_pad] codes from the packed int4 layout: 1 KB
+    blocks of 16 rows x 128 K; lane 16 c + r of a block owns 16 bytes, 8 per
+    group of 64 K; dword d of those 8 holds k % 16 in [8d, 8d + 8), k % 4 in
+    its byte, low nibble for k % 8 < 4. Nibbles are sign-extended."""
+    b = raw.reshape(n_pad // 16, k_pad // 128, 4, 16, 2, 2, 4)  # [rb, pb, c, r, g, d, byte]
+    lo = b & 0x0F
+    hi = b >> 4
+    nib = torch.stack([lo, hi], dim=6)                        # [rb, pb, c, r, g, d, half, byte]
+    nib = nib.to(torch.int16)
+    val = torch.where(nib >= 8, nib - 16, nib).to(torch.int8)
+    # k = 128 pb + 64 g + 16 c + 8 d + 4 half + byte
+    return val.permute(0, 3, 1, 4, 2, 5, 6, 7).reshape(n_pad, k_pad)
+
+
 @dataclass
 class PackedWeights:
     """A prepared weight buffer and its host descriptor."""
@@ -93,6 +108,9 @@ class PackedWeights:
         """Codes as [N_pad, K_pad], row-major. The int8 buffer stores 1 KB blocks
         of 16 rows x 64 K (see qgemm_wdesc); those come back as a row-major copy."""
         d = self.desc
+        if d.fmt == FMT_INT4_SYM:
+            raw = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad // 2]
+            return unblock_int4_codes(raw, d.N_pad, d.K_pad)
         raw = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad]
         if d.fmt != FMT_INT8_SYM:
             return raw.view(d.N_pad, d.K_pad)
@@ -103,6 +121,10 @@ class PackedWeights:
         if d.fmt == FMT_INT8_SYM:
             n = 1 if d.gran == GRAN_TENSOR else d.N_pad
             return self.packed[d.scales_off: d.scales_off + 4 * n].view(torch.float32)
+        if d.fmt == FMT_INT4_SYM:  # [N_pad, K_pad / 64] from 32 per code block: [rb, pb, r, g]
+            n = d.N_pad * (d.K_pad // 64)
+            raw = self.packed[d.scales_off: d.scales_off + 4 * n].view(torch.float32)
+            return raw.reshape(d.N_pad // 16, d.K_pad // 128, 16, 2).permute(0, 2, 1, 3).reshape(d.N_pad, d.K_pad // 64)
         return self.packed[d.scales_off: d.scales_off + d.N_pad * (d.K_pad // 32)].view(d.N_pad, d.K_pad // 32)
 
     def colsum(self) -> torch.Tensor:
@@ -174,7 +196,8 @@ def qgemm_rmsnorm_quantize_rows(x: torch.Tensor, gamma: torch.Tensor, eps: float
 
 def qgemm_prepack_weights(w: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = GRAN_ROW,
                           stream=None) -> PackedWeights:
-    """Prepare a float32 [N, K] weight (per-channel / per-tensor int8, or MXFP8)."""
+    """Prepare a float32 [N, K] weight (per-channel / per-tensor int8, MXFP8,
+    or int4 with a scale per group of 64 K)."""
     lib = L.load()
     assert w.dtype == torch.float32 and w.dim() == 2 and w.stride(1) == 1
     N, K = w.shape
@@ -233,4 +256,21 @@ def qgemm_run_mx(a: QuantizedRows, w: PackedWeights, out: Optional[torch.Tensor]
                           ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0), mode,
                           _bias_ptr(bias, N), None, 0, ctypes.c_void_p(_stream(dev, stream)))
     _check("qgemm_run_mx", st)
+    return out[:, :N]
+
+
+def qgemm_run_w4a8(a: QuantizedRows, w: PackedWeights, out_type: int = OUT_F32,
+                   out: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """int8 activations x int4 weights with per-group-64 scales (float32 or
+    bfloat16 out, plus an optional float32 bias [N]); returns out[:, :N]."""
+    lib = L.load()
+    dev = a.q.device
+    N = w.N
+    if out is None:
+        out = _alloc_out(a.M, N, _OUT_DTYPES[out_type], dev)
+    st = lib.qgemm_run_w4a8(_ptr(a.q), a.q.stride(0), _ptr(a.scales), a.gran, a.M,
+                            ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0), out_type,
+                            _bias_ptr(bias, N), None, 0, ctypes.c_void_p(_stream(dev, stream)))
+    _check("qgemm_run_w4a8", st)
     return out[:, :N]

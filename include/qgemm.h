@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define QGEMM_ABI_VERSION 3
+#define QGEMM_ABI_VERSION 4
 #define QGEMM_WDESC_MAGIC 0x51474d57u /* "WMGQ" */
 
 /* Status codes. Every entry point returns one of these. */
@@ -72,14 +72,20 @@ typedef enum {
   QGEMM_FMT_UINT8_ASYM = 1,
   /* OCP e4m3fn data with one E8M0 power-of-two scale per 32 K-elements.
    * [TL27] sections 2.2 and 2.3. */
-  QGEMM_FMT_MXFP8_E4M3 = 2
+  QGEMM_FMT_MXFP8_E4M3 = 2,
+  /* Symmetric int4 weights, codes in [-8, 7], x = q * s with one scale per
+   * group of 64 consecutive K-elements of a row (weights only).
+   * [TL27] sections 2.4 (s = absmax / 7, clip to [-8, 7]), 3.3(c) and 5.1
+   * (int8 activations times int4 weights in groups of 64). */
+  QGEMM_FMT_INT4_SYM = 3
 } qgemm_format;
 
 /* Scale granularity. */
 typedef enum {
   QGEMM_GRAN_TENSOR = 0,  /* one scale (and zero point) for the whole matrix          */
   QGEMM_GRAN_ROW = 1,     /* one per row: per token for A, per output channel for W   */
-  QGEMM_GRAN_BLOCK32 = 2  /* one per 32 contiguous K-elements of a row (MX only)      */
+  QGEMM_GRAN_BLOCK32 = 2, /* one per 32 contiguous K-elements of a row (MX only)      */
+  QGEMM_GRAN_GROUP64 = 3  /* one per 64 contiguous K-elements of a row (INT4 only)    */
 } qgemm_granularity;
 
 /* Output element type of qgemm_run. */
@@ -122,12 +128,22 @@ typedef enum {
  *           [16c, 16c+16) (so each block is one 16x16x64 int8 matrix-core
  *           operand in lane order and a streamed 1 KB load).
  *           QGEMM_FMT_MXFP8_E4M3: e4m3 codes [N_pad][K_pad], row-major.
+ *           QGEMM_FMT_INT4_SYM: N_pad x K_pad / 2 bytes in 1 KB blocks of 16
+ *           rows x 128 K; block (n/16, k/128) starts at byte
+ *           ((n/16)*(K_pad/128) + k/128) * 1024. Row n%16 and c = (k%64)/16
+ *           own the 16 bytes at 16*(16c + n%16): bytes 0-7 for k%128 < 64,
+ *           8-15 for the other group; in those 8 bytes, the 16 codes of
+ *           kk = k%16 sit in byte 4*(kk/8) + kk%4, in the low nibble when
+ *           kk%8 < 4, else the high one; a nibble is the code's low four
+ *           two's-complement bits ([TL27] 3.3(b) and pitfall 9).
  *   scales  at scales_off: INT8: float32 [N_pad] (GRAN_ROW; rows >= N are 0)
  *           or float32 [1] (GRAN_TENSOR). MX: E8M0 bytes [N_pad][K_pad/32]
- *           row-major, padding blocks hold 127 (scale 1.0).
+ *           row-major, padding blocks hold 127 (scale 1.0). INT4: float32,
+ *           32 per code block: the scale of row n, group g at float index
+ *           ((n/16)*(K_pad/128) + g/2) * 32 + 2*(n%16) + g%2; padding is 0.
  *   colsum  at colsum_off: INT8 only: int32 [N_pad], colsum[n] = sum_k q_w[n,k]
  *           ([D98] "The program, and the gate that has to be per column":
- *           computed once, when the weights are quantized). -1 for MX.
+ *           computed once, when the weights are quantized). -1 for MX and INT4.
  */
 typedef struct qgemm_wdesc {
   uint32_t magic;      /* QGEMM_WDESC_MAGIC                        */
@@ -242,6 +258,10 @@ int qgemm_rmsnorm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ld
  *     colsum[n] = sum_k q_w[n,k]  ([AQ] "The integer GEMM, written out",
  *     quantize_per_channel; [D98] the column sums of the zero-point row).
  *   MXFP8_E4M3, BLOCK32: the MX rule of qgemm_quantize_rows on each row of W.
+ *   INT4_SYM, GROUP64: per row n and group g of 64 K (a last, shorter group
+ *     takes the elements it has), s = max(amax / 7, 1e-8) in float32,
+ *     q = clamp(rint(w / s), -8, 7) with a correctly rounded quotient
+ *     ([TL27] 2.4; 5.1 for the group of 64).
  *   Writes the packed layout described at qgemm_wdesc (including zero padding)
  *   and fills *desc on the host.
  *
@@ -323,6 +343,41 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
                  float* out, int64_t ldo, int mode, const float* bias,
                  void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/*
+ * qgemm_run_w4a8 -- int8 activations times int4 weights with one scale per
+ * group of 64 K ([TL27] 3.3(c) and 5.1).
+ *
+ *   P_g[m,n] = sum_{k in group g} q_a[m,k] * q_w[n,k]            exact int32
+ *   out[m,n] = s_a[m] * sum_g s_w[n,g] * P_g[m,n]                float32
+ *              (each group's scale multiplies its own partial sum inside
+ *              the K loop: [TL27] 4.3, a scale that varies along K cannot
+ *              be applied once after the sum)
+ *   out[m,n] = out[m,n] + bias[n]                                if bias != NULL
+ *   cast to float32 or bfloat16 (round to nearest even).
+ *   Rounding: float32 accumulation over the groups; |out - exact| is within
+ *   (K_pad / 64 + 16) * 2^-24 * (sum_g |s_a s_w[n,g] P_g| + |bias[n]|) for
+ *   float32 output.
+ *
+ *   a_q      device int8 codes [M][lda] (QGEMM_FMT_INT8_SYM activations from
+ *            qgemm_quantize_rows), lda >= K, lda % 16 == 0, 16-byte aligned;
+ *            (min(M, 16) - 1) * lda + K_pad + 65536 < 2^32 (QGEMM_E_SHAPE).
+ *   a_scales device float32 [M] (a_gran QGEMM_GRAN_ROW) or [1] (TENSOR).
+ *   M        0 <= M <= 16 * 65535 (QGEMM_E_SHAPE).
+ *   w_desc   host descriptor of QGEMM_FMT_INT4_SYM / QGEMM_GRAN_GROUP64 weights.
+ *   out      device [M][ldo] of out_type (QGEMM_OUT_F32 or QGEMM_OUT_BF16;
+ *            QGEMM_OUT_I32 is QGEMM_E_MODE: there is no single integer sum),
+ *            ldo >= N, ldo % 4 == 0, 16-byte aligned.
+ *   bias     device float32 [N] or NULL.
+ *   K <= 2^27 (QGEMM_E_SHAPE); no tighter limit: every group's partial sum
+ *   is exact in int32 and in float32.
+ *   workspace unused by this version (pass NULL, 0).
+ */
+int qgemm_run_w4a8(const int8_t* a_q, int64_t lda, const float* a_scales, int a_gran, int64_t M,
+                   const qgemm_wdesc* w_desc, const void* w_packed,
+                   void* out, int64_t ldo, int out_type, const float* bias,
+                   void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,8 +15,8 @@ from block_scaled_quantized_qgemm_amd import _lib as L  # noqa: E402
 HEADER = os.path.join(ROOT, "include", "qgemm.h")
 
 OK, E_NULL, E_SHAPE, E_MODE, E_ALIGN, E_OVERFLOW, E_DEVICE, E_DESC, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8
-INT8, UINT8, MX = 0, 1, 2
-TENSOR, ROW, BLK = 0, 1, 2
+INT8, UINT8, MX, INT4 = 0, 1, 2, 3
+TENSOR, ROW, BLK, G64 = 0, 1, 2, 3
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.qgemm_abi_version() == 3
+    assert lib.qgemm_abi_version() == 4
     for s in range(-9, 1):
         assert lib.qgemm_status_string(s).startswith(b"QGEMM_")
     assert lib.qgemm_status_string(-100) == b"unknown qgemm status"
@@ -58,6 +58,12 @@ def test_sizes(lib):
     assert lib.qgemm_workspace_bytes(64, 256, UINT8, TENSOR) == 512
     assert lib.qgemm_workspace_bytes(64, 256, INT8, ROW) == 0
     assert lib.qgemm_workspace_bytes(64, 256, MX, BLK) == 0
+    # int4: codes [256][512 / 2], then float32 scales [256][512 / 64]
+    assert lib.qgemm_packed_weight_bytes(100, 300, INT4, G64) == 256 * 256 + 4 * 256 * 8
+    assert lib.qgemm_packed_weight_bytes(14336, 4096, INT4, G64) == 14336 * 2048 + 4 * 14336 * 64
+    assert lib.qgemm_packed_weight_bytes(100, 300, INT4, ROW) == 0
+    assert lib.qgemm_packed_weight_bytes(100, 300, INT8, G64) == 0
+    assert lib.qgemm_workspace_bytes(64, 256, INT4, G64) == 0
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
@@ -91,7 +97,7 @@ def test_quantize_rows_validation(lib):
 
 
 def _wdesc(**kw):
-    d = L.WDesc(magic=0x51474D57, version=3, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=4, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 512, colsum_off=256 * 512 + 1024, bytes=256 * 512 + 2048)
     for k, v in kw.items():
         setattr(d, k, v)
@@ -137,7 +143,7 @@ def test_run_validation(lib):
 
 def test_run_mx_validation(lib):
     nb = lib.qgemm_packed_weight_bytes(100, 320, MX, BLK)
-    d = L.WDesc(magic=0x51474D57, version=3, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=4, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 512, colsum_off=-1, bytes=nb)
     call = lambda **kw: lib.qgemm_run_mx(kw.get("a", FAKE), kw.get("lda", 320), kw.get("e", FAKE),
                                          kw.get("ldas", 10), kw.get("M", 4), ctypes.byref(kw.get("d", d)),
@@ -187,7 +193,51 @@ def test_prepack_validation(lib):
     assert f(p=0x100000 + 128) == E_ALIGN
     assert f(pb=100) == E_SHAPE
     assert f(gran=TENSOR) == E_WS
+    assert f(fmt=INT4, gran=ROW) == E_MODE
+    assert f(fmt=INT8, gran=G64) == E_MODE
+    assert f(fmt=INT4, gran=G64, pb=100) == E_SHAPE
     assert d.magic == 0                                   # untouched on error
+
+
+def _w4desc(**kw):
+    nb = 256 * 256 + 4 * 256 * 8
+    d = L.WDesc(magic=0x51474D57, version=4, fmt=INT4, gran=G64, N=100, K=300, N_pad=256, K_pad=512,
+                codes_off=0, scales_off=256 * 256, colsum_off=-1, bytes=nb)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _run4(lib, d, a=FAKE, lda=304, s=FAKE, gran=ROW, M=8, w=FAKE, out=FAKE, ldo=100, ot=0, bias=None):
+    return lib.qgemm_run_w4a8(a, lda, s, gran, M, ctypes.byref(d), w, out, ldo, ot, bias, None, 0, None)
+
+
+def test_run_w4a8_validation(lib):
+    good = _w4desc()
+    assert lib.qgemm_packed_weight_bytes(100, 300, INT4, G64) == good.bytes
+    assert _run4(lib, _wdesc()) == E_DESC                 # an int8 descriptor
+    assert _run4(lib, _w4desc(colsum_off=0)) == E_DESC
+    assert _run4(lib, _w4desc(scales_off=256 * 512)) == E_DESC
+    assert lib.qgemm_run_w4a8(FAKE, 304, FAKE, ROW, 8, None, FAKE, FAKE, 100, 0, None, None, 0, None) == E_NULL
+    assert _run(lib, good) == E_DESC                      # int4 weights through the int8 call
+    assert _run4(lib, good, gran=BLK) == E_MODE
+    assert _run4(lib, good, ot=2) == E_MODE               # no single integer sum to export
+    assert _run4(lib, good, M=-1) == E_SHAPE
+    assert _run4(lib, good, M=16 * 65535 + 1) == E_SHAPE
+    assert _run4(lib, good, M=0, a=None, s=None, w=None, out=None) == OK
+    assert _run4(lib, good, s=None) == E_NULL
+    assert _run4(lib, good, lda=288) == E_SHAPE
+    assert _run4(lib, good, lda=312) == E_ALIGN
+    assert _run4(lib, good, ldo=99) == E_SHAPE
+    assert _run4(lib, good, ldo=102) == E_ALIGN
+    assert _run4(lib, good, w=FAKE + 16) == E_ALIGN
+    assert _run4(lib, good, bias=FAKE + 2) == E_ALIGN
+    assert _run4(lib, good, lda=1 << 29, M=17) == E_SHAPE  # 32-bit offsets over a 16-row band
+    K = (1 << 27) + 1
+    kp = (K + 255) // 256 * 256
+    huge = _w4desc(N=16, K=K, K_pad=kp, scales_off=256 * kp // 2,
+                   bytes=lib.qgemm_packed_weight_bytes(16, K, INT4, G64))
+    assert _run4(lib, huge, lda=kp, M=1) == E_SHAPE
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
@@ -195,6 +245,7 @@ def test_no_device_is_an_error_not_a_fallback(lib):
     # fully valid arguments: the only thing missing is a gfx950
     assert _q(lib) == E_DEVICE
     assert _run(lib, _wdesc()) == E_DEVICE
+    assert _run4(lib, _w4desc()) == E_DEVICE
     assert lib.qgemm_rmsnorm_quantize_rows(FAKE, 4, 64, 64, FAKE, 1e-6, INT8, ROW, FAKE, 64, FAKE, None,
                                            None) == E_DEVICE
 
@@ -214,3 +265,25 @@ def test_packed_int8_block_layout_round_trip():
             off = ((n // 16) * kb + k // 64) * 1024 + 256 * ((k % 64) // 16) + 16 * (n % 16) + k % 16
             raw[off] = ref[n, k]
     assert torch.equal(unblock_int8_codes(raw, n_pad, k_pad), ref)
+
+
+def test_packed_int4_block_layout_round_trip():
+    """The Python view of packed int4 codes inverts the documented layout:
+    block (n // 16, k // 128) at ((n // 16) * (K_pad // 128) + k // 128) KB;
+    lane 16 c + n % 16 (c = (k % 64) // 16) owns 16 bytes, 8 per group of 64;
+    code kk = k % 16 in byte 4 (kk // 8) + kk % 4, low nibble iff kk % 8 < 4."""
+    import torch
+    from block_scaled_quantized_qgemm_amd.ops import unblock_int4_codes
+    n_pad, k_pad = 32, 256
+    ref = torch.randint(-8, 8, (n_pad, k_pad), dtype=torch.int32)
+    raw = [0] * (n_pad * k_pad // 2)
+    pb = k_pad // 128
+    for n in range(n_pad):
+        for k in range(k_pad):
+            c, kk = (k % 64) // 16, k % 16
+            off = ((n // 16) * pb + k // 128) * 1024 + 16 * (16 * c + n % 16) + 8 * ((k % 128) // 64) \
+                + 4 * (kk // 8) + kk % 4
+            nib = int(ref[n, k]) & 0xF
+            raw[off] |= nib if kk % 8 < 4 else nib << 4
+    got = unblock_int4_codes(torch.tensor(raw, dtype=torch.uint8), n_pad, k_pad)
+    assert torch.equal(got.to(torch.int32), ref)
