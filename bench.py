@@ -2,7 +2,7 @@
 
 A step is one pass of the whole hot path over one batch: quantize the float32
 activations (qgemm_quantize_rows) and run the GEMM with its fused epilogue
-(qgemm_run / qgemm_run_mx). Weights are prepared once beforehand (offline, as
+(qgemm_run / qgemm_run_mx, or qgemm_run_w4a8 with --w4a8). Weights are prepared once beforehand (offline, as
 on the pages) and every input is resident in HBM before the timed region.
 Activation / weight / output buffers rotate over enough copies that the
 256 MB Infinity Cache cannot hold the working set.
@@ -49,17 +49,21 @@ DESCRIPTION = {
 }
 
 
-def algorithmic(name, M, K, N):
+def algorithmic(name, M, K, N, w4a8=False):
     """Ops and algorithmic bytes: whole step, and the GEMM kernel alone.
 
     Whole step: float32 A read once, W codes + per-channel scales/column sums
-    (or E8M0 scales) read once, output written once. GEMM kernel: the same
-    with A as 1-byte codes plus its per-row scale (and zero point).
+    (or E8M0 scales, or int4 codes + float32 scales per group of 64 K) read
+    once, output written once. GEMM kernel: the same with A as 1-byte codes
+    plus its per-row scale (and zero point).
     """
     act, _, _, out, _ = WORKLOADS[name]
     ob = {"f32": 4, "bf16": 2}[out]
     ops = 2.0 * M * N * K
-    if act == "mxfp8":
+    if w4a8:
+        w = N * K / 2 + 4 * N * math.ceil(K / 64)
+        a_codes = M * K + 4 * M
+    elif act == "mxfp8":
         w = N * K + N * (K // 32)
         a_codes = M * K + M * (K // 32)
     else:
@@ -70,15 +74,16 @@ def algorithmic(name, M, K, N):
     return ops, step_bytes, gemm_bytes
 
 
-def source_digest():
+def source_digest(w4a8=False):
+    """Digest of the sources of the GEMM kernel a workload times."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.hpp", "kernels.hpp"):
+    for f in ("gemm_w4a8.hip" if w4a8 else "gemm.hip", "common.hpp", "kernels.hpp"):
         with open(os.path.join(ROOT, "block_scaled_quantized_qgemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name, launches_per_step=1):
+def measured_traffic(name):
     """HBM bytes per GEMM launch from committed rocprofv3 counter runs, or None.
 
     profiles/traffic_<workload>.json holds FETCH_SIZE / WRITE_SIZE per dispatch
@@ -91,14 +96,15 @@ def measured_traffic(name, launches_per_step=1):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("source_digest") != source_digest():
+    if t.get("source_digest") != source_digest(name.endswith("_w4a8")):
         return None
     return float(t["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(name, A, W, budget_s=10.0, fused=None):
+def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False):
     """The oracle, untuned, on a bounded sample of the same workload.
-    fused: (gamma, eps, bias) to time the RMSNorm-fused step with a bias."""
+    fused: (gamma, eps, bias) to time the RMSNorm-fused step with a bias;
+    w4a8: int4 per-group-64 weights and the per-group GEMM."""
     import numpy as np
     import oracle as O
     try:
@@ -114,6 +120,10 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None):
         Wq, We = O.quantize_mx(W)                     # offline weight preparation, untimed
         Wd = O.mx_dequantize(Wq, We)
         sample = f"{rows} of {M} rows of A against all of W (W prepared outside the timing)"
+    elif w4a8:
+        rows = min(M, 256)
+        Wq4, Ws4 = O.quantize_int4_groups(W)
+        sample = f"{rows} of {M} rows of A against all of W (W prepared outside the timing)"
     else:
         rows = min(M, 256)
         Wq, Ws, _ = O.prepare_weights_int8(W, per_channel=True)
@@ -124,6 +134,14 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None):
         if act == "mxfp8":
             qa, Ea = O.quantize_mx(As)
             _ = O.mx_dequantize(qa, Ea) @ Wd.T
+        elif w4a8:
+            if fused is not None:
+                qa, sa = O.rmsnorm_quantize(As, fused[0], fused[1], act="sym_row")[:2]
+            else:
+                qa, sa = O.quantize_sym_int8(As, per_row=(gran == "row"))
+            y, _ = O.w4a8_gemm(qa, sa, Wq4, Ws4)
+            if fused is not None:
+                y = y + fused[2].astype(np.float64)[None, :]
         else:
             if fused is not None:
                 r = O.rmsnorm_quantize(As, fused[0], fused[1], act="asym_row" if act == "uint8_asym" else "sym_row")
@@ -142,7 +160,7 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None):
     ops = 2.0 * rows * K * N * reps
     unit = "GB/s" if WORKLOADS[name][4] == "GB/s" else WORKLOADS[name][4]
     if unit == "GB/s":
-        _, step_bytes, _ = algorithmic(name, rows, K, N)
+        _, step_bytes, _ = algorithmic(name, rows, K, N, w4a8)
         value = step_bytes * reps / el / 1e9
     else:
         value = ops / el / 1e12
@@ -167,6 +185,9 @@ def main():
                          "(qgemm_rmsnorm_quantize_rows) and a float32 bias in the GEMM epilogue")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying a captured HIP graph")
+    ap.add_argument("--w4a8", action="store_true",
+                    help="symmetric int8 workloads: int4 weights with a float32 scale per group of 64 K "
+                         "(qgemm_run_w4a8)")
     ap.add_argument("--mx-mode", default="exact", choices=["exact", "scaled-mfma"],
                     help="MX workload: exact products (bf16 matrix cores) or block-scaled fp8 matrix cores")
     args = ap.parse_args()
@@ -186,6 +207,9 @@ def main():
     if args.fused and (act == "mxfp8" or gran != "row"):
         print("bench.py: --fused applies to the per-token int8 / uint8 workloads", file=sys.stderr)
         sys.exit(2)
+    if args.w4a8 and act != "int8_sym":
+        print("bench.py: --w4a8 applies to the symmetric int8 workloads", file=sys.stderr)
+        sys.exit(2)
     M, K, N, _, _ = SHAPES[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -201,9 +225,11 @@ def main():
     A0 = torch.from_numpy(A_np).to(dev)
     W0 = torch.from_numpy(W_np).to(dev)
     wfmt = ops.FMT_MXFP8_E4M3 if act == "mxfp8" else ops.FMT_INT8_SYM   # weights are symmetric
+    if args.w4a8:
+        wfmt, wgr = ops.FMT_INT4_SYM, ops.GRAN_GROUP64
     w0 = ops.qgemm_prepack_weights(W0, wfmt, wgr)
     torch.cuda.synchronize()
-    ops_count, step_bytes, gemm_bytes = algorithmic(name, M, K, N)
+    ops_count, step_bytes, gemm_bytes = algorithmic(name, M, K, N, args.w4a8)
     if args.fused:  # the norm weight and the bias are read once more
         step_bytes += 4 * K + 4 * N
         gemm_bytes += 4 * N
@@ -240,6 +266,8 @@ def main():
         Ai, wi, qi, oi = sets[i % nsets]
         if fmt == ops.FMT_MXFP8_E4M3:
             ops.qgemm_run_mx(qi, wi, out=oi, mode=mx_mode)
+        elif args.w4a8:
+            ops.qgemm_run_w4a8(qi, wi, otype, out=oi, bias=bias if args.fused else None)
         else:
             ops.qgemm_run(qi, wi, otype, out=oi, bias=bias if args.fused else None)
 
@@ -299,7 +327,7 @@ def main():
             peak = PEAK_INT8_TOPS
         roof = {"bound": "mfma", "achieved": gemm_achieved, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(name)
+    roof["traffic"] = measured_traffic(name + ("_w4a8" if args.w4a8 else ""))
 
     line = {
         "metric": METRIC,
@@ -312,11 +340,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3" if act == "mxfp8" else "i8",
+        "dtype": "fp8-e4m3" if act == "mxfp8" else ("i8 x i4" if args.w4a8 else "i8"),
         "data": "synthetic (seeded generator with the workload's shapes and distributions)",
         "config": {"workload": f"{name}: {DESCRIPTION[name]}"
                    + (f" ({args.mx_mode} mode)" if act == "mxfp8" else "")
-                   + (" with RMSNorm fused into the quantizer and a float32 bias" if args.fused else ""),
+                   + (" with RMSNorm fused into the quantizer and a float32 bias" if args.fused else "")
+                   + (" -- W4A8: int4 W with a float32 scale per group of 64 K" if args.w4a8 else ""),
                    "M": M, "K": K, "N": N,
                    "rotating_buffer_sets": nsets, "gemm_ms": gemm_ms,
                    "launch": "eager" if args.eager else "hip graph (K steps captured, replayed once)",
@@ -335,7 +364,8 @@ def main():
           f"wall {wall:.3f} s for {K_steps} steps", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(name, A_np, W_np, args.cpu_budget,
-                                            (gamma.cpu().numpy(), eps, bias.cpu().numpy()) if args.fused else None)
+                                            (gamma.cpu().numpy(), eps, bias.cpu().numpy()) if args.fused else None,
+                                            args.w4a8)
     print(json.dumps(line), flush=True)
 
 

@@ -32,6 +32,9 @@ __device__ inline int wave_sum(int v) {
   return v;
 }
 
+// dword 3 of a raw buffer descriptor: 32-bit data format, no swizzle
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // Round-to-nearest-even of a finite float32 to bfloat16 (the upper half of a
 // float32): add 0x7fff plus the lowest kept bit, then drop the low 16 bits.
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
@@ -52,6 +55,18 @@ __device__ inline int ceil_to_ue8m0(float t) {
 __device__ inline float e8m0_inverse(int E) {
   int be = 254 - E;  // biased exponent of 2^(127-E)
   return be >= 1 ? __uint_as_float((uint32_t)be << 23) : __uint_as_float(0x00400000u);
+}
+
+// One output element: OUT 0 float32 y, 1 bfloat16 of y, 2 the int32 c.
+template <int OUT>
+__device__ inline void store_one(void* out, int64_t idx, int c, float y) {
+  if constexpr (OUT == 2) {
+    reinterpret_cast<int32_t*>(out)[idx] = c;
+  } else if constexpr (OUT == 0) {
+    reinterpret_cast<float*>(out)[idx] = y;
+  } else {
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(y);
+  }
 }
 
 }  // namespace qg

@@ -6,6 +6,8 @@
 //  * gemm_i8_decode_kernel -- M <= 16: a stream over the weights with
 //    v_mfma_i32_16x16x64_i8, every weight byte read once into registers.
 //
+// (int8 x int4 with per-group scales lives in gemm_w4a8.hip.)
+//
 // MX (e4m3 + E8M0 per 32 K), float32 output, gemm_mx_kernel in two modes:
 //  * MXB -- exact products: each e4m3 value is multiplied by its block's
 //           power-of-two scale while the tile is moved into LDS
@@ -359,8 +361,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
 // vmcnt wait and one barrier per K step; the fragments of sub-step kk + 1 are
 // read while the matrix cores work on sub-step kk.
 // ---------------------------------------------------------------------------
-// dword 3 of a raw buffer descriptor: 32-bit data format, no swizzle
-constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
 
 #define QG_LDSP(x) ((__attribute__((address_space(3))) void*)(x))
@@ -659,17 +659,6 @@ static hipError_t launch_dma(const GemmArgs& a, hipStream_t st) {
 // from the range-checked buffer loads. The eight partial int32 tiles are
 // summed through LDS before the epilogue, so the result is exact.
 // ---------------------------------------------------------------------------
-template <int OUT>
-__device__ inline void store_one(void* out, int64_t idx, int c, float y) {
-  if constexpr (OUT == 2) {
-    reinterpret_cast<int32_t*>(out)[idx] = c;
-  } else if constexpr (OUT == 0) {
-    reinterpret_cast<float*>(out)[idx] = y;
-  } else {
-    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(y);
-  }
-}
-
 constexpr int kDecWaves = 8;  // waves per workgroup, each on its own K range
 constexpr int kDecBatch = 8;  // 64-deep steps per load batch
 
@@ -762,121 +751,6 @@ static hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// W4A8: int8 activations x int4 weights with one float32 scale per group of
-// 64 K ("TileLang tutorial, chapter 27", sections 3.3(c) and 5.1), for 16-row
-// bands of A: the decode kernel's stream over W at half the bytes. A
-// workgroup owns 16 weight rows over all of K; its eight waves take
-// contiguous ranges of 128-deep steps (two groups). Per step a lane loads 16
-// bytes of codes (its 16-K chunk of both groups), two 16-byte activation
-// chunks and the two group scales of its weight row.
-//
-// Sign extension without a shift back: a nibble moved to the top of its byte
-// (masking with 0xF0 per byte after a 4-bit shift for the low nibble) is the
-// int8 value 16 q exactly, so the int8 matrix cores give 16 P_g exactly
-// (|16 P_g| <= 16 * 64 * 127 * 8 < 2^24, also exact as a float32). Each group
-// then enters a float32 sum through one FMA with its own scale (section 4.3:
-// a scale that changes along K is applied per block inside the loop, never
-// after the sum); 1/16 is folded into the final s_a multiply, which is exact
-// because it is a power of two.
-// ---------------------------------------------------------------------------
-constexpr int kW4Batch = 4;  // 128-deep steps per load batch
-
-template <int OUT, bool ONE>
-__global__ __launch_bounds__(kDecWaves * 64) void gemm_w4a8_kernel(GemmArgs p) {
-  constexpr int U = kW4Batch;
-  constexpr int kHi = (int)0xF0F0F0F0u;
-  __shared__ v4f red[kDecWaves][64];
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t m0 = (int64_t)blockIdx.y * 16;
-  const int64_t mrows = p.M - m0 < 16 ? p.M - m0 : 16;
-  const int pairs = (int)(p.K_pad / 128);
-  // steps of each wave, a whole number of batches; steps at or past K_pad
-  // read zero codes and zero scales from outside the block's ranges
-  const int per = ONE ? U : (pairs + kDecWaves * U - 1) / (kDecWaves * U) * U;
-  const int pbeg = wid * per;
-  const int row = lane & 15;
-  const int chunk = (lane >> 4) * 16;
-  constexpr uint32_t kOff = 0x80000000u;
-  const int64_t blk0 = (n0 >> 4) * pairs;  // first code block of the workgroup's rows
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.w + blk0 * 1024), (short)0, (int)(pairs * 1024), kRawBufferWord3);
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.sw + blk0 * 32), (short)0, (int)(pairs * 128), kRawBufferWord3);
-  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.a + m0 * p.lda), (short)0, (int)((mrows - 1) * p.lda + ((p.K + 15) & ~(int64_t)15)),
-      kRawBufferWord3);
-  const uint32_t woff = (uint32_t)pbeg * 1024u + (uint32_t)(lane * 16);
-  const uint32_t soff = (uint32_t)pbeg * 128u + (uint32_t)(row * 8);
-  const uint32_t aoff = row < mrows ? (uint32_t)(row * p.lda + pbeg * 128 + chunk) : kOff;
-
-  v4f y = {0.f, 0.f, 0.f, 0.f};
-  for (int b = 0; b < (ONE ? U : per); b += U) {
-    v4i wv[U], a0[U], a1[U];
-    v2f sv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      wv[u] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)(woff + (uint32_t)((b + u) * 1024)), 0, 0));
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      a0[u] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)(aoff + (uint32_t)((b + u) * 128)), 0, 0));
-      a1[u] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)(aoff + (uint32_t)((b + u) * 128 + 64)), 0, 0));
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      sv[u] = __builtin_bit_cast(
-          v2f, __builtin_amdgcn_raw_buffer_load_b64(srs, (int)(soff + (uint32_t)((b + u) * 128)), 0, 0));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const v4i w = wv[u];
-      const v4i w0 = {(w.x << 4) & kHi, w.x & kHi, (w.y << 4) & kHi, w.y & kHi};
-      const v4i w1 = {(w.z << 4) & kHi, w.z & kHi, (w.w << 4) & kHi, w.w & kHi};
-      const v4i zero = {0, 0, 0, 0};
-      const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[u], w0, zero, 0, 0, 0);
-      const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[u], w1, zero, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = __builtin_fmaf(sv[u].x, (float)c0[i], y[i]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = __builtin_fmaf(sv[u].y, (float)c1[i], y[i]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  red[wid][lane] = y;
-  __syncthreads();
-
-  // thread t < 256 finishes item t / 64 of lane t % 64: row 4 * (l / 16) + item, column l % 16
-  for (int t = threadIdx.x; t < 256; t += kDecWaves * 64) {
-    const int l = t & 63, item = t >> 6;
-    const int64_t m = m0 + 4 * (l >> 4) + item;
-    const int64_t n = n0 + (l & 15);
-    if (m < p.M && n < p.N) {
-      float acc = red[0][l][item];
-#pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) acc += red[w][l][item];
-      const float sa = p.a_per_tensor ? p.sa[0] : p.sa[m];
-      float yv = acc * (sa * 0.0625f);  // the codes entered as 16 q
-      if (p.bias) yv = yv + p.bias[n];
-      store_one<OUT>(p.out, m * p.ldo + n, 0, yv);
-    }
-  }
-}
-
-template <int OUT>
-static hipError_t launch_w4a8(const GemmArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 15) / 16));
-  if (a.K_pad <= 128 * kW4Batch * kDecWaves)
-    hipLaunchKernelGGL((gemm_w4a8_kernel<OUT, true>), grid, dim3(kDecWaves * 64), 0, st, a);
-  else
-    hipLaunchKernelGGL((gemm_w4a8_kernel<OUT, false>), grid, dim3(kDecWaves * 64), 0, st, a);
-  return hipGetLastError();
-}
-
 template <bool ASYM, int OUT>
 static hipError_t launch_i8(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 16) return launch_decode<ASYM, OUT>(a, st);
@@ -935,11 +809,6 @@ hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_
   return launch_i8<false, 2>(a, st);
 }
 
-hipError_t launch_gemm_w4a8(const GemmArgs& a, int out_type, hipStream_t st) {
-  if (a.M == 0) return hipSuccess;
-  if (out_type == 1) return launch_w4a8<1>(a, st);
-  return launch_w4a8<0>(a, st);
-}
 
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st) {
   if (a.M == 0) return hipSuccess;

@@ -48,7 +48,8 @@ struct GemmArgs {
   // 8 bytes, dword d holds kk = k % 16 in [8d, 8d + 8), kk % 4 in its byte,
   // the low nibble for kk % 8 < 4 and the high one otherwise.
   const uint8_t* w;
-  const float* sw;      // int8: [N_pad] or [1]; INT4: 32 per code block, 2 (n % 16) + g % 2
+  const float* sw;      // int8: [N_pad] or [1]; INT4: 64 per 16 rows x 256 K, at
+                        // ((n / 16) * (K_pad / 256) + g / 4) * 64 + 4 (n % 16) + g % 4
   const int32_t* colsum;
   const uint8_t* ew;    // mx: E8M0 [N_pad][K_pad/32]
   int w_per_tensor;

@@ -421,7 +421,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __re
 // tutorial, chapter 27", section 2.4, with the groups of 64 of its section
 // 5.1). The lane of the lower K of each (k, k + 4) pair takes its partner's
 // code and writes the byte holding both (low nibble first); lane 0 writes the
-// scale. Groups wholly past K exit (their codes and scales stay zero).
+// scale (16 rows x 4 groups of scales per 64 floats, a row's four together). Groups wholly past K exit (their codes and scales stay zero).
 __global__ __launch_bounds__(kRowThreads) void quant_int4_groups_kernel(const float* __restrict__ w, int64_t ldw,
                                                                         int64_t K, int64_t K_pad,
                                                                         uint8_t* __restrict__ codes,
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_int4_groups_kernel(const fl
   const int kk = lane & 15, c = lane >> 4;
   if ((lane & 4) == 0)
     codes[(blk << 10) + ((16 * c + (n & 15)) << 4) + 8 * (g & 1) + 4 * (kk >> 3) + (kk & 3)] = (uint8_t)(nib | (up << 4));
-  if (lane == 0) scales[blk * 32 + 2 * (n & 15) + (g & 1)] = s;
+  if (lane == 0) scales[((n >> 4) * (K_pad >> 8) + (g >> 2)) * 64 + 4 * (n & 15) + (g & 3)] = s;
 }
 
 // ---------------------------------------------------------------------------

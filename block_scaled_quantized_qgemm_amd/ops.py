@@ -121,10 +121,10 @@ class PackedWeights:
         if d.fmt == FMT_INT8_SYM:
             n = 1 if d.gran == GRAN_TENSOR else d.N_pad
             return self.packed[d.scales_off: d.scales_off + 4 * n].view(torch.float32)
-        if d.fmt == FMT_INT4_SYM:  # [N_pad, K_pad / 64] from 32 per code block: [rb, pb, r, g]
+        if d.fmt == FMT_INT4_SYM:  # [N_pad, K_pad / 64] from 64 per 16 rows x 256 K: [rb, qb, r, g]
             n = d.N_pad * (d.K_pad // 64)
             raw = self.packed[d.scales_off: d.scales_off + 4 * n].view(torch.float32)
-            return raw.reshape(d.N_pad // 16, d.K_pad // 128, 16, 2).permute(0, 2, 1, 3).reshape(d.N_pad, d.K_pad // 64)
+            return raw.reshape(d.N_pad // 16, d.K_pad // 256, 16, 4).permute(0, 2, 1, 3).reshape(d.N_pad, d.K_pad // 64)
         return self.packed[d.scales_off: d.scales_off + d.N_pad * (d.K_pad // 32)].view(d.N_pad, d.K_pad // 32)
 
     def colsum(self) -> torch.Tensor:

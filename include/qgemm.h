@@ -139,8 +139,9 @@ typedef enum {
  *   scales  at scales_off: INT8: float32 [N_pad] (GRAN_ROW; rows >= N are 0)
  *           or float32 [1] (GRAN_TENSOR). MX: E8M0 bytes [N_pad][K_pad/32]
  *           row-major, padding blocks hold 127 (scale 1.0). INT4: float32,
- *           32 per code block: the scale of row n, group g at float index
- *           ((n/16)*(K_pad/128) + g/2) * 32 + 2*(n%16) + g%2; padding is 0.
+ *           64 per 16 rows x 256 K: the scale of row n, group g at float
+ *           index ((n/16)*(K_pad/256) + g/4) * 64 + 4*(n%16) + g%4 (one
+ *           16-byte load gives a row the scales of four groups); padding is 0.
  *   colsum  at colsum_off: INT8 only: int32 [N_pad], colsum[n] = sum_k q_w[n,k]
  *           ([D98] "The program, and the gate that has to be per column":
  *           computed once, when the weights are quantized). -1 for MX and INT4.
