@@ -662,20 +662,17 @@ static hipError_t launch_dma(const GemmArgs& a, hipStream_t st) {
 constexpr int kDecWaves = 8;  // waves per workgroup, each on its own K range
 constexpr int kDecBatch = 8;  // 64-deep steps per load batch
 
-template <bool ASYM>
-__device__ inline void decode_batch_mfma(const v4i (&av)[kDecBatch], const v4i (&wv)[kDecBatch], v4i& acc) {
-#pragma unroll
-  for (int u = 0; u < kDecBatch; ++u) {
-    v4i a = av[u];
-    if (ASYM) a ^= (int)0x80808080u;  // uint8 codes enter as q - 128 (a dead step still meets zero weights)
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wv[u], acc, 0, 0, 0);
-  }
-}
-
-// ONE: K_pad <= 512 * kDecWaves, one batch per wave (no loop)
-template <bool ASYM, int OUT, bool ONE>
+// ONE: K_pad <= 512 * kDecWaves, one batch per wave (no loop).
+// MLE8 (M <= 8): rows 8-15 of the 16-row activation operand only feed output
+// rows that are never stored, so one 16-byte load per lane carries two steps
+// (lanes 16c + r: chunk c of step s for row r; lanes 16c + 8 + r: chunk c of
+// step s + 1) and a DPP rotate by 8 lanes within each row of 16 lanes gives
+// the second step's operand. Half the activation loads, and 16 fewer VGPRs
+// per batch.
+template <bool ASYM, int OUT, bool ONE, bool MLE8>
 __global__ __launch_bounds__(kDecWaves * 64) void gemm_i8_decode_kernel(GemmArgs p) {
   constexpr int U = kDecBatch;
+  constexpr int UA = MLE8 ? U / 2 : U;  // activation loads per batch
   __shared__ v4i red[kDecWaves][64];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -688,34 +685,45 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_i8_decode_kernel(GemmArgs
   const int per = ONE ? U : (steps + kDecWaves * U - 1) / (kDecWaves * U) * U;
   const int sbeg = wid * per;
 
-  // operand lanes: lane l carries row l % 16 and the 16-byte K chunk l / 16
-  // of every 64-deep step. Rows >= M read A as zeros through an offset beyond
-  // its range.
-  const int row = lane & 15;
-  const int chunk = (lane >> 4) * 16;
+  // operand lanes: lane l carries weight row l % 16 and the 16-byte K chunk
+  // l / 16 of every 64-deep step; the activation lanes as described above.
+  // Rows >= M read A as zeros through an offset beyond its range.
+  const int arow = MLE8 ? (lane & 7) : (lane & 15);
+  const int akin = (MLE8 ? ((lane >> 3) & 1) * 64 : 0) + (lane >> 4) * 16;
   constexpr uint32_t kOff = 0x80000000u;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.w + n0 * p.K_pad), (short)0, (int)(16 * p.K_pad), kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.a, (short)0, (int)((p.M - 1) * p.lda + ((p.K + 15) & ~(int64_t)15)), kRawBufferWord3);
   const uint32_t woff = (uint32_t)sbeg * 1024u + (uint32_t)(lane * 16);  // 16 x 64 blocks, lane order
-  const uint32_t aoff = row < p.M ? (uint32_t)(row * p.lda + sbeg * 64 + chunk) : kOff;
+  const uint32_t aoff = arow < p.M ? (uint32_t)(arow * p.lda + sbeg * 64 + akin) : kOff;
 
-  // one batch at a time: the data of a batch takes 64 VGPRs, which leaves
-  // room for three workgroups per CU; their loads overlap each other's waits
+  // one batch at a time: its loads are all issued before the first MFMA
   v4i acc = {0, 0, 0, 0};
   for (int b = 0; b < (ONE ? U : per); b += U) {
-    v4i av[U], wv[U];
+    v4i av[UA], wv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
       wv[u] = __builtin_bit_cast(
           v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)(woff + (uint32_t)((b + u) * 1024)), 0, 0));
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < UA; ++u)
       av[u] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)(aoff + (uint32_t)((b + u) * 64)), 0, 0));
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                   ars, (int)(aoff + (uint32_t)((b + (MLE8 ? 2 * u : u)) * 64)), 0, 0));
     __builtin_amdgcn_sched_barrier(0);
-    decode_batch_mfma<ASYM>(av, wv, acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v4i a;
+      if (MLE8 && (u & 1)) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) a[d] = __builtin_amdgcn_update_dpp(0, av[u / 2][d], 0x128, 0xF, 0xF, false);  // row_ror:8
+      } else {
+        a = av[MLE8 ? u / 2 : u];
+      }
+      if (ASYM) a ^= (int)0x80808080u;  // uint8 codes enter as q - 128 (a dead step still meets zero weights)
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wv[u], acc, 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   red[wid][lane] = acc;
@@ -741,13 +749,23 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_i8_decode_kernel(GemmArgs
   }
 }
 
-template <bool ASYM, int OUT>
-static hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
+template <bool ASYM, int OUT, bool MLE8>
+static void launch_decode_rows(const GemmArgs& a, hipStream_t st) {
   const int64_t groups = (a.N + 15) / 16;
   if (a.K_pad <= 64 * kDecBatch * kDecWaves)
-    hipLaunchKernelGGL((gemm_i8_decode_kernel<ASYM, OUT, true>), dim3((unsigned)groups), dim3(kDecWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((gemm_i8_decode_kernel<ASYM, OUT, true, MLE8>), dim3((unsigned)groups), dim3(kDecWaves * 64),
+                       0, st, a);
   else
-    hipLaunchKernelGGL((gemm_i8_decode_kernel<ASYM, OUT, false>), dim3((unsigned)groups), dim3(kDecWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((gemm_i8_decode_kernel<ASYM, OUT, false, MLE8>), dim3((unsigned)groups),
+                       dim3(kDecWaves * 64), 0, st, a);
+}
+
+template <bool ASYM, int OUT>
+static hipError_t launch_decode(const GemmArgs& a, hipStream_t st) {
+  if (a.M <= 8)
+    launch_decode_rows<ASYM, OUT, true>(a, st);
+  else
+    launch_decode_rows<ASYM, OUT, false>(a, st);
   return hipGetLastError();
 }
 
