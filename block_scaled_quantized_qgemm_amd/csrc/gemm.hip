@@ -62,6 +62,19 @@ __device__ inline int lds_off(int row, int chunk) {
   return row * RB + ((chunk ^ ((row / RPL) % CPR)) << 4);
 }
 
+// The exact MX mode's bf16 tiles have 128-byte rows, written as converted
+// 16-byte chunks (four lanes per row: chunks 2c or 2c + 1, c = lane % 4) and
+// read as MFMA fragments (16 lanes on 16 consecutive rows at one chunk).
+// gfx950 serves 16-byte reads 16 consecutive lanes per cycle over its 64
+// four-byte banks, and 16-byte writes 8 consecutive lanes per cycle over a
+// 128-byte window (fitted to bank-conflict counter measurements). Reads then
+// need the row's chunk XOR to be a bijection on row bits 1-3 (the 8 rows of
+// one parity share a bank half), and writes need it to flip chunk parity
+// between the two rows of a cycle: XOR with (row / 2) % 8 and with row % 2.
+__device__ inline int lds_off_bf16(int row, int chunk) {
+  return row * 128 + (((chunk ^ ((row >> 1) & 7) ^ (row & 1)) & 7) << 4);
+}
+
 // LDS offset of the 16-byte chunk `chunk` (K bytes [16 chunk, 16 chunk + 16)
 // of the stage) of W tile row `row` when the stage holds the packed weight
 // blocks of 16 rows x 64 K in order (row block major, BK / 64 blocks per row
@@ -103,6 +116,7 @@ struct MxCfg {
   static constexpr int LDS = 2 * STAGE > EPI ? 2 * STAGE : EPI;
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile / thread mismatch");
   static_assert(MODE != MXF || BK % 64 == 0, "scaled fp8 steps are 64 deep");
+  static_assert(MODE != MXB || RB == 128, "exact-mode staging: 128-byte bf16 rows");
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
 
@@ -182,8 +196,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
       if constexpr (MODE == MXB) {                                                              \
         v4i lo, hi;                                                                             \
         fp8x16_to_bf16(RA[i], e8m0_to_f32(EA[i]), lo, hi);                                      \
-        *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, 2 * c)) = lo;                              \
-        *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, 2 * c + 1)) = hi;                          \
+        *reinterpret_cast<v4i*>(sa_ + lds_off_bf16(r, 2 * c)) = lo;                             \
+        *reinterpret_cast<v4i*>(sa_ + lds_off_bf16(r, 2 * c + 1)) = hi;                         \
       } else {                                                                                  \
         *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, c)) = RA[i];                               \
       }                                                                                         \
@@ -194,8 +208,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
       if constexpr (MODE == MXB) {                                                              \
         v4i lo, hi;                                                                             \
         fp8x16_to_bf16(RB_[i], e8m0_to_f32(EB[i]), lo, hi);                                     \
-        *reinterpret_cast<v4i*>(sb_ + lds_off<RB>(r, 2 * c)) = lo;                              \
-        *reinterpret_cast<v4i*>(sb_ + lds_off<RB>(r, 2 * c + 1)) = hi;                          \
+        *reinterpret_cast<v4i*>(sb_ + lds_off_bf16(r, 2 * c)) = lo;                             \
+        *reinterpret_cast<v4i*>(sb_ + lds_off_bf16(r, 2 * c + 1)) = hi;                         \
       } else {                                                                                  \
         *reinterpret_cast<v4i*>(sb_ + lds_off<RB>(r, c)) = RB_[i];                              \
       }                                                                                         \
@@ -241,9 +255,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
         const int ch = kk * 2 + (lane >> 5);                                                    \
         v8bf af[FM], bf[FN];                                                                    \
         _Pragma("unroll") for (int i = 0; i < FM; ++i) af[i] =                                  \
-            *reinterpret_cast<const v8bf*>(sa + lds_off<RB>(wm * TM + i * 32 + (lane & 31), ch)); \
+            *reinterpret_cast<const v8bf*>(sa + lds_off_bf16(wm * TM + i * 32 + (lane & 31), ch)); \
         _Pragma("unroll") for (int j = 0; j < FN; ++j) bf[j] =                                  \
-            *reinterpret_cast<const v8bf*>(sb + lds_off<RB>(wn * TN + j * 32 + (lane & 31), ch)); \
+            *reinterpret_cast<const v8bf*>(sb + lds_off_bf16(wn * TN + j * 32 + (lane & 31), ch)); \
         _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
           _Pragma("unroll") for (int j = 0; j < FN; ++j)                                        \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0); \
