@@ -42,6 +42,7 @@ SCALE_FLOOR = F32(1e-8)  # [AQ] "The integer GEMM, written out": floor for all-z
 MX_BLOCK = 32            # [TL27] 2.3(a): one shared scale per 32 elements
 E4M3_MAX = 448.0         # [TL27] 2.2 item 1: largest finite e4m3 value, 1.75 * 2^8
 MX_AMAX_FLOOR = F32(1e-4)  # [TL27] 2.2 item 3: amax.clamp_min(1e-4)
+E2M1_MAX = 6.0           # reading: the largest fp4 e2m1 value, 1.5 * 2^2 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit)
 
 INT4_QMAX = 7            # [TL27] 2.4: int4 takes qmax = 7, codes clipped to [-qmax - 1, qmax]
 W4_GROUP = 64            # [TL27] 5.1: the W4A8 check uses int8 X and int4 W per group of 64
@@ -493,16 +494,88 @@ def quantize_mx(x):
     return codes, E
 
 
-def mx_dequantize(codes, E):
-    """float64 values codes * 2^(E - 127), E broadcast over each 32-block."""
+def _e2m1_table():
+    """Values of the 16 fp4 e2m1 codes ([TL27] 1.2 and 8 name the format and
+    its u = 2^-2; the field layout is the format's name): sign bit 3,
+    exponent bits 2-1 with bias 1, mantissa bit 0. Exponent field 0 is
+    subnormal, m * 0.5. No infinities or NaNs: the largest value is
+    1.5 * 2^2 = 6. Code 8 is -0."""
+    vals = np.empty(16, dtype=np.float64)
+    for c in range(16):
+        s = -1.0 if c & 0x8 else 1.0
+        e = (c >> 1) & 0x3
+        m = c & 0x1
+        vals[c] = s * (m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return vals
+
+
+E2M1_VALUES = _e2m1_table()
+_E2M1_POS = E2M1_VALUES[:8]  # codes 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6
+
+
+def e2m1_decode(codes):
+    """float64 value of each e2m1 code (0..15)."""
+    return E2M1_VALUES[np.asarray(codes, dtype=np.uint8) & np.uint8(0xF)]
+
+
+def e2m1_encode_rne(y):
+    """Nearest e2m1 code to each float32 y, ties to the even code (the even
+    mantissa bit), sign carried separately (-0.0 and negatives that round to
+    zero give code 8). |y| > 6 is rejected: the MX scale keeps every scaled
+    value within the format."""
+    y = np.asarray(y, dtype=F32)
+    a = np.abs(y).astype(np.float64)
+    if np.any(~np.isfinite(a)) or np.any(a > E2M1_MAX):
+        raise ValueError("e2m1 input outside [-6, 6]")
+    hi = np.minimum(np.searchsorted(_E2M1_POS, a, side="left"), 7)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E2M1_POS[lo]
+    d_hi = _E2M1_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(y), code | np.uint8(0x8), code).astype(np.uint8)
+
+
+def quantize_mxfp4(x):
+    """MXFP4 quantization: e2m1 codes plus one E8M0 scale per 32 K-elements.
+
+    [TL27] 2.3: the MX block of 32 with an E8M0 power-of-two scale, which
+    moves only the exponent. The pages print the recipe for e4m3 (amax
+    floored at 1e-4, sf = ceil_to_ue8m0(amax / 448)); reading for e2m1: the
+    same recipe with the format's largest value, sf = ceil_to_ue8m0(amax / 6),
+    codes = e2m1(x * (1/sf)) rounded to nearest, ties to even. Every scaled
+    value is then <= 6 in magnitude.
+
+    x: float32 [R, K] with K % 32 == 0. Returns (codes uint8 [R, K], one
+    code 0..15 per element, E uint8 [R, K/32]); ``pack_int4_pairs`` gives the
+    stored two-codes-per-byte form.
+    """
+    x = np.asarray(x, dtype=F32)
+    R, K = x.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blocks = x.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blocks), axis=2) if R else np.zeros((0, K // MX_BLOCK), F32)
+    amax = np.maximum(amax, MX_AMAX_FLOOR).astype(F32)
+    E = ceil_to_ue8m0(amax / F32(E2M1_MAX))
+    inv = np.ldexp(F32(1.0), (127 - E.astype(np.int32))).astype(F32)
+    y = (blocks * inv[:, :, None]).astype(F32)
+    codes = e2m1_encode_rne(y).reshape(R, K)
+    return codes, E
+
+
+def mx_dequantize(codes, E, fmt: str = "e4m3"):
+    """float64 values codes * 2^(E - 127), E broadcast over each 32-block;
+    codes are e4m3 bytes or (fmt "e2m1") one e2m1 code per element."""
     codes = np.asarray(codes, dtype=np.uint8)
     R, K = codes.shape
-    v = e4m3_decode(codes).reshape(R, K // MX_BLOCK, MX_BLOCK)
+    dec = e2m1_decode if fmt == "e2m1" else e4m3_decode
+    v = dec(codes).reshape(R, K // MX_BLOCK, MX_BLOCK)
     v = v * e8m0_value(E)[:, :, None]
     return v.reshape(R, K)
 
 
-def mx_gemm_ref(qa, Ea, qw, Ew):
+def mx_gemm_ref(qa, Ea, qw, Ew, fmt_a: str = "e4m3", fmt_w: str = "e4m3"):
     """out[m, n] = sum_b 2^(Ea[m,b]-127) 2^(Ew[n,b]-127) sum_{k in b} a[m,k] w[n,k].
 
     [TL27] 4.1: the block-scaled product is (A * scale_A)(B * scale_B) + D;
@@ -513,15 +586,15 @@ def mx_gemm_ref(qa, Ea, qw, Ew):
     Also returns S[m, n] = sum_k |a[m,k] w[n,k]|, the error basis of
     [TL27] 2.5. Both [M, N] float64.
     """
-    A = mx_dequantize(qa, Ea)
-    W = mx_dequantize(qw, Ew)
+    A = mx_dequantize(qa, Ea, fmt_a)
+    W = mx_dequantize(qw, Ew, fmt_w)
     return A @ W.T, np.abs(A) @ np.abs(W).T
 
 
-def mx_gemm_ref_entries(qa, Ea, qw, Ew, rows, cols):
+def mx_gemm_ref_entries(qa, Ea, qw, Ew, rows, cols, fmt_a: str = "e4m3", fmt_w: str = "e4m3"):
     """``mx_gemm_ref`` at the (rows[i], cols[i]) pairs only."""
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
-    A = mx_dequantize(qa[rows], Ea[rows])
-    W = mx_dequantize(qw[cols], Ew[cols])
+    A = mx_dequantize(qa[rows], Ea[rows], fmt_a)
+    W = mx_dequantize(qw[cols], Ew[cols], fmt_w)
     return np.einsum("ik,ik->i", A, W), np.einsum("ik,ik->i", np.abs(A), np.abs(W))

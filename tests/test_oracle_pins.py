@@ -650,3 +650,82 @@ def test_int4_pair_packing_bytes_and_sign_restoration():
     # odd K pads one zero code
     assert O.pack_int4_pairs(np.array([[3, -2, -8]], np.int8)).tolist() == [[0xE3, 0x08]]
     assert O.unpack_int4_pairs(np.array([[0xE3, 0x08]], np.uint8), 3).tolist() == [[3, -2, -8]]
+
+
+# --------------------------------------------------------------------------
+# fp4 e2m1 and MXFP4 ([TL27] 1.2, 2.3, 8; the e2m1 recipe is a reading)
+# --------------------------------------------------------------------------
+def test_e2m1_values_from_the_format_fields():
+    """Derived independently from the bit fields: exponent bias 1, one
+    mantissa bit, field 0 subnormal; largest value 1.5 * 2^2; code 8 is -0."""
+    v = O.E2M1_VALUES
+    pos = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert v[:8].tolist() == pos and (v[8:] == -np.array(pos)).all()
+    assert v[7] == O.E2M1_MAX == 1.5 * 2 ** 2
+    assert math.copysign(1, v[8]) == -1
+    assert not np.isnan(v).any()
+
+
+def test_e2m1_rounding_ties_even_and_u():
+    """Every midpoint between neighbours goes to the even code; elsewhere the
+    nearest value; on the normal range the relative error is within
+    u = 2^-2 ([TL27] 1.2 and 8: fp4 e2m1 2.5e-1)."""
+    g = _golden("format_constants.json")
+    mids = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6}
+    for a, code in mids.items():
+        assert int(O.e2m1_encode_rne(np.float32(a))) == code, a
+        assert int(O.e2m1_encode_rne(np.float32(-a))) == code | 8, -a
+    assert int(O.e2m1_encode_rne(np.float32(-0.0))) == 8
+    rng = rng_for(21)
+    y = rng.uniform(-6, 6, 200000).astype(np.float32)
+    c = O.e2m1_encode_rne(y)
+    d = np.abs(O.e2m1_decode(c) - y.astype(np.float64))
+    # nearest: no grid value is closer
+    best = np.min(np.abs(O.E2M1_VALUES[None, :] - y.astype(np.float64)[:, None]), axis=1)
+    assert np.array_equal(d, best)
+    normal = np.abs(y) >= 1.0
+    assert (d[normal] / np.abs(y[normal]) <= g["e2m1_u"]).all()
+    with pytest.raises(ValueError):
+        O.e2m1_encode_rne(np.float32(6.01))
+
+
+def test_mxfp4_scaling_and_error():
+    """sf is the smallest power of two with amax / sf <= 6; scaled values
+    stay within e2m1; every block has its own scale; the error per element is
+    within u of the value on the normal range and within 0.25 sf below it."""
+    A, _ = make_inputs("c5_mxfp8", M=16, K=512, N=1, seed=23)
+    q, E = O.quantize_mxfp4(A)
+    sf = O.e8m0_value(E)
+    amax = np.maximum(np.abs(A.reshape(16, 16, 32)).max(axis=2), 1e-4).astype(np.float64)
+    assert (amax / sf <= 6.0).all() and (amax / (sf / 2) > 6.0).all()
+    deq = O.mx_dequantize(q, E, "e2m1").reshape(16, 16, 32)
+    x = A.astype(np.float64).reshape(16, 16, 32)
+    err = np.abs(deq - x)
+    scaled = np.abs(x) / sf[:, :, None]
+    assert (err[scaled >= 1] <= 0.25 * np.abs(x[scaled >= 1]) + 1e-300).all()
+    assert (err[scaled < 1] <= 0.25 * np.broadcast_to(sf[:, :, None], x.shape)[scaled < 1]).all()
+    # one block with an outlier spends its own range only
+    B = np.ones((1, 64), np.float32)
+    B[0, 5] = 600.0
+    qb, Eb = O.quantize_mxfp4(B)
+    assert Eb[0, 0] > Eb[0, 1] and (O.mx_dequantize(qb, Eb, "e2m1")[0, 32:] == 1.0).all()
+
+
+def test_mxfp4_gemm_reference_against_exact_rationals():
+    """The float64 reference over dequantized e2m1 values against exact
+    rational arithmetic, and fp4 packing round trip of the codes."""
+    A, W = make_inputs("c5_mxfp8", M=3, K=96, N=4, seed=24)
+    qa, Ea = O.quantize_mxfp4(A)
+    qw, Ew = O.quantize_mxfp4(W)
+    out, S = O.mx_gemm_ref(qa, Ea, qw, Ew, "e2m1", "e2m1")
+    for m in range(3):
+        for n in range(4):
+            tot = Fraction(0)
+            for k in range(96):
+                b = k // 32
+                av = Fraction(O.E2M1_VALUES[qa[m, k]]) * Fraction(2) ** (int(Ea[m, b]) - 127)
+                wv = Fraction(O.E2M1_VALUES[qw[n, k]]) * Fraction(2) ** (int(Ew[n, b]) - 127)
+                tot += av * wv
+            assert abs(Fraction(out[m, n]) - tot) <= Fraction(S[m, n]) * Fraction(1, 2 ** 50)
+    packed = O.pack_int4_pairs(qa.astype(np.int8))
+    assert np.array_equal(O.unpack_int4_pairs(packed, 96).astype(np.uint8) & 0xF, qa)
