@@ -11,7 +11,7 @@ the names below resolve on first use.
 _BINDING = {
     "qgemm_quantize_rows", "qgemm_rmsnorm_quantize_rows", "qgemm_prepack_weights", "qgemm_run", "qgemm_run_mx", "qgemm_run_w4a8",
     "qgemm_workspace_bytes", "qgemm_packed_weight_bytes", "QgemmError", "QuantizedRows", "PackedWeights",
-    "FMT_INT8_SYM", "FMT_UINT8_ASYM", "FMT_MXFP8_E4M3", "FMT_INT4_SYM", "GRAN_TENSOR", "GRAN_ROW",
+    "FMT_INT8_SYM", "FMT_UINT8_ASYM", "FMT_MXFP8_E4M3", "FMT_INT4_SYM", "FMT_MXFP4_E2M1", "GRAN_TENSOR", "GRAN_ROW",
     "GRAN_BLOCK32", "GRAN_GROUP64",
     "OUT_F32", "OUT_BF16", "OUT_I32", "MX_EXACT", "MX_SCALED_MFMA",
 }

@@ -39,6 +39,9 @@ int check_device() {
 }
 
 bool is_int_fmt(int f) { return f == QGEMM_FMT_INT8_SYM || f == QGEMM_FMT_UINT8_ASYM; }
+bool is_mx_fmt(int f) { return f == QGEMM_FMT_MXFP8_E4M3 || f == QGEMM_FMT_MXFP4_E2M1; }
+// bytes a row of K codes occupies
+int64_t code_bytes(int fmt, int64_t K) { return fmt == QGEMM_FMT_MXFP4_E2M1 ? K / 2 : K; }
 bool is_int_gran(int g) { return g == QGEMM_GRAN_TENSOR || g == QGEMM_GRAN_ROW; }
 
 struct Layout {
@@ -49,7 +52,7 @@ bool weight_layout(int64_t N, int64_t K, int fmt, int gran, Layout* L) {
   if (N < 1 || K < 1 || N > kMaxRows || K > (int64_t)1 << 30) return false;
   if (fmt == QGEMM_FMT_INT8_SYM) {
     if (!is_int_gran(gran)) return false;
-  } else if (fmt == QGEMM_FMT_MXFP8_E4M3) {
+  } else if (is_mx_fmt(fmt)) {
     if (gran != QGEMM_GRAN_BLOCK32 || K % 32 != 0) return false;
   } else if (fmt == QGEMM_FMT_INT4_SYM) {
     if (gran != QGEMM_GRAN_GROUP64) return false;
@@ -65,7 +68,7 @@ bool weight_layout(int64_t N, int64_t K, int fmt, int gran, Layout* L) {
     L->bytes = round_up(L->scales_off + 4 * L->N_pad * (L->K_pad / 64), 256);
     return true;
   }
-  L->scales_off = round_up(L->N_pad * L->K_pad, 256);
+  L->scales_off = round_up(L->N_pad * code_bytes(fmt, L->K_pad), 256);
   if (fmt == QGEMM_FMT_INT8_SYM) {
     L->colsum_off = round_up(L->scales_off + 4 * L->N_pad, 256);
     L->bytes = round_up(L->colsum_off + 4 * L->N_pad, 256);
@@ -76,9 +79,11 @@ bool weight_layout(int64_t N, int64_t K, int fmt, int gran, Layout* L) {
   return true;
 }
 
+// want_fmt < 0: any MX weight format
 int check_desc(const qgemm_wdesc* d, int want_fmt) {
   if (!d) return QGEMM_E_NULL;
-  if (d->magic != QGEMM_WDESC_MAGIC || d->version != QGEMM_ABI_VERSION || d->fmt != want_fmt) return QGEMM_E_DESC;
+  if (d->magic != QGEMM_WDESC_MAGIC || d->version != QGEMM_ABI_VERSION) return QGEMM_E_DESC;
+  if (want_fmt >= 0 ? d->fmt != want_fmt : !is_mx_fmt(d->fmt)) return QGEMM_E_DESC;
   Layout L;
   if (!weight_layout(d->N, d->K, d->fmt, d->gran, &L)) return QGEMM_E_DESC;
   if (L.N_pad != d->N_pad || L.K_pad != d->K_pad || L.codes_off != d->codes_off || L.scales_off != d->scales_off ||
@@ -129,7 +134,7 @@ size_t qgemm_workspace_bytes(int64_t rows, int64_t K, int fmt, int gran) {
 int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int fmt, int gran, void* q,
                         int64_t ldq, float* scales, int32_t* zero_points, uint8_t* mx_scales, int64_t ld_mx,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  const bool mx = fmt == QGEMM_FMT_MXFP8_E4M3;
+  const bool mx = is_mx_fmt(fmt);
   if (mx) {
     if (gran != QGEMM_GRAN_BLOCK32) return QGEMM_E_MODE;
   } else if (!is_int_fmt(fmt) || !is_int_gran(gran)) {
@@ -139,7 +144,7 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int f
   if (mx && K % 32 != 0) return QGEMM_E_SHAPE;
   if (M == 0) return QGEMM_OK;
   if (!x || !q) return QGEMM_E_NULL;
-  if (ldx < K || ldq < K) return QGEMM_E_SHAPE;
+  if (ldx < K || ldq < code_bytes(fmt, K)) return QGEMM_E_SHAPE;
   if (!aligned(x, 4) || ldq % 16 != 0 || !aligned(q, 16)) return QGEMM_E_ALIGN;
   if (mx) {
     if (!mx_scales) return QGEMM_E_NULL;
@@ -157,7 +162,7 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int f
 
   hipStream_t st = as_stream(stream);
   if (mx) {
-    qg::launch_quantize_mx(x, M, K, ldx, (uint8_t*)q, ldq, mx_scales, ld_mx, st);
+    qg::launch_quantize_mx(x, M, K, ldx, fmt == QGEMM_FMT_MXFP4_E2M1, (uint8_t*)q, ldq, mx_scales, ld_mx, st);
   } else {
     qg::launch_quantize_int(x, M, K, ldx, fmt == QGEMM_FMT_UINT8_ASYM, gran == QGEMM_GRAN_TENSOR,
                             (uint8_t*)q, ldq, 0, scales, zero_points, nullptr, (float*)workspace, st);
@@ -187,9 +192,9 @@ int qgemm_rmsnorm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ld
 int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int fmt, int gran, void* packed,
                           size_t packed_bytes, qgemm_wdesc* desc, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  if (fmt != QGEMM_FMT_INT8_SYM && fmt != QGEMM_FMT_MXFP8_E4M3 && fmt != QGEMM_FMT_INT4_SYM) return QGEMM_E_MODE;
+  if (fmt != QGEMM_FMT_INT8_SYM && !is_mx_fmt(fmt) && fmt != QGEMM_FMT_INT4_SYM) return QGEMM_E_MODE;
   if (fmt == QGEMM_FMT_INT8_SYM && !is_int_gran(gran)) return QGEMM_E_MODE;
-  if (fmt == QGEMM_FMT_MXFP8_E4M3 && gran != QGEMM_GRAN_BLOCK32) return QGEMM_E_MODE;
+  if (is_mx_fmt(fmt) && gran != QGEMM_GRAN_BLOCK32) return QGEMM_E_MODE;
   if (fmt == QGEMM_FMT_INT4_SYM && gran != QGEMM_GRAN_GROUP64) return QGEMM_E_MODE;
   Layout L;
   if (!weight_layout(N, K, fmt, gran, &L)) return QGEMM_E_SHAPE;
@@ -215,7 +220,8 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int
   } else {
     if (hipMemsetAsync(base + L.scales_off, 127, (size_t)(L.N_pad * (L.K_pad / 32)), st) != hipSuccess)
       return QGEMM_E_HIP;
-    qg::launch_quantize_mx(w, N, K, ldw, base + L.codes_off, L.K_pad, base + L.scales_off, L.K_pad / 32, st);
+    qg::launch_quantize_mx(w, N, K, ldw, fmt == QGEMM_FMT_MXFP4_E2M1, base + L.codes_off, code_bytes(fmt, L.K_pad),
+                           base + L.scales_off, L.K_pad / 32, st);
   }
   int rc = launch_status();
   if (rc != QGEMM_OK) return rc;
@@ -282,19 +288,23 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
   return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
 }
 
-int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s, int64_t M,
+int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s, int a_fmt, int64_t M,
                  const qgemm_wdesc* w_desc, const void* w_packed, float* out, int64_t ldo, int mode,
                  const float* bias, void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   if (mode != QGEMM_MX_EXACT && mode != QGEMM_MX_SCALED_MFMA) return QGEMM_E_MODE;
-  int rc = check_desc(w_desc, QGEMM_FMT_MXFP8_E4M3);
+  if (!is_mx_fmt(a_fmt)) return QGEMM_E_MODE;
+  int rc = check_desc(w_desc, -1);
   if (rc != QGEMM_OK) return rc;
+  // the block-scaled fp8 matrix cores are used for e4m3 x e4m3 only
+  if (mode == QGEMM_MX_SCALED_MFMA && (a_fmt != QGEMM_FMT_MXFP8_E4M3 || w_desc->fmt != QGEMM_FMT_MXFP8_E4M3))
+    return QGEMM_E_MODE;
   const int64_t N = w_desc->N, K = w_desc->K;
   if (M < 0 || M > kMaxRows) return QGEMM_E_SHAPE;
   if (M == 0) return QGEMM_OK;
   if (!a_codes || !a_e8m0 || !w_packed || !out) return QGEMM_E_NULL;
-  if (lda < K || lda_s < K / 32 || ldo < N) return QGEMM_E_SHAPE;
+  if (lda < code_bytes(a_fmt, K) || lda_s < K / 32 || ldo < N) return QGEMM_E_SHAPE;
   if (lda % 16 != 0 || !aligned(a_codes, 16) || ldo % 4 != 0 || !aligned(out, 16) || !aligned(w_packed, 256) ||
       (bias && !aligned(bias, 4)))
     return QGEMM_E_ALIGN;
@@ -309,6 +319,8 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
   g.lda_s = lda_s;
   g.w = base + w_desc->codes_off;
   g.ew = base + w_desc->scales_off;
+  g.a_fp4 = a_fmt == QGEMM_FMT_MXFP4_E2M1;
+  g.w_fp4 = w_desc->fmt == QGEMM_FMT_MXFP4_E2M1;
   g.M = M;
   g.N = N;
   g.K = K;

@@ -8,7 +8,7 @@
 //
 // (int8 x int4 with per-group scales lives in gemm_w4a8.hip.)
 //
-// MX (e4m3 + E8M0 per 32 K), float32 output, gemm_mx_kernel in two modes:
+// MX (e4m3 or e2m1 + E8M0 per 32 K), float32 output, gemm_mx_kernel in two modes:
 //  * MXB -- exact products: each e4m3 value is multiplied by its block's
 //           power-of-two scale while the tile is moved into LDS
 //           (v_cvt_scalef32_pk_bf16_fp8; e4m3 times a power of two is exactly
@@ -101,6 +101,23 @@ __device__ inline void fp8x16_to_bf16(const v4i& q, float scale, v4i& lo, v4i& h
   hi = v4i{w[4], w[5], w[6], w[7]};
 }
 
+// Sixteen e2m1 codes (8 bytes, element 2i in the low nibble of byte i) times
+// 2^(E-127) as sixteen bf16 (exact: two significant bits).
+__device__ inline void fp4x16_to_bf16(const v4i& q, float scale, v4i& lo, v4i& hi) {
+  v2bf t[8];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    t[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((unsigned)q[d], scale, 0);
+    t[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((unsigned)q[d], scale, 1);
+    t[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((unsigned)q[d], scale, 2);
+    t[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((unsigned)q[d], scale, 3);
+  }
+  int w[8];
+  __builtin_memcpy(w, t, 32);
+  lo = v4i{w[0], w[1], w[2], w[3]};
+  hi = v4i{w[4], w[5], w[6], w[7]};
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int MODE>
 struct MxCfg {
   static constexpr int NT = WM * WN * 64;
@@ -120,9 +137,13 @@ struct MxCfg {
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int MODE>
+// FA4 / FW4 (exact mode only): the activations / weights are e2m1, two codes
+// per byte; a 16-K chunk is then 8 bytes, converted to the same two bf16
+// LDS chunks as sixteen e4m3 codes.
+template <int BM, int BN, int BK, int WM, int WN, int MODE, bool FA4 = false, bool FW4 = false>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
   using C = MxCfg<BM, BN, BK, WM, WN, MODE>;
+  static_assert(MODE == MXB || (!FA4 && !FW4), "e2m1 operands take the exact mode");
   constexpr int NT = C::NT, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RB = C::RB;
   constexpr int A_CH = C::A_CH, B_CH = C::B_CH, STAGE = C::STAGE;
 
@@ -174,14 +195,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
       /* are zeroed at the store for MX, where a stray code could be NaN). */                   \
       const int64_t m = min(m0 + r, p.M - 1), k = k0_ + c * 16;                                  \
       const int64_t kc = k < p.K ? k : 0;                                                       \
-      RA[i] = *reinterpret_cast<const v4i*>(p.a + m * p.lda + kc);                              \
+      if constexpr (FA4) {                                                                      \
+        const uint2 h_ = *reinterpret_cast<const uint2*>(p.a + m * p.lda + (kc >> 1));          \
+        RA[i] = v4i{(int)h_.x, (int)h_.y, 0, 0};                                                \
+      } else {                                                                                  \
+        RA[i] = *reinterpret_cast<const v4i*>(p.a + m * p.lda + kc);                            \
+      }                                                                                         \
       if constexpr (MODE == MXB) EA[i] = (int)p.ea[m * p.lda_s + (kc >> 5)];                    \
     }                                                                                           \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                          \
       const int id = tid + i * NT;                                                              \
       const int r = id / CPR, c = id % CPR;                                                     \
       const int64_t n = n0 + r, k = k0_ + c * 16;                                               \
-      RB_[i] = *reinterpret_cast<const v4i*>(p.w + n * p.K_pad + k);                            \
+      if constexpr (FW4) {                                                                      \
+        const uint2 h_ = *reinterpret_cast<const uint2*>(p.w + n * (p.K_pad >> 1) + (k >> 1));  \
+        RB_[i] = v4i{(int)h_.x, (int)h_.y, 0, 0};                                               \
+      } else {                                                                                  \
+        RB_[i] = *reinterpret_cast<const v4i*>(p.w + n * p.K_pad + k);                          \
+      }                                                                                         \
       if constexpr (MODE == MXB) EB[i] = (int)p.ew[n * wblocks + (k >> 5)];                     \
     }                                                                                           \
   }
@@ -195,7 +226,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
       if ((int64_t)(KT) * BK + c * 16 >= p.K) RA[i] = v4i{0, 0, 0, 0};                          \
       if constexpr (MODE == MXB) {                                                              \
         v4i lo, hi;                                                                             \
-        fp8x16_to_bf16(RA[i], e8m0_to_f32(EA[i]), lo, hi);                                      \
+        if constexpr (FA4)                                                                      \
+          fp4x16_to_bf16(RA[i], e8m0_to_f32(EA[i]), lo, hi);                                    \
+        else                                                                                    \
+          fp8x16_to_bf16(RA[i], e8m0_to_f32(EA[i]), lo, hi);                                    \
         *reinterpret_cast<v4i*>(sa_ + lds_off_bf16(r, 2 * c)) = lo;                             \
         *reinterpret_cast<v4i*>(sa_ + lds_off_bf16(r, 2 * c + 1)) = hi;                         \
       } else {                                                                                  \
@@ -207,7 +241,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
       const int r = id / CPR, c = id % CPR;                                                     \
       if constexpr (MODE == MXB) {                                                              \
         v4i lo, hi;                                                                             \
-        fp8x16_to_bf16(RB_[i], e8m0_to_f32(EB[i]), lo, hi);                                     \
+        if constexpr (FW4)                                                                      \
+          fp4x16_to_bf16(RB_[i], e8m0_to_f32(EB[i]), lo, hi);                                   \
+        else                                                                                    \
+          fp8x16_to_bf16(RB_[i], e8m0_to_f32(EB[i]), lo, hi);                                   \
         *reinterpret_cast<v4i*>(sb_ + lds_off_bf16(r, 2 * c)) = lo;                             \
         *reinterpret_cast<v4i*>(sb_ + lds_off_bf16(r, 2 * c + 1)) = hi;                         \
       } else {                                                                                  \
@@ -803,10 +840,10 @@ static hipError_t launch_i8(const GemmArgs& a, hipStream_t st) {
   return launch_dma<64, 128, 128, 2, 4, 6, ASYM, OUT>(a, st);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int MODE>
+template <int BM, int BN, int BK, int WM, int WN, int MODE, bool FA4, bool FW4>
 static hipError_t launch_mx_cfg(const GemmArgs& a, hipStream_t st) {
   using C = MxCfg<BM, BN, BK, WM, WN, MODE>;
-  auto kern = gemm_mx_kernel<BM, BN, BK, WM, WN, MODE>;
+  auto kern = gemm_mx_kernel<BM, BN, BK, WM, WN, MODE, FA4, FW4>;
   const size_t lds = C::LDS;
   if (lds > 65536) {  // above the default dynamic-LDS limit (gfx950 has 160 KiB)
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -817,7 +854,7 @@ static hipError_t launch_mx_cfg(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, bool FA4 = false, bool FW4 = false>
 static hipError_t launch_mx(const GemmArgs& a, hipStream_t st) {
   // Large problems: 256x256 tiles (8 waves of 128x64); otherwise 128x128 (4
   // waves of 64x64). The bf16 staging of the exact mode doubles the LDS row,
@@ -825,8 +862,8 @@ static hipError_t launch_mx(const GemmArgs& a, hipStream_t st) {
   // and 64 deep on large ones (its scales need registers too).
   constexpr int BK = MODE == MXB ? 64 : 128;
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big_tiles >= 256) return launch_mx_cfg<256, 256, 64, 2, 4, MODE>(a, st);
-  return launch_mx_cfg<128, 128, BK, 2, 2, MODE>(a, st);
+  if (big_tiles >= 256) return launch_mx_cfg<256, 256, 64, 2, 4, MODE, FA4, FW4>(a, st);
+  return launch_mx_cfg<128, 128, BK, 2, 2, MODE, FA4, FW4>(a, st);
 }
 
 hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_t st) {
@@ -844,7 +881,10 @@ hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_
 
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  if (mode == 1) return launch_mx<MXF>(a, st);
+  if (mode == 1) return launch_mx<MXF>(a, st);  // e4m3 x e4m3 (the caller checks)
+  if (a.a_fp4 && a.w_fp4) return launch_mx<MXB, true, true>(a, st);
+  if (a.a_fp4) return launch_mx<MXB, true, false>(a, st);
+  if (a.w_fp4) return launch_mx<MXB, false, true>(a, st);
   return launch_mx<MXB>(a, st);
 }
 

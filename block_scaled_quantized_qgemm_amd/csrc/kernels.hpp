@@ -20,8 +20,9 @@ void launch_quantize_int(const float* x, int64_t rows, int64_t K, int64_t ldx, b
 void launch_rmsnorm_quantize(const float* x, int64_t rows, int64_t K, int64_t ldx, const float* gamma, float eps,
                              bool asym, uint8_t* q, int64_t ldq, float* scales, int32_t* zeros, hipStream_t st);
 
-// MXFP8 (e4m3 codes, E8M0 per 32 K-elements) row quantization; K % 32 == 0.
-void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+// MXFP8 (e4m3 codes) or, fp4, MXFP4 (e2m1 codes, two per byte, element 2i
+// in the low nibble) row quantization with E8M0 per 32 K-elements; K % 32 == 0.
+void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, bool fp4, uint8_t* q, int64_t ldq,
                         uint8_t* e8, int64_t lde, hipStream_t st);
 
 // int4 weights, symmetric, one scale per group of 64 K of each row, into the
@@ -53,6 +54,7 @@ struct GemmArgs {
   const int32_t* colsum;
   const uint8_t* ew;    // mx: E8M0 [N_pad][K_pad/32]
   int w_per_tensor;
+  int a_fp4, w_fp4;     // mx: e2m1 codes (two per byte) instead of e4m3
   int64_t M, N, K, K_pad;
   void* out;
   int64_t ldo;

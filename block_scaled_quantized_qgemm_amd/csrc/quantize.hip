@@ -10,8 +10,9 @@
 // "Fusion: making quantization nearly free".
 //
 // MX kernel: eight lanes own one 32-element block (a float4 each), so the
-// block amax is a three-step shuffle; codes are converted two at a time with
-// the hardware e4m3 conversion (round to nearest even, OCP e4m3fn on gfx950).
+// block amax is a three-step shuffle; e4m3 codes are converted two at a time
+// with the hardware conversion (round to nearest even, OCP e4m3fn on gfx950),
+// e2m1 codes by comparisons with the midpoints of the fp4 grid.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -378,9 +379,22 @@ __global__ __launch_bounds__(kRowThreads) void tensor_scale_kernel(const float* 
   }
 }
 
-// MXFP8: grid (rows, ceil(K / 1024)); each thread one float4, eight threads
-// per 32-element block.
-template <bool VEC>
+// e2m1 code of v (|v| <= 6): the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+// ties to the even code, as the count of midpoints below |v| (a midpoint
+// whose upper neighbour has the even code counts when reached, the others
+// only when passed); sign in bit 3 (negative values and -0 that round to
+// zero keep it).
+__device__ inline uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | (__builtin_signbit(v) ? 8u : 0u);
+}
+
+// MX rows: grid (rows, ceil(K / 1024)); each thread one float4, eight
+// threads per 32-element block. e4m3 (scale from amax / 448) or, FP4, e2m1
+// (amax / 6, two codes per byte).
+template <bool VEC, bool FP4>
 __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __restrict__ x, int64_t ldx,
                                                                int64_t K, uint8_t* __restrict__ q, int64_t ldq,
                                                                uint8_t* __restrict__ e8, int64_t lde) {
@@ -399,9 +413,22 @@ __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __re
   a = fmaxf(a, __shfl_xor(a, 2, kWave));
   a = fmaxf(a, __shfl_xor(a, 4, kWave));
   a = fmaxf(a, 1e-4f);
-  const int E = ceil_to_ue8m0(a / 448.0f);
+  const int E = ceil_to_ue8m0(a / (FP4 ? 6.0f : 448.0f));
   const float inv = e8m0_inverse(E);
   if (!valid) return;
+  if constexpr (FP4) {
+    const uint32_t h = e2m1_code(v.x * inv) | (e2m1_code(v.y * inv) << 4) | (e2m1_code(v.z * inv) << 8) |
+                       (e2m1_code(v.w * inv) << 12);
+    uint8_t* qr = q + row * ldq + (k >> 1);
+    if (VEC) {
+      *reinterpret_cast<uint16_t*>(qr) = (uint16_t)h;
+    } else {
+      qr[0] = (uint8_t)h;
+      qr[1] = (uint8_t)(h >> 8);
+    }
+    if ((threadIdx.x & 7) == 0) e8[row * lde + (k >> 5)] = (uint8_t)E;
+    return;
+  }
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(v.x * inv, v.y * inv, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(v.z * inv, v.w * inv, w, true);
   uint8_t* qr = q + row * ldq + k;
@@ -512,15 +539,21 @@ void launch_quantize_int4(const float* w, int64_t rows, int64_t K, int64_t ldw, 
   quant_int4_groups_kernel<<<grid, block, 0, st>>>(w, ldw, K, K_pad, codes, scales);
 }
 
-void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, bool fp4, uint8_t* q, int64_t ldq,
                         uint8_t* e8, int64_t lde, hipStream_t st) {
   if (rows == 0) return;
   dim3 grid((unsigned)rows, (unsigned)((K + 4 * kRowThreads - 1) / (4 * kRowThreads))), block(kRowThreads);
   const bool vec = ldx % 4 == 0 && ((uintptr_t)x % 16) == 0 && ldq % 4 == 0 && ((uintptr_t)q % 4) == 0;
-  if (vec)
-    quant_mx_kernel<true><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
-  else
-    quant_mx_kernel<false><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+  if (fp4) {
+    if (vec)
+      quant_mx_kernel<true, true><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+    else
+      quant_mx_kernel<false, true><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+  } else if (vec) {
+    quant_mx_kernel<true, false><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+  } else {
+    quant_mx_kernel<false, false><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+  }
 }
 
 }  // namespace qg

@@ -14,7 +14,8 @@ import torch
 
 from . import _lib as L
 
-FMT_INT8_SYM, FMT_UINT8_ASYM, FMT_MXFP8_E4M3, FMT_INT4_SYM = 0, 1, 2, 3
+FMT_INT8_SYM, FMT_UINT8_ASYM, FMT_MXFP8_E4M3, FMT_INT4_SYM, FMT_MXFP4_E2M1 = 0, 1, 2, 3, 4
+_MX_FMTS = (FMT_MXFP8_E4M3, FMT_MXFP4_E2M1)
 GRAN_TENSOR, GRAN_ROW, GRAN_BLOCK32, GRAN_GROUP64 = 0, 1, 2, 3
 OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
 MX_EXACT, MX_SCALED_MFMA = 0, 1
@@ -48,9 +49,18 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def unpack_fp4_codes(packed: torch.Tensor, K: int) -> torch.Tensor:
+    """One e2m1 code (0..15) per element from two-codes-per-byte rows
+    (element 2i in the low nibble of byte i); returns uint8 [rows, K]."""
+    lo = packed & 0x0F
+    hi = packed >> 4
+    return torch.stack([lo, hi], dim=-1).reshape(packed.shape[0], -1)[:, :K]
+
+
 @dataclass
 class QuantizedRows:
-    """Codes [M, ld] (first K columns valid) plus scales / zero points / E8M0 scales."""
+    """Codes [M, ld] (the first K columns valid; MXFP4: the first K / 2 bytes,
+    two codes per byte) plus scales / zero points / E8M0 scales."""
     q: torch.Tensor
     K: int
     fmt: int
@@ -64,7 +74,14 @@ class QuantizedRows:
         return self.q.shape[0]
 
     def codes(self) -> torch.Tensor:
-        return self.q[:, : self.K]
+        """The stored codes: [M, K] bytes, or [M, K / 2] packed bytes for MXFP4."""
+        return self.q[:, : self.K // 2] if self.fmt == FMT_MXFP4_E2M1 else self.q[:, : self.K]
+
+    def element_codes(self) -> torch.Tensor:
+        """One code per element, [M, K] (MXFP4 codes unpacked)."""
+        if self.fmt == FMT_MXFP4_E2M1:
+            return unpack_fp4_codes(self.q[:, : self.K // 2], self.K)
+        return self.codes()
 
 
 def unblock_int8_codes(raw: torch.Tensor, n_pad: int, k_pad: int) -> torch.Tensor:
@@ -111,6 +128,9 @@ class PackedWeights:
         if d.fmt == FMT_INT4_SYM:
             raw = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad // 2]
             return unblock_int4_codes(raw, d.N_pad, d.K_pad)
+        if d.fmt == FMT_MXFP4_E2M1:  # one code per element, [N_pad, K_pad]
+            raw = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad // 2]
+            return unpack_fp4_codes(raw.view(d.N_pad, d.K_pad // 2), d.K_pad)
         raw = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad]
         if d.fmt != FMT_INT8_SYM:
             return raw.view(d.N_pad, d.K_pad)
@@ -149,10 +169,10 @@ def qgemm_quantize_rows(x: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = GR
     M, K = x.shape
     dev = x.device
     if out is None:
-        ld = _round_up(max(K, 1), 16)
+        ld = _round_up(max(K // 2 if fmt == FMT_MXFP4_E2M1 else K, 1), 16)
         q = torch.empty((M, ld), dtype=torch.int8 if fmt == FMT_INT8_SYM else torch.uint8, device=dev)
         scales = zeros = mx = None
-        if fmt == FMT_MXFP8_E4M3:
+        if fmt in _MX_FMTS:
             mx = torch.empty((M, max(K // 32, 1)), dtype=torch.uint8, device=dev)
         else:
             scales = torch.empty((1 if gran == GRAN_TENSOR else M,), dtype=torch.float32, device=dev)
@@ -246,13 +266,14 @@ def qgemm_run(a: QuantizedRows, w: PackedWeights, out_type: int = OUT_F32,
 
 def qgemm_run_mx(a: QuantizedRows, w: PackedWeights, out: Optional[torch.Tensor] = None,
                  mode: int = MX_EXACT, bias: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Block-scaled e4m3 GEMM (float32 out, plus an optional float32 bias [N]); returns out[:, :N]."""
+    """Block-scaled GEMM of e4m3 or e2m1 activations and weights (float32
+    out, plus an optional float32 bias [N]); returns out[:, :N]."""
     lib = L.load()
     dev = a.q.device
     N = w.N
     if out is None:
         out = _alloc_out(a.M, N, torch.float32, dev)
-    st = lib.qgemm_run_mx(_ptr(a.q), a.q.stride(0), _ptr(a.mx_scales), a.mx_scales.stride(0), a.M,
+    st = lib.qgemm_run_mx(_ptr(a.q), a.q.stride(0), _ptr(a.mx_scales), a.mx_scales.stride(0), a.fmt, a.M,
                           ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0), mode,
                           _bias_ptr(bias, N), None, 0, ctypes.c_void_p(_stream(dev, stream)))
     _check("qgemm_run_mx", st)

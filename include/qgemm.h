@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define QGEMM_ABI_VERSION 4
+#define QGEMM_ABI_VERSION 5
 #define QGEMM_WDESC_MAGIC 0x51474d57u /* "WMGQ" */
 
 /* Status codes. Every entry point returns one of these. */
@@ -77,7 +77,11 @@ typedef enum {
    * group of 64 consecutive K-elements of a row (weights only).
    * [TL27] sections 2.4 (s = absmax / 7, clip to [-8, 7]), 3.3(c) and 5.1
    * (int8 activations times int4 weights in groups of 64). */
-  QGEMM_FMT_INT4_SYM = 3
+  QGEMM_FMT_INT4_SYM = 3,
+  /* fp4 e2m1 data, two codes per byte (element 2i in the low nibble), with
+   * one E8M0 power-of-two scale per 32 K-elements. [TL27] sections 1.2 and 8
+   * (e2m1, u = 2^-2), 2.3 (the MX block and E8M0), 3.1 (the packed e2m1 storage). */
+  QGEMM_FMT_MXFP4_E2M1 = 4
 } qgemm_format;
 
 /* Scale granularity. */
@@ -128,6 +132,8 @@ typedef enum {
  *           [16c, 16c+16) (so each block is one 16x16x64 int8 matrix-core
  *           operand in lane order and a streamed 1 KB load).
  *           QGEMM_FMT_MXFP8_E4M3: e4m3 codes [N_pad][K_pad], row-major.
+ *           QGEMM_FMT_MXFP4_E2M1: e2m1 codes [N_pad][K_pad/2] bytes, row-major,
+ *           two per byte (element 2i in the low nibble).
  *           QGEMM_FMT_INT4_SYM: N_pad x K_pad / 2 bytes in 1 KB blocks of 16
  *           rows x 128 K; block (n/16, k/128) starts at byte
  *           ((n/16)*(K_pad/128) + k/128) * 1024. Row n%16 and c = (k%64)/16
@@ -138,7 +144,8 @@ typedef enum {
  *           two's-complement bits ([TL27] 3.3(b) and pitfall 9).
  *   scales  at scales_off: INT8: float32 [N_pad] (GRAN_ROW; rows >= N are 0)
  *           or float32 [1] (GRAN_TENSOR). MX: E8M0 bytes [N_pad][K_pad/32]
- *           row-major, padding blocks hold 127 (scale 1.0). INT4: float32,
+ *           row-major, padding blocks hold 127 (scale 1.0) (the same for
+ *           MXFP4). INT4: float32,
  *           64 per 16 rows x 256 K: the scale of row n, group g at float
  *           index ((n/16)*(K_pad/256) + g/4) * 64 + 4*(n%16) + g%4 (one
  *           16-byte load gives a row the scales of four groups); padding is 0.
@@ -196,6 +203,9 @@ size_t qgemm_workspace_bytes(int64_t rows, int64_t K, int fmt, int gran);
  *     per row and 32-block b: amax = max(max|x|, 1e-4);
  *     E = ceil_to_ue8m0(amax / 448) in [1, 254]  (scale 2^(E-127));
  *     q = e4m3(x * 2^(127-E)), round to nearest even.
+ *   MXFP4_E2M1, BLOCK32 (K % 32 == 0): the same with e2m1's largest value 6:
+ *     E = ceil_to_ue8m0(amax / 6); q = e2m1(x * 2^(127-E)), round to nearest,
+ *     ties to the even code; two codes per byte, element 2i in the low nibble.
  *   Division is the correctly rounded float32 x / s (no reciprocal), rint is
  *   round-half-to-even, so codes, scales and zero points are bit-exact
  *   against a float32 evaluation of the same formulas.
@@ -204,9 +214,11 @@ size_t qgemm_workspace_bytes(int64_t rows, int64_t K, int fmt, int gran);
  *   x            device, float32 [M][ldx], ldx >= K, 4-byte aligned (rows that start on
  *                16-byte boundaries, ldx % 4 == 0, are read with 16-byte loads).
  *   M, K         M >= 0, K >= 1.
- *   fmt, gran    INT8_SYM or UINT8_ASYM with TENSOR or ROW; MXFP8_E4M3 with BLOCK32.
- *   q            device, codes [M][ldq] bytes, ldq >= K, ldq % 16 == 0, 16-byte aligned.
- *                Columns >= K are not written.
+ *   fmt, gran    INT8_SYM or UINT8_ASYM with TENSOR or ROW; MXFP8_E4M3 or
+ *                MXFP4_E2M1 with BLOCK32.
+ *   q            device, codes [M][ldq] bytes, ldq >= K (MXFP4: ldq >= K/2),
+ *                ldq % 16 == 0, 16-byte aligned. Bytes past the row's codes are
+ *                not written.
  *   scales       device float32 [M] (ROW) or [1] (TENSOR); NULL for MX.
  *   zero_points  device int32 [M] or [1] for UINT8_ASYM; NULL otherwise.
  *   mx_scales    device E8M0 bytes [M][ld_mx] for MX (ld_mx >= K/32); NULL otherwise.
@@ -258,7 +270,8 @@ int qgemm_rmsnorm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ld
  *     s_w = max(amax / 127, 1e-8); q_w = clamp(rint(w / s_w), -127, 127);
  *     colsum[n] = sum_k q_w[n,k]  ([AQ] "The integer GEMM, written out",
  *     quantize_per_channel; [D98] the column sums of the zero-point row).
- *   MXFP8_E4M3, BLOCK32: the MX rule of qgemm_quantize_rows on each row of W.
+ *   MXFP8_E4M3 or MXFP4_E2M1, BLOCK32: the MX rule of qgemm_quantize_rows on
+ *     each row of W.
  *   INT4_SYM, GROUP64: per row n and group g of 64 K (a last, shorter group
  *     takes the elements it has), s = max(amax / 7, 1e-8) in float32,
  *     q = clamp(rint(w / s), -8, 7) with a correctly rounded quotient
@@ -317,29 +330,36 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
               void* stream);
 
 /*
- * qgemm_run_mx -- block-scaled fp8 GEMM (step MXG).
+ * qgemm_run_mx -- block-scaled GEMM (step MXG): e4m3 or e2m1 activations
+ * times e4m3 or e2m1 weights, each with one E8M0 scale per 32 K-elements.
  *
  *   out[m,n] = sum_b 2^(Ea[m,b]-127) * 2^(Ew[n,b]-127) *
- *              sum_{k in block b} e4m3(a[m,k]) * e4m3(w[n,k])
+ *              sum_{k in block b} a[m,k] * w[n,k]
  *   Each 32-element K block is multiplied by its own pair of scales inside
  *   the K loop ([TL27] 4.1: (A*scale_A)(B*scale_B); 4.3: a per-K-block scale
  *   cannot be moved out of the sum). float32 accumulation and output; how
  *   exactly the products and sums are formed depends on `mode`. With a bias,
  *   out[m,n] + bias[n] in float32 (the bias term of the MX formula
- *   C = (scale_A x A)(scale_B x B) + bias on the [TL27] pages).
+ *   C = (scale_A x A)(scale_B x B) + bias on the [TL27] pages; [TL27] 4.2
+ *   lists e4m3 x e2m1 and e2m1 x e2m1 MX matmuls).
  *
- *   a_codes  device e4m3 [M][lda], lda >= K, lda % 16 == 0, 16-byte aligned.
+ *   a_codes  device codes [M][lda] bytes: e4m3 (a_fmt QGEMM_FMT_MXFP8_E4M3,
+ *            lda >= K) or packed e2m1 (QGEMM_FMT_MXFP4_E2M1, lda >= K/2), as
+ *            written by qgemm_quantize_rows; lda % 16 == 0, 16-byte aligned.
  *   a_e8m0   device E8M0 [M][lda_s], lda_s >= K/32.
- *   w_desc   descriptor of MXFP8_E4M3 weights with the same K (K % 32 == 0).
+ *   a_fmt    QGEMM_FMT_MXFP8_E4M3 or QGEMM_FMT_MXFP4_E2M1 (else QGEMM_E_MODE).
+ *   w_desc   descriptor of MXFP8_E4M3 or MXFP4_E2M1 weights with the same K
+ *            (K % 32 == 0).
  *   out      device float32 [M][ldo], ldo >= N, ldo % 4 == 0, 16-byte aligned.
- *   mode     qgemm_mx_mode: QGEMM_MX_EXACT (products exact, float32 sums) or
- *            QGEMM_MX_SCALED_MFMA (block-scaled fp8 matrix cores; see the enum).
+ *   mode     qgemm_mx_mode: QGEMM_MX_EXACT (products exact, float32 sums; any
+ *            pair of formats) or QGEMM_MX_SCALED_MFMA (block-scaled fp8 matrix
+ *            cores; e4m3 x e4m3 only, else QGEMM_E_MODE; see the enum).
  *            Both need E8M0 codes in [3, 240] for exactness of the scaled values,
  *            which qgemm_quantize_rows always produces for inputs below 2^120.
  *   bias     device float32 [N] or NULL.
  *   workspace unused by this version (pass NULL, 0).
  */
-int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s,
+int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s, int a_fmt,
                  int64_t M, const qgemm_wdesc* w_desc, const void* w_packed,
                  float* out, int64_t ldo, int mode, const float* bias,
                  void* workspace, size_t workspace_bytes,

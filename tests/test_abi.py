@@ -15,7 +15,7 @@ from block_scaled_quantized_qgemm_amd import _lib as L  # noqa: E402
 HEADER = os.path.join(ROOT, "include", "qgemm.h")
 
 OK, E_NULL, E_SHAPE, E_MODE, E_ALIGN, E_OVERFLOW, E_DEVICE, E_DESC, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8
-INT8, UINT8, MX, INT4 = 0, 1, 2, 3
+INT8, UINT8, MX, INT4, MX4 = 0, 1, 2, 3, 4
 TENSOR, ROW, BLK, G64 = 0, 1, 2, 3
 
 
@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.qgemm_abi_version() == 4
+    assert lib.qgemm_abi_version() == 5
     for s in range(-9, 1):
         assert lib.qgemm_status_string(s).startswith(b"QGEMM_")
     assert lib.qgemm_status_string(-100) == b"unknown qgemm status"
@@ -64,6 +64,10 @@ def test_sizes(lib):
     assert lib.qgemm_packed_weight_bytes(100, 300, INT4, ROW) == 0
     assert lib.qgemm_packed_weight_bytes(100, 300, INT8, G64) == 0
     assert lib.qgemm_workspace_bytes(64, 256, INT4, G64) == 0
+    # MXFP4: codes [256][512 / 2], E8M0 [256][512 / 32]
+    assert lib.qgemm_packed_weight_bytes(100, 320, MX4, BLK) == 256 * 256 + 256 * 16
+    assert lib.qgemm_packed_weight_bytes(64, 100, MX4, BLK) == 0      # K % 32
+    assert lib.qgemm_packed_weight_bytes(64, 96, MX4, ROW) == 0
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
@@ -94,10 +98,13 @@ def test_quantize_rows_validation(lib):
     assert _q(lib, fmt=MX, gran=BLK, s=None, mx=FAKE, ldmx=1) == E_SHAPE
     assert _q(lib, gran=TENSOR) == E_WS
     assert _q(lib, gran=TENSOR, ws=FAKE, wsb=15) == E_WS
+    assert _q(lib, fmt=MX4, gran=ROW) == E_MODE
+    assert _q(lib, fmt=MX4, gran=BLK, s=None, mx=FAKE, ldmx=2, ldq=16) == E_SHAPE   # K / 2 = 32 bytes
+    assert _q(lib, fmt=MX4, gran=BLK, s=None, mx=FAKE, ldmx=2, ldq=40) == E_ALIGN
 
 
 def _wdesc(**kw):
-    d = L.WDesc(magic=0x51474D57, version=4, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=5, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 512, colsum_off=256 * 512 + 1024, bytes=256 * 512 + 2048)
     for k, v in kw.items():
         setattr(d, k, v)
@@ -143,10 +150,11 @@ def test_run_validation(lib):
 
 def test_run_mx_validation(lib):
     nb = lib.qgemm_packed_weight_bytes(100, 320, MX, BLK)
-    d = L.WDesc(magic=0x51474D57, version=4, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=5, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 512, colsum_off=-1, bytes=nb)
     call = lambda **kw: lib.qgemm_run_mx(kw.get("a", FAKE), kw.get("lda", 320), kw.get("e", FAKE),
-                                         kw.get("ldas", 10), kw.get("M", 4), ctypes.byref(kw.get("d", d)),
+                                         kw.get("ldas", 10), kw.get("af", MX), kw.get("M", 4),
+                                         ctypes.byref(kw.get("d", d)),
                                          FAKE, kw.get("out", FAKE), kw.get("ldo", 100), kw.get("mode", 0),
                                          kw.get("bias", None), None, 0, None)
     assert call(d=_wdesc()) == E_DESC                     # an int8 descriptor
@@ -157,6 +165,15 @@ def test_run_mx_validation(lib):
     assert call(M=0, a=None, e=None, out=None) == OK
     assert call(mode=2) == E_MODE
     assert call(bias=FAKE + 1) == E_ALIGN
+    assert call(af=INT8) == E_MODE
+    assert call(af=MX4, mode=1) == E_MODE                 # scaled fp8 matrix cores: e4m3 only
+    assert call(af=MX4, lda=160, M=0, a=None, e=None, out=None) == OK
+    assert call(af=MX4, lda=144) == E_SHAPE               # packed e2m1 rows need K / 2 bytes
+    nb4 = lib.qgemm_packed_weight_bytes(100, 320, MX4, BLK)
+    d4 = L.WDesc(magic=0x51474D57, version=5, fmt=MX4, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
+                 codes_off=0, scales_off=256 * 256, colsum_off=-1, bytes=nb4)
+    assert call(d=d4, mode=1) == E_MODE
+    assert call(d=_w4desc()) == E_DESC                    # int4 weights are not MX
 
 
 def test_rmsnorm_quantize_validation(lib):
@@ -194,6 +211,8 @@ def test_prepack_validation(lib):
     assert f(pb=100) == E_SHAPE
     assert f(gran=TENSOR) == E_WS
     assert f(fmt=INT4, gran=ROW) == E_MODE
+    assert f(fmt=MX4, gran=ROW) == E_MODE
+    assert f(fmt=MX4, gran=BLK, K=40, ldw=40) == E_SHAPE
     assert f(fmt=INT8, gran=G64) == E_MODE
     assert f(fmt=INT4, gran=G64, pb=100) == E_SHAPE
     assert d.magic == 0                                   # untouched on error
@@ -201,7 +220,7 @@ def test_prepack_validation(lib):
 
 def _w4desc(**kw):
     nb = 256 * 256 + 4 * 256 * 8
-    d = L.WDesc(magic=0x51474D57, version=4, fmt=INT4, gran=G64, N=100, K=300, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=5, fmt=INT4, gran=G64, N=100, K=300, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 256, colsum_off=-1, bytes=nb)
     for k, v in kw.items():
         setattr(d, k, v)

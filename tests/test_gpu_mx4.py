@@ -1,0 +1,138 @@
+"""GPU parity of MXFP4 (fp4 e2m1 codes, two per byte, with one E8M0 scale per
+32 K-elements), through the C ABI, against the CPU oracle.
+
+Codes (one per element and as packed bytes) and E8M0 bytes are bit-exact.
+The block-scaled GEMM in the exact mode, for e2m1 x e2m1 and the mixed
+e4m3 / e2m1 pairs, is within 1e-5 * S of the float64 reference over the
+dequantized values (S = sum_k |a_k w_k|): every product is exact and the
+float32 sums round at 2^-24 per addition.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from block_scaled_quantized_qgemm_amd.inputs import make_inputs, rng_for
+from conftest import print_case
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+MX_STOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def ops():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_scaled_quantized_qgemm_amd import ops as _ops
+    _ops.L.load()
+    return _ops
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _edge_rows(K, rng):
+    rows = [np.zeros(K), np.full(K, 3.25), np.full(K, -2.0), rng.standard_normal(K) * 1e-30,
+            rng.standard_normal(K) * 6.0e4]
+    # a block whose amax is 6 has scale 1, so these sit exactly on e2m1 midpoints
+    ties = np.tile(np.array([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5,
+                             -5.0, -6.0]), K // 16 + 1)[:K]
+    rows.append(ties)
+    spike = np.zeros(K)
+    spike[K // 2] = -7.0
+    rows.append(spike)
+    return np.stack(rows).astype(np.float32)
+
+
+FMT = {"e4m3": 2, "e2m1": 4}
+
+
+def _quant(x, fmt):
+    return O.quantize_mxfp4(x) if fmt == "e2m1" else O.quantize_mx(x)
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 64), (17, 96), (64, 1024), (130, 4192), (8, 8192)])
+def test_quantize_mxfp4_bit_exact(ops, M, K):
+    print_case("quantize mxfp4", M, K)
+    A, _ = make_inputs("c5_mxfp8", M=M, K=K, N=1, seed=M * 37 + K)
+    if M >= 8:
+        A[-7:] = _edge_rows(K, rng_for(K))
+    r = ops.qgemm_quantize_rows(dev(A), ops.FMT_MXFP4_E2M1, ops.GRAN_BLOCK32)
+    codes, E = O.quantize_mxfp4(A)
+    assert np.array_equal(host(r.element_codes()), codes)
+    assert np.array_equal(host(r.codes()), O.pack_int4_pairs(codes.astype(np.int8)))
+    assert np.array_equal(host(r.mx_scales)[:, : K // 32], E)
+
+
+def test_quantize_mxfp4_ties_go_to_even(ops):
+    print_case("quantize mxfp4 ties")
+    A = _edge_rows(64, rng_for(2))[5:6]
+    r = ops.qgemm_quantize_rows(dev(A), ops.FMT_MXFP4_E2M1, ops.GRAN_BLOCK32)
+    got = host(r.element_codes())[0, :16].tolist()
+    assert got == [7, 0, 2, 2, 4, 4, 6, 6, 8, 10, 10, 12, 12, 14, 14, 15]
+    assert host(r.mx_scales)[0, 0] == 127
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (70, 96), (300, 1024), (257, 4128)])
+def test_prepack_mxfp4_bit_exact(ops, N, K):
+    print_case("prepack mxfp4", N, K)
+    _, W = make_inputs("c5_mxfp8", M=1, K=K, N=N, seed=N + 3 * K)
+    pw = ops.qgemm_prepack_weights(dev(W), ops.FMT_MXFP4_E2M1, ops.GRAN_BLOCK32)
+    codes, E = O.quantize_mxfp4(W)
+    got = host(pw.codes())
+    assert np.array_equal(got[:N, :K], codes)
+    assert not got[N:].any() and not got[:, K:].any()
+    e = host(pw.scales())
+    assert np.array_equal(e[:N, : K // 32], E)
+    assert (e[N:] == 127).all() and (e[:, K // 32:] == 127).all()
+
+
+def _gemm_check(ops, A, W, fa, fw, bias=None):
+    qa, Ea = _quant(A, fa)
+    qw, Ew = _quant(W, fw)
+    ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew, fa, fw)
+    a = ops.qgemm_quantize_rows(dev(A), FMT[fa], ops.GRAN_BLOCK32)
+    pw = ops.qgemm_prepack_weights(dev(W), FMT[fw], ops.GRAN_BLOCK32)
+    got = host(ops.qgemm_run_mx(a, pw, mode=ops.MX_EXACT,
+                                bias=None if bias is None else dev(bias))).astype(np.float64)
+    if bias is not None:
+        ref = ref + bias.astype(np.float64)[None, :]
+        S = S + np.abs(bias.astype(np.float64))[None, :]
+    err = np.abs(got - ref)
+    bad = err > MX_STOL * S
+    assert not bad.any(), (np.argwhere(bad)[:5], err.max())
+    return got, ref
+
+
+PAIRS = [("e2m1", "e2m1"), ("e4m3", "e2m1"), ("e2m1", "e4m3")]
+
+
+@pytest.mark.parametrize("fa,fw", PAIRS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (33, 65, 96), (130, 260, 320), (64, 64, 1024), (300, 200, 2080)])
+def test_gemm_mxfp4_exact_parity(ops, M, N, K, fa, fw):
+    print_case("gemm mxfp4", M, N, K, fa, fw)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=M + 7 * N + K)
+    _gemm_check(ops, A, W, fa, fw)
+
+
+@pytest.mark.parametrize("fa,fw", [("e2m1", "e2m1"), ("e4m3", "e2m1")])
+def test_gemm_mxfp4_large_tiles(ops, fa, fw):
+    """4096 x 4096 output tiles: the 256 x 256 tile configuration."""
+    print_case("gemm mxfp4 large tiles", fa, fw)
+    A, W = make_inputs("c5_mxfp8", M=4096, K=256, N=4096, seed=99)
+    got, ref = _gemm_check(ops, A, W, fa, fw)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-6
+
+
+def test_gemm_mxfp4_bias(ops):
+    print_case("gemm mxfp4 bias")
+    A, W = make_inputs("c5_mxfp8", M=40, K=160, N=70, seed=5)
+    b = rng_for(70).normal(0.0, 10.0, size=70).astype(np.float32)
+    _gemm_check(ops, A, W, "e2m1", "e2m1", bias=b)
