@@ -29,6 +29,7 @@ METRIC = "quantized GEMM TOPS (quant+GEMM+epilogue) and % of MFMA peak; decode-M
 PEAK_INT8_TOPS = 5000.0   # dense int8 MFMA, MI355X
 PEAK_FP8_TFLOPS = 5000.0  # dense fp8 / MXFP8 MFMA, MI355X
 PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X (the exact MX mode runs on these)
+PEAK_FP4_TFLOPS = 10100.0  # dense fp4 / fp6 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0     # HBM3E
 MALL_BYTES = 256 << 20
 
@@ -49,7 +50,7 @@ DESCRIPTION = {
 }
 
 
-def algorithmic(name, M, K, N, w4a8=False):
+def algorithmic(name, M, K, N, w4a8=False, fp4=False):
     """Ops and algorithmic bytes: whole step, and the GEMM kernel alone.
 
     Whole step: float32 A read once, W codes + per-channel scales/column sums
@@ -64,8 +65,9 @@ def algorithmic(name, M, K, N, w4a8=False):
         w = N * K / 2 + 4 * N * math.ceil(K / 64)
         a_codes = M * K + 4 * M
     elif act == "mxfp8":
-        w = N * K + N * (K // 32)
-        a_codes = M * K + M * (K // 32)
+        cb = 0.5 if fp4 else 1.0  # code bytes per element: e2m1 packs two per byte
+        w = cb * N * K + N * (K // 32)
+        a_codes = cb * M * K + M * (K // 32)
     else:
         w = N * K + 8 * N
         a_codes = M * K + 8 * M
@@ -101,7 +103,7 @@ def measured_traffic(name):
     return float(t["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False):
+def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False, fp4=False):
     """The oracle, untuned, on a bounded sample of the same workload.
     fused: (gamma, eps, bias) to time the RMSNorm-fused step with a bias;
     w4a8: int4 per-group-64 weights and the per-group GEMM."""
@@ -117,8 +119,10 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False):
     N = W.shape[0]
     if act == "mxfp8":
         rows = min(M, 64)
-        Wq, We = O.quantize_mx(W)                     # offline weight preparation, untimed
-        Wd = O.mx_dequantize(Wq, We)
+        quant = O.quantize_mxfp4 if fp4 else O.quantize_mx
+        fmt = "e2m1" if fp4 else "e4m3"
+        Wq, We = quant(W)                             # offline weight preparation, untimed
+        Wd = O.mx_dequantize(Wq, We, fmt)
         sample = f"{rows} of {M} rows of A against all of W (W prepared outside the timing)"
     elif w4a8:
         rows = min(M, 256)
@@ -132,8 +136,8 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False):
     reps, t0 = 0, time.perf_counter()
     while True:
         if act == "mxfp8":
-            qa, Ea = O.quantize_mx(As)
-            _ = O.mx_dequantize(qa, Ea) @ Wd.T
+            qa, Ea = quant(As)
+            _ = O.mx_dequantize(qa, Ea, fmt) @ Wd.T
         elif w4a8:
             if fused is not None:
                 qa, sa = O.rmsnorm_quantize(As, fused[0], fused[1], act="sym_row")[:2]
@@ -160,7 +164,7 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False):
     ops = 2.0 * rows * K * N * reps
     unit = "GB/s" if WORKLOADS[name][4] == "GB/s" else WORKLOADS[name][4]
     if unit == "GB/s":
-        _, step_bytes, _ = algorithmic(name, rows, K, N, w4a8)
+        _, step_bytes, _ = algorithmic(name, rows, K, N, w4a8, fp4)
         value = step_bytes * reps / el / 1e9
     else:
         value = ops / el / 1e12
@@ -188,6 +192,8 @@ def main():
     ap.add_argument("--w4a8", action="store_true",
                     help="symmetric int8 workloads: int4 weights with a float32 scale per group of 64 K "
                          "(qgemm_run_w4a8)")
+    ap.add_argument("--mx-format", default="e4m3", choices=["e4m3", "e2m1"],
+                    help="MX workload: element format of activations and weights (e2m1: MXFP4)")
     ap.add_argument("--mx-mode", default="exact", choices=["exact", "scaled-mfma"],
                     help="MX workload: exact products (bf16 matrix cores) or block-scaled fp8 matrix cores")
     args = ap.parse_args()
@@ -210,12 +216,17 @@ def main():
     if args.w4a8 and act != "int8_sym":
         print("bench.py: --w4a8 applies to the symmetric int8 workloads", file=sys.stderr)
         sys.exit(2)
+    fp4 = args.mx_format == "e2m1"
+    if fp4 and act != "mxfp8":
+        print("bench.py: --mx-format e2m1 applies to the MX workload", file=sys.stderr)
+        sys.exit(2)
     M, K, N, _, _ = SHAPES[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     A_np, W_np = make_inputs(name)
-    fmt = {"int8_sym": ops.FMT_INT8_SYM, "uint8_asym": ops.FMT_UINT8_ASYM, "mxfp8": ops.FMT_MXFP8_E4M3}[act]
+    fmt = {"int8_sym": ops.FMT_INT8_SYM, "uint8_asym": ops.FMT_UINT8_ASYM,
+           "mxfp8": ops.FMT_MXFP4_E2M1 if fp4 else ops.FMT_MXFP8_E4M3}[act]
     agr = {"tensor": ops.GRAN_TENSOR, "row": ops.GRAN_ROW, "block32": ops.GRAN_BLOCK32}[gran]
     wgr = {"tensor": ops.GRAN_TENSOR, "channel": ops.GRAN_ROW, "block32": ops.GRAN_BLOCK32}[wgran]
     otype = {"f32": ops.OUT_F32, "bf16": ops.OUT_BF16}[out]
@@ -224,12 +235,12 @@ def main():
     mx_mode = ops.MX_EXACT if args.mx_mode == "exact" else ops.MX_SCALED_MFMA
     A0 = torch.from_numpy(A_np).to(dev)
     W0 = torch.from_numpy(W_np).to(dev)
-    wfmt = ops.FMT_MXFP8_E4M3 if act == "mxfp8" else ops.FMT_INT8_SYM   # weights are symmetric
+    wfmt = fmt if act == "mxfp8" else ops.FMT_INT8_SYM   # weights are symmetric
     if args.w4a8:
         wfmt, wgr = ops.FMT_INT4_SYM, ops.GRAN_GROUP64
     w0 = ops.qgemm_prepack_weights(W0, wfmt, wgr)
     torch.cuda.synchronize()
-    ops_count, step_bytes, gemm_bytes = algorithmic(name, M, K, N, args.w4a8)
+    ops_count, step_bytes, gemm_bytes = algorithmic(name, M, K, N, args.w4a8, fp4)
     if args.fused:  # the norm weight and the bias are read once more
         step_bytes += 4 * K + 4 * N
         gemm_bytes += 4 * N
@@ -322,12 +333,12 @@ def main():
         value = ops_count / (ms_per_step * 1e-3) / 1e12
         gemm_achieved = ops_count / (gemm_ms * 1e-3) / 1e12
         if act == "mxfp8":
-            peak = PEAK_BF16_TFLOPS if mx_mode == ops.MX_EXACT else PEAK_FP8_TFLOPS
+            peak = PEAK_BF16_TFLOPS if mx_mode == ops.MX_EXACT else (PEAK_FP4_TFLOPS if fp4 else PEAK_FP8_TFLOPS)
         else:
             peak = PEAK_INT8_TOPS
         roof = {"bound": "mfma", "achieved": gemm_achieved, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(name + ("_w4a8" if args.w4a8 else ""))
+    roof["traffic"] = measured_traffic(name + ("_w4a8" if args.w4a8 else "") + ("_fp4" if fp4 else ""))
 
     line = {
         "metric": METRIC,
@@ -340,10 +351,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3" if act == "mxfp8" else ("i8 x i4" if args.w4a8 else "i8"),
+        "dtype": ("fp4-e2m1" if fp4 else "fp8-e4m3") if act == "mxfp8" else ("i8 x i4" if args.w4a8 else "i8"),
         "data": "synthetic (seeded generator with the workload's shapes and distributions)",
         "config": {"workload": f"{name}: {DESCRIPTION[name]}"
                    + (f" ({args.mx_mode} mode)" if act == "mxfp8" else "")
+                   + (" -- MXFP4: e2m1 A and W, E8M0 per 32" if fp4 else "")
                    + (" with RMSNorm fused into the quantizer and a float32 bias" if args.fused else "")
                    + (" -- W4A8: int4 W with a float32 scale per group of 64 K" if args.w4a8 else ""),
                    "M": M, "K": K, "N": N,
@@ -365,7 +377,7 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(name, A_np, W_np, args.cpu_budget,
                                             (gamma.cpu().numpy(), eps, bias.cpu().numpy()) if args.fused else None,
-                                            args.w4a8)
+                                            args.w4a8, fp4)
     print(json.dumps(line), flush=True)
 
 

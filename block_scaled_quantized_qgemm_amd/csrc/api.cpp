@@ -297,9 +297,8 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
   if (!is_mx_fmt(a_fmt)) return QGEMM_E_MODE;
   int rc = check_desc(w_desc, -1);
   if (rc != QGEMM_OK) return rc;
-  // the block-scaled fp8 matrix cores are used for e4m3 x e4m3 only
-  if (mode == QGEMM_MX_SCALED_MFMA && (a_fmt != QGEMM_FMT_MXFP8_E4M3 || w_desc->fmt != QGEMM_FMT_MXFP8_E4M3))
-    return QGEMM_E_MODE;
+  // the block-scaled matrix cores take e4m3 x e4m3 or e2m1 x e2m1
+  if (mode == QGEMM_MX_SCALED_MFMA && a_fmt != w_desc->fmt) return QGEMM_E_MODE;
   const int64_t N = w_desc->N, K = w_desc->K;
   if (M < 0 || M > kMaxRows) return QGEMM_E_SHAPE;
   if (M == 0) return QGEMM_OK;

@@ -118,13 +118,15 @@ __device__ inline void fp4x16_to_bf16(const v4i& q, float scale, v4i& lo, v4i& h
   hi = v4i{w[4], w[5], w[6], w[7]};
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int MODE>
+// F4 (scaled mode): e2m1 operands staged raw, 32 codes per 16-byte chunk.
+template <int BM, int BN, int BK, int WM, int WN, int MODE, bool F4 = false>
 struct MxCfg {
   static constexpr int NT = WM * WN * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int CPR = BK / 16;                    // 16-byte global chunks per row and K step
-  static constexpr int RB = MODE == MXB ? 2 * BK : BK;   // LDS bytes per row
+  static constexpr int KPC = MODE == MXF && F4 ? 32 : 16;             // K per global chunk
+  static constexpr int CPR = BK / KPC;                                 // global chunks per row and K step
+  static constexpr int RB = MODE == MXB ? 2 * BK : (F4 ? BK / 2 : BK);  // LDS bytes per row
   static constexpr int A_CH = BM * CPR / NT, B_CH = BN * CPR / NT;
   static constexpr int STAGE = (BM + BN) * RB;
   static constexpr int RS = TN + 8;  // epilogue staging row stride in words: rows r and r+4
@@ -137,14 +139,21 @@ struct MxCfg {
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
 
-// FA4 / FW4 (exact mode only): the activations / weights are e2m1, two codes
-// per byte; a 16-K chunk is then 8 bytes, converted to the same two bf16
-// LDS chunks as sixteen e4m3 codes.
+// FA4 / FW4: the activations / weights are e2m1, two codes per byte. In the
+// exact mode a 16-K chunk is then 8 bytes, converted to the same two bf16 LDS
+// chunks as sixteen e4m3 codes. In the scaled mode (both operands e2m1) the
+// codes go to LDS as they are, and a lane's operand for a 64-deep step is the
+// 16 bytes holding K 32h .. 32h + 31 of its row (lane 32h + r; measured), fed
+// to the matrix cores with the e2m1 format code: e2m1 products span under 8
+// binades, so the hardware's 8-product alignment drops nothing and the sums
+// are float32 sums.
 template <int BM, int BN, int BK, int WM, int WN, int MODE, bool FA4 = false, bool FW4 = false>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
-  using C = MxCfg<BM, BN, BK, WM, WN, MODE>;
-  static_assert(MODE == MXB || (!FA4 && !FW4), "e2m1 operands take the exact mode");
+  constexpr bool F4 = MODE == MXF && FA4;
+  using C = MxCfg<BM, BN, BK, WM, WN, MODE, F4>;
+  static_assert(MODE == MXB || FA4 == FW4, "the scaled mode takes e4m3 x e4m3 or e2m1 x e2m1");
   constexpr int NT = C::NT, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RB = C::RB;
+  constexpr int KPC = C::KPC;
   constexpr int A_CH = C::A_CH, B_CH = C::B_CH, STAGE = C::STAGE;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -193,9 +202,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
       /* value before the LDS store, so the loads stay in flight. Rows >= M only */             \
       /* feed outputs that are never stored; columns >= K meet zero weights (and */             \
       /* are zeroed at the store for MX, where a stray code could be NaN). */                   \
-      const int64_t m = min(m0 + r, p.M - 1), k = k0_ + c * 16;                                  \
+      const int64_t m = min(m0 + r, p.M - 1), k = k0_ + c * KPC;                                 \
       const int64_t kc = k < p.K ? k : 0;                                                       \
-      if constexpr (FA4) {                                                                      \
+      if constexpr (F4) {                                                                       \
+        RA[i] = *reinterpret_cast<const v4i*>(p.a + m * p.lda + (kc >> 1));                     \
+      } else if constexpr (FA4) {                                                               \
         const uint2 h_ = *reinterpret_cast<const uint2*>(p.a + m * p.lda + (kc >> 1));          \
         RA[i] = v4i{(int)h_.x, (int)h_.y, 0, 0};                                                \
       } else {                                                                                  \
@@ -206,8 +217,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                          \
       const int id = tid + i * NT;                                                              \
       const int r = id / CPR, c = id % CPR;                                                     \
-      const int64_t n = n0 + r, k = k0_ + c * 16;                                               \
-      if constexpr (FW4) {                                                                      \
+      const int64_t n = n0 + r, k = k0_ + c * KPC;                                              \
+      if constexpr (F4) {                                                                       \
+        RB_[i] = *reinterpret_cast<const v4i*>(p.w + n * (p.K_pad >> 1) + (k >> 1));            \
+      } else if constexpr (FW4) {                                                               \
         const uint2 h_ = *reinterpret_cast<const uint2*>(p.w + n * (p.K_pad >> 1) + (k >> 1));  \
         RB_[i] = v4i{(int)h_.x, (int)h_.y, 0, 0};                                               \
       } else {                                                                                  \
@@ -223,7 +236,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                          \
       const int id = tid + i * NT;                                                              \
       const int r = id / CPR, c = id % CPR;                                                     \
-      if ((int64_t)(KT) * BK + c * 16 >= p.K) RA[i] = v4i{0, 0, 0, 0};                          \
+      if ((int64_t)(KT) * BK + c * KPC >= p.K) RA[i] = v4i{0, 0, 0, 0};                         \
       if constexpr (MODE == MXB) {                                                              \
         v4i lo, hi;                                                                             \
         if constexpr (FA4)                                                                      \
@@ -301,26 +314,28 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);                                                      \
       }                                                                                         \
     } else {                                                                                    \
-      /* 64-deep scaled fp8 steps: lane 32h + r holds K 16h.. and 32+16h.. */                   \
+      /* 64-deep scaled steps: e4m3, lane 32h + r holds K 16h.. and 32+16h..; */                \
+      /* e2m1, lane 32h + r holds K 32h .. 32h+31 in its first 16 bytes */                      \
       _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                       \
-        const int c0 = ks * 4 + (lane >> 5), c1 = c0 + 2;                                       \
+        const int c0 = F4 ? ks * 2 + (lane >> 5) : ks * 4 + (lane >> 5), c1 = c0 + 2;           \
         v8i af[FM], bf[FN];                                                                     \
         _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                        \
           const int r = wm * TM + i * 32 + (lane & 31);                                         \
           const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<RB>(r, c0));                \
-          const v4i hi = *reinterpret_cast<const v4i*>(sa + lds_off<RB>(r, c1));                \
+          const v4i hi = F4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sa + lds_off<RB>(r, c1)); \
           af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                  \
         }                                                                                       \
         _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                        \
           const int r = wn * TN + j * 32 + (lane & 31);                                         \
           const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<RB>(r, c0));                \
-          const v4i hi = *reinterpret_cast<const v4i*>(sb + lds_off<RB>(r, c1));                \
+          const v4i hi = F4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sb + lds_off<RB>(r, c1)); \
           bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                  \
         }                                                                                       \
         _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
           _Pragma("unroll") for (int j = 0; j < FN; ++j)                                        \
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                        \
-                af[i], bf[j], acc[i][j], 0, 0, 0, esa[ks * FM + i], 0, esb[ks * FN + j]);       \
+                af[i], bf[j], acc[i][j], F4 ? 4 : 0, F4 ? 4 : 0, 0, esa[ks * FM + i], 0,        \
+                esb[ks * FN + j]);                                                              \
         __builtin_amdgcn_sched_barrier(0);                                                      \
       }                                                                                         \
     }                                                                                           \
@@ -842,7 +857,7 @@ static hipError_t launch_i8(const GemmArgs& a, hipStream_t st) {
 
 template <int BM, int BN, int BK, int WM, int WN, int MODE, bool FA4, bool FW4>
 static hipError_t launch_mx_cfg(const GemmArgs& a, hipStream_t st) {
-  using C = MxCfg<BM, BN, BK, WM, WN, MODE>;
+  using C = MxCfg<BM, BN, BK, WM, WN, MODE, MODE == MXF && FA4>;
   auto kern = gemm_mx_kernel<BM, BN, BK, WM, WN, MODE, FA4, FW4>;
   const size_t lds = C::LDS;
   if (lds > 65536) {  // above the default dynamic-LDS limit (gfx950 has 160 KiB)
@@ -881,7 +896,10 @@ hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_
 
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
-  if (mode == 1) return launch_mx<MXF>(a, st);  // e4m3 x e4m3 (the caller checks)
+  if (mode == 1) {  // e4m3 x e4m3 or e2m1 x e2m1 (the caller checks)
+    if (a.a_fp4) return launch_mx<MXF, true, true>(a, st);
+    return launch_mx<MXF>(a, st);
+  }
   if (a.a_fp4 && a.w_fp4) return launch_mx<MXB, true, true>(a, st);
   if (a.a_fp4) return launch_mx<MXB, true, false>(a, st);
   if (a.w_fp4) return launch_mx<MXB, false, true>(a, st);

@@ -110,12 +110,13 @@ typedef enum {
    * bfloat16 holds exactly -- and the bf16 matrix cores form every product
    * exactly and sum in float32. Error: float32 summation only. */
   QGEMM_MX_EXACT = 0,
-  /* gfx950 block-scaled fp8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4),
-   * fed the e4m3 codes and one E8M0 byte per lane and block. Twice the peak
-   * rate of QGEMM_MX_EXACT, but inside each group of 8 consecutive K the
+  /* gfx950 block-scaled matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4),
+   * fed the codes and one E8M0 byte per lane and block. For e4m3: twice the
+   * peak rate of QGEMM_MX_EXACT, but inside each group of 8 consecutive K the
    * hardware aligns the products to the largest one and drops the bits more
    * than 13 binades below it (measured), so
-   * |out - exact| <= 2^-10 * sum_k |a_k w_k| plus float32 summation. */
+   * |out - exact| <= 2^-10 * sum_k |a_k w_k| plus float32 summation. For
+   * e2m1 x e2m1: four times the exact mode's peak and float32 sums only. */
   QGEMM_MX_SCALED_MFMA = 1
 } qgemm_mx_mode;
 
@@ -352,8 +353,11 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
  *            (K % 32 == 0).
  *   out      device float32 [M][ldo], ldo >= N, ldo % 4 == 0, 16-byte aligned.
  *   mode     qgemm_mx_mode: QGEMM_MX_EXACT (products exact, float32 sums; any
- *            pair of formats) or QGEMM_MX_SCALED_MFMA (block-scaled fp8 matrix
- *            cores; e4m3 x e4m3 only, else QGEMM_E_MODE; see the enum).
+ *            pair of formats) or QGEMM_MX_SCALED_MFMA (block-scaled matrix
+ *            cores; e4m3 x e4m3 or e2m1 x e2m1, else QGEMM_E_MODE; see the
+ *            enum -- for e2m1 x e2m1 the products span under 8 binades, so
+ *            nothing is dropped and the sums are float32 sums, as in the exact
+ *            mode, at twice the e4m3 rate).
  *            Both need E8M0 codes in [3, 240] for exactness of the scaled values,
  *            which qgemm_quantize_rows always produces for inputs below 2^120.
  *   bias     device float32 [N] or NULL.
