@@ -275,7 +275,7 @@ def main():
 
     def gemm(i):
         Ai, wi, qi, oi = sets[i % nsets]
-        if fmt == ops.FMT_MXFP8_E4M3:
+        if act == "mxfp8":
             ops.qgemm_run_mx(qi, wi, out=oi, mode=mx_mode)
         elif args.w4a8:
             ops.qgemm_run_w4a8(qi, wi, otype, out=oi, bias=bias if args.fused else None)
@@ -338,7 +338,8 @@ def main():
             peak = PEAK_INT8_TOPS
         roof = {"bound": "mfma", "achieved": gemm_achieved, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(name + ("_w4a8" if args.w4a8 else "") + ("_fp4" if fp4 else ""))
+    roof["traffic"] = measured_traffic(name + ("_w4a8" if args.w4a8 else "") + ("_fp4" if fp4 else "")
+                                       + ("_scaled" if act == "mxfp8" and mx_mode != ops.MX_EXACT else ""))
 
     line = {
         "metric": METRIC,
