@@ -266,10 +266,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
     }                                                                                           \
   }
 
-  // ---- MXF: per lane one E8M0 byte per (fragment, 64-deep step), loaded a stage ahead
+  // ---- MXF: per lane one E8M0 byte per (fragment, 64-deep step)
   constexpr int KS = MODE == MXF ? BK / 64 : 1;
-  int esa[MODE == MXF ? FM * KS : 1], esb[MODE == MXF ? FN * KS : 1];
-  int nsa[MODE == MXF ? FM * KS : 1], nsb[MODE == MXF ? FN * KS : 1];
+  // Scales travel with the stage data: loaded into the register set of the
+  // stage (fs*0 / fs*1), copied to the LDS buffer's set (es*0 / es*1) when the
+  // stage is stored, used two steps after their load.
+  constexpr int SA = MODE == MXF ? FM * KS : 1, SB = MODE == MXF ? FN * KS : 1;
+  int fsa0[SA], fsb0[SB], fsa1[SA], fsb1[SB], esa0[SA], esb0[SB], esa1[SA], esb1[SB];
 #define QG_LOAD_SCALES(KT, DA, DB)                                                              \
   if constexpr (MODE == MXF) {                                                                  \
     _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                         \
@@ -334,22 +337,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
         _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
           _Pragma("unroll") for (int j = 0; j < FN; ++j)                                        \
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                        \
-                af[i], bf[j], acc[i][j], F4 ? 4 : 0, F4 ? 4 : 0, 0, esa[ks * FM + i], 0,        \
-                esb[ks * FN + j]);                                                              \
+                af[i], bf[j], acc[i][j], F4 ? 4 : 0, F4 ? 4 : 0, 0,                             \
+                (S) == 0 ? esa0[ks * FM + i] : esa1[ks * FM + i], 0,                            \
+                (S) == 0 ? esb0[ks * FN + j] : esb1[ks * FN + j]);                              \
         __builtin_amdgcn_sched_barrier(0);                                                      \
       }                                                                                         \
     }                                                                                           \
   }
-#define QG_NEXT_SCALES()                                                                        \
+#define QG_KEEP_SCALES(DA, DB, SA_, SB_)                                                        \
   if constexpr (MODE == MXF) {                                                                  \
-    _Pragma("unroll") for (int t = 0; t < FM * KS; ++t) esa[t] = nsa[t];                        \
-    _Pragma("unroll") for (int t = 0; t < FN * KS; ++t) esb[t] = nsb[t];                        \
+    _Pragma("unroll") for (int t = 0; t < FM * KS; ++t) DA[t] = SA_[t];                         \
+    _Pragma("unroll") for (int t = 0; t < FN * KS; ++t) DB[t] = SB_[t];                         \
   }
 
-  QG_LOAD_SCALES(0, esa, esb)
+  QG_LOAD_SCALES(0, esa0, esb0)
   QG_LOAD_STAGE(0, ra0, rb0, ea0, eb0)
   QG_STORE_STAGE(0, 0, ra0, rb0, ea0, eb0)
   QG_LOAD_STAGE(1, ra1, rb1, ea1, eb1)
+  QG_LOAD_SCALES(min(1, nkt - 1), fsa1, fsb1)
   __syncthreads();
 
   // nkt is even: the packed K is a multiple of 256 and BK divides 128. The
@@ -358,24 +363,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
   for (int kt = 0; kt < nkt; kt += 2) {
     // even stage kt: LDS buffer 0; set 1 holds stage kt+1; stage kt+2 goes into set 0
     QG_LOAD_STAGE(min(kt + 2, nkt - 1), ra0, rb0, ea0, eb0)
-    QG_LOAD_SCALES(kt + 1, nsa, nsb)
+    QG_LOAD_SCALES(min(kt + 2, nkt - 1), fsa0, fsb0)
     QG_COMPUTE(0)
     QG_STORE_STAGE(kt + 1, 1, ra1, rb1, ea1, eb1)
-    QG_NEXT_SCALES()
+    QG_KEEP_SCALES(esa1, esb1, fsa1, fsb1)
     __syncthreads();
     // odd stage kt+1: LDS buffer 1; set 0 holds stage kt+2; stage kt+3 goes into set 1
     QG_LOAD_STAGE(min(kt + 3, nkt - 1), ra1, rb1, ea1, eb1)
-    QG_LOAD_SCALES(min(kt + 2, nkt - 1), nsa, nsb)
+    QG_LOAD_SCALES(min(kt + 3, nkt - 1), fsa1, fsb1)
     QG_COMPUTE(1)
     QG_STORE_STAGE(kt + 2, 0, ra0, rb0, ea0, eb0)
-    QG_NEXT_SCALES()
+    QG_KEEP_SCALES(esa0, esb0, fsa0, fsb0)
     __syncthreads();
   }
 #undef QG_LOAD_STAGE
 #undef QG_STORE_STAGE
 #undef QG_LOAD_SCALES
 #undef QG_COMPUTE
-#undef QG_NEXT_SCALES
+#undef QG_KEEP_SCALES
 
   // ---- epilogue through LDS. Lane l of a 32x32 block holds column l%32 and
   // rows 8*(e/4) + 4*(l/32) + e%4 of its 16 values e. Each wave writes one
