@@ -57,6 +57,28 @@ __device__ inline float e8m0_inverse(int E) {
   return be >= 1 ? __uint_as_float((uint32_t)be << 23) : __uint_as_float(0x00400000u);
 }
 
+// LDS row of RB bytes made of 16-byte chunks. gfx950 serves a 16-byte-per-lane
+// LDS access 16 lanes at a time over 64 four-byte banks (256 bytes), so the 16
+// rows that 16 lanes read at the same logical chunk must land in 16 distinct
+// 16-byte slots of a 256-byte bank line: the chunk index is XOR-ed with the
+// row's position among the rows that share a bank line.
+template <int RB>
+__device__ inline int lds_off(int row, int chunk) {
+  constexpr int CPR = RB / 16;
+  constexpr int RPL = RB >= 256 ? 1 : 256 / RB;  // rows sharing one 256-byte bank line
+  return row * RB + ((chunk ^ ((row / RPL) % CPR)) << 4);
+}
+
+// E8M0 code E as the float32 2^(E-127) (E in [1, 254]).
+__device__ inline float e8m0_to_f32(int E) { return __uint_as_float((uint32_t)E << 23); }
+
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (expcnt and lgkmcnt left at "no wait").
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
+
+// an LDS pointer as the address-space-3 pointer the LDS-DMA builtin takes
+#define QG_LDSP(x) ((__attribute__((address_space(3))) void*)(x))
+
 // One output element: OUT 0 float32 y, 1 bfloat16 of y, 2 the int32 c.
 template <int OUT>
 __device__ inline void store_one(void* out, int64_t idx, int c, float y) {

@@ -50,18 +50,6 @@ enum MxMode { MXB = 1, MXF = 2 };
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
-// LDS row of RB bytes made of 16-byte chunks. gfx950 serves a 16-byte-per-lane
-// LDS access 16 lanes at a time over 64 four-byte banks (256 bytes), so the 16
-// rows that 16 lanes read at the same logical chunk must land in 16 distinct
-// 16-byte slots of a 256-byte bank line: the chunk index is XOR-ed with the
-// row's position among the rows that share a bank line.
-template <int RB>
-__device__ inline int lds_off(int row, int chunk) {
-  constexpr int CPR = RB / 16;
-  constexpr int RPL = RB >= 256 ? 1 : 256 / RB;  // rows sharing one 256-byte bank line
-  return row * RB + ((chunk ^ ((row / RPL) % CPR)) << 4);
-}
-
 // The exact MX mode's bf16 tiles have 128-byte rows, written as converted
 // 16-byte chunks (four lanes per row: chunks 2c or 2c + 1, c = lane % 4) and
 // read as MFMA fragments (16 lanes on 16 consecutive rows at one chunk).
@@ -84,8 +72,6 @@ template <int BK>
 __device__ inline int w_blk_off(int row, int chunk) {
   return (((row >> 4) * (BK / 64) + (chunk >> 2)) << 10) + ((chunk & 3) << 8) + ((row & 15) << 4);
 }
-
-__device__ inline float e8m0_to_f32(int E) { return __uint_as_float((uint32_t)E << 23); }
 
 // Sixteen e4m3 codes times 2^(E-127) as sixteen bf16 (exact for E in [3, 240]).
 __device__ inline void fp8x16_to_bf16(const v4i& q, float scale, v4i& lo, v4i& hi) {
@@ -432,10 +418,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
 // vmcnt wait and one barrier per K step; the fragments of sub-step kk + 1 are
 // read while the matrix cores work on sub-step kk.
 // ---------------------------------------------------------------------------
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14); }
-
-#define QG_LDSP(x) ((__attribute__((address_space(3))) void*)(x))
-
 template <int BM, int BN, int BK, int WM, int WN, int NS, bool ASYM, int OUT>
 struct DmaCfg {
   static constexpr int NT = WM * WN * 64, NW = WM * WN;
@@ -693,8 +675,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_i8_dma_kernel(GemmArgs p) {
   }
 }
 
-// Compute units of the current device (cached per device).
-static int cu_count() {
+int cu_count() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -901,6 +882,7 @@ hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_
 
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
+  if (mx_dma_eligible(a, mode)) return launch_gemm_mx_dma(a, mode, st);
   if (mode == 1) {  // e4m3 x e4m3 or e2m1 x e2m1 (the caller checks)
     if (a.a_fp4) return launch_mx<MXF, true, true>(a, st);
     return launch_mx<MXF>(a, st);

@@ -1,0 +1,321 @@
+// MX GEMM (e4m3 x e4m3, one E8M0 scale per 32 K of each row of A and W,
+// float32 output) on an LDS-DMA ring, for gfx950.
+//
+// The block-scaled product ("TileLang tutorial, chapter 27", sections 4.1 and
+// 4.3): out[m][n] = sum over 32-blocks b of 2^(Ea[m][b]-127) 2^(Ew[n][b]-127)
+// times the block's sum of e4m3 products; a scale that changes along K is
+// applied per block inside the K loop, never after the sum.
+//
+// e4m3 codes are bytes, so the tiles travel like the int8 GEMM's: global
+// memory -> LDS directly (buffer_load ... lds), each lane fetching the
+// 16-byte chunk that belongs at its slot of the XOR-swizzled row-major tile,
+// NS stages in a ring so NS - 1 are in flight without holding registers. Each
+// stage (64 K) also carries its E8M0 bytes: one dword per tile row (the four
+// blocks of the 128-deep stage pair the stage belongs to, fetched by a
+// 4-byte-per-lane DMA), so a stage's scales arrive with its data and the scale
+// layout in global memory stays the public row-major [rows][K/32].
+//
+// Per 64-deep stage a wave reads, per 32-row fragment, the two 16-byte chunks
+// the 32x32x64 operand wants (lane 32h + r: K 16h .. 16h+15 and 32 + 16h ..
+// 32 + 16h + 15 of row r) and the E8M0 byte of (row r, block h), and issues
+// v_mfma_scale_f32_32x32x64_f8f6f4 (the block-scaled fp8 matrix cores; the
+// hardware aligns the products of each group of 8 consecutive K to the
+// largest and drops bits more than 13 binades below it, so the sums are not
+// float32-exact). The MFMAs of a stage come in two halves: the first half with
+// the next ring stage's DMA spread between them, then the wait and barrier for
+// the following stage and its fragment reads, then the second half, which
+// hides those reads.
+//
+// Taken when every stage lies inside K (K % 64 == 0) and the activation scale
+// rows are dword-aligned; the register-staged kernel in gemm.hip covers the
+// rest (and the other format pairs and the exact mode).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qg {
+
+template <int BM, int BN, int WM, int WN, int NS>
+struct MxDmaCfg {
+  static constexpr int BK = 64;                      // K per stage (two 32-blocks)
+  static constexpr int NT = WM * WN * 64, NW = WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int DATA = (BM + BN) * BK;        // code bytes per stage
+  static constexpr int SCL = (BM + BN) * 4;          // one scale dword per tile row
+  static constexpr int STAGE = DATA + SCL;
+  static constexpr int IA = BM * BK / 1024;          // the first IA 1 KB data loads carry A
+  static constexpr int IPD = DATA / 1024 / NW;       // 1 KB data loads per wave and stage
+  static constexpr int IPS = (BM + BN) / 64 / NW;    // 256 B scale loads per wave and stage
+  static constexpr int IPW = IPD + IPS;
+  static constexpr int SLOTS = (FM / 2) * FN;        // MFMAs of the first half
+  static constexpr int RS = TN + 8;                  // epilogue staging row stride (words)
+  static constexpr int EPI = NW * 32 * RS * 4;
+  static constexpr int LDS = NS * STAGE > EPI ? NS * STAGE : EPI;
+  static_assert(DATA % (1024 * NW) == 0 && (BM + BN) % (64 * NW) == 0 && BM % 64 == 0, "loads per wave");
+  static_assert(FM % 2 == 0 && FN >= 1, "two halves of a stage's MFMAs");
+  static_assert(NS >= 3 && (NS - 2) * IPW < 64, "vmcnt range");
+  static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
+};
+
+template <int BM, int BN, int WM, int WN, int NS>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
+  using C = MxDmaCfg<BM, BN, WM, WN, NS>;
+  constexpr int BK = C::BK, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
+  constexpr int STAGE = C::STAGE, DATA = C::DATA, IPD = C::IPD, IPS = C::IPS, IPW = C::IPW, SLOTS = C::SLOTS;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wm = wid / WN, wn = wid % WN;
+  const int h = lane >> 5;
+
+  // Tile order (as the int8 GEMM): workgroups are dealt round-robin over the 8
+  // XCDs; each XCD gets a contiguous run of tiles, walked in groups of 8
+  // tile-rows so that neighbours share A rows and W columns in its L2.
+  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
+  const int ntiles = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  {
+    const int per = ntiles / 8;
+    if (per > 0 && pid < per * 8) pid = (pid % 8) * per + pid / 8;
+  }
+  constexpr int GROUP = 8;
+  const int group_tiles = GROUP * tiles_n;
+  const int g = pid / group_tiles;
+  const int first_m = g * GROUP;
+  const int gsize = min(tiles_m - first_m, GROUP);
+  const int tile_m = first_m + (pid % group_tiles) % gsize;
+  const int tile_n = (pid % group_tiles) / gsize;
+  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+  const int nkt = (int)(p.K / BK);  // every stage inside K (the launcher checks K % 64 == 0)
+  const int64_t ldw = p.K_pad, ldws = p.K_pad / 32;
+
+  // Loads of a stage. Data: wave wid issues the stage's 1 KB loads
+  // wid*IPD .. wid*IPD+IPD-1; lane l of load j fetches the 16-byte chunk that
+  // belongs at LDS slot 16 l of the swizzled row-major tile (A for j < IA,
+  // then W). Scales: load js (wave wid issues wid*IPS ..) covers 64 tile rows
+  // (A rows, then W rows), lane l the dword of row 64 js + l, landing at
+  // 4 (64 js + l) after the stage's data. Per-lane offsets do not change along
+  // K; the stage's K offset goes in the scalar offset. A rows >= M are clamped
+  // to row M - 1 (their outputs are never stored); the buffer ranges end at
+  // the last row's K (codes) and at its last scale dword, so nothing past them
+  // is read. Stages past the last one get an empty range: their loads move no
+  // data and still count in vmcnt.
+  const int64_t last_a_row = min((int64_t)BM - 1, p.M - 1 - m0);
+  const uint8_t* const abase = p.a + m0 * p.lda;
+  const uint8_t* const wbase = p.w + n0 * ldw;
+  const uint8_t* const eabase = p.ea + m0 * p.lda_s;
+  const uint8_t* const ewbase = p.ew + n0 * ldws;
+  const uint32_t nrec_a = (uint32_t)(last_a_row * p.lda + p.K);
+  const uint32_t nrec_w = (uint32_t)(BN * ldw);
+  const uint32_t nrec_ea = (uint32_t)(last_a_row * p.lda_s + ((p.K / 32 + 3) & ~(int64_t)3));
+  const uint32_t nrec_ew = (uint32_t)(BN * ldws);
+  uint32_t voff[IPW];
+#pragma unroll
+  for (int i = 0; i < IPD; ++i) {
+    const int j = wid * IPD + i;
+    const bool ja = j < C::IA;
+    const int P = (ja ? j : j - C::IA) * 1024 + lane * 16;
+    const int r = P / BK;
+    const int c = ((P % BK) >> 4) ^ ((r / 4) % 4);  // lds_off<64>: four rows share a bank line
+    voff[i] = ja ? (uint32_t)(min((int64_t)r, last_a_row) * p.lda) + (uint32_t)(c * 16)
+                 : (uint32_t)(r * ldw) + (uint32_t)(c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < IPS; ++i) {
+    const int js = wid * IPS + i;
+    const int r = js * 64 + lane;
+    voff[IPD + i] = r < BM ? (uint32_t)(min((int64_t)r, last_a_row) * p.lda_s) : (uint32_t)((r - BM) * ldws);
+  }
+  auto dma = [&](int kt, int s, int i, bool live) {
+    if (i < IPD) {
+      const int j = wid * IPD + i;
+      const bool ja = j < C::IA;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(ja ? abase : wbase), (short)0, live ? (int)(ja ? nrec_a : nrec_w) : 0, kRawBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, QG_LDSP(smem + s * STAGE + j * 1024), 16, (int)voff[i], kt * BK, 0,
+                                               0);
+    } else {
+      const int js = wid * IPS + (i - IPD);
+      const bool ja = js * 64 < BM;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(ja ? eabase : ewbase), (short)0, live ? (int)(ja ? nrec_ea : nrec_ew) : 0, kRawBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, QG_LDSP(smem + s * STAGE + DATA + js * 256), 4, (int)voff[i],
+                                               (kt >> 1) * 4, 0, 0);
+    }
+  };
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  // Fragments and scale bytes of one stage. The stage's scale dword holds the
+  // blocks 4 (kt / 2) .. + 3; this stage's block h sits in byte 2 (kt % 2) + h.
+  struct Frag {
+    v8i a[FM], b[FN];
+    int sa[FM], sb[FN];
+  };
+  auto load_frags = [&](int s, int odd, Frag& f) {
+    const uint8_t* sa = smem + s * STAGE;
+    const uint8_t* sb = sa + BM * BK;
+    const int* ssa = reinterpret_cast<const int*>(sa + DATA);
+    const int* ssb = ssa + BM;
+    const int sh = 16 * odd + 8 * h;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * TM + i * 32 + (lane & 31);
+      const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, h));
+      const v4i hi = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, h + 2));
+      f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f.sa[i] = (ssa[r] >> sh) & 0xff;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * TN + j * 32 + (lane & 31);
+      const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, h));
+      const v4i hi = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, h + 2));
+      f.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f.sb[j] = (ssb[r] >> sh) & 0xff;
+    }
+  };
+  auto mfma = [&](const Frag& f, int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.sa[i], 0,
+                                                                 f.sb[j]);
+  };
+
+  // One stage kt (fragments in `cur`, the next stage's into `nxt`).
+  auto stage = [&](int kt, const Frag& cur, Frag& nxt) {
+    // Stage kt + NS - 1 refills the slot every wave finished reading before
+    // the previous barrier; its loads go between the first half's MFMAs.
+    const int ks = kt + NS - 1;
+    const bool live = ks < nkt;
+    const int sl = ks % NS;
+#pragma unroll
+    for (int i = 0; i < FM / 2; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        mfma(cur, i, j);
+        const int slot = i * FN + j;
+#pragma unroll
+        for (int d = 0; d < IPW; ++d)
+          if ((d * SLOTS) / IPW == slot) dma(ks, sl, d, live);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    // stage kt + 1 landed (vmcnt counts the loads issued after it), this
+    // wave's LDS reads are done (lgkmcnt 0); after the barrier everyone's are
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW) & ~(15 << 8));
+    __builtin_amdgcn_s_barrier();
+    load_frags((kt + 1) % NS, (kt + 1) & 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = FM / 2; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        mfma(cur, i, j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+
+  // prologue: stages 0 .. NS-2 in flight
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) dma(s, s, i, s < nkt);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW));
+  __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+  load_frags(0, 0, f0);
+
+  // two stages per trip so the fragment sets alternate without copies
+  int kt = 0;
+  for (; kt + 1 < nkt; kt += 2) {
+    stage(kt, f0, f1);
+    stage(kt + 1, f1, f0);
+  }
+  if (kt < nkt) stage(kt, f0, f1);
+
+  // the empty loads past the last stage may still be in flight
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  // ---- epilogue through LDS. Lane l of a 32x32 block holds column l%32 and
+  // rows 8*(e/4) + 4*(l/32) + e%4 of its 16 values e. Each wave writes one
+  // 32-row slab of its sub-tile to its own LDS region, then reads it back row
+  // by row so that every lane finishes 4 consecutive columns of one row.
+  constexpr int LPR = TN / 4;
+  constexpr int RPI = 64 / LPR;
+  constexpr int RS = C::RS;
+  uint8_t* wreg = smem + wid * (32 * RS * 4);
+  const int cq = (lane % LPR) * 4;
+  const int64_t nq = n0 + wn * TN + cq;
+  float bs4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (p.bias) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (nq + t < p.N) bs4[t] = p.bias[nq + t];
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        reinterpret_cast<float*>(wreg)[r * RS + j * 32 + (lane & 31)] = acc[i][j][e];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPI; ++pass) {
+      const int r = pass * RPI + lane / LPR;
+      const int64_t m = m0 + wm * TM + i * 32 + r;
+      v4f y = *reinterpret_cast<const v4f*>(wreg + (r * RS + cq) * 4);
+      if (m < p.M && nq < p.N) {
+        if (p.bias) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) y[t] = y[t] + bs4[t];  // the bias after the scales, in float32
+        }
+        float* o = reinterpret_cast<float*>(p.out) + m * p.ldo + nq;
+        if (nq + 3 < p.N)
+          *reinterpret_cast<v4f*>(o) = y;
+        else
+          for (int t = 0; t < 4 && nq + t < p.N; ++t) o[t] = y[t];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+static hipError_t launch_mx_dma_cfg(const GemmArgs& a, hipStream_t st) {
+  using C = MxDmaCfg<BM, BN, WM, WN, NS>;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_mx_dma_kernel<BM, BN, WM, WN, NS>), dim3((unsigned)tiles), dim3(C::NT), 0, st, a);
+  return hipGetLastError();
+}
+
+bool mx_dma_eligible(const GemmArgs& a, int mode) {
+  if (mode != 1 || a.a_fp4 || a.w_fp4) return false;
+  if (a.K % 64 != 0 || a.lda_s % 4 != 0 || ((uintptr_t)a.ea & 3) != 0) return false;
+  // one 256-row band of A (codes and scales) and of W in 32-bit byte offsets
+  const int64_t rows = a.M < 256 ? a.M : 256;
+  return (rows - 1) * a.lda + a.K < (int64_t(1) << 31) && (rows - 1) * a.lda_s + a.K / 32 + 4 < (int64_t(1) << 31) &&
+         256 * a.K_pad < (int64_t(1) << 31);
+}
+
+hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st) {
+  (void)mode;
+  // 256 x 256 tiles (8 waves of 128 x 64, a 4-stage 136 KB ring, one
+  // workgroup per CU) when they fill every CU; otherwise 128 x 128 tiles
+  // (4 waves of 64 x 64, 68 KB, two workgroups per CU).
+  const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  if (big >= cu_count()) return launch_mx_dma_cfg<256, 256, 2, 4, 4>(a, st);
+  return launch_mx_dma_cfg<128, 128, 2, 2, 4>(a, st);
+}
+
+}  // namespace qg

@@ -30,6 +30,9 @@ void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, bo
 void launch_quantize_int4(const float* w, int64_t rows, int64_t K, int64_t ldw, int64_t K_pad, uint8_t* codes,
                           float* scales, hipStream_t st);
 
+// Compute units of the current device (cached per device).
+int cu_count();
+
 struct GemmArgs {
   const uint8_t* a;     // activation codes [M][lda]
   int64_t lda;
@@ -66,6 +69,11 @@ hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_
 // qgemm_run_mx: block-scaled e4m3 GEMM, float32 output. mode 0: exact products
 // (bf16 matrix cores on dequantized values), mode 1: block-scaled fp8 matrix cores.
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st);
+// The e4m3 x e4m3 block-scaled GEMM on an LDS-DMA ring (gemm_mx_dma.hip):
+// whether it takes these arguments (mode 1, K % 64 == 0, dword-aligned
+// activation scale rows), and its launcher.
+bool mx_dma_eligible(const GemmArgs& a, int mode);
+hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st);
 // qgemm_run_w4a8: int8 activations x int4 weights, per-group scales inside
 // the K loop, float32 sums. out_type: 0 f32, 1 bf16.
 hipError_t launch_gemm_w4a8(const GemmArgs& a, int out_type, hipStream_t st);

@@ -173,7 +173,9 @@ def qgemm_quantize_rows(x: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = GR
         q = torch.empty((M, ld), dtype=torch.int8 if fmt == FMT_INT8_SYM else torch.uint8, device=dev)
         scales = zeros = mx = None
         if fmt in _MX_FMTS:
-            mx = torch.empty((M, max(K // 32, 1)), dtype=torch.uint8, device=dev)
+            # E8M0 rows padded to a multiple of 4 bytes: the GEMM's DMA path
+            # fetches them a dword at a time
+            mx = torch.empty((M, _round_up(max(K // 32, 1), 4)), dtype=torch.uint8, device=dev)
         else:
             scales = torch.empty((1 if gran == GRAN_TENSOR else M,), dtype=torch.float32, device=dev)
             if fmt == FMT_UINT8_ASYM:

@@ -347,7 +347,10 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
  *   a_codes  device codes [M][lda] bytes: e4m3 (a_fmt QGEMM_FMT_MXFP8_E4M3,
  *            lda >= K) or packed e2m1 (QGEMM_FMT_MXFP4_E2M1, lda >= K/2), as
  *            written by qgemm_quantize_rows; lda % 16 == 0, 16-byte aligned.
- *   a_e8m0   device E8M0 [M][lda_s], lda_s >= K/32.
+ *   a_e8m0   device E8M0 [M][lda_s], lda_s >= K/32. With lda_s % 4 == 0, a
+ *            4-byte aligned a_e8m0 and K % 64 == 0, e4m3 x e4m3 in
+ *            QGEMM_MX_SCALED_MFMA mode runs on the LDS-DMA kernel, which
+ *            reads each row's scales a dword at a time (never past lda_s).
  *   a_fmt    QGEMM_FMT_MXFP8_E4M3 or QGEMM_FMT_MXFP4_E2M1 (else QGEMM_E_MODE).
  *   w_desc   descriptor of MXFP8_E4M3 or MXFP4_E2M1 weights with the same K
  *            (K % 32 == 0).

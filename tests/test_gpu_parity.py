@@ -284,6 +284,48 @@ def test_gemm_mx_parity(ops, M, N, K, mode):
         assert O.metrics.rel_l2(got, ref) < 1e-6
 
 
+def _mx_check(got, A, W, tol):
+    qa, Ea = O.quantize_mx(A)
+    qw, Ew = O.quantize_mx(W)
+    ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew)
+    err = np.abs(got.astype(np.float64) - ref)
+    assert (err <= tol * S).all(), (err / np.maximum(S, 1e-300)).max()
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_gemm_mx_large_tiles_ragged(ops, mode):
+    """At least one 256x256 tile per CU, M and N not multiples of the tile:
+    the large-tile configuration of both modes, with clamped rows and padded
+    weight columns."""
+    M, N, K = 4000, 4352 - 40, 256
+    print_case("gemm mx large tiles", M, N, K, "mode", mode)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=4242)
+    a = ops.qgemm_quantize_rows(dev(A), 2, 2)
+    pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
+    _mx_check(host(ops.qgemm_run_mx(a, pw, mode=mode)), A, W, MX_STOL if mode == 0 else MX_SCALED_STOL)
+
+
+@pytest.mark.parametrize("M,N,K", [(130, 260, 320), (600, 700, 1088)])
+def test_gemm_mx_scaled_both_scale_pitches(ops, M, N, K):
+    """K % 64 == 0: the LDS-DMA kernel (E8M0 rows padded to a dword) and the
+    register-staged kernel (E8M0 rows of exactly K/32 bytes, not a multiple of
+    4) both meet the scaled mode's bound, and give the same bits: the same
+    matrix-core instruction sums the same 64-deep steps in the same order."""
+    print_case("gemm mx scaled pitches", M, N, K)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=M + N + K)
+    a = ops.qgemm_quantize_rows(dev(A), 2, 2)
+    pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
+    assert a.mx_scales.stride(0) % 4 == 0 and (K // 32) % 4 != 0
+    tight = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+    tight.copy_(a.mx_scales[:, : K // 32])
+    b = ops.QuantizedRows(a.q, K, a.fmt, a.gran, None, None, tight)
+    got_dma = host(ops.qgemm_run_mx(a, pw, mode=1))
+    got_reg = host(ops.qgemm_run_mx(b, pw, mode=1))
+    _mx_check(got_dma, A, W, MX_SCALED_STOL)
+    _mx_check(got_reg, A, W, MX_SCALED_STOL)
+    assert np.array_equal(got_dma.view(np.uint32), got_reg.view(np.uint32))
+
+
 def test_gemm_mx_modes_on_an_8_group_with_a_wide_exponent_spread(ops):
     """448 and 2^-6 in one group of 8 K: exact mode keeps the small product;
     the block-scaled fp8 matrix cores drop it (the behaviour qgemm.h documents)."""
