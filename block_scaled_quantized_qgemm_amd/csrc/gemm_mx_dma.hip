@@ -26,15 +26,37 @@
 // the following stage and its fragment reads, then the second half, which
 // hides those reads.
 //
+// EXACT (the exact mode): the same ring and fragment reads, then each lane
+// turns its 32 e4m3 codes per fragment into bf16 times the block's scale
+// (v_cvt_scalef32_pk_bf16_fp8; exact, since e4m3 times a power of two in the
+// quantizer's range is a bf16) and feeds v_mfma_f32_32x32x16_bf16: exact
+// products, float32 sums. The 64-deep step becomes four 16-deep ones: chunk t
+// of a lane's fragment (its codes 8t .. 8t + 7) is the MFMA's 8 K values for
+// that lane, the same K positions for A and W, so the four MFMAs together form
+// every product of the step once.
+//
 // Taken when every stage lies inside K (K % 64 == 0) and the activation scale
 // rows are dword-aligned; the register-staged kernel in gemm.hip covers the
-// rest (and the other format pairs and the exact mode).
+// rest (and the e2m1 formats).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace qg {
 
-template <int BM, int BN, int WM, int WN, int NS>
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+
+// Eight e4m3 codes (dwords d0, d1; code i in byte i % 4 of dword i / 4) times
+// `scale` as eight bf16, in order.
+__device__ inline v8bf_t fp8x8_to_bf16(int d0, int d1, float scale) {
+  const v2bf_t t0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d0, scale, false);
+  const v2bf_t t1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d0, scale, true);
+  const v2bf_t t2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d1, scale, false);
+  const v2bf_t t3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d1, scale, true);
+  return v8bf_t{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+}
+
+template <int BM, int BN, int WM, int WN, int NS, bool EXACT>
 struct MxDmaCfg {
   static constexpr int BK = 64;                      // K per stage (two 32-blocks)
   static constexpr int NT = WM * WN * 64, NW = WM * WN;
@@ -47,7 +69,7 @@ struct MxDmaCfg {
   static constexpr int IPD = DATA / 1024 / NW;       // 1 KB data loads per wave and stage
   static constexpr int IPS = (BM + BN) / 64 / NW;    // 256 B scale loads per wave and stage
   static constexpr int IPW = IPD + IPS;
-  static constexpr int SLOTS = (FM / 2) * FN;        // MFMAs of the first half
+  static constexpr int SLOTS = (EXACT ? 2 : 1) * (FM / 2) * FN;  // MFMAs of the first half
   static constexpr int RS = TN + 8;                  // epilogue staging row stride (words)
   static constexpr int EPI = NW * 32 * RS * 4;
   static constexpr int LDS = NS * STAGE > EPI ? NS * STAGE : EPI;
@@ -57,9 +79,9 @@ struct MxDmaCfg {
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NS, bool EXACT>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
-  using C = MxDmaCfg<BM, BN, WM, WN, NS>;
+  using C = MxDmaCfg<BM, BN, WM, WN, NS, EXACT>;
   constexpr int BK = C::BK, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
   constexpr int STAGE = C::STAGE, DATA = C::DATA, IPD = C::IPD, IPS = C::IPS, IPW = C::IPW, SLOTS = C::SLOTS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
@@ -157,6 +179,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
 
   // Fragments and scale bytes of one stage. The stage's scale dword holds the
   // blocks 4 (kt / 2) .. + 3; this stage's block h sits in byte 2 (kt % 2) + h.
+  // The scaled mode keeps the lane's block (h) in the low byte; the exact mode
+  // keeps both blocks of the stage (low byte: K 0-31, next byte: K 32-63).
   struct Frag {
     v8i a[FM], b[FN];
     int sa[FM], sb[FN];
@@ -166,14 +190,15 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
     const uint8_t* sb = sa + BM * BK;
     const int* ssa = reinterpret_cast<const int*>(sa + DATA);
     const int* ssb = ssa + BM;
-    const int sh = 16 * odd + 8 * h;
+    const int sh = EXACT ? 16 * odd : 16 * odd + 8 * h;
+    constexpr int mask = EXACT ? 0xffff : 0xff;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * TM + i * 32 + (lane & 31);
       const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, h));
       const v4i hi = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, h + 2));
       f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      f.sa[i] = (ssa[r] >> sh) & 0xff;
+      f.sa[i] = (ssa[r] >> sh) & mask;
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -181,12 +206,42 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
       const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, h));
       const v4i hi = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, h + 2));
       f.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      f.sb[j] = (ssb[r] >> sh) & 0xff;
+      f.sb[j] = (ssb[r] >> sh) & mask;
     }
   };
   auto mfma = [&](const Frag& f, int i, int j) {
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.sa[i], 0,
                                                                  f.sb[j]);
+  };
+
+  // Exact mode: 16-deep chunk t (codes 8t .. 8t + 7 of each lane's fragment,
+  // dwords 2t and 2t + 1) of every fragment as bf16 times its block's scale
+  // (chunks 0-1: the stage's first block, 2-3: its second), then the
+  // fragments' bf16 MFMAs; `first` is the index of the first of them among
+  // the stage's first half (for the DMA slots), or -1 outside it.
+  // The W chunks are converted first, each A chunk just before its MFMAs
+  // (fewer bf16 registers live at once).
+  auto exact_chunk = [&](const Frag& f, int t, int first, int ks, int sl, bool live) {
+    v8bf_t bb[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bb[j] = fp8x8_to_bf16(f.b[j][2 * t], f.b[j][2 * t + 1], e8m0_to_f32((f.sb[j] >> (t < 2 ? 0 : 8)) & 0xff));
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const v8bf_t ab =
+          fp8x8_to_bf16(f.a[i][2 * t], f.a[i][2 * t + 1], e8m0_to_f32((f.sa[i] >> (t < 2 ? 0 : 8)) & 0xff));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, bb[j], acc[i][j], 0, 0, 0);
+        if (first >= 0) {
+          const int slot = first + i * FN + j;
+#pragma unroll
+          for (int d = 0; d < IPW; ++d)
+            if ((d * SLOTS) / IPW == slot) dma(ks, sl, d, live);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
 
   // One stage kt (fragments in `cur`, the next stage's into `nxt`).
@@ -196,30 +251,40 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
     const int ks = kt + NS - 1;
     const bool live = ks < nkt;
     const int sl = ks % NS;
+    if constexpr (EXACT) {
+      exact_chunk(cur, 0, 0, ks, sl, live);
+      exact_chunk(cur, 1, FM * FN, ks, sl, live);
+    } else {
 #pragma unroll
-    for (int i = 0; i < FM / 2; ++i)
+      for (int i = 0; i < FM / 2; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        mfma(cur, i, j);
-        const int slot = i * FN + j;
+        for (int j = 0; j < FN; ++j) {
+          mfma(cur, i, j);
+          const int slot = i * FN + j;
 #pragma unroll
-        for (int d = 0; d < IPW; ++d)
-          if ((d * SLOTS) / IPW == slot) dma(ks, sl, d, live);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+          for (int d = 0; d < IPW; ++d)
+            if ((d * SLOTS) / IPW == slot) dma(ks, sl, d, live);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
     // stage kt + 1 landed (vmcnt counts the loads issued after it), this
     // wave's LDS reads are done (lgkmcnt 0); after the barrier everyone's are
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW) & ~(15 << 8));
     __builtin_amdgcn_s_barrier();
     load_frags((kt + 1) % NS, (kt + 1) & 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (EXACT) {
+      exact_chunk(cur, 2, -1, ks, sl, live);
+      exact_chunk(cur, 3, -1, ks, sl, live);
+    } else {
 #pragma unroll
-    for (int i = FM / 2; i < FM; ++i)
+      for (int i = FM / 2; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        mfma(cur, i, j);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        for (int j = 0; j < FN; ++j) {
+          mfma(cur, i, j);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
   };
 
   // prologue: stages 0 .. NS-2 in flight
@@ -291,16 +356,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NS, bool EXACT>
 static hipError_t launch_mx_dma_cfg(const GemmArgs& a, hipStream_t st) {
-  using C = MxDmaCfg<BM, BN, WM, WN, NS>;
+  using C = MxDmaCfg<BM, BN, WM, WN, NS, EXACT>;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_mx_dma_kernel<BM, BN, WM, WN, NS>), dim3((unsigned)tiles), dim3(C::NT), 0, st, a);
+  hipLaunchKernelGGL((gemm_mx_dma_kernel<BM, BN, WM, WN, NS, EXACT>), dim3((unsigned)tiles), dim3(C::NT), 0, st, a);
   return hipGetLastError();
 }
 
 bool mx_dma_eligible(const GemmArgs& a, int mode) {
-  if (mode != 1 || a.a_fp4 || a.w_fp4) return false;
+  if ((mode != 0 && mode != 1) || a.a_fp4 || a.w_fp4) return false;
   if (a.K % 64 != 0 || a.lda_s % 4 != 0 || ((uintptr_t)a.ea & 3) != 0) return false;
   // one 256-row band of A (codes and scales) and of W in 32-bit byte offsets
   const int64_t rows = a.M < 256 ? a.M : 256;
@@ -308,14 +373,18 @@ bool mx_dma_eligible(const GemmArgs& a, int mode) {
          256 * a.K_pad < (int64_t(1) << 31);
 }
 
-hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st) {
-  (void)mode;
+template <bool EXACT>
+static hipError_t launch_mx_dma(const GemmArgs& a, hipStream_t st) {
   // 256 x 256 tiles (8 waves of 128 x 64, a 4-stage 136 KB ring, one
   // workgroup per CU) when they fill every CU; otherwise 128 x 128 tiles
   // (4 waves of 64 x 64, 68 KB, two workgroups per CU).
   const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big >= cu_count()) return launch_mx_dma_cfg<256, 256, 2, 4, 4>(a, st);
-  return launch_mx_dma_cfg<128, 128, 2, 2, 4>(a, st);
+  if (big >= cu_count()) return launch_mx_dma_cfg<256, 256, 2, 4, 4, EXACT>(a, st);
+  return launch_mx_dma_cfg<128, 128, 2, 2, 4, EXACT>(a, st);
+}
+
+hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st) {
+  return mode == 0 ? launch_mx_dma<true>(a, st) : launch_mx_dma<false>(a, st);
 }
 
 }  // namespace qg

@@ -69,8 +69,8 @@ hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_
 // qgemm_run_mx: block-scaled e4m3 GEMM, float32 output. mode 0: exact products
 // (bf16 matrix cores on dequantized values), mode 1: block-scaled fp8 matrix cores.
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st);
-// The e4m3 x e4m3 block-scaled GEMM on an LDS-DMA ring (gemm_mx_dma.hip):
-// whether it takes these arguments (mode 1, K % 64 == 0, dword-aligned
+// The e4m3 x e4m3 block-scaled GEMM on an LDS-DMA ring (gemm_mx_dma.hip), in
+// either mode: whether it takes these arguments (K % 64 == 0, dword-aligned
 // activation scale rows), and its launcher.
 bool mx_dma_eligible(const GemmArgs& a, int mode);
 hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st);

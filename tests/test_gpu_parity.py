@@ -305,13 +305,16 @@ def test_gemm_mx_large_tiles_ragged(ops, mode):
     _mx_check(host(ops.qgemm_run_mx(a, pw, mode=mode)), A, W, MX_STOL if mode == 0 else MX_SCALED_STOL)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(130, 260, 320), (600, 700, 1088)])
-def test_gemm_mx_scaled_both_scale_pitches(ops, M, N, K):
+def test_gemm_mx_both_scale_pitches(ops, M, N, K, mode):
     """K % 64 == 0: the LDS-DMA kernel (E8M0 rows padded to a dword) and the
     register-staged kernel (E8M0 rows of exactly K/32 bytes, not a multiple of
-    4) both meet the scaled mode's bound, and give the same bits: the same
-    matrix-core instruction sums the same 64-deep steps in the same order."""
-    print_case("gemm mx scaled pitches", M, N, K)
+    4) both meet the mode's bound. In the scaled mode they also give the same
+    bits: the same matrix-core instruction sums the same 64-deep steps in the
+    same order (the exact mode's two kernels sum in different orders)."""
+    print_case("gemm mx pitches", M, N, K, "mode", mode)
+    tol = MX_STOL if mode == 0 else MX_SCALED_STOL
     A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=M + N + K)
     a = ops.qgemm_quantize_rows(dev(A), 2, 2)
     pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
@@ -319,19 +322,22 @@ def test_gemm_mx_scaled_both_scale_pitches(ops, M, N, K):
     tight = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
     tight.copy_(a.mx_scales[:, : K // 32])
     b = ops.QuantizedRows(a.q, K, a.fmt, a.gran, None, None, tight)
-    got_dma = host(ops.qgemm_run_mx(a, pw, mode=1))
-    got_reg = host(ops.qgemm_run_mx(b, pw, mode=1))
-    _mx_check(got_dma, A, W, MX_SCALED_STOL)
-    _mx_check(got_reg, A, W, MX_SCALED_STOL)
-    assert np.array_equal(got_dma.view(np.uint32), got_reg.view(np.uint32))
+    got_dma = host(ops.qgemm_run_mx(a, pw, mode=mode))
+    got_reg = host(ops.qgemm_run_mx(b, pw, mode=mode))
+    _mx_check(got_dma, A, W, tol)
+    _mx_check(got_reg, A, W, tol)
+    if mode == 1:
+        assert np.array_equal(got_dma.view(np.uint32), got_reg.view(np.uint32))
 
 
-def test_gemm_mx_modes_on_an_8_group_with_a_wide_exponent_spread(ops):
+@pytest.mark.parametrize("K", [32, 64])
+def test_gemm_mx_modes_on_an_8_group_with_a_wide_exponent_spread(ops, K):
     """448 and 2^-6 in one group of 8 K: exact mode keeps the small product;
-    the block-scaled fp8 matrix cores drop it (the behaviour qgemm.h documents)."""
-    A = np.zeros((1, 32), np.float32)
+    the block-scaled fp8 matrix cores drop it (the behaviour qgemm.h documents).
+    K = 32 runs the register-staged kernel, K = 64 the LDS-DMA one."""
+    A = np.zeros((1, K), np.float32)
     A[0, 0], A[0, 1] = 448.0, 2.0 ** -6
-    W = np.ones((1, 32), np.float32)
+    W = np.ones((1, K), np.float32)
     a = ops.qgemm_quantize_rows(dev(A), 2, 2)
     pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
     qa, Ea = O.quantize_mx(A)
