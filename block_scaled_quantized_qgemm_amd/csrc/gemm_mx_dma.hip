@@ -56,34 +56,46 @@ __device__ inline v8bf_t fp8x8_to_bf16(int d0, int d1, float scale) {
   return v8bf_t{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool EXACT>
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool EXACT>
 struct MxDmaCfg {
-  static constexpr int BK = 64;                      // K per stage (two 32-blocks)
   static constexpr int NT = WM * WN * 64, NW = WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int NKK = BK / 64;                // 64-deep matrix-core steps per stage
   static constexpr int DATA = (BM + BN) * BK;        // code bytes per stage
-  static constexpr int SCL = (BM + BN) * 4;          // one scale dword per tile row
-  static constexpr int STAGE = DATA + SCL;
+  static constexpr int STAGE = DATA;
+  static constexpr int SPS = BK / 32;                // E8M0 bytes per row and stage
+  static constexpr int SS = 16 / SPS;                // stages whose scales one 16-byte row load brings
+  static constexpr int SUPER = (BM + BN) * 16;       // one scale slot: 16 bytes per tile row
+  static constexpr int SCALES = NS * STAGE;          // two scale slots after the ring
   static constexpr int IA = BM * BK / 1024;          // the first IA 1 KB data loads carry A
   static constexpr int IPD = DATA / 1024 / NW;       // 1 KB data loads per wave and stage
-  static constexpr int IPS = (BM + BN) / 64 / NW;    // 256 B scale loads per wave and stage
+  static constexpr int NSL = (BM + BN) / 64;         // 1 KB scale loads per scale slot
+  static constexpr int IPS = (NSL + NW - 1) / NW;    // ... per wave and stage (see the loads)
   static constexpr int IPW = IPD + IPS;
-  static constexpr int SLOTS = (EXACT ? 2 : 1) * (FM / 2) * FN;  // MFMAs of the first half
+  static constexpr int MPS = (EXACT ? 4 : 1) * FM * FN;  // matrix-core instructions per 64-deep step
+  // instructions the stage's loads are spread over: the first half of the
+  // only step (BK 64), or every step before the last (BK 128)
+  static constexpr int SLOTS = NKK == 1 ? MPS / 2 : (NKK - 1) * MPS;
   static constexpr int RS = TN + 8;                  // epilogue staging row stride (words)
   static constexpr int EPI = NW * 32 * RS * 4;
-  static constexpr int LDS = NS * STAGE > EPI ? NS * STAGE : EPI;
-  static_assert(DATA % (1024 * NW) == 0 && (BM + BN) % (64 * NW) == 0 && BM % 64 == 0, "loads per wave");
-  static_assert(FM % 2 == 0 && FN >= 1, "two halves of a stage's MFMAs");
-  static_assert(NS >= 3 && (NS - 2) * IPW < 64, "vmcnt range");
+  static constexpr int SINK = SCALES + 2 * SUPER;   // 1 KB that the empty scale loads target
+  static constexpr int LDS = SINK + 1024 > EPI ? SINK + 1024 : EPI;
+  static_assert(BK == 64 || BK == 128, "stage depth");
+  static_assert(DATA % (1024 * NW) == 0 && (BM + BN) % 64 == 0 && BM % 64 == 0, "loads per wave");
+  static_assert(FM % 2 == 0 && FN >= 1, "two halves of a step's MFMAs");
+  static_assert(NS >= 2 && (NS - 2) * IPW < 64, "vmcnt range");
+  // a scale slot is refilled NS - 1 stages before its first stage, after the
+  // last stage of its previous contents
+  static_assert(NS <= SS + 1, "scale slot reuse");
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
 
-template <int BM, int BN, int WM, int WN, int NS, bool EXACT>
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool EXACT>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
-  using C = MxDmaCfg<BM, BN, WM, WN, NS, EXACT>;
-  constexpr int BK = C::BK, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
-  constexpr int STAGE = C::STAGE, DATA = C::DATA, IPD = C::IPD, IPS = C::IPS, IPW = C::IPW, SLOTS = C::SLOTS;
+  using C = MxDmaCfg<BM, BN, BK, WM, WN, NS, EXACT>;
+  constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, NKK = C::NKK, MPS = C::MPS;
+  constexpr int STAGE = C::STAGE, IPD = C::IPD, IPS = C::IPS, IPW = C::IPW, SLOTS = C::SLOTS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
   const int tid = threadIdx.x;
@@ -111,18 +123,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   const int tile_m = first_m + (pid % group_tiles) % gsize;
   const int tile_n = (pid % group_tiles) / gsize;
   const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
-  const int nkt = (int)(p.K / BK);  // every stage inside K (the launcher checks K % 64 == 0)
+  const int nkt = (int)(p.K / BK);  // every stage inside K (the launcher checks K % BK == 0)
   const int64_t ldw = p.K_pad, ldws = p.K_pad / 32;
 
   // Loads of a stage. Data: wave wid issues the stage's 1 KB loads
   // wid*IPD .. wid*IPD+IPD-1; lane l of load j fetches the 16-byte chunk that
   // belongs at LDS slot 16 l of the swizzled row-major tile (A for j < IA,
-  // then W). Scales: load js (wave wid issues wid*IPS ..) covers 64 tile rows
-  // (A rows, then W rows), lane l the dword of row 64 js + l, landing at
-  // 4 (64 js + l) after the stage's data. Per-lane offsets do not change along
-  // K; the stage's K offset goes in the scalar offset. A rows >= M are clamped
-  // to row M - 1 (their outputs are never stored); the buffer ranges end at
-  // the last row's K (codes) and at its last scale dword, so nothing past them
+  // then W). Scales: every SS-th stage also brings the E8M0 bytes of itself and
+  // the next SS - 1 stages, 16 per tile row (one 16-byte lane per row, so a
+  // 1 KB load covers 64 rows instead of 64 cache lines per 256 bytes), into
+  // one of two scale slots; load js (wave wid issues wid*IPS ..) covers tile
+  // rows 64 js .. 64 js + 63 (A rows, then W rows). The other stages (and
+  // js >= NSL) issue the same number of loads with an empty range into a
+  // spare 1 KB, so every wave counts IPW loads per stage. Per-lane offsets do
+  // not change along K; the stage's K offset goes in the scalar offset. A rows
+  // >= M are clamped to row M - 1 (their outputs are never stored); the buffer
+  // ranges end at the last row's K (codes) and at its last scale dword
+  // (dwords past a range read as zero: only bytes of blocks past K/32 or of
+  // the next row fall there, and they are never used), so nothing past them
   // is read. Stages past the last one get an empty range: their loads move no
   // data and still count in vmcnt.
   const int64_t last_a_row = min((int64_t)BM - 1, p.M - 1 - m0);
@@ -141,14 +159,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
     const bool ja = j < C::IA;
     const int P = (ja ? j : j - C::IA) * 1024 + lane * 16;
     const int r = P / BK;
-    const int c = ((P % BK) >> 4) ^ ((r / 4) % 4);  // lds_off<64>: four rows share a bank line
+    const int c = ((P % BK) >> 4) ^ ((r / (256 / BK)) % (BK / 16));  // the chunk swizzle of lds_off<BK>
     voff[i] = ja ? (uint32_t)(min((int64_t)r, last_a_row) * p.lda) + (uint32_t)(c * 16)
                  : (uint32_t)(r * ldw) + (uint32_t)(c * 16);
   }
 #pragma unroll
   for (int i = 0; i < IPS; ++i) {
     const int js = wid * IPS + i;
-    const int r = js * 64 + lane;
+    const int r = min(js * 64 + lane, BM + BN - 1);
     voff[IPD + i] = r < BM ? (uint32_t)(min((int64_t)r, last_a_row) * p.lda_s) : (uint32_t)((r - BM) * ldws);
   }
   auto dma = [&](int kt, int s, int i, bool live) {
@@ -161,12 +179,23 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
                                                0);
     } else {
       const int js = wid * IPS + (i - IPD);
-      const bool ja = js * 64 < BM;
+      const bool ja = js * 64 < BM, real = js < C::NSL && kt % C::SS == 0;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(ja ? eabase : ewbase), (short)0, live ? (int)(ja ? nrec_ea : nrec_ew) : 0, kRawBufferWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, QG_LDSP(smem + s * STAGE + DATA + js * 256), 4, (int)voff[i],
-                                               (kt >> 1) * 4, 0, 0);
+          (void*)(ja ? eabase : ewbase), (short)0, live && real ? (int)(ja ? nrec_ea : nrec_ew) : 0, kRawBufferWord3);
+      // (the scalar offset goes through a named variable: written inline in
+      // the call, this hipcc dropped the kernel's host stub without a message)
+      const int soff = (kt / C::SS) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, QG_LDSP(smem + (real ? C::SCALES + ((kt / C::SS) & 1) * C::SUPER + js * 1024 : C::SINK)), 16, (int)voff[i],
+          soff, 0, 0);
     }
+  };
+  // the stage's loads that go after matrix-core instruction `slot` of the
+  // instructions before its barrier
+  auto dma_slot = [&](int slot, int ks, int sl, bool live) {
+#pragma unroll
+    for (int d = 0; d < IPW; ++d)
+      if ((d * SLOTS) / IPW == slot) dma(ks, sl, d, live);
   };
 
   v16f acc[FM][FN];
@@ -177,113 +206,119 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-  // Fragments and scale bytes of one stage. The stage's scale dword holds the
-  // blocks 4 (kt / 2) .. + 3; this stage's block h sits in byte 2 (kt % 2) + h.
-  // The scaled mode keeps the lane's block (h) in the low byte; the exact mode
-  // keeps both blocks of the stage (low byte: K 0-31, next byte: K 32-63).
+  // Fragments and scale bytes of one 64-deep step kk of stage kt. The step's
+  // block h sits in byte 2 kk + h of dword (kt % SS) * SPS / 4 of the row's 16
+  // scale bytes, shifted by b0 = (kt % SS) * SPS % 4 bytes. The scaled mode
+  // keeps the lane's block in the low byte; the exact mode keeps both blocks
+  // of the step (low byte: K 0-31 of the step, next byte: K 32-63).
   struct Frag {
     v8i a[FM], b[FN];
     int sa[FM], sb[FN];
   };
-  auto load_frags = [&](int s, int odd, Frag& f) {
-    const uint8_t* sa = smem + s * STAGE;
+  auto load_frags = [&](int kt, int kk, Frag& f) {
+    const uint8_t* sa = smem + (kt % NS) * STAGE;
     const uint8_t* sb = sa + BM * BK;
-    const int* ssa = reinterpret_cast<const int*>(sa + DATA);
-    const int* ssb = ssa + BM;
-    const int sh = EXACT ? 16 * odd : 16 * odd + 8 * h;
+    const int q = kt % C::SS;
+    const int* ssa = reinterpret_cast<const int*>(smem + C::SCALES + ((kt / C::SS) & 1) * C::SUPER) + q * C::SPS / 4;
+    const int* ssb = ssa + 4 * BM;
+    const int sh = 8 * (q * C::SPS % 4 + 2 * kk) + (EXACT ? 0 : 8 * h);
     constexpr int mask = EXACT ? 0xffff : 0xff;
+    const int c0 = 4 * kk + h;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * TM + i * 32 + (lane & 31);
-      const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, h));
-      const v4i hi = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, h + 2));
+      const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, c0));
+      const v4i hi = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, c0 + 2));
       f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      f.sa[i] = (ssa[r] >> sh) & mask;
+      f.sa[i] = (ssa[4 * r] >> sh) & mask;
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int r = wn * TN + j * 32 + (lane & 31);
-      const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, h));
-      const v4i hi = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, h + 2));
+      const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, c0));
+      const v4i hi = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, c0 + 2));
       f.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      f.sb[j] = (ssb[r] >> sh) & mask;
+      f.sb[j] = (ssb[4 * r] >> sh) & mask;
     }
   };
-  auto mfma = [&](const Frag& f, int i, int j) {
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.sa[i], 0,
-                                                                 f.sb[j]);
-  };
 
-  // Exact mode: 16-deep chunk t (codes 8t .. 8t + 7 of each lane's fragment,
-  // dwords 2t and 2t + 1) of every fragment as bf16 times its block's scale
-  // (chunks 0-1: the stage's first block, 2-3: its second), then the
-  // fragments' bf16 MFMAs; `first` is the index of the first of them among
-  // the stage's first half (for the DMA slots), or -1 outside it.
-  // The W chunks are converted first, each A chunk just before its MFMAs
-  // (fewer bf16 registers live at once).
-  auto exact_chunk = [&](const Frag& f, int t, int first, int ks, int sl, bool live) {
-    v8bf_t bb[FN];
+  // The matrix-core instructions m0_ .. m1_ - 1 of one 64-deep step (index
+  // (i, j) in the scaled mode; (t, i, j) in the exact mode, t the 16-deep
+  // chunk), the stage's loads after those with slot (index - first) when
+  // first >= 0. Exact mode: chunk t (codes 8t .. 8t + 7 of each lane's
+  // fragment, dwords 2t and 2t + 1) as bf16 times its block's scale (chunks
+  // 0-1: the step's first block, 2-3: its second); the W chunks are converted
+  // first, each A chunk just before its MFMAs.
+  auto mfmas = [&](const Frag& f, int m0_, int m1_, int first, int ks, int sl, bool live) {
+    if constexpr (EXACT) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      bb[j] = fp8x8_to_bf16(f.b[j][2 * t], f.b[j][2 * t + 1], e8m0_to_f32((f.sb[j] >> (t < 2 ? 0 : 8)) & 0xff));
+      for (int t = 0; t < 4; ++t) {
+        if (t * FM * FN < m0_ || t * FM * FN >= m1_) continue;
+        v8bf_t bb[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const v8bf_t ab =
-          fp8x8_to_bf16(f.a[i][2 * t], f.a[i][2 * t + 1], e8m0_to_f32((f.sa[i] >> (t < 2 ? 0 : 8)) & 0xff));
+        for (int j = 0; j < FN; ++j)
+          bb[j] = fp8x8_to_bf16(f.b[j][2 * t], f.b[j][2 * t + 1], e8m0_to_f32((f.sb[j] >> (t < 2 ? 0 : 8)) & 0xff));
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, bb[j], acc[i][j], 0, 0, 0);
-        if (first >= 0) {
-          const int slot = first + i * FN + j;
+        for (int i = 0; i < FM; ++i) {
+          const v8bf_t ab =
+              fp8x8_to_bf16(f.a[i][2 * t], f.a[i][2 * t + 1], e8m0_to_f32((f.sa[i] >> (t < 2 ? 0 : 8)) & 0xff));
 #pragma unroll
-          for (int d = 0; d < IPW; ++d)
-            if ((d * SLOTS) / IPW == slot) dma(ks, sl, d, live);
+          for (int j = 0; j < FN; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, bb[j], acc[i][j], 0, 0, 0);
+            if (first >= 0) dma_slot(t * FM * FN + i * FN + j - first, ks, sl, live);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int x = i * FN + j;
+          if (x < m0_ || x >= m1_) continue;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.sa[i], 0,
+                                                                       f.sb[j]);
+          if (first >= 0) dma_slot(x - first, ks, sl, live);
+          __builtin_amdgcn_sched_barrier(0);
+        }
     }
   };
 
-  // One stage kt (fragments in `cur`, the next stage's into `nxt`).
-  auto stage = [&](int kt, const Frag& cur, Frag& nxt) {
-    // Stage kt + NS - 1 refills the slot every wave finished reading before
-    // the previous barrier; its loads go between the first half's MFMAs.
+  // stage kt + 1 landed (vmcnt counts the loads issued after it), this wave's
+  // LDS reads are done (lgkmcnt 0); after the barrier everyone's are
+  auto stage_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW) & ~(15 << 8));
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // One stage kt: `f0` holds its first step's fragments; on return `f0`
+  // holds the next stage's. Stage kt + NS - 1 refills the slot every wave
+  // finished reading before the previous barrier; its loads go between the
+  // instructions before this stage's barrier.
+  Frag f0, f1;
+  auto stage = [&](int kt, Frag& fa, Frag& fb) {
     const int ks = kt + NS - 1;
     const bool live = ks < nkt;
     const int sl = ks % NS;
-    if constexpr (EXACT) {
-      exact_chunk(cur, 0, 0, ks, sl, live);
-      exact_chunk(cur, 1, FM * FN, ks, sl, live);
+    if constexpr (NKK == 1) {
+      // first half with the loads, barrier, the next stage's fragment reads
+      // under the second half
+      mfmas(fa, 0, MPS / 2, 0, ks, sl, live);
+      stage_barrier();
+      load_frags(kt + 1, 0, fb);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(fa, MPS / 2, MPS, -1, ks, sl, live);
     } else {
-#pragma unroll
-      for (int i = 0; i < FM / 2; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          mfma(cur, i, j);
-          const int slot = i * FN + j;
-#pragma unroll
-          for (int d = 0; d < IPW; ++d)
-            if ((d * SLOTS) / IPW == slot) dma(ks, sl, d, live);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    // stage kt + 1 landed (vmcnt counts the loads issued after it), this
-    // wave's LDS reads are done (lgkmcnt 0); after the barrier everyone's are
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW) & ~(15 << 8));
-    __builtin_amdgcn_s_barrier();
-    load_frags((kt + 1) % NS, (kt + 1) & 1, nxt);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (EXACT) {
-      exact_chunk(cur, 2, -1, ks, sl, live);
-      exact_chunk(cur, 3, -1, ks, sl, live);
-    } else {
-#pragma unroll
-      for (int i = FM / 2; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          mfma(cur, i, j);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      // step 0 (fragments in fa) with the loads while step 1's are read into
+      // fb; barrier; step 1 while the next stage's step 0 is read into fa
+      load_frags(kt, 1, fb);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(fa, 0, MPS, 0, ks, sl, live);
+      stage_barrier();
+      load_frags(kt + 1, 0, fa);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(fb, 0, MPS, -1, ks, sl, live);
     }
   };
 
@@ -294,16 +329,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
     for (int i = 0; i < IPW; ++i) dma(s, s, i, s < nkt);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW));
   __builtin_amdgcn_s_barrier();
-  Frag f0, f1;
   load_frags(0, 0, f0);
 
-  // two stages per trip so the fragment sets alternate without copies
-  int kt = 0;
-  for (; kt + 1 < nkt; kt += 2) {
-    stage(kt, f0, f1);
-    stage(kt + 1, f1, f0);
+  if constexpr (NKK == 1) {
+    // two stages per trip so the fragment sets alternate without copies
+    int kt = 0;
+    for (; kt + 1 < nkt; kt += 2) {
+      stage(kt, f0, f1);
+      stage(kt + 1, f1, f0);
+    }
+    if (kt < nkt) stage(kt, f0, f1);
+  } else {
+    for (int kt = 0; kt < nkt; ++kt) stage(kt, f0, f1);
   }
-  if (kt < nkt) stage(kt, f0, f1);
 
   // the empty loads past the last stage may still be in flight
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -356,11 +394,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool EXACT>
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool EXACT>
 static hipError_t launch_mx_dma_cfg(const GemmArgs& a, hipStream_t st) {
-  using C = MxDmaCfg<BM, BN, WM, WN, NS, EXACT>;
+  using C = MxDmaCfg<BM, BN, BK, WM, WN, NS, EXACT>;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_mx_dma_kernel<BM, BN, WM, WN, NS, EXACT>), dim3((unsigned)tiles), dim3(C::NT), 0, st, a);
+  hipLaunchKernelGGL((gemm_mx_dma_kernel<BM, BN, BK, WM, WN, NS, EXACT>), dim3((unsigned)tiles), dim3(C::NT), 0, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -379,8 +418,8 @@ static hipError_t launch_mx_dma(const GemmArgs& a, hipStream_t st) {
   // workgroup per CU) when they fill every CU; otherwise 128 x 128 tiles
   // (4 waves of 64 x 64, 68 KB, two workgroups per CU).
   const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big >= cu_count()) return launch_mx_dma_cfg<256, 256, 2, 4, 4, EXACT>(a, st);
-  return launch_mx_dma_cfg<128, 128, 2, 2, 4, EXACT>(a, st);
+  if (big >= cu_count()) return launch_mx_dma_cfg<256, 256, 64, 2, 4, 4, EXACT>(a, st);
+  return launch_mx_dma_cfg<128, 128, 64, 2, 2, 4, EXACT>(a, st);
 }
 
 hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st) {
