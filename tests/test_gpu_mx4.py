@@ -140,14 +140,39 @@ def test_gemm_mxfp4_bias(ops):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (33, 65, 96), (130, 260, 320), (64, 64, 1024), (300, 200, 2080),
-                                   (4096, 4096, 256)])
+                                   (257, 300, 1152), (4096, 4096, 256), (4000, 4312, 384)])
 def test_gemm_mxfp4_scaled_matrix_cores(ops, M, N, K):
     """e2m1 x e2m1 on the block-scaled matrix cores: products of e2m1 values
     span under 8 binades, so the hardware's alignment inside 8-product groups
-    drops nothing and the result meets the exact mode's bar."""
+    drops nothing and the result meets the exact mode's bar. K % 128 == 0 runs
+    the LDS-DMA kernel (the last two shapes its 256x256 tiles), the others the
+    register-staged one."""
     print_case("gemm mxfp4 scaled mfma", M, N, K)
     A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=M + 5 * N + 3 * K)
     _gemm_check(ops, A, W, "e2m1", "e2m1", mode=1)
+
+
+@pytest.mark.parametrize("M,N,K", [(130, 260, 1152), (520, 530, 640)])
+def test_gemm_mxfp4_scaled_both_kernels_same_bits(ops, M, N, K):
+    """K % 128 == 0: E8M0 rows padded to a dword take the LDS-DMA kernel, rows
+    of K/32 + 1 bytes (not a multiple of 4) the register-staged one. The same
+    instruction sums the same 64-deep steps in the same order, so the two
+    results are the same bits."""
+    print_case("gemm mxfp4 scaled, both kernels", M, N, K)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=M + N + 7 * K)
+    a = ops.qgemm_quantize_rows(dev(A), ops.FMT_MXFP4_E2M1, ops.GRAN_BLOCK32)
+    pw = ops.qgemm_prepack_weights(dev(W), ops.FMT_MXFP4_E2M1, ops.GRAN_BLOCK32)
+    assert a.mx_scales.stride(0) % 4 == 0
+    odd = torch.zeros((M, K // 32 + 1), dtype=torch.uint8, device="cuda")
+    odd[:, : K // 32].copy_(a.mx_scales[:, : K // 32])
+    b = ops.QuantizedRows(a.q, K, a.fmt, a.gran, None, None, odd)
+    got_dma = host(ops.qgemm_run_mx(a, pw, mode=1))
+    got_reg = host(ops.qgemm_run_mx(b, pw, mode=1))
+    qa, Ea = O.quantize_mxfp4(A)
+    qw, Ew = O.quantize_mxfp4(W)
+    ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew, "e2m1", "e2m1")
+    assert (np.abs(got_dma.astype(np.float64) - ref) <= MX_STOL * S).all()
+    assert np.array_equal(got_dma.view(np.uint32), got_reg.view(np.uint32))
 
 
 def test_gemm_mxfp4_scaled_rejects_mixed_formats(ops):
