@@ -79,7 +79,8 @@ def algorithmic(name, M, K, N, w4a8=False, fp4=False):
 def source_digest(w4a8=False):
     """Digest of the sources of the GEMM kernel a workload times."""
     h = hashlib.sha256()
-    for f in ("gemm_w4a8.hip" if w4a8 else "gemm.hip", "common.hpp", "kernels.hpp"):
+    srcs = ("gemm_w4a8.hip",) if w4a8 else ("gemm.hip", "gemm_mx_dma.hip")
+    for f in srcs + ("common.hpp", "kernels.hpp"):
         with open(os.path.join(ROOT, "block_scaled_quantized_qgemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
