@@ -330,6 +330,61 @@ def test_gemm_mx_both_scale_pitches(ops, M, N, K, mode):
         assert np.array_equal(got_dma.view(np.uint32), got_reg.view(np.uint32))
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (1, 300, 128), (2, 3, 192), (33, 17, 64), (129, 1, 448)])
+def test_gemm_mx_dma_small_and_ragged(ops, M, N, K, mode):
+    """K % 64 == 0 (the LDS-DMA kernel) with one-row, one-column and ragged
+    tiles: clamped A rows, padded weight rows, masked output columns."""
+    print_case("gemm mx dma small", M, N, K, "mode", mode)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=3 * M + N + K)
+    a = ops.qgemm_quantize_rows(dev(A), 2, 2)
+    pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
+    _mx_check(host(ops.qgemm_run_mx(a, pw, mode=mode)), A, W, MX_STOL if mode == 0 else MX_SCALED_STOL)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_gemm_mx_dma_ignores_row_padding(ops, mode):
+    """Activation rows wider than K whose padding holds e4m3 NaN codes (0x7f)
+    and E8M0 NaN bytes (0xff): the LDS-DMA kernel reads codes [0, K) and the
+    scale bytes of blocks [0, K/32) only, so the result is the unpadded one."""
+    M, N, K = 70, 90, 192
+    print_case("gemm mx dma padded rows", M, N, K, "mode", mode)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=77)
+    a = ops.qgemm_quantize_rows(dev(A), 2, 2)
+    pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
+    q = torch.full((M, K + 48), 0x7F, dtype=torch.uint8, device="cuda")
+    q[:, :K].copy_(a.q[:, :K])
+    e = torch.full((M, K // 32 + 6), 0xFF, dtype=torch.uint8, device="cuda")
+    e[:, : K // 32].copy_(a.mx_scales[:, : K // 32])
+    assert e.stride(0) % 4 == 0 and q.stride(0) % 16 == 0
+    b = ops.QuantizedRows(q, K, a.fmt, a.gran, None, None, e)
+    got = host(ops.qgemm_run_mx(b, pw, mode=mode))
+    assert np.isfinite(got).all()
+    _mx_check(got, A, W, MX_STOL if mode == 0 else MX_SCALED_STOL)
+    assert np.array_equal(got.view(np.uint32), host(ops.qgemm_run_mx(a, pw, mode=mode)).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt,mode", [(2, 0), (2, 1), (4, 1)])
+def test_gemm_mx_dma_bias(ops, fmt, mode):
+    """The float32 bias after the block-scaled sum on the LDS-DMA kernel
+    (e4m3 in both modes, e2m1 on the fp4 matrix cores)."""
+    M, N, K = 70, 200, 256
+    print_case("gemm mx dma bias", M, N, K, "fmt", fmt, "mode", mode)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=fmt * 10 + mode)
+    b = rng_for(N + fmt).normal(0.0, 10.0, size=N).astype(np.float32)
+    a = ops.qgemm_quantize_rows(dev(A), fmt, 2)
+    pw = ops.qgemm_prepack_weights(dev(W), fmt, 2)
+    got = host(ops.qgemm_run_mx(a, pw, mode=mode, bias=dev(b))).astype(np.float64)
+    quant = O.quantize_mxfp4 if fmt == 4 else O.quantize_mx
+    f = "e2m1" if fmt == 4 else "e4m3"
+    qa, Ea = quant(A)
+    qw, Ew = quant(W)
+    ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew, f, f)
+    ref = ref + b.astype(np.float64)[None, :]
+    tol = MX_SCALED_STOL if (mode == 1 and fmt == 2) else MX_STOL
+    assert (np.abs(got - ref) <= tol * S + F32_RTOL * np.abs(ref)).all()
+
+
 @pytest.mark.parametrize("K", [32, 64])
 def test_gemm_mx_modes_on_an_8_group_with_a_wide_exponent_spread(ops, K):
     """448 and 2^-6 in one group of 8 K: exact mode keeps the small product;
