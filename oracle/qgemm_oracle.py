@@ -598,3 +598,33 @@ def mx_gemm_ref_entries(qa, Ea, qw, Ew, rows, cols, fmt_a: str = "e4m3", fmt_w: 
     A = mx_dequantize(qa[rows], Ea[rows], fmt_a)
     W = mx_dequantize(qw[cols], Ew[cols], fmt_w)
     return np.einsum("ik,ik->i", A, W), np.einsum("ik,ik->i", np.abs(A), np.abs(W))
+
+
+# ----------------------------------------------------------------------------
+# Grouped (MoE) block-scaled GEMM
+# ----------------------------------------------------------------------------
+def mx_grouped_gemm_ref(qa, Ea, offsets, qw, Ew, fmt_a: str = "e4m3", fmt_w: str = "e4m3"):
+    """Grouped MX GEMM: the rows offsets[e] .. offsets[e+1] - 1 of A (the
+    tokens routed to expert e, concatenated in expert order) times expert e's
+    weights, each product the block-scaled product of ``mx_gemm_ref``.
+
+    [TL27] 6.2, MoE point 3: a grouped MX matmul takes A as the concatenation
+    of the experts' rows, with A's scales indexed by the concatenated row,
+    and one weight matrix per expert, with W's scales indexed by expert and
+    output column. qa [M_total, K] codes with Ea [M_total, K/32]; qw
+    [E, N, K] codes with Ew [E, N, K/32]; offsets: E + 1 non-decreasing row
+    offsets from 0 to M_total. Returns out and S (``mx_gemm_ref``'s error
+    basis), both [M_total, N] float64.
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E = len(offsets) - 1
+    M, N = qa.shape[0], qw.shape[1]
+    assert qw.shape[0] == E and Ew.shape[0] == E
+    assert offsets[0] == 0 and offsets[-1] == M and np.all(np.diff(offsets) >= 0)
+    out = np.zeros((M, N))
+    S = np.zeros((M, N))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            out[lo:hi], S[lo:hi] = mx_gemm_ref(qa[lo:hi], Ea[lo:hi], qw[e], Ew[e], fmt_a, fmt_w)
+    return out, S

@@ -729,3 +729,61 @@ def test_mxfp4_gemm_reference_against_exact_rationals():
             assert abs(Fraction(out[m, n]) - tot) <= Fraction(S[m, n]) * Fraction(1, 2 ** 50)
     packed = O.pack_int4_pairs(qa.astype(np.int8))
     assert np.array_equal(O.unpack_int4_pairs(packed, 96).astype(np.uint8) & 0xF, qa)
+
+
+# --------------------------------------------------------------------------
+# Grouped (MoE) MX GEMM ([TL27] 6.2, MoE point 3)
+# --------------------------------------------------------------------------
+def _grouped_inputs(sizes, N=6, K=96, seed=31):
+    M = int(sum(sizes))
+    E = len(sizes)
+    A, Wall = make_inputs("c5_mxfp8", M=M, K=K, N=E * N, seed=seed)
+    qa, Ea = O.quantize_mx(A)
+    qw, Ew = O.quantize_mx(Wall)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    return qa, Ea, qw.reshape(E, N, K), Ew.reshape(E, N, K // 32), offsets
+
+
+def test_mx_grouped_reference_equals_row_wise_expert_selection():
+    # An independent formulation: every row against every expert (no
+    # slicing), then each row keeps the product with its own expert, found
+    # by searching the offsets.
+    sizes = [3, 0, 5, 1, 4]
+    qa, Ea, qw, Ew, off = _grouped_inputs(sizes)
+    ref, S = O.mx_grouped_gemm_ref(qa, Ea, off, qw, Ew)
+    A = O.mx_dequantize(qa, Ea)
+    E, N, K = qw.shape
+    Wd = O.mx_dequantize(qw.reshape(E * N, K), Ew.reshape(E * N, K // 32)).reshape(E, N, K)
+    every = np.einsum("mk,enk->emn", A, Wd)
+    expert = np.searchsorted(off, np.arange(qa.shape[0]), side="right") - 1
+    direct = every[expert, np.arange(qa.shape[0])]
+    assert np.allclose(ref, direct, rtol=1e-13, atol=0)
+    assert np.allclose(S, np.einsum("mk,enk->emn", np.abs(A), np.abs(Wd))[expert, np.arange(qa.shape[0])],
+                       rtol=1e-13, atol=0)
+
+
+def test_mx_grouped_reference_catches_routing_and_scale_index_mistakes():
+    sizes = [4, 3, 5]
+    qa, Ea, qw, Ew, off = _grouped_inputs(sizes, seed=32)
+    ref, S = O.mx_grouped_gemm_ref(qa, Ea, off, qw, Ew)
+    # a row routed to the neighbouring expert (an off-by-one offset)
+    shifted = off.copy()
+    shifted[1] += 1
+    bad, _ = O.mx_grouped_gemm_ref(qa, Ea, shifted, qw, Ew)
+    assert not np.allclose(bad[4], ref[4], rtol=1e-3)
+    assert np.array_equal(bad[:4], ref[:4]) and np.array_equal(bad[5:], ref[5:])
+    # expert 1's weights scaled with expert 0's scales (a wrong expert index)
+    Ew_bad = Ew.copy()
+    Ew_bad[1] = Ew[0]
+    bad2, _ = O.mx_grouped_gemm_ref(qa, Ea, off, qw, Ew_bad)
+    assert np.array_equal(bad2[:4], ref[:4]) and not np.allclose(bad2[4:7], ref[4:7], rtol=1e-3)
+
+
+def test_mx_grouped_reference_single_and_empty_groups():
+    qa, Ea, qw, Ew, off = _grouped_inputs([7], seed=33)
+    ref, S = O.mx_grouped_gemm_ref(qa, Ea, off, qw, Ew)
+    dense, Sd = O.mx_gemm_ref(qa, Ea, qw[0], Ew[0])
+    assert np.array_equal(ref, dense) and np.array_equal(S, Sd)
+    qa, Ea, qw, Ew, off = _grouped_inputs([0, 0, 2, 0], seed=34)
+    ref, _ = O.mx_grouped_gemm_ref(qa, Ea, off, qw, Ew)
+    assert np.array_equal(ref, O.mx_gemm_ref(qa, Ea, qw[2], Ew[2])[0])
