@@ -45,6 +45,8 @@ SIGNATURES = {
                           c_vp, c_i64, c_int, c_vp, c_vp, c_size, c_vp]),
     "qgemm_run_mx": (c_int, [c_vp, c_i64, c_vp, c_i64, c_int, c_i64, ctypes.POINTER(WDesc), c_vp,
                              c_vp, c_i64, c_int, c_vp, c_vp, c_size, c_vp]),
+    "qgemm_run_mx_grouped": (c_int, [c_vp, c_i64, c_vp, c_i64, c_int, c_i64, c_vp, c_i64,
+                                     ctypes.POINTER(WDesc), c_vp, c_vp, c_i64, c_int, c_vp, c_vp, c_size, c_vp]),
     "qgemm_run_w4a8": (c_int, [c_vp, c_i64, c_vp, c_int, c_i64, ctypes.POINTER(WDesc), c_vp,
                                c_vp, c_i64, c_int, c_vp, c_vp, c_size, c_vp]),
 }

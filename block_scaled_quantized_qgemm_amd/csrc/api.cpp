@@ -17,6 +17,7 @@ constexpr int64_t kKPad = 256;   // packed columns are padded to this multiple (
 constexpr int64_t kSymKMax = 133144;   // 127*127*K < 2^31
 constexpr int64_t kAsymKMax = 66311;   // 255*127*K < 2^31
 constexpr int64_t kMaxRows = 0x7fffffff;
+constexpr int64_t kMaxExperts = 4096;  // grouped MX GEMM: experts per call
 constexpr int64_t kW4MaxRows = 16 * 65535;  // 16-row bands along the grid's second dimension
 constexpr int64_t kW4MaxK = int64_t(1) << 27;  // a 16-row block's codes (8 K_pad bytes) in one 32-bit range
 
@@ -328,6 +329,59 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
   g.ldo = ldo;
   g.bias = bias;
   hipError_t e = qg::launch_gemm_mx(g, mode, as_stream(stream));
+  return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
+}
+
+int qgemm_run_mx_grouped(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s, int a_fmt,
+                         int64_t M_total, const int64_t* offsets, int64_t E, const qgemm_wdesc* w_desc,
+                         const void* w_packed, float* out, int64_t ldo, int mode, const float* bias, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (mode != QGEMM_MX_EXACT && mode != QGEMM_MX_SCALED_MFMA) return QGEMM_E_MODE;
+  if (!is_mx_fmt(a_fmt)) return QGEMM_E_MODE;
+  int rc = check_desc(w_desc, -1);
+  if (rc != QGEMM_OK) return rc;
+  // one kernel serves the grouped call: e4m3 x e4m3 in either mode, e2m1 x e2m1 scaled
+  if (a_fmt != w_desc->fmt) return QGEMM_E_MODE;
+  const bool f4 = a_fmt == QGEMM_FMT_MXFP4_E2M1;
+  if (f4 && mode != QGEMM_MX_SCALED_MFMA) return QGEMM_E_MODE;
+  const int64_t N = w_desc->N, K = w_desc->K;
+  if (M_total < 0 || M_total > kMaxRows || E < 1 || E > kMaxExperts) return QGEMM_E_SHAPE;
+  if (K % (f4 ? 128 : 64) != 0) return QGEMM_E_SHAPE;
+  if (M_total == 0) return QGEMM_OK;
+  if (!a_codes || !a_e8m0 || !offsets || !w_packed || !out) return QGEMM_E_NULL;
+  if (lda < code_bytes(a_fmt, K) || lda_s < K / 32 || ldo < N) return QGEMM_E_SHAPE;
+  if (lda % 16 != 0 || !aligned(a_codes, 16) || lda_s % 4 != 0 || !aligned(a_e8m0, 4) || ldo % 4 != 0 ||
+      !aligned(out, 16) || !aligned(w_packed, 256) || !aligned(offsets, 8) || (bias && !aligned(bias, 4)))
+    return QGEMM_E_ALIGN;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+
+  const uint8_t* base = (const uint8_t*)w_packed;
+  qg::GemmArgs g{};
+  g.a = a_codes;
+  g.lda = lda;
+  g.ea = a_e8m0;
+  g.lda_s = lda_s;
+  g.w = base + w_desc->codes_off;
+  g.ew = base + w_desc->scales_off;
+  g.a_fp4 = f4;
+  g.w_fp4 = f4;
+  g.M = M_total;
+  g.N = N;
+  g.K = K;
+  g.K_pad = w_desc->K_pad;
+  g.out = out;
+  g.ldo = ldo;
+  g.bias = bias;
+  g.groups = offsets;
+  g.num_groups = (int)E;
+  g.w_stride = w_desc->bytes;
+  // the kernel addresses one 256-row band of A and one expert's weights with
+  // 32-bit byte offsets
+  if (!qg::mx_dma_eligible(g, mode)) return QGEMM_E_SHAPE;
+  hipError_t e = qg::launch_gemm_mx_grouped(g, mode, as_stream(stream));
   return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
 }
 

@@ -100,7 +100,60 @@ struct MxDmaCfg {
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int NS, bool EXACT, bool F4>
+// Grouped GEMM: the tile-rows of all experts, in expert order. Expert e owns
+// rows [off[e], off[e+1]) of A (offsets clamped to [0, M]; a decreasing pair
+// is empty) and ceil(rows / BM) tile-rows. Wave-cooperative, 64 experts per
+// pass (an inclusive scan of the tile-row counts across the lanes); every
+// lane returns the total count and, for tile-row tm, its expert, first row
+// and the expert's row end (e = -1 when tm is not below the total).
+struct GroupTile {
+  int e;
+  int64_t row0, row_end;
+};
+__device__ inline int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <int BM>
+__device__ inline int group_tiles(const int64_t* off, int E, int64_t M, int tm, GroupTile& gt) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  gt.e = -1;
+  gt.row0 = gt.row_end = 0;
+  for (int c = 0; c < E; c += 64) {
+    const int e = c + lane;
+    int64_t lo = 0, hi = 0;
+    if (e < E) {
+      lo = min(max(off[e], (int64_t)0), M);
+      hi = min(max(off[e + 1], (int64_t)0), M);
+      hi = hi < lo ? lo : hi;
+    }
+    const int cnt = (int)((hi - lo + BM - 1) / BM);
+    int inc = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += t;
+    }
+    const int excl = inc - cnt;
+    const bool mine = e < E && tm >= base + excl && tm < base + inc;
+    const unsigned long long ball = __ballot(mine);
+    if (ball) {
+      const int L = __ffsll((long long)ball) - 1;
+      gt.e = c + L;
+      gt.row0 = __shfl(lo + (int64_t)(tm - base - excl) * BM, L, 64);
+      gt.row_end = __shfl(hi, L, 64);
+    }
+    base += __shfl(inc, 63, 64);
+  }
+  // wave-uniform: keep them in scalar registers
+  gt.e = __builtin_amdgcn_readfirstlane(gt.e);
+  gt.row0 = uniform64(gt.row0);
+  gt.row_end = uniform64(gt.row_end);
+  return __builtin_amdgcn_readfirstlane(base);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool EXACT, bool F4, bool GROUPED>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   using C = MxDmaCfg<BM, BN, BK, WM, WN, NS, EXACT, F4>;
   constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, NKK = C::NKK, MPS = C::MPS;
@@ -115,23 +168,37 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
 
   // Tile order (as the int8 GEMM): workgroups are dealt round-robin over the 8
   // XCDs; each XCD gets a contiguous run of tiles, walked in groups of 8
-  // tile-rows so that neighbours share A rows and W columns in its L2.
-  const int tiles_m = (int)((p.M + BM - 1) / BM);
+  // tile-rows so that neighbours share A rows and W columns in its L2. The
+  // grouped GEMM lists the experts' tile-rows one after the other; the grid
+  // is an upper bound on the tiles, and the workgroups past the real count
+  // leave before touching memory or a barrier.
+  GroupTile gt{0, 0, p.M};
+  const int tiles_m =
+      GROUPED ? group_tiles<BM>(p.groups, p.num_groups, p.M, -1, gt) : (int)((p.M + BM - 1) / BM);
   const int tiles_n = (int)((p.N + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
   int pid = blockIdx.x;
+  if (GROUPED && pid >= ntiles) return;
   {
     const int per = ntiles / 8;
     if (per > 0 && pid < per * 8) pid = (pid % 8) * per + pid / 8;
   }
   constexpr int GROUP = 8;
-  const int group_tiles = GROUP * tiles_n;
-  const int g = pid / group_tiles;
-  const int first_m = g * GROUP;
+  const int group_size = GROUP * tiles_n;
+  const int first_m = pid / group_size * GROUP;
   const int gsize = min(tiles_m - first_m, GROUP);
-  const int tile_m = first_m + (pid % group_tiles) % gsize;
-  const int tile_n = (pid % group_tiles) / gsize;
-  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
+  const int tile_m = first_m + (pid % group_size) % gsize;
+  const int tile_n = (pid % group_size) / gsize;
+  if (GROUPED) {
+    group_tiles<BM>(p.groups, p.num_groups, p.M, tile_m, gt);
+  } else {
+    gt.row0 = (int64_t)tile_m * BM;
+  }
+  const int64_t m0 = gt.row0, m_end = gt.row_end, n0 = (int64_t)tile_n * BN;
+  // the expert's weights, scales and bias (expert 0 for the plain GEMM)
+  const uint8_t* const wexp = GROUPED ? p.w + gt.e * p.w_stride : p.w;
+  const uint8_t* const ewexp = GROUPED ? p.ew + gt.e * p.w_stride : p.ew;
+  const float* const bias = GROUPED && p.bias ? p.bias + gt.e * p.N : p.bias;
   const int nkt = (int)(p.K / C::KPS);  // every stage inside K (the launcher checks K % KPS == 0)
   const int64_t kbytes = F4 ? p.K / 2 : p.K;  // code bytes of a row's K
   const int64_t ldw = F4 ? p.K_pad / 2 : p.K_pad, ldws = p.K_pad / 32;
@@ -153,11 +220,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   // the next row fall there, and they are never used), so nothing past them
   // is read. Stages past the last one get an empty range: their loads move no
   // data and still count in vmcnt.
-  const int64_t last_a_row = min((int64_t)BM - 1, p.M - 1 - m0);
+  const int64_t last_a_row = min((int64_t)BM - 1, m_end - 1 - m0);
   const uint8_t* const abase = p.a + m0 * p.lda;
-  const uint8_t* const wbase = p.w + n0 * ldw;
+  const uint8_t* const wbase = wexp + n0 * ldw;
   const uint8_t* const eabase = p.ea + m0 * p.lda_s;
-  const uint8_t* const ewbase = p.ew + n0 * ldws;
+  const uint8_t* const ewbase = ewexp + n0 * ldws;
   const uint32_t nrec_a = (uint32_t)(last_a_row * p.lda + kbytes);
   const uint32_t nrec_w = (uint32_t)(BN * ldw);
   const uint32_t nrec_ea = (uint32_t)(last_a_row * p.lda_s + ((p.K / 32 + 3) & ~(int64_t)3));
@@ -370,10 +437,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   const int cq = (lane % LPR) * 4;
   const int64_t nq = n0 + wn * TN + cq;
   float bs4[4] = {0.f, 0.f, 0.f, 0.f};
-  if (p.bias) {
+  if (bias) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      if (nq + t < p.N) bs4[t] = p.bias[nq + t];
+      if (nq + t < p.N) bs4[t] = bias[nq + t];
   }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -390,8 +457,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
       const int r = pass * RPI + lane / LPR;
       const int64_t m = m0 + wm * TM + i * 32 + r;
       v4f y = *reinterpret_cast<const v4f*>(wreg + (r * RS + cq) * 4);
-      if (m < p.M && nq < p.N) {
-        if (p.bias) {
+      if (m < m_end && nq < p.N) {
+        if (bias) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) y[t] = y[t] + bs4[t];  // the bias after the scales, in float32
         }
@@ -406,12 +473,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NS, bool EXACT, bool F4>
+template <int BM, int BN, int BK, int WM, int WN, int NS, bool EXACT, bool F4, bool GROUPED>
 static hipError_t launch_mx_dma_cfg(const GemmArgs& a, hipStream_t st) {
   using C = MxDmaCfg<BM, BN, BK, WM, WN, NS, EXACT, F4>;
-  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_mx_dma_kernel<BM, BN, BK, WM, WN, NS, EXACT, F4>), dim3((unsigned)tiles), dim3(C::NT), 0,
-                     st, a);
+  // grouped: each expert adds at most one partial tile-row
+  const int64_t tiles = ((a.M + BM - 1) / BM + (GROUPED ? a.num_groups : 0)) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_mx_dma_kernel<BM, BN, BK, WM, WN, NS, EXACT, F4, GROUPED>), dim3((unsigned)tiles),
+                     dim3(C::NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -427,20 +495,27 @@ bool mx_dma_eligible(const GemmArgs& a, int mode) {
          256 * a.K_pad < (int64_t(1) << 31);
 }
 
-template <bool EXACT, bool F4>
+template <bool EXACT, bool F4, bool GROUPED>
 static hipError_t launch_mx_dma(const GemmArgs& a, hipStream_t st) {
   // 256 x 256 tiles (8 waves of 128 x 64, a 4-stage ring, one workgroup per
   // CU) when they fill every CU; otherwise 128 x 128 tiles (4 waves of
   // 64 x 64, two workgroups per CU). Stages of 64 bytes per row: 64 K of
   // e4m3, 128 K of e2m1.
   const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big >= cu_count()) return launch_mx_dma_cfg<256, 256, 64, 2, 4, 4, EXACT, F4>(a, st);
-  return launch_mx_dma_cfg<128, 128, 64, 2, 2, 4, EXACT, F4>(a, st);
+  if (big >= cu_count()) return launch_mx_dma_cfg<256, 256, 64, 2, 4, 4, EXACT, F4, GROUPED>(a, st);
+  return launch_mx_dma_cfg<128, 128, 64, 2, 2, 4, EXACT, F4, GROUPED>(a, st);
 }
 
-hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st) {
-  if (a.a_fp4) return launch_mx_dma<false, true>(a, st);
-  return mode == 0 ? launch_mx_dma<true, false>(a, st) : launch_mx_dma<false, false>(a, st);
+template <bool GROUPED>
+static hipError_t launch_mode(const GemmArgs& a, int mode, hipStream_t st) {
+  if (a.a_fp4) return launch_mx_dma<false, true, GROUPED>(a, st);
+  return mode == 0 ? launch_mx_dma<true, false, GROUPED>(a, st) : launch_mx_dma<false, false, GROUPED>(a, st);
+}
+
+hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st) { return launch_mode<false>(a, mode, st); }
+
+hipError_t launch_gemm_mx_grouped(const GemmArgs& a, int mode, hipStream_t st) {
+  return launch_mode<true>(a, mode, st);
 }
 
 }  // namespace qg

@@ -62,6 +62,12 @@ struct GemmArgs {
   void* out;
   int64_t ldo;
   const float* bias;    // [N] added to each output row after the scales (float32), or null
+  // grouped MX GEMM: rows groups[e] .. groups[e + 1] - 1 of A belong to
+  // expert e, whose packed weights start w_stride bytes after expert e - 1's
+  // (w and ew point into expert 0's); the bias is [num_groups][N]
+  const int64_t* groups;
+  int num_groups;
+  int64_t w_stride;
 };
 
 // qgemm_run: int8 GEMM + epilogue. out_type: 0 f32, 1 bf16, 2 i32 (no bias).
@@ -74,6 +80,9 @@ hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st);
 // activation scale rows), and its launcher.
 bool mx_dma_eligible(const GemmArgs& a, int mode);
 hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st);
+// qgemm_run_mx_grouped: the same kernel over E experts' row groups (a.M is
+// the total row count, a.groups device offsets; mx_dma_eligible must hold).
+hipError_t launch_gemm_mx_grouped(const GemmArgs& a, int mode, hipStream_t st);
 // qgemm_run_w4a8: int8 activations x int4 weights, per-group scales inside
 // the K loop, float32 sums. out_type: 0 f32, 1 bf16.
 hipError_t launch_gemm_w4a8(const GemmArgs& a, int out_type, hipStream_t st);

@@ -152,6 +152,23 @@ class PackedWeights:
         return self.packed[d.colsum_off: d.colsum_off + 4 * d.N_pad].view(torch.int32)
 
 
+@dataclass
+class PackedExperts:
+    """E experts' prepared weights back to back (expert e at byte
+    e * desc.bytes) and the descriptor they share."""
+    packed: torch.Tensor
+    desc: L.WDesc
+    E: int
+
+    @property
+    def N(self) -> int:
+        return int(self.desc.N)
+
+    def expert(self, e: int) -> PackedWeights:
+        nb = int(self.desc.bytes)
+        return PackedWeights(self.packed[e * nb:(e + 1) * nb], self.desc)
+
+
 def qgemm_workspace_bytes(rows: int, K: int, fmt: int, gran: int) -> int:
     return int(L.load().qgemm_workspace_bytes(rows, K, fmt, gran))
 
@@ -237,6 +254,25 @@ def qgemm_prepack_weights(w: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = 
     return PackedWeights(packed, desc)
 
 
+def qgemm_prepack_experts(w: torch.Tensor, fmt: int = FMT_MXFP8_E4M3, stream=None) -> PackedExperts:
+    """Prepare E experts' float32 [E, N, K] MX weights into one buffer for
+    qgemm_run_mx_grouped (one qgemm_prepack_weights call per expert slice)."""
+    lib = L.load()
+    assert w.dtype == torch.float32 and w.dim() == 3 and w.stride(2) == 1
+    E, N, K = w.shape
+    dev = w.device
+    nb = qgemm_packed_weight_bytes(N, K, fmt, GRAN_BLOCK32)
+    if nb == 0:
+        raise QgemmError("qgemm_prepack_weights", -2)
+    packed = torch.empty((E * nb,), dtype=torch.uint8, device=dev)
+    desc = L.WDesc()
+    for e in range(E):
+        st = lib.qgemm_prepack_weights(_ptr(w[e]), N, K, w.stride(1), fmt, GRAN_BLOCK32, _ptr(packed[e * nb:]), nb,
+                                       ctypes.byref(desc), None, 0, ctypes.c_void_p(_stream(dev, stream)))
+        _check("qgemm_prepack_weights", st)
+    return PackedExperts(packed, desc, E)
+
+
 def _alloc_out(M: int, N: int, dtype, dev):
     buf = torch.empty((M, _round_up(N, 8)), dtype=dtype, device=dev)
     return buf
@@ -279,6 +315,28 @@ def qgemm_run_mx(a: QuantizedRows, w: PackedWeights, out: Optional[torch.Tensor]
                           ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0), mode,
                           _bias_ptr(bias, N), None, 0, ctypes.c_void_p(_stream(dev, stream)))
     _check("qgemm_run_mx", st)
+    return out[:, :N]
+
+
+def qgemm_run_mx_grouped(a: QuantizedRows, w: PackedExperts, offsets: torch.Tensor,
+                         out: Optional[torch.Tensor] = None, mode: int = MX_EXACT,
+                         bias: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Grouped (MoE) block-scaled GEMM: rows offsets[e] .. offsets[e+1] - 1
+    of A times expert e's weights (offsets: device int64 [E + 1]); float32
+    out, plus an optional float32 bias [E, N]. Returns out[:, :N]."""
+    lib = L.load()
+    dev = a.q.device
+    N = w.N
+    assert offsets.dtype == torch.int64 and offsets.dim() == 1 and offsets.numel() == w.E + 1
+    assert offsets.is_contiguous() and offsets.device == dev
+    if bias is not None:
+        assert bias.dtype == torch.float32 and bias.shape == (w.E, N) and bias.is_contiguous()
+    if out is None:
+        out = _alloc_out(a.M, N, torch.float32, dev)
+    st = lib.qgemm_run_mx_grouped(_ptr(a.q), a.q.stride(0), _ptr(a.mx_scales), a.mx_scales.stride(0), a.fmt, a.M,
+                                  _ptr(offsets), w.E, ctypes.byref(w.desc), _ptr(w.packed), _ptr(out), out.stride(0),
+                                  mode, _ptr(bias), None, 0, ctypes.c_void_p(_stream(dev, stream)))
+    _check("qgemm_run_mx_grouped", st)
     return out[:, :N]
 
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define QGEMM_ABI_VERSION 5
+#define QGEMM_ABI_VERSION 6
 #define QGEMM_WDESC_MAGIC 0x51474d57u /* "WMGQ" */
 
 /* Status codes. Every entry point returns one of these. */
@@ -371,6 +371,47 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
                  float* out, int64_t ldo, int mode, const float* bias,
                  void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/*
+ * qgemm_run_mx_grouped -- grouped (MoE) block-scaled GEMM: the rows of A
+ * routed to expert e, stored one expert after the other, times expert e's
+ * weights ([TL27] 6.2, MoE point 3: A is the concatenation of the experts'
+ * rows, its scales indexed by the concatenated row; one weight matrix per
+ * expert, its scales indexed by expert and output column).
+ *
+ *   out[m,n] = qgemm_run_mx's out[m,n] for row m of A against the weights of
+ *              the expert e whose rows offsets[e] .. offsets[e+1] - 1 hold m,
+ *              plus bias[e][n] when bias != NULL.
+ *   Row m's result does not depend on the other rows or experts: it is the
+ *   bits qgemm_run_mx gives for that row and expert on this kernel.
+ *
+ *   a_codes, lda, a_e8m0, lda_s, a_fmt, out, ldo, mode: as qgemm_run_mx,
+ *            for M_total rows; in addition lda_s % 4 == 0 and a_e8m0 4-byte
+ *            aligned (QGEMM_E_ALIGN), and K % 64 == 0 for e4m3, K % 128 == 0
+ *            for e2m1 (QGEMM_E_SHAPE). e2m1 runs in QGEMM_MX_SCALED_MFMA only.
+ *   M_total  rows of A and out, >= 0 (0: nothing is launched).
+ *   offsets  device int64 [E + 1], non-decreasing, offsets[0] = 0 and
+ *            offsets[E] = M_total, 8-byte aligned. It stays on the device (a
+ *            router on the GPU needs no host copy). Values outside
+ *            [0, M_total] are clamped and a decreasing pair is an empty
+ *            group, so nothing outside the buffers is accessed; the results
+ *            are then unspecified.
+ *   E        number of experts, 1 .. 4096 (QGEMM_E_SHAPE).
+ *   w_desc   descriptor of one expert's weights (QGEMM_FMT_MXFP8_E4M3 or
+ *            QGEMM_FMT_MXFP4_E2M1, N x K), shared by all experts.
+ *   w_packed the E experts' prepared weights back to back: expert e's at
+ *            w_packed + e * w_desc->bytes (each written by
+ *            qgemm_prepack_weights with w_desc's shape and format); 256-byte
+ *            aligned.
+ *   bias     device float32 [E][N] or NULL.
+ *   workspace unused by this version (pass NULL, 0).
+ */
+int qgemm_run_mx_grouped(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int64_t lda_s, int a_fmt,
+                         int64_t M_total, const int64_t* offsets, int64_t E,
+                         const qgemm_wdesc* w_desc, const void* w_packed,
+                         float* out, int64_t ldo, int mode, const float* bias,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * qgemm_run_w4a8 -- int8 activations times int4 weights with one scale per

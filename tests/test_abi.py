@@ -17,6 +17,7 @@ HEADER = os.path.join(ROOT, "include", "qgemm.h")
 OK, E_NULL, E_SHAPE, E_MODE, E_ALIGN, E_OVERFLOW, E_DEVICE, E_DESC, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8
 INT8, UINT8, MX, INT4, MX4 = 0, 1, 2, 3, 4
 TENSOR, ROW, BLK, G64 = 0, 1, 2, 3
+ABI = 6
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.qgemm_abi_version() == 5
+    assert lib.qgemm_abi_version() == ABI
     for s in range(-9, 1):
         assert lib.qgemm_status_string(s).startswith(b"QGEMM_")
     assert lib.qgemm_status_string(-100) == b"unknown qgemm status"
@@ -104,7 +105,7 @@ def test_quantize_rows_validation(lib):
 
 
 def _wdesc(**kw):
-    d = L.WDesc(magic=0x51474D57, version=5, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=ABI, fmt=INT8, gran=ROW, N=100, K=300, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 512, colsum_off=256 * 512 + 1024, bytes=256 * 512 + 2048)
     for k, v in kw.items():
         setattr(d, k, v)
@@ -150,7 +151,7 @@ def test_run_validation(lib):
 
 def test_run_mx_validation(lib):
     nb = lib.qgemm_packed_weight_bytes(100, 320, MX, BLK)
-    d = L.WDesc(magic=0x51474D57, version=5, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=ABI, fmt=MX, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 512, colsum_off=-1, bytes=nb)
     call = lambda **kw: lib.qgemm_run_mx(kw.get("a", FAKE), kw.get("lda", 320), kw.get("e", FAKE),
                                          kw.get("ldas", 10), kw.get("af", MX), kw.get("M", 4),
@@ -170,10 +171,51 @@ def test_run_mx_validation(lib):
     assert call(af=MX4, lda=160, M=0, a=None, e=None, out=None) == OK
     assert call(af=MX4, lda=144) == E_SHAPE               # packed e2m1 rows need K / 2 bytes
     nb4 = lib.qgemm_packed_weight_bytes(100, 320, MX4, BLK)
-    d4 = L.WDesc(magic=0x51474D57, version=5, fmt=MX4, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
+    d4 = L.WDesc(magic=0x51474D57, version=ABI, fmt=MX4, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
                  codes_off=0, scales_off=256 * 256, colsum_off=-1, bytes=nb4)
     assert call(d=d4, mode=1) == E_MODE
     assert call(d=_w4desc()) == E_DESC                    # int4 weights are not MX
+
+
+def _mxdesc(N=100, K=320, fmt=MX):
+    nb = L.load().qgemm_packed_weight_bytes(N, K, fmt, BLK)
+    kp = (K + 255) // 256 * 256
+    np_ = (N + 255) // 256 * 256
+    cb = kp // 2 if fmt == MX4 else kp
+    return L.WDesc(magic=0x51474D57, version=ABI, fmt=fmt, gran=BLK, N=N, K=K, N_pad=np_, K_pad=kp,
+                   codes_off=0, scales_off=(np_ * cb + 255) // 256 * 256, colsum_off=-1, bytes=nb)
+
+
+def _grouped(lib, **kw):
+    d = kw.get("d", _mxdesc(K=kw.get("K", 320)))
+    return lib.qgemm_run_mx_grouped(kw.get("a", FAKE), kw.get("lda", d.K), kw.get("e", FAKE), kw.get("ldas", 12),
+                                    kw.get("af", MX), kw.get("M", 40), kw.get("off", FAKE), kw.get("E", 3),
+                                    ctypes.byref(d), kw.get("w", FAKE), kw.get("out", FAKE), kw.get("ldo", d.N),
+                                    kw.get("mode", 0), kw.get("bias", None), None, 0, None)
+
+
+def test_run_mx_grouped_validation(lib):
+    assert _grouped(lib, d=_wdesc()) == E_DESC                 # an int8 descriptor
+    assert _grouped(lib, mode=2) == E_MODE
+    assert _grouped(lib, af=INT8) == E_MODE
+    assert _grouped(lib, af=MX4) == E_MODE                     # a format other than the weights'
+    d4 = _mxdesc(K=384, fmt=MX4)
+    assert _grouped(lib, d=d4, af=MX4, lda=192, ldas=12, mode=0) == E_MODE   # e2m1 runs scaled only
+    assert _grouped(lib, E=0) == E_SHAPE
+    assert _grouped(lib, E=4097) == E_SHAPE
+    assert _grouped(lib, M=-1) == E_SHAPE
+    assert _grouped(lib, d=_mxdesc(K=96), lda=96, ldas=4) == E_SHAPE         # K % 64 != 0 (e4m3)
+    assert _grouped(lib, d=_mxdesc(K=320, fmt=MX4), af=MX4, lda=160, ldas=12, mode=1) == E_SHAPE  # K % 128
+    assert _grouped(lib, M=0, a=None, e=None, off=None, out=None) == OK
+    assert _grouped(lib, off=None) == E_NULL
+    assert _grouped(lib, w=None) == E_NULL
+    assert _grouped(lib, ldas=9) == E_SHAPE
+    assert _grouped(lib, ldas=14) == E_ALIGN                   # scale rows are read a dword at a time
+    assert _grouped(lib, e=FAKE + 2) == E_ALIGN
+    assert _grouped(lib, off=FAKE + 4) == E_ALIGN
+    assert _grouped(lib, lda=328) == E_ALIGN
+    assert _grouped(lib, w=FAKE + 16) == E_ALIGN
+    assert _grouped(lib, bias=FAKE + 2) == E_ALIGN
 
 
 def test_rmsnorm_quantize_validation(lib):
@@ -220,7 +262,7 @@ def test_prepack_validation(lib):
 
 def _w4desc(**kw):
     nb = 256 * 256 + 4 * 256 * 8
-    d = L.WDesc(magic=0x51474D57, version=5, fmt=INT4, gran=G64, N=100, K=300, N_pad=256, K_pad=512,
+    d = L.WDesc(magic=0x51474D57, version=ABI, fmt=INT4, gran=G64, N=100, K=300, N_pad=256, K_pad=512,
                 codes_off=0, scales_off=256 * 256, colsum_off=-1, bytes=nb)
     for k, v in kw.items():
         setattr(d, k, v)
@@ -265,6 +307,7 @@ def test_no_device_is_an_error_not_a_fallback(lib):
     assert _q(lib) == E_DEVICE
     assert _run(lib, _wdesc()) == E_DEVICE
     assert _run4(lib, _w4desc()) == E_DEVICE
+    assert _grouped(lib) == E_DEVICE
     assert lib.qgemm_rmsnorm_quantize_rows(FAKE, 4, 64, 64, FAKE, 1e-6, INT8, ROW, FAKE, 64, FAKE, None,
                                            None) == E_DEVICE
 
