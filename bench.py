@@ -2,7 +2,8 @@
 
 A step is one pass of the whole hot path over one batch: quantize the float32
 activations (qgemm_quantize_rows) and run the GEMM with its fused epilogue
-(qgemm_run / qgemm_run_mx, or qgemm_run_w4a8 with --w4a8). Weights are prepared once beforehand (offline, as
+(qgemm_run / qgemm_run_mx, qgemm_run_w4a8 with --w4a8, or qgemm_run_mx_grouped for the
+grouped MoE workload). Weights are prepared once beforehand (offline, as
 on the pages) and every input is resident in HBM before the timed region.
 Activation / weight / output buffers rotate over enough copies that the
 256 MB Infinity Cache cannot hold the working set.
@@ -32,6 +33,7 @@ PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X (the exact MX mode runs on 
 PEAK_FP4_TFLOPS = 10100.0  # dense fp4 / fp6 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0     # HBM3E
 MALL_BYTES = 256 << 20
+MOE = ("c6_moe_mxfp8",)   # grouped (MoE) workloads: bench.main_grouped
 
 # name -> (activation format, granularity, weight granularity, output type, headline unit)
 WORKLOADS = {
@@ -40,6 +42,7 @@ WORKLOADS = {
     "c3_asym_uint8": ("uint8_asym", "row", "channel", "bf16", "TOPS"),
     "c4_decode": ("int8_sym", "row", "channel", "f32", "GB/s"),
     "c5_mxfp8": ("mxfp8", "block32", "block32", "f32", "TFLOPS"),
+    "c6_moe_mxfp8": ("mxfp8", "block32", "block32", "f32", "TFLOPS"),
 }
 DESCRIPTION = {
     "c1_tiny": "64x256x64 per-tensor int8 A, per-channel int8 W, fp32 out",
@@ -47,6 +50,8 @@ DESCRIPTION = {
     "c3_asym_uint8": "2048x4096x11008 per-token asymmetric uint8 A with zero point, per-channel int8 W, bf16 out",
     "c4_decode": "8x4096x14336 decode-shaped, per-token int8 A quantized on the fly, prepacked int8 W, fp32 out",
     "c5_mxfp8": "8192x8192x8192 MXFP8 (e4m3 + E8M0 per 32 K) A and W, fp32 out",
+    "c6_moe_mxfp8": "grouped (MoE) MXFP8: 8 experts, 8192 routed rows of K=4096 split unevenly over them, "
+                    "N=4096 per expert, fp32 out",
 }
 
 
@@ -173,6 +178,166 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False, fp4=False):
             "sample": f"{sample}; {reps} passes in {el:.1f} s"}
 
 
+def timed(fn, steps, eager):
+    """Milliseconds per call of fn(i), i = 0 .. steps-1, on the current stream,
+    and the host wall time. The calls are captured once into a HIP graph and
+    replayed (eager: launched from Python), bracketed by events on the stream."""
+    import torch
+    if eager:
+        run = lambda: [fn(i) for i in range(steps)]  # noqa: E731
+    else:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                fn(i)
+        run = graph.replay
+        run()  # one untimed replay
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    run()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps, time.perf_counter() - t0
+
+
+def calibration_copy(mib, dev):
+    """A plain device copy of known size after the timed region (its counters
+    calibrate the GEMM's FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    nb = mib << 20
+    src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def cpu_baseline_grouped(A, W, sizes, fp4, budget_s=10.0):
+    """The oracle's grouped reference, untuned, on a bounded sample: up to 16
+    rows of every expert against the first 1024 output columns of its weights
+    (prepared outside the timing)."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    quant = O.quantize_mxfp4 if fp4 else O.quantize_mx
+    f = "e2m1" if fp4 else "e4m3"
+    W = np.ascontiguousarray(W[:, :1024])
+    E, N, K = W.shape
+    qw, Ew = quant(W.reshape(E * N, K))
+    qw, Ew = qw.reshape(E, N, K), Ew.reshape(E, N, K // 32)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    take = [np.arange(off[e], off[e] + min(16, sizes[e])) for e in range(E)]
+    As = A[np.concatenate(take)]
+    offs = np.concatenate([[0], np.cumsum([len(t) for t in take])])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        qa, Ea = quant(As)
+        O.mx_grouped_gemm_ref(qa, Ea, offs, qw, Ew, f, f)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    return {"value": 2.0 * len(As) * N * K * reps / el / 1e12, "unit": "TFLOPS", "cores": int(cores),
+            "kind": "oracle", "sample": f"up to 16 rows of each expert ({len(As)} rows) against {N} columns of its weights "
+                                        f"(weights prepared outside the timing); {reps} passes in {el:.1f} s"}
+
+
+def main_grouped(args):
+    """The grouped (MoE) MX workload: quantize the routed rows, then one
+    grouped GEMM over all experts."""
+    import numpy as np
+    import torch
+    from block_scaled_quantized_qgemm_amd import ops
+    from block_scaled_quantized_qgemm_amd.inputs import make_moe_inputs
+
+    name = args.workload
+    fp4 = args.mx_format == "e2m1"
+    mx_mode = ops.MX_EXACT if args.mx_mode == "exact" else ops.MX_SCALED_MFMA
+    if fp4 and mx_mode == ops.MX_EXACT:
+        print("bench.py: the grouped GEMM runs e2m1 on the block-scaled matrix cores only "
+              "(--mx-mode scaled-mfma)", file=sys.stderr)
+        sys.exit(2)
+    if args.fused or args.w4a8:
+        print("bench.py: --fused and --w4a8 do not apply to the grouped workload", file=sys.stderr)
+        sys.exit(2)
+    fmt = ops.FMT_MXFP4_E2M1 if fp4 else ops.FMT_MXFP8_E4M3
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A_np, W_np, sizes = make_moe_inputs(name)
+    E, N, K = W_np.shape
+    M = A_np.shape[0]
+    A0 = torch.from_numpy(A_np).to(dev)
+    W0 = torch.from_numpy(W_np).to(dev)
+    w0 = ops.qgemm_prepack_experts(W0, fmt)
+    del W0
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)).to(dev)
+    torch.cuda.synchronize()
+
+    ops_count = 2.0 * M * N * K
+    cb = 0.5 if fp4 else 1.0
+    w_bytes = E * (cb * N * K + N * (K // 32))
+    step_bytes = 4.0 * M * K + w_bytes + 4.0 * M * N
+    set_bytes = A0.numel() * 4 + w0.packed.numel() + M * N * 4 + M * K
+    nsets = args.rotate or max(1, min(64, math.ceil(3 * MALL_BYTES / set_bytes)))
+    sets = []
+    for i in range(nsets):
+        Ai = A0 if i == 0 else A0.clone()
+        wi = w0 if i == 0 else ops.PackedExperts(w0.packed.clone(), w0.desc, E)
+        qi = ops.qgemm_quantize_rows(Ai, fmt, ops.GRAN_BLOCK32)
+        oi = torch.empty((M, N), dtype=torch.float32, device=dev)
+        sets.append((Ai, wi, qi, oi))
+    torch.cuda.synchronize()
+
+    def quantize(i):
+        Ai, wi, qi, oi = sets[i % nsets]
+        ops.qgemm_quantize_rows(Ai, fmt, ops.GRAN_BLOCK32, out=qi)
+
+    def gemm(i):
+        Ai, wi, qi, oi = sets[i % nsets]
+        ops.qgemm_run_mx_grouped(qi, wi, offsets, out=oi, mode=mx_mode)
+
+    def step(i):
+        quantize(i)
+        gemm(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step, wall = timed(step, args.steps, args.eager)
+    gemm_ms, _ = timed(gemm, args.steps, args.eager)
+    peak = PEAK_BF16_TFLOPS if mx_mode == ops.MX_EXACT else (PEAK_FP4_TFLOPS if fp4 else PEAK_FP8_TFLOPS)
+    roof = {"bound": "mfma", "achieved": ops_count / (gemm_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(name + ("_fp4" if fp4 else "") + ("_scaled" if mx_mode != ops.MX_EXACT else ""))
+    line = {
+        "metric": METRIC, "value": ops_count / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp4-e2m1" if fp4 else "fp8-e4m3",
+        "data": "synthetic (seeded generator with the workload's shapes and distributions)",
+        "config": {"workload": f"{name}: {DESCRIPTION[name]} ({args.mx_mode} mode)"
+                               + (" -- MXFP4: e2m1 A and W, E8M0 per 32" if fp4 else ""),
+                   "experts": E, "M_total": M, "K": K, "N": N, "rows_per_expert": [int(x) for x in sizes],
+                   "rotating_buffer_sets": nsets, "gemm_ms": gemm_ms,
+                   "launch": "eager" if args.eager else "hip graph (K steps captured, replayed once)",
+                   "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9},
+        "roofline": roof,
+    }
+    if args.calibration_copy:
+        calibration_copy(args.calibration_copy, dev)
+    print(f"[bench] {name}: {ms_per_step * 1e3:.2f} us/step, gemm {gemm_ms * 1e3:.2f} us, "
+          f"wall {wall:.3f} s for {args.steps} steps", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_grouped(A_np, W_np, sizes, fp4, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +368,8 @@ def main():
         print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
+    if args.workload in MOE:
+        return main_grouped(args)
 
     import numpy as np
     import torch
@@ -298,33 +465,12 @@ def main():
     # launches every step from Python instead.
     K_steps = args.steps
 
-    def timed(fn):
-        """Milliseconds per call of fn(i), i = 0 .. K-1, on the current stream."""
-        if args.eager:
-            run = lambda: [fn(i) for i in range(K_steps)]  # noqa: E731
-        else:
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for i in range(K_steps):
-                    fn(i)
-            run = graph.replay
-            run()  # one untimed replay
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record()
-        run()
-        stop.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(stop) / K_steps, time.perf_counter() - t0
-
     # Timed region 1: K whole steps (quantize + GEMM + epilogue) back to back.
-    ms_per_step, wall = timed(step)
+    ms_per_step, wall = timed(step, K_steps, args.eager)
     # Timed region 2: the GEMM kernel alone, K launches over the same rotating
     # buffer sets, bracketed by events on the stream it runs on; the average
     # launch duration feeds the roofline.
-    gemm_ms, _ = timed(gemm)
+    gemm_ms, _ = timed(gemm, K_steps, args.eager)
 
     if unit == "GB/s":
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -367,13 +513,7 @@ def main():
         "roofline": roof,
     }
     if args.calibration_copy:
-        nb = args.calibration_copy << 20
-        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(args.calibration_copy, dev)
     print(f"[bench] {name}: {ms_per_step * 1e3:.2f} us/step, gemm {gemm_ms * 1e3:.2f} us, "
           f"wall {wall:.3f} s for {K_steps} steps", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:

@@ -26,12 +26,19 @@ pages' experiments:
 * ``c4_decode`` -- 8 tokens against a wide weight, A ~ N(0,1),
   W ~ N(0, 0.02^2).
 * ``c5_mxfp8`` -- A, W ~ N(0,1) with each element x64 with probability 0.01.
+
+One grouped workload, for the grouped (MoE) MX GEMM of "TileLang tutorial,
+chapter 27", section 6.2 (MoE): ``make_moe_inputs`` draws E experts' weights
+``W [E, N, K]``, the per-expert row counts of the routed activations (a
+multinomial over the experts with uneven routing probabilities, softmax of
+N(0, 0.5^2) logits), and ``A [M_total, K]`` with every expert's rows stored
+one expert after the other; values as ``c5_mxfp8``.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["WORKLOADS", "make_inputs", "rng_for"]
+__all__ = ["WORKLOADS", "MOE_WORKLOADS", "make_inputs", "make_moe_inputs", "rng_for"]
 
 # name -> (M, K, N, seed, recipe)
 WORKLOADS = {
@@ -40,6 +47,11 @@ WORKLOADS = {
     "c3_asym_uint8": (2048, 4096, 11008, 103, "relu"),
     "c4_decode": (8, 4096, 14336, 104, "normal"),
     "c5_mxfp8": (8192, 8192, 8192, 105, "spiky"),
+}
+
+# name -> (experts E, routed rows M_total (tokens x top-k), K, N per expert, seed)
+MOE_WORKLOADS = {
+    "c6_moe_mxfp8": (8, 8192, 4096, 4096, 106),
 }
 
 _OUTLIER_CHANNELS = (7, 1031, 2055, 3079)
@@ -103,3 +115,24 @@ def make_inputs(name: str, M: int | None = None, K: int | None = None,
     else:  # pragma: no cover
         raise ValueError(recipe)
     return np.ascontiguousarray(A, dtype=np.float32), np.ascontiguousarray(W, dtype=np.float32)
+
+
+def make_moe_inputs(name: str = "c6_moe_mxfp8", E: int | None = None, M: int | None = None,
+                    K: int | None = None, N: int | None = None, seed: int | None = None):
+    """Return ``(A, W, sizes)`` for a grouped workload: A [M_total, K] (rows of
+    expert e at sizes[:e].sum() ..), W [E, N, K], sizes [E] int64."""
+    dE, dM, dK, dN, dseed = MOE_WORKLOADS[name]
+    E = dE if E is None else int(E)
+    M = dM if M is None else int(M)
+    K = dK if K is None else int(K)
+    N = dN if N is None else int(N)
+    seed = dseed if seed is None else int(seed)
+    rng = rng_for(seed)
+    logits = rng.normal(0.0, 0.5, size=E)
+    p = np.exp(logits - logits.max())
+    sizes = rng.multinomial(M, p / p.sum()).astype(np.int64)
+    A = _normal(rng, (M, K))
+    A[rng.random((M, K), dtype=np.float32) < np.float32(0.01)] *= np.float32(64.0)
+    W = _normal(rng, (E, N, K))
+    W[rng.random((E, N, K), dtype=np.float32) < np.float32(0.01)] *= np.float32(64.0)
+    return np.ascontiguousarray(A), np.ascontiguousarray(W), sizes
