@@ -9,11 +9,13 @@
 // e4m3 codes are bytes, so the tiles travel like the int8 GEMM's: global
 // memory -> LDS directly (buffer_load ... lds), each lane fetching the
 // 16-byte chunk that belongs at its slot of the XOR-swizzled row-major tile,
-// NS stages in a ring so NS - 1 are in flight without holding registers. Each
-// stage (64 K) also carries its E8M0 bytes: one dword per tile row (the four
-// blocks of the 128-deep stage pair the stage belongs to, fetched by a
-// 4-byte-per-lane DMA), so a stage's scales arrive with its data and the scale
-// layout in global memory stays the public row-major [rows][K/32].
+// NS stages in a ring so NS - 1 are in flight without holding registers. The
+// E8M0 bytes travel with the stages too: every SS-th stage also brings 16
+// scale bytes of each tile row (its own stage and the next SS - 1) into one of
+// two scale slots, a 16-byte lane per row, so one 1 KB load covers 64 rows
+// (a dword per row and stage would touch 64 cache lines per 256 bytes and
+// double the stage's line requests); the scale layout in global memory stays
+// the public row-major [rows][K/32].
 //
 // Per 64-deep stage a wave reads, per 32-row fragment, the two 16-byte chunks
 // the 32x32x64 operand wants (lane 32h + r: K 16h .. 16h+15 and 32 + 16h ..
@@ -41,6 +43,12 @@
 // unused), fed to the same instruction with the e2m1 format code. e2m1
 // products span under 8 binades, so the hardware's 8-product alignment drops
 // nothing and the sums are float32 sums.
+//
+// GROUPED (the grouped MoE GEMM, same section 6.2 of the tutorial): the rows
+// routed to each expert are stored one expert after the other; the experts'
+// tile-rows are listed in expert order, each workgroup finds its expert from
+// the device-resident row offsets, and the tile's rows, weights, scales and
+// bias are that expert's. The rest of the kernel is unchanged.
 //
 // Taken when every stage lies inside K (K % 64 == 0, e2m1: K % 128 == 0) and
 // the activation scale rows are dword-aligned; the register-staged kernel in
