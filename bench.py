@@ -82,12 +82,18 @@ def algorithmic(name, M, K, N, w4a8=False, fp4=False):
 
 
 def source_digest(w4a8=False):
-    """Digest of the sources of the GEMM kernel a workload times."""
+    """Digest of the code of the GEMM kernel a workload times: its sources
+    with comments and whitespace removed, so only a code change makes the
+    stored counter figures stale."""
+    import re
     h = hashlib.sha256()
     srcs = ("gemm_w4a8.hip",) if w4a8 else ("gemm.hip", "gemm_mx_dma.hip")
     for f in srcs + ("common.hpp", "kernels.hpp"):
-        with open(os.path.join(ROOT, "block_scaled_quantized_qgemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "block_scaled_quantized_qgemm_amd", "csrc", f)) as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update("".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
