@@ -160,6 +160,49 @@ def test_w4a8_ignores_activation_bytes_past_k(ops):
     _check(host(ops.qgemm_run_w4a8(a, pw, 0)), y, S, K, 0)
 
 
+@pytest.mark.parametrize("out_type", [0, 1])
+def test_w4a8_tiled_large_tiles_ragged(ops, out_type):
+    """More than 16 rows runs the tiled kernel; at least one 128 x 128 tile
+    per CU takes its large-tile configuration. M and N are not multiples of
+    the tile, K not of the 128-deep stage."""
+    M, N, K = 2000, 2100, 320
+    print_case("w4a8 tiled large", M, N, K, out_type)
+    A, W = make_inputs("c2_per_token", M=M, K=K, N=N, seed=23 + out_type)
+    y, S = _w4a8_ref(A, W)
+    a = ops.qgemm_quantize_rows(dev(A), ops.FMT_INT8_SYM, ops.GRAN_ROW)
+    pw = ops.qgemm_prepack_weights(dev(W), ops.FMT_INT4_SYM, ops.GRAN_GROUP64)
+    _check(host(ops.qgemm_run_w4a8(a, pw, out_type)), y, S, K, out_type)
+
+
+def test_w4a8_tiled_ignores_activation_bytes_past_k(ops):
+    """The tiled kernel (more than 16 rows): bytes of A's rows between K and
+    lda meet zero weight codes."""
+    M, N, K = 40, 150, 200
+    print_case("w4a8 tiled junk past K", M, N, K)
+    A, W = make_inputs("c4_decode", M=M, K=K, N=N, seed=19)
+    y, S = _w4a8_ref(A, W)
+    a = ops.qgemm_quantize_rows(dev(A), ops.FMT_INT8_SYM, ops.GRAN_ROW)
+    a.q[:, K:] = -77
+    pw = ops.qgemm_prepack_weights(dev(W), ops.FMT_INT4_SYM, ops.GRAN_GROUP64)
+    _check(host(ops.qgemm_run_w4a8(a, pw, 0)), y, S, K, 0)
+
+
+def test_w4a8_prefill_shape_full_size(ops):
+    """W4A8 at the per-token workload's full size (512 x 4096 x 4096, the
+    tiled kernel's 64 x 128 tiles as the benchmark launches them), checked on
+    64 rows spread over all row tiles against the oracle (each output row
+    depends only on its own activation row)."""
+    print_case("w4a8 prefill full size")
+    A, W = make_inputs("c2_per_token")
+    M, K = A.shape
+    a = ops.qgemm_quantize_rows(dev(A), ops.FMT_INT8_SYM, ops.GRAN_ROW)
+    pw = ops.qgemm_prepack_weights(dev(W), ops.FMT_INT4_SYM, ops.GRAN_GROUP64)
+    got = host(ops.qgemm_run_w4a8(a, pw, 0))
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, M - 1], rng_for(5).choice(M, 59, replace=False)]))
+    y, S = _w4a8_ref(A[rows], W)
+    _check(got[rows], y, S, K, 0)
+
+
 def test_w4a8_decode_workload_full_size(ops):
     """The decode-shaped workload at its full size (8 x 4096 x 14336), the
     launch the benchmark times, element by element against the full oracle."""
