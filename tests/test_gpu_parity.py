@@ -253,6 +253,56 @@ def test_gemm_large_tile_configs(ops, M, N, K, act):
     _check_out(host(ops.qgemm_run(a, pw, 0)), ref["y"], 0)
 
 
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("M", [8, 17, 300])
+def test_gemm_int32_at_the_k_limit(ops, M, asym):
+    """The largest K the boundary accepts for the format (the oracle's k_limit,
+    rounded down to a whole 256), with every activation code at its extreme
+    (127; uint8: 255 against zero point 0) and weight rows of +127 and -127
+    codes, so the sums reach within 0.02% of 2^31; one activation row and one
+    weight row are random. The decode kernel (8 rows) and the tiled kernel
+    (17 and 300 rows) must return the oracle's exact sums."""
+    K = O.k_limit(asym) // 256 * 256
+    N = 40
+    print_case("gemm i32 k limit", M, N, K, "asym", asym)
+    rng = rng_for(7 + M + int(asym))
+    A = np.ones((M, K), np.float32)
+    if asym:
+        A[:, 0] = 0.0   # row min 0, max 1: s = 1/255, z = 0, codes 0 and 255
+    A[-1] = rng.standard_normal(K)
+    W = np.where(np.arange(N)[:, None] % 2 == 0, 1.0, -1.0) * np.ones((N, K))
+    W[-1] = rng.standard_normal(K)
+    W = W.astype(np.float32)
+    act = "asym_row" if asym else "sym_row"
+    ref = O.quantized_linear(A, W, act=act, wgt="channel")
+    assert np.abs(ref["C"]).max() > 0.9998 * 2**31
+    _check_out(_run_int(ops, A, W, act, "channel", 2), None, 2, ref["C"])
+
+
+@pytest.mark.parametrize("M,N,asym", [(1100, 3900, False), (4100, 4100, False), (4000, 4090, False),
+                                      (4000, 4090, True)])
+def test_gemm_int32_at_the_k_limit_large_tiles(ops, M, N, asym):
+    """The 128x128, 128x256 (two per CU) and 256x256 tile configurations at
+    the largest K, on inputs whose exact sums have a closed form: every
+    activation code at its extreme and weight rows of alternating +127 and
+    -127 codes give C[m][n] = +-127 * 127 * K (uint8: +-255 * 127 * (K - 1),
+    the first column being code 0)."""
+    K = O.k_limit(asym) // 256 * 256
+    print_case("gemm i32 k limit tiles", M, N, K, "asym", asym)
+    A = torch.ones((M, K), device="cuda")
+    if asym:
+        A[:, 0] = 0.0
+    sign = np.where(np.arange(N) % 2 == 0, 1, -1).astype(np.int64)
+    W = torch.from_numpy(sign.astype(np.float32)).cuda()[:, None].expand(N, K).contiguous()
+    a = ops.qgemm_quantize_rows(A, 1 if asym else 0, 1)
+    pw = ops.qgemm_prepack_weights(W, 0, 1)
+    del A, W
+    got = host(ops.qgemm_run(a, pw, 2))
+    per = 255 * 127 * (K - 1) if asym else 127 * 127 * K
+    assert per < 2**31
+    assert np.array_equal(got, np.broadcast_to((per * sign)[None, :], (M, N)))
+
+
 def test_gemm_empty_m(ops):
     pw = ops.qgemm_prepack_weights(dev(np.ones((8, 64), np.float32)), 0, 1)
     a = ops.qgemm_quantize_rows(torch.empty((0, 64), device="cuda"), 0, 1)
