@@ -298,8 +298,6 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
   if (!is_mx_fmt(a_fmt)) return QGEMM_E_MODE;
   int rc = check_desc(w_desc, -1);
   if (rc != QGEMM_OK) return rc;
-  // the block-scaled matrix cores take e4m3 x e4m3 or e2m1 x e2m1
-  if (mode == QGEMM_MX_SCALED_MFMA && a_fmt != w_desc->fmt) return QGEMM_E_MODE;
   const int64_t N = w_desc->N, K = w_desc->K;
   if (M < 0 || M > kMaxRows) return QGEMM_E_SHAPE;
   if (M == 0) return QGEMM_OK;
@@ -342,13 +340,13 @@ int qgemm_run_mx_grouped(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e
   if (!is_mx_fmt(a_fmt)) return QGEMM_E_MODE;
   int rc = check_desc(w_desc, -1);
   if (rc != QGEMM_OK) return rc;
-  // one kernel serves the grouped call: e4m3 x e4m3 in either mode, e2m1 x e2m1 scaled
-  if (a_fmt != w_desc->fmt) return QGEMM_E_MODE;
-  const bool f4 = a_fmt == QGEMM_FMT_MXFP4_E2M1;
-  if (f4 && mode != QGEMM_MX_SCALED_MFMA) return QGEMM_E_MODE;
+  // one kernel serves the grouped call: e4m3 x e4m3 in either mode, pairs
+  // with an e2m1 operand on the block-scaled matrix cores
+  const bool a4 = a_fmt == QGEMM_FMT_MXFP4_E2M1, w4 = w_desc->fmt == QGEMM_FMT_MXFP4_E2M1;
+  if ((a4 || w4) && mode != QGEMM_MX_SCALED_MFMA) return QGEMM_E_MODE;
   const int64_t N = w_desc->N, K = w_desc->K;
   if (M_total < 0 || M_total > kMaxRows || E < 1 || E > kMaxExperts) return QGEMM_E_SHAPE;
-  if (K % (f4 ? 128 : 64) != 0) return QGEMM_E_SHAPE;
+  if (K % (a4 && w4 ? 128 : 64) != 0) return QGEMM_E_SHAPE;
   if (M_total == 0) return QGEMM_OK;
   if (!a_codes || !a_e8m0 || !offsets || !w_packed || !out) return QGEMM_E_NULL;
   if (lda < code_bytes(a_fmt, K) || lda_s < K / 32 || ldo < N) return QGEMM_E_SHAPE;
@@ -366,8 +364,8 @@ int qgemm_run_mx_grouped(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e
   g.lda_s = lda_s;
   g.w = base + w_desc->codes_off;
   g.ew = base + w_desc->scales_off;
-  g.a_fp4 = f4;
-  g.w_fp4 = f4;
+  g.a_fp4 = a4;
+  g.w_fp4 = w4;
   g.M = M_total;
   g.N = N;
   g.K = K;

@@ -104,42 +104,47 @@ __device__ inline void fp4x16_to_bf16(const v4i& q, float scale, v4i& lo, v4i& h
   hi = v4i{w[4], w[5], w[6], w[7]};
 }
 
-// F4 (scaled mode): e2m1 operands staged raw, 32 codes per 16-byte chunk.
-template <int BM, int BN, int BK, int WM, int WN, int MODE, bool F4 = false>
+// FA4 / FW4 in the scaled mode: that operand's e2m1 codes are staged raw, 32
+// codes per 16-byte chunk (so its LDS rows are half as long as e4m3 rows).
+template <int BM, int BN, int BK, int WM, int WN, int MODE, bool FA4 = false, bool FW4 = false>
 struct MxCfg {
   static constexpr int NT = WM * WN * 64;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int KPC = MODE == MXF && F4 ? 32 : 16;             // K per global chunk
-  static constexpr int CPR = BK / KPC;                                 // global chunks per row and K step
-  static constexpr int RB = MODE == MXB ? 2 * BK : (F4 ? BK / 2 : BK);  // LDS bytes per row
-  static constexpr int A_CH = BM * CPR / NT, B_CH = BN * CPR / NT;
-  static constexpr int STAGE = (BM + BN) * RB;
+  static constexpr bool A4 = MODE == MXF && FA4, W4 = MODE == MXF && FW4;  // raw e2m1 staging
+  static constexpr int KPCA = A4 ? 32 : 16, KPCW = W4 ? 32 : 16;          // K per global chunk
+  static constexpr int CPRA = BK / KPCA, CPRW = BK / KPCW;                 // global chunks per row and K step
+  // LDS bytes per row: bf16 in the exact mode, the codes as they are otherwise
+  static constexpr int RBA = MODE == MXB ? 2 * BK : (A4 ? BK / 2 : BK);
+  static constexpr int RBW = MODE == MXB ? 2 * BK : (W4 ? BK / 2 : BK);
+  static constexpr int A_CH = BM * CPRA / NT, B_CH = BN * CPRW / NT;
+  static constexpr int STAGE = BM * RBA + BN * RBW;
   static constexpr int RS = TN + 8;  // epilogue staging row stride in words: rows r and r+4
                                      // (the two half-waves) start 32 banks apart
   static constexpr int EPI = WM * WN * 32 * RS * 4;      // per-wave 32 x TN float staging
   static constexpr int LDS = 2 * STAGE > EPI ? 2 * STAGE : EPI;
-  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "tile / thread mismatch");
+  static_assert(BM * CPRA % NT == 0 && BN * CPRW % NT == 0, "tile / thread mismatch");
   static_assert(MODE != MXF || BK % 64 == 0, "scaled fp8 steps are 64 deep");
-  static_assert(MODE != MXB || RB == 128, "exact-mode staging: 128-byte bf16 rows");
+  static_assert(MODE != MXB || (RBA == 128 && RBW == 128), "exact-mode staging: 128-byte bf16 rows");
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
 
 // FA4 / FW4: the activations / weights are e2m1, two codes per byte. In the
 // exact mode a 16-K chunk is then 8 bytes, converted to the same two bf16 LDS
-// chunks as sixteen e4m3 codes. In the scaled mode (both operands e2m1) the
-// codes go to LDS as they are, and a lane's operand for a 64-deep step is the
-// 16 bytes holding K 32h .. 32h + 31 of its row (lane 32h + r; measured), fed
-// to the matrix cores with the e2m1 format code: e2m1 products span under 8
-// binades, so the hardware's 8-product alignment drops nothing and the sums
-// are float32 sums.
+// chunks as sixteen e4m3 codes. In the scaled mode the codes go to LDS as they
+// are, each operand in its own format: an e2m1 lane operand for a 64-deep step
+// is the 16 bytes holding K 32h .. 32h + 31 of its row (lane 32h + r;
+// measured), an e4m3 one the 32 bytes of K 16h .. and 32 + 16h .., and each
+// operand's format code goes to the instruction (so e4m3 x e2m1 pairs run
+// too). e2m1 x e2m1 products span under 8 binades, so the hardware's
+// 8-product alignment drops nothing and the sums are float32 sums; a pair
+// with an e4m3 operand has the e4m3 bound of the scaled mode.
 template <int BM, int BN, int BK, int WM, int WN, int MODE, bool FA4 = false, bool FW4 = false>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
-  constexpr bool F4 = MODE == MXF && FA4;
-  using C = MxCfg<BM, BN, BK, WM, WN, MODE, F4>;
-  static_assert(MODE == MXB || FA4 == FW4, "the scaled mode takes e4m3 x e4m3 or e2m1 x e2m1");
-  constexpr int NT = C::NT, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, CPR = C::CPR, RB = C::RB;
-  constexpr int KPC = C::KPC;
+  using C = MxCfg<BM, BN, BK, WM, WN, MODE, FA4, FW4>;
+  constexpr bool A4 = C::A4, W4 = C::W4;
+  constexpr int NT = C::NT, TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
+  constexpr int CPRA = C::CPRA, CPRW = C::CPRW, RBA = C::RBA, RBW = C::RBW, KPCA = C::KPCA, KPCW = C::KPCW;
   constexpr int A_CH = C::A_CH, B_CH = C::B_CH, STAGE = C::STAGE;
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -183,14 +188,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
     const int64_t k0_ = (int64_t)(KT) * BK;                                                     \
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                          \
       const int id = tid + i * NT;                                                              \
-      const int r = id / CPR, c = id % CPR;                                                     \
+      const int r = id / CPRA, c = id % CPRA;                                                   \
       /* Unconditional load from a clamped address: no branch and no use of the */             \
       /* value before the LDS store, so the loads stay in flight. Rows >= M only */             \
       /* feed outputs that are never stored; columns >= K meet zero weights (and */             \
       /* are zeroed at the store for MX, where a stray code could be NaN). */                   \
-      const int64_t m = min(m0 + r, p.M - 1), k = k0_ + c * KPC;                                 \
+      const int64_t m = min(m0 + r, p.M - 1), k = k0_ + c * KPCA;                                \
       const int64_t kc = k < p.K ? k : 0;                                                       \
-      if constexpr (F4) {                                                                       \
+      if constexpr (A4) {                                                                       \
         RA[i] = *reinterpret_cast<const v4i*>(p.a + m * p.lda + (kc >> 1));                     \
       } else if constexpr (FA4) {                                                               \
         const uint2 h_ = *reinterpret_cast<const uint2*>(p.a + m * p.lda + (kc >> 1));          \
@@ -202,9 +207,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
     }                                                                                           \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                          \
       const int id = tid + i * NT;                                                              \
-      const int r = id / CPR, c = id % CPR;                                                     \
-      const int64_t n = n0 + r, k = k0_ + c * KPC;                                              \
-      if constexpr (F4) {                                                                       \
+      const int r = id / CPRW, c = id % CPRW;                                                   \
+      const int64_t n = n0 + r, k = k0_ + c * KPCW;                                             \
+      if constexpr (W4) {                                                                       \
         RB_[i] = *reinterpret_cast<const v4i*>(p.w + n * (p.K_pad >> 1) + (k >> 1));            \
       } else if constexpr (FW4) {                                                               \
         const uint2 h_ = *reinterpret_cast<const uint2*>(p.w + n * (p.K_pad >> 1) + (k >> 1));  \
@@ -218,11 +223,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
 #define QG_STORE_STAGE(KT, S, RA, RB_, EA, EB)                                                  \
   {                                                                                             \
     uint8_t* sa_ = smem + (S) * STAGE;                                                          \
-    uint8_t* sb_ = sa_ + BM * RB;                                                               \
+    uint8_t* sb_ = sa_ + BM * RBA;                                                              \
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                          \
       const int id = tid + i * NT;                                                              \
-      const int r = id / CPR, c = id % CPR;                                                     \
-      if ((int64_t)(KT) * BK + c * KPC >= p.K) RA[i] = v4i{0, 0, 0, 0};                         \
+      const int r = id / CPRA, c = id % CPRA;                                                   \
+      if ((int64_t)(KT) * BK + c * KPCA >= p.K) RA[i] = v4i{0, 0, 0, 0};                        \
       if constexpr (MODE == MXB) {                                                              \
         v4i lo, hi;                                                                             \
         if constexpr (FA4)                                                                      \
@@ -232,12 +237,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
         *reinterpret_cast<v4i*>(sa_ + lds_off_bf16(r, 2 * c)) = lo;                             \
         *reinterpret_cast<v4i*>(sa_ + lds_off_bf16(r, 2 * c + 1)) = hi;                         \
       } else {                                                                                  \
-        *reinterpret_cast<v4i*>(sa_ + lds_off<RB>(r, c)) = RA[i];                               \
+        *reinterpret_cast<v4i*>(sa_ + lds_off<RBA>(r, c)) = RA[i];                              \
       }                                                                                         \
     }                                                                                           \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                          \
       const int id = tid + i * NT;                                                              \
-      const int r = id / CPR, c = id % CPR;                                                     \
+      const int r = id / CPRW, c = id % CPRW;                                                   \
       if constexpr (MODE == MXB) {                                                              \
         v4i lo, hi;                                                                             \
         if constexpr (FW4)                                                                      \
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
         *reinterpret_cast<v4i*>(sb_ + lds_off_bf16(r, 2 * c)) = lo;                             \
         *reinterpret_cast<v4i*>(sb_ + lds_off_bf16(r, 2 * c + 1)) = hi;                         \
       } else {                                                                                  \
-        *reinterpret_cast<v4i*>(sb_ + lds_off<RB>(r, c)) = RB_[i];                              \
+        *reinterpret_cast<v4i*>(sb_ + lds_off<RBW>(r, c)) = RB_[i];                             \
       }                                                                                         \
     }                                                                                           \
   }
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
 #define QG_COMPUTE(S)                                                                           \
   {                                                                                             \
     const uint8_t* sa = smem + (S) * STAGE;                                                     \
-    const uint8_t* sb = sa + BM * RB;                                                           \
+    const uint8_t* sb = sa + BM * RBA;                                                          \
     if constexpr (MODE == MXB) {                                                                \
       /* 16-deep bf16 steps: lane 32h + r holds K 8h..8h+7 of the step */                      \
       _Pragma("unroll") for (int kk = 0; kk < BK / 16; ++kk) {                                  \
@@ -306,24 +311,25 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
       /* 64-deep scaled steps: e4m3, lane 32h + r holds K 16h.. and 32+16h..; */                \
       /* e2m1, lane 32h + r holds K 32h .. 32h+31 in its first 16 bytes */                      \
       _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                       \
-        const int c0 = F4 ? ks * 2 + (lane >> 5) : ks * 4 + (lane >> 5), c1 = c0 + 2;           \
+        const int ca = A4 ? ks * 2 + (lane >> 5) : ks * 4 + (lane >> 5);                        \
+        const int cw = W4 ? ks * 2 + (lane >> 5) : ks * 4 + (lane >> 5);                        \
         v8i af[FM], bf[FN];                                                                     \
         _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                        \
           const int r = wm * TM + i * 32 + (lane & 31);                                         \
-          const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<RB>(r, c0));                \
-          const v4i hi = F4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sa + lds_off<RB>(r, c1)); \
+          const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<RBA>(r, ca));               \
+          const v4i hi = A4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sa + lds_off<RBA>(r, ca + 2)); \
           af[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                  \
         }                                                                                       \
         _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                        \
           const int r = wn * TN + j * 32 + (lane & 31);                                         \
-          const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<RB>(r, c0));                \
-          const v4i hi = F4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sb + lds_off<RB>(r, c1)); \
+          const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<RBW>(r, cw));               \
+          const v4i hi = W4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sb + lds_off<RBW>(r, cw + 2)); \
           bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};                  \
         }                                                                                       \
         _Pragma("unroll") for (int i = 0; i < FM; ++i)                                          \
           _Pragma("unroll") for (int j = 0; j < FN; ++j)                                        \
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                        \
-                af[i], bf[j], acc[i][j], F4 ? 4 : 0, F4 ? 4 : 0, 0,                             \
+                af[i], bf[j], acc[i][j], A4 ? 4 : 0, W4 ? 4 : 0, 0,                             \
                 (S) == 0 ? esa0[ks * FM + i] : esa1[ks * FM + i], 0,                            \
                 (S) == 0 ? esb0[ks * FN + j] : esb1[ks * FN + j]);                              \
         __builtin_amdgcn_sched_barrier(0);                                                      \
@@ -843,7 +849,7 @@ static hipError_t launch_i8(const GemmArgs& a, hipStream_t st) {
 
 template <int BM, int BN, int BK, int WM, int WN, int MODE, bool FA4, bool FW4>
 static hipError_t launch_mx_cfg(const GemmArgs& a, hipStream_t st) {
-  using C = MxCfg<BM, BN, BK, WM, WN, MODE, MODE == MXF && FA4>;
+  using C = MxCfg<BM, BN, BK, WM, WN, MODE, FA4, FW4>;
   auto kern = gemm_mx_kernel<BM, BN, BK, WM, WN, MODE, FA4, FW4>;
   const size_t lds = C::LDS;
   if (lds > 65536) {  // above the default dynamic-LDS limit (gfx950 has 160 KiB)
@@ -883,8 +889,10 @@ hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st) {
   if (a.M == 0) return hipSuccess;
   if (mx_dma_eligible(a, mode)) return launch_gemm_mx_dma(a, mode, st);
-  if (mode == 1) {  // e4m3 x e4m3 or e2m1 x e2m1 (the caller checks)
-    if (a.a_fp4) return launch_mx<MXF, true, true>(a, st);
+  if (mode == 1) {  // any pair of e4m3 / e2m1 operands, each with its own format code
+    if (a.a_fp4 && a.w_fp4) return launch_mx<MXF, true, true>(a, st);
+    if (a.a_fp4) return launch_mx<MXF, true, false>(a, st);
+    if (a.w_fp4) return launch_mx<MXF, false, true>(a, st);
     return launch_mx<MXF>(a, st);
   }
   if (a.a_fp4 && a.w_fp4) return launch_mx<MXB, true, true>(a, st);

@@ -37,12 +37,14 @@
 // that lane, the same K positions for A and W, so the four MFMAs together form
 // every product of the step once.
 //
-// F4 (e2m1 x e2m1, scaled mode only): two codes per byte, so a stage of BK
-// bytes per row holds 2 BK K; a lane's operand for a 64-deep step is the 16
-// bytes holding K 32h .. 32h + 31 of its row (the upper half of the operand
-// unused), fed to the same instruction with the e2m1 format code. e2m1
-// products span under 8 binades, so the hardware's 8-product alignment drops
-// nothing and the sums are float32 sums.
+// A4 / W4 (e2m1 activations / weights, scaled mode only): two codes per byte,
+// so that operand's stage rows hold KPS / 2 bytes; its lane operand for a
+// 64-deep step is the 16 bytes holding K 32h .. 32h + 31 of its row (the
+// upper half of the operand unused), and the instruction gets each operand's
+// own format code, so e4m3 x e2m1 pairs run as well. e2m1 x e2m1 products
+// span under 8 binades, so the hardware's 8-product alignment drops nothing
+// and the sums are float32 sums; a pair with an e4m3 operand has the e4m3
+// bound.
 //
 // GROUPED (the grouped MoE GEMM, same section 6.2 of the tutorial): the rows
 // routed to each expert are stored one expert after the other; the experts'
@@ -50,9 +52,9 @@
 // the device-resident row offsets, and the tile's rows, weights, scales and
 // bias are that expert's. The rest of the kernel is unchanged.
 //
-// Taken when every stage lies inside K (K % 64 == 0, e2m1: K % 128 == 0) and
-// the activation scale rows are dword-aligned; the register-staged kernel in
-// gemm.hip covers the rest (and the mixed e4m3 / e2m1 pairs).
+// Taken when every stage lies inside K (K % 64 == 0, e2m1 x e2m1: K % 128 ==
+// 0) and the activation scale rows are dword-aligned; the register-staged
+// kernel in gemm.hip covers the rest (and the exact mode of e2m1 operands).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -71,35 +73,37 @@ __device__ inline v8bf_t fp8x8_to_bf16(int d0, int d1, float scale) {
   return v8bf_t{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NS, bool EXACT, bool F4>
+template <int BM, int BN, int KPS, int WM, int WN, int NS, bool EXACT, bool A4, bool W4>
 struct MxDmaCfg {
   static constexpr int NT = WM * WN * 64, NW = WM * WN;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int KPS = F4 ? 2 * BK : BK;       // K per stage (BK bytes per row)
+  static constexpr int RBA = A4 ? KPS / 2 : KPS;     // code bytes per A row and stage (KPS K)
+  static constexpr int RBW = W4 ? KPS / 2 : KPS;     // ... per W row
   static constexpr int NKK = KPS / 64;               // 64-deep matrix-core steps per stage
-  static constexpr int DATA = (BM + BN) * BK;        // code bytes per stage
+  static constexpr int DATA = BM * RBA + BN * RBW;   // code bytes per stage
   static constexpr int STAGE = DATA;
   static constexpr int SPS = KPS / 32;               // E8M0 bytes per row and stage
   static constexpr int SS = 16 / SPS;                // stages whose scales one 16-byte row load brings
   static constexpr int SUPER = (BM + BN) * 16;       // one scale slot: 16 bytes per tile row
   static constexpr int SCALES = NS * STAGE;          // two scale slots after the ring
-  static constexpr int IA = BM * BK / 1024;          // the first IA 1 KB data loads carry A
+  static constexpr int IA = BM * RBA / 1024;         // the first IA 1 KB data loads carry A
   static constexpr int IPD = DATA / 1024 / NW;       // 1 KB data loads per wave and stage
   static constexpr int NSL = (BM + BN) / 64;         // 1 KB scale loads per scale slot
   static constexpr int IPS = (NSL + NW - 1) / NW;    // ... per wave and stage (see the loads)
   static constexpr int IPW = IPD + IPS;
   static constexpr int MPS = (EXACT ? 4 : 1) * FM * FN;  // matrix-core instructions per 64-deep step
   // instructions the stage's loads are spread over: the first half of the
-  // only step (BK 64), or every step before the last (BK 128)
+  // only step (KPS 64), or every step before the last (KPS 128)
   static constexpr int SLOTS = NKK == 1 ? MPS / 2 : (NKK - 1) * MPS;
   static constexpr int RS = TN + 8;                  // epilogue staging row stride (words)
   static constexpr int EPI = NW * 32 * RS * 4;
   static constexpr int SINK = SCALES + 2 * SUPER;   // 1 KB that the empty scale loads target
   static constexpr int LDS = SINK + 1024 > EPI ? SINK + 1024 : EPI;
-  static_assert(BK == 64 || BK == 128, "stage depth");
-  static_assert(!(EXACT && F4), "e2m1 runs in the scaled mode");
-  static_assert(DATA % (1024 * NW) == 0 && (BM + BN) % 64 == 0 && BM % 64 == 0, "loads per wave");
+  static_assert(KPS == 64 || KPS == 128, "stage depth");
+  static_assert(!(EXACT && (A4 || W4)), "e2m1 runs in the scaled mode");
+  static_assert(DATA % (1024 * NW) == 0 && (BM * RBA) % 1024 == 0 && (BM + BN) % 64 == 0 && BM % 64 == 0,
+                "loads per wave");
   static_assert(FM % 2 == 0 && FN >= 1, "two halves of a step's MFMAs");
   static_assert(NS >= 2 && (NS - 2) * IPW < 64, "vmcnt range");
   // a scale slot is refilled NS - 1 stages before its first stage, after the
@@ -161,9 +165,10 @@ __device__ inline int group_tiles(const int64_t* off, int E, int64_t M, int tm, 
   return __builtin_amdgcn_readfirstlane(base);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NS, bool EXACT, bool F4, bool GROUPED>
+template <int BM, int BN, int KPS, int WM, int WN, int NS, bool EXACT, bool A4, bool W4, bool GROUPED>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
-  using C = MxDmaCfg<BM, BN, BK, WM, WN, NS, EXACT, F4>;
+  using C = MxDmaCfg<BM, BN, KPS, WM, WN, NS, EXACT, A4, W4>;
+  constexpr int RBA = C::RBA, RBW = C::RBW;
   constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, NKK = C::NKK, MPS = C::MPS;
   constexpr int STAGE = C::STAGE, IPD = C::IPD, IPS = C::IPS, IPW = C::IPW, SLOTS = C::SLOTS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
@@ -207,9 +212,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   const uint8_t* const wexp = GROUPED ? p.w + gt.e * p.w_stride : p.w;
   const uint8_t* const ewexp = GROUPED ? p.ew + gt.e * p.w_stride : p.ew;
   const float* const bias = GROUPED && p.bias ? p.bias + gt.e * p.N : p.bias;
-  const int nkt = (int)(p.K / C::KPS);  // every stage inside K (the launcher checks K % KPS == 0)
-  const int64_t kbytes = F4 ? p.K / 2 : p.K;  // code bytes of a row's K
-  const int64_t ldw = F4 ? p.K_pad / 2 : p.K_pad, ldws = p.K_pad / 32;
+  const int nkt = (int)(p.K / KPS);  // every stage inside K (the launcher checks K % KPS == 0)
+  const int64_t kbytes = A4 ? p.K / 2 : p.K;  // code bytes of an A row's K
+  const int64_t ldw = W4 ? p.K_pad / 2 : p.K_pad, ldws = p.K_pad / 32;
 
   // Loads of a stage. Data: wave wid issues the stage's 1 KB loads
   // wid*IPD .. wid*IPD+IPD-1; lane l of load j fetches the 16-byte chunk that
@@ -242,11 +247,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   for (int i = 0; i < IPD; ++i) {
     const int j = wid * IPD + i;
     const bool ja = j < C::IA;
-    const int P = (ja ? j : j - C::IA) * 1024 + lane * 16;
-    const int r = P / BK;
-    const int c = ((P % BK) >> 4) ^ ((r / (256 / BK)) % (BK / 16));  // the chunk swizzle of lds_off<BK>
-    voff[i] = ja ? (uint32_t)(min((int64_t)r, last_a_row) * p.lda) + (uint32_t)(c * 16)
-                 : (uint32_t)(r * ldw) + (uint32_t)(c * 16);
+    // the (row, chunk) whose slot is P under the chunk swizzle of lds_off<RB>
+    if (ja) {
+      const int P = j * 1024 + lane * 16;
+      const int r = P / RBA;
+      const int c = ((P % RBA) >> 4) ^ ((r / (256 / RBA)) % (RBA / 16));
+      voff[i] = (uint32_t)(min((int64_t)r, last_a_row) * p.lda) + (uint32_t)(c * 16);
+    } else {
+      const int P = (j - C::IA) * 1024 + lane * 16;
+      const int r = P / RBW;
+      const int c = ((P % RBW) >> 4) ^ ((r / (256 / RBW)) % (RBW / 16));
+      voff[i] = (uint32_t)(r * ldw) + (uint32_t)(c * 16);
+    }
   }
 #pragma unroll
   for (int i = 0; i < IPS; ++i) {
@@ -260,8 +272,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
       const bool ja = j < C::IA;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(ja ? abase : wbase), (short)0, live ? (int)(ja ? nrec_a : nrec_w) : 0, kRawBufferWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, QG_LDSP(smem + s * STAGE + j * 1024), 16, (int)voff[i], kt * BK, 0,
-                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, QG_LDSP(smem + s * STAGE + j * 1024), 16, (int)voff[i],
+                                               kt * (ja ? RBA : RBW), 0, 0);
     } else {
       const int js = wid * IPS + (i - IPD);
       const bool ja = js * 64 < BM, real = js < C::NSL && kt % C::SS == 0;
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   };
   auto load_frags = [&](int kt, int kk, Frag& f) {
     const uint8_t* sa = smem + (kt % NS) * STAGE;
-    const uint8_t* sb = sa + BM * BK;
+    const uint8_t* sb = sa + BM * RBA;
     const int q = kt % C::SS;
     const int* ssa = reinterpret_cast<const int*>(smem + C::SCALES + ((kt / C::SS) & 1) * C::SUPER) + q * C::SPS / 4;
     const int* ssb = ssa + 4 * BM;
@@ -310,20 +322,20 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
     constexpr int mask = EXACT ? 0xffff : 0xff;
     // e4m3: chunks 4 kk + h and 4 kk + h + 2 (K 16h .. and 32 + 16h ..);
     // e2m1: chunk 2 kk + h (K 32h .. 32h + 31)
-    const int c0 = F4 ? 2 * kk + h : 4 * kk + h;
+    const int ca = A4 ? 2 * kk + h : 4 * kk + h, cw = W4 ? 2 * kk + h : 4 * kk + h;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * TM + i * 32 + (lane & 31);
-      const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, c0));
-      const v4i hi = F4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sa + lds_off<BK>(r, c0 + 2));
+      const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<RBA>(r, ca));
+      const v4i hi = A4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sa + lds_off<RBA>(r, ca + 2));
       f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       f.sa[i] = (ssa[4 * r] >> sh) & mask;
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int r = wn * TN + j * 32 + (lane & 31);
-      const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, c0));
-      const v4i hi = F4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sb + lds_off<BK>(r, c0 + 2));
+      const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<RBW>(r, cw));
+      const v4i hi = W4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sb + lds_off<RBW>(r, cw + 2));
       f.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       f.sb[j] = (ssb[4 * r] >> sh) & mask;
     }
@@ -364,7 +376,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
         for (int j = 0; j < FN; ++j) {
           const int x = i * FN + j;
           if (x < m0_ || x >= m1_) continue;
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], F4 ? 4 : 0, F4 ? 4 : 0,
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], A4 ? 4 : 0, W4 ? 4 : 0,
                                                                        0, f.sa[i], 0, f.sb[j]);
           if (first >= 0) dma_slot(x - first, ks, sl, live);
           __builtin_amdgcn_sched_barrier(0);
@@ -481,43 +493,47 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NS, bool EXACT, bool F4, bool GROUPED>
+template <int BM, int BN, int KPS, int WM, int WN, int NS, bool EXACT, bool A4, bool W4, bool GROUPED>
 static hipError_t launch_mx_dma_cfg(const GemmArgs& a, hipStream_t st) {
-  using C = MxDmaCfg<BM, BN, BK, WM, WN, NS, EXACT, F4>;
+  using C = MxDmaCfg<BM, BN, KPS, WM, WN, NS, EXACT, A4, W4>;
   // grouped: each expert adds at most one partial tile-row
   const int64_t tiles = ((a.M + BM - 1) / BM + (GROUPED ? a.num_groups : 0)) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_mx_dma_kernel<BM, BN, BK, WM, WN, NS, EXACT, F4, GROUPED>), dim3((unsigned)tiles),
+  hipLaunchKernelGGL((gemm_mx_dma_kernel<BM, BN, KPS, WM, WN, NS, EXACT, A4, W4, GROUPED>), dim3((unsigned)tiles),
                      dim3(C::NT), 0, st, a);
   return hipGetLastError();
 }
 
 bool mx_dma_eligible(const GemmArgs& a, int mode) {
   if (mode != 0 && mode != 1) return false;
-  // e4m3 x e4m3 in either mode; e2m1 x e2m1 in the scaled mode
-  const bool f4 = a.a_fp4 && a.w_fp4;
-  if (a.a_fp4 != a.w_fp4 || (f4 && mode != 1)) return false;
-  if (a.K % (f4 ? 128 : 64) != 0 || a.lda_s % 4 != 0 || ((uintptr_t)a.ea & 3) != 0) return false;
+  // e4m3 x e4m3 in either mode; any pair with an e2m1 operand in the scaled mode
+  const bool any4 = a.a_fp4 || a.w_fp4, both4 = a.a_fp4 && a.w_fp4;
+  if (any4 && mode != 1) return false;
+  if (a.K % (both4 ? 128 : 64) != 0 || a.lda_s % 4 != 0 || ((uintptr_t)a.ea & 3) != 0) return false;
   // one 256-row band of A (codes and scales) and of W in 32-bit byte offsets
   const int64_t rows = a.M < 256 ? a.M : 256;
   return (rows - 1) * a.lda + a.K < (int64_t(1) << 31) && (rows - 1) * a.lda_s + a.K / 32 + 4 < (int64_t(1) << 31) &&
          256 * a.K_pad < (int64_t(1) << 31);
 }
 
-template <bool EXACT, bool F4, bool GROUPED>
+template <bool EXACT, bool A4, bool W4, bool GROUPED>
 static hipError_t launch_mx_dma(const GemmArgs& a, hipStream_t st) {
   // 256 x 256 tiles (8 waves of 128 x 64, a 4-stage ring, one workgroup per
   // CU) when they fill every CU; otherwise 128 x 128 tiles (4 waves of
-  // 64 x 64, two workgroups per CU). Stages of 64 bytes per row: 64 K of
-  // e4m3, 128 K of e2m1.
+  // 64 x 64, two workgroups per CU). Stages of 64 K (rows of 64 bytes of
+  // e4m3, 32 of e2m1), or 128 K when both operands are e2m1 (64-byte rows).
+  constexpr int KPS = A4 && W4 ? 128 : 64;
   const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big >= cu_count()) return launch_mx_dma_cfg<256, 256, 64, 2, 4, 4, EXACT, F4, GROUPED>(a, st);
-  return launch_mx_dma_cfg<128, 128, 64, 2, 2, 4, EXACT, F4, GROUPED>(a, st);
+  if (big >= cu_count()) return launch_mx_dma_cfg<256, 256, KPS, 2, 4, 4, EXACT, A4, W4, GROUPED>(a, st);
+  return launch_mx_dma_cfg<128, 128, KPS, 2, 2, 4, EXACT, A4, W4, GROUPED>(a, st);
 }
 
 template <bool GROUPED>
 static hipError_t launch_mode(const GemmArgs& a, int mode, hipStream_t st) {
-  if (a.a_fp4) return launch_mx_dma<false, true, GROUPED>(a, st);
-  return mode == 0 ? launch_mx_dma<true, false, GROUPED>(a, st) : launch_mx_dma<false, false, GROUPED>(a, st);
+  if (a.a_fp4 && a.w_fp4) return launch_mx_dma<false, true, true, GROUPED>(a, st);
+  if (a.a_fp4) return launch_mx_dma<false, true, false, GROUPED>(a, st);
+  if (a.w_fp4) return launch_mx_dma<false, false, true, GROUPED>(a, st);
+  return mode == 0 ? launch_mx_dma<true, false, false, GROUPED>(a, st)
+                   : launch_mx_dma<false, false, false, GROUPED>(a, st);
 }
 
 hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st) { return launch_mode<false>(a, mode, st); }

@@ -116,7 +116,8 @@ typedef enum {
    * hardware aligns the products to the largest one and drops the bits more
    * than 13 binades below it (measured), so
    * |out - exact| <= 2^-10 * sum_k |a_k w_k| plus float32 summation. For
-   * e2m1 x e2m1: four times the exact mode's peak and float32 sums only. */
+   * e2m1 x e2m1: four times the exact mode's peak and float32 sums only. A
+   * mixed pair (e4m3 x e2m1 either way) has the e4m3 bound. */
   QGEMM_MX_SCALED_MFMA = 1
 } qgemm_mx_mode;
 
@@ -355,12 +356,12 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
  *   w_desc   descriptor of MXFP8_E4M3 or MXFP4_E2M1 weights with the same K
  *            (K % 32 == 0).
  *   out      device float32 [M][ldo], ldo >= N, ldo % 4 == 0, 16-byte aligned.
- *   mode     qgemm_mx_mode: QGEMM_MX_EXACT (products exact, float32 sums; any
- *            pair of formats) or QGEMM_MX_SCALED_MFMA (block-scaled matrix
- *            cores; e4m3 x e4m3 or e2m1 x e2m1, else QGEMM_E_MODE; see the
- *            enum -- for e2m1 x e2m1 the products span under 8 binades, so
- *            nothing is dropped and the sums are float32 sums, as in the exact
- *            mode, at twice the e4m3 rate).
+ *   mode     qgemm_mx_mode: QGEMM_MX_EXACT (products exact, float32 sums) or
+ *            QGEMM_MX_SCALED_MFMA (block-scaled matrix cores, each operand
+ *            with its own format code; see the enum -- for e2m1 x e2m1 the
+ *            products span under 8 binades, so nothing is dropped and the sums
+ *            are float32 sums, as in the exact mode, at twice the e4m3 rate).
+ *            Both modes take any pair of the two formats.
  *            Both need E8M0 codes in [3, 240] for exactness of the scaled values,
  *            which qgemm_quantize_rows always produces for inputs below 2^120.
  *   bias     device float32 [N] or NULL.

@@ -167,13 +167,15 @@ def test_run_mx_validation(lib):
     assert call(mode=2) == E_MODE
     assert call(bias=FAKE + 1) == E_ALIGN
     assert call(af=INT8) == E_MODE
-    assert call(af=MX4, mode=1) == E_MODE                 # scaled fp8 matrix cores: e4m3 only
+    # the block-scaled matrix cores take any e4m3 / e2m1 pair (M = 0: validation only)
+    assert call(af=MX4, lda=160, mode=1, M=0, a=None, e=None, out=None) == OK
     assert call(af=MX4, lda=160, M=0, a=None, e=None, out=None) == OK
     assert call(af=MX4, lda=144) == E_SHAPE               # packed e2m1 rows need K / 2 bytes
     nb4 = lib.qgemm_packed_weight_bytes(100, 320, MX4, BLK)
     d4 = L.WDesc(magic=0x51474D57, version=ABI, fmt=MX4, gran=BLK, N=100, K=320, N_pad=256, K_pad=512,
                  codes_off=0, scales_off=256 * 256, colsum_off=-1, bytes=nb4)
-    assert call(d=d4, mode=1) == E_MODE
+    assert call(d=d4, mode=1, M=0, a=None, e=None, out=None) == OK
+    assert call(d=d4, mode=2) == E_MODE
     assert call(d=_w4desc()) == E_DESC                    # int4 weights are not MX
 
 
@@ -198,7 +200,8 @@ def test_run_mx_grouped_validation(lib):
     assert _grouped(lib, d=_wdesc()) == E_DESC                 # an int8 descriptor
     assert _grouped(lib, mode=2) == E_MODE
     assert _grouped(lib, af=INT8) == E_MODE
-    assert _grouped(lib, af=MX4) == E_MODE                     # a format other than the weights'
+    assert _grouped(lib, af=MX4) == E_MODE                     # an e2m1 operand runs scaled only
+    assert _grouped(lib, af=MX4, lda=160, mode=1, M=0, a=None, e=None, off=None, out=None) == OK  # mixed pair
     d4 = _mxdesc(K=384, fmt=MX4)
     assert _grouped(lib, d=d4, af=MX4, lda=192, ldas=12, mode=0) == E_MODE   # e2m1 runs scaled only
     assert _grouped(lib, E=0) == E_SHAPE

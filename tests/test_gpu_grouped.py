@@ -42,7 +42,7 @@ def host(t):
     return t.cpu().numpy()
 
 
-def _setup(ops, sizes, N, K, fmt=E4M3, seed=0):
+def _setup(ops, sizes, N, K, fmt=E4M3, seed=0, wfmt=None):
     E = len(sizes)
     M = int(sum(sizes))
     A, Wall = make_inputs("c5_mxfp8", M=max(M, 1), K=K, N=E * N, seed=seed)
@@ -50,17 +50,19 @@ def _setup(ops, sizes, N, K, fmt=E4M3, seed=0):
     W = Wall.reshape(E, N, K)
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
     a = ops.qgemm_quantize_rows(dev(A), fmt, ops.GRAN_BLOCK32)
-    w = ops.qgemm_prepack_experts(dev(W), fmt)
+    w = ops.qgemm_prepack_experts(dev(W), fmt if wfmt is None else wfmt)
     return A, W, offsets, a, w
 
 
-def _ref(A, W, offsets, fmt=E4M3):
-    quant = O.quantize_mxfp4 if fmt == E2M1 else O.quantize_mx
-    f = "e2m1" if fmt == E2M1 else "e4m3"
+def _quant(x, fmt):
+    return (O.quantize_mxfp4(x), "e2m1") if fmt == E2M1 else (O.quantize_mx(x), "e4m3")
+
+
+def _ref(A, W, offsets, fmt=E4M3, wfmt=None):
     E, N, K = W.shape
-    qa, Ea = quant(A)
-    qw, Ew = quant(W.reshape(E * N, K))
-    return O.mx_grouped_gemm_ref(qa, Ea, offsets, qw.reshape(E, N, K), Ew.reshape(E, N, K // 32), f, f)
+    (qa, Ea), fa = _quant(A, fmt)
+    (qw, Ew), fw = _quant(W.reshape(E * N, K), fmt if wfmt is None else wfmt)
+    return O.mx_grouped_gemm_ref(qa, Ea, offsets, qw.reshape(E, N, K), Ew.reshape(E, N, K // 32), fa, fw)
 
 
 def _check(got, ref, S, tol):
@@ -101,6 +103,19 @@ def test_grouped_mxfp4_scaled(ops):
     got = host(ops.qgemm_run_mx_grouped(a, w, dev(off), mode=1))
     ref, S = _ref(A, W, off, fmt=E2M1)
     _check(got, ref, S, MX_STOL)
+
+
+@pytest.mark.parametrize("fa,fw", [(E4M3, E2M1), (E2M1, E4M3)])
+@pytest.mark.parametrize("sizes,N,K", [([40, 300, 0, 129], 150, 384), ([700, 0, 1, 1023, 256, 513, 900, 710], 4320, 128)])
+def test_grouped_mx_mixed_pairs(ops, sizes, N, K, fa, fw):
+    """e4m3 x e2m1 either way on the block-scaled matrix cores, each operand
+    in its own layout and format code (the second case on 256 x 256 tiles),
+    within the scaled mode's e4m3 bound."""
+    print_case("grouped mx mixed", sizes, N, K, fa, fw)
+    A, W, off, a, w = _setup(ops, sizes, N, K, fmt=fa, wfmt=fw, seed=17 + K)
+    got = host(ops.qgemm_run_mx_grouped(a, w, dev(off), mode=1))
+    ref, S = _ref(A, W, off, fmt=fa, wfmt=fw)
+    _check(got, ref, S, MX_SCALED_STOL)
 
 
 @pytest.mark.parametrize("fmt,mode", [(E4M3, 0), (E4M3, 1), (E2M1, 1)])
