@@ -340,13 +340,12 @@ int qgemm_run_mx_grouped(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e
   if (!is_mx_fmt(a_fmt)) return QGEMM_E_MODE;
   int rc = check_desc(w_desc, -1);
   if (rc != QGEMM_OK) return rc;
-  // one kernel serves the grouped call: e4m3 x e4m3 in either mode, pairs
-  // with an e2m1 operand on the block-scaled matrix cores
+  // one kernel serves the grouped call: any pair of e4m3 / e2m1 operands in
+  // either mode, in stages of 64 K (128 K for e2m1 x e2m1 in the scaled mode)
   const bool a4 = a_fmt == QGEMM_FMT_MXFP4_E2M1, w4 = w_desc->fmt == QGEMM_FMT_MXFP4_E2M1;
-  if ((a4 || w4) && mode != QGEMM_MX_SCALED_MFMA) return QGEMM_E_MODE;
   const int64_t N = w_desc->N, K = w_desc->K;
   if (M_total < 0 || M_total > kMaxRows || E < 1 || E > kMaxExperts) return QGEMM_E_SHAPE;
-  if (K % (a4 && w4 ? 128 : 64) != 0) return QGEMM_E_SHAPE;
+  if (K % (a4 && w4 && mode == QGEMM_MX_SCALED_MFMA ? 128 : 64) != 0) return QGEMM_E_SHAPE;
   if (M_total == 0) return QGEMM_OK;
   if (!a_codes || !a_e8m0 || !offsets || !w_packed || !out) return QGEMM_E_NULL;
   if (lda < code_bytes(a_fmt, K) || lda_s < K / 32 || ldo < N) return QGEMM_E_SHAPE;

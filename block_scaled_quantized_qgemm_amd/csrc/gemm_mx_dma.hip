@@ -37,14 +37,17 @@
 // that lane, the same K positions for A and W, so the four MFMAs together form
 // every product of the step once.
 //
-// A4 / W4 (e2m1 activations / weights, scaled mode only): two codes per byte,
-// so that operand's stage rows hold KPS / 2 bytes; its lane operand for a
-// 64-deep step is the 16 bytes holding K 32h .. 32h + 31 of its row (the
+// A4 / W4 (e2m1 activations / weights): two codes per byte, so that
+// operand's stage rows hold KPS / 2 bytes. Scaled mode: its lane operand for
+// a 64-deep step is the 16 bytes holding K 32h .. 32h + 31 of its row (the
 // upper half of the operand unused), and the instruction gets each operand's
 // own format code, so e4m3 x e2m1 pairs run as well. e2m1 x e2m1 products
 // span under 8 binades, so the hardware's 8-product alignment drops nothing
 // and the sums are float32 sums; a pair with an e4m3 operand has the e4m3
-// bound.
+// bound. Exact mode: a lane reads the e2m1 codes of the same K positions as
+// an e4m3 fragment (K 16h .. 16h + 15 and 32 + 16h .., two 8-byte halves of
+// the step's two chunks), so chunk t is again the K of the t-th 16-deep
+// MFMA for any pair, and converts them with v_cvt_scalef32_pk_bf16_fp4.
 //
 // GROUPED (the grouped MoE GEMM, same section 6.2 of the tutorial): the rows
 // routed to each expert are stored one expert after the other; the experts'
@@ -52,9 +55,9 @@
 // the device-resident row offsets, and the tile's rows, weights, scales and
 // bias are that expert's. The rest of the kernel is unchanged.
 //
-// Taken when every stage lies inside K (K % 64 == 0, e2m1 x e2m1: K % 128 ==
-// 0) and the activation scale rows are dword-aligned; the register-staged
-// kernel in gemm.hip covers the rest (and the exact mode of e2m1 operands).
+// Taken when every stage lies inside K (K % 64 == 0; e2m1 x e2m1 in the
+// scaled mode: K % 128 == 0) and the activation scale rows are
+// dword-aligned; the register-staged kernel in gemm.hip covers the rest.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -70,6 +73,16 @@ __device__ inline v8bf_t fp8x8_to_bf16(int d0, int d1, float scale) {
   const v2bf_t t1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d0, scale, true);
   const v2bf_t t2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d1, scale, false);
   const v2bf_t t3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)d1, scale, true);
+  return v8bf_t{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+}
+
+// Eight e2m1 codes (dword d; code i in nibble i % 2 of byte i / 2, low
+// nibble first) times `scale` as eight bf16, in order.
+__device__ inline v8bf_t fp4x8_to_bf16(int d, float scale) {
+  const v2bf_t t0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((unsigned)d, scale, 0);
+  const v2bf_t t1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((unsigned)d, scale, 1);
+  const v2bf_t t2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((unsigned)d, scale, 2);
+  const v2bf_t t3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((unsigned)d, scale, 3);
   return v8bf_t{t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
 }
 
@@ -101,7 +114,7 @@ struct MxDmaCfg {
   static constexpr int SINK = SCALES + 2 * SUPER;   // 1 KB that the empty scale loads target
   static constexpr int LDS = SINK + 1024 > EPI ? SINK + 1024 : EPI;
   static_assert(KPS == 64 || KPS == 128, "stage depth");
-  static_assert(!(EXACT && (A4 || W4)), "e2m1 runs in the scaled mode");
+  static_assert(!(EXACT && KPS != 64), "exact-mode stages are 64 deep");
   static_assert(DATA % (1024 * NW) == 0 && (BM * RBA) % 1024 == 0 && (BM + BN) % 64 == 0 && BM % 64 == 0,
                 "loads per wave");
   static_assert(FM % 2 == 0 && FN >= 1, "two halves of a step's MFMAs");
@@ -323,20 +336,34 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
     // e4m3: chunks 4 kk + h and 4 kk + h + 2 (K 16h .. and 32 + 16h ..);
     // e2m1: chunk 2 kk + h (K 32h .. 32h + 31)
     const int ca = A4 ? 2 * kk + h : 4 * kk + h, cw = W4 ? 2 * kk + h : 4 * kk + h;
+    // exact mode, e2m1: the 8-byte halves h of chunks 2 kk and 2 kk + 1 (K
+    // 16h .. 16h + 15 and 32 + 16h ..), one dword per 16-deep chunk t
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int r = wm * TM + i * 32 + (lane & 31);
-      const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<RBA>(r, ca));
-      const v4i hi = A4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sa + lds_off<RBA>(r, ca + 2));
-      f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if constexpr (EXACT && A4) {
+        const uint2 x0 = *reinterpret_cast<const uint2*>(sa + lds_off<RBA>(r, 2 * kk) + 8 * h);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(sa + lds_off<RBA>(r, 2 * kk + 1) + 8 * h);
+        f.a[i] = v8i{(int)x0.x, (int)x0.y, (int)x1.x, (int)x1.y, 0, 0, 0, 0};
+      } else {
+        const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<RBA>(r, ca));
+        const v4i hi = A4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sa + lds_off<RBA>(r, ca + 2));
+        f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
       f.sa[i] = (ssa[4 * r] >> sh) & mask;
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int r = wn * TN + j * 32 + (lane & 31);
-      const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<RBW>(r, cw));
-      const v4i hi = W4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sb + lds_off<RBW>(r, cw + 2));
-      f.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if constexpr (EXACT && W4) {
+        const uint2 x0 = *reinterpret_cast<const uint2*>(sb + lds_off<RBW>(r, 2 * kk) + 8 * h);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(sb + lds_off<RBW>(r, 2 * kk + 1) + 8 * h);
+        f.b[j] = v8i{(int)x0.x, (int)x0.y, (int)x1.x, (int)x1.y, 0, 0, 0, 0};
+      } else {
+        const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<RBW>(r, cw));
+        const v4i hi = W4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sb + lds_off<RBW>(r, cw + 2));
+        f.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
       f.sb[j] = (ssb[4 * r] >> sh) & mask;
     }
   };
@@ -356,11 +383,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
         v8bf_t bb[FN];
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          bb[j] = fp8x8_to_bf16(f.b[j][2 * t], f.b[j][2 * t + 1], e8m0_to_f32((f.sb[j] >> (t < 2 ? 0 : 8)) & 0xff));
+          bb[j] = W4 ? fp4x8_to_bf16(f.b[j][t], e8m0_to_f32((f.sb[j] >> (t < 2 ? 0 : 8)) & 0xff))
+                     : fp8x8_to_bf16(f.b[j][2 * t], f.b[j][2 * t + 1], e8m0_to_f32((f.sb[j] >> (t < 2 ? 0 : 8)) & 0xff));
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const v8bf_t ab =
-              fp8x8_to_bf16(f.a[i][2 * t], f.a[i][2 * t + 1], e8m0_to_f32((f.sa[i] >> (t < 2 ? 0 : 8)) & 0xff));
+          const float sc = e8m0_to_f32((f.sa[i] >> (t < 2 ? 0 : 8)) & 0xff);
+          const v8bf_t ab = A4 ? fp4x8_to_bf16(f.a[i][t], sc) : fp8x8_to_bf16(f.a[i][2 * t], f.a[i][2 * t + 1], sc);
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, bb[j], acc[i][j], 0, 0, 0);
@@ -505,10 +533,10 @@ static hipError_t launch_mx_dma_cfg(const GemmArgs& a, hipStream_t st) {
 
 bool mx_dma_eligible(const GemmArgs& a, int mode) {
   if (mode != 0 && mode != 1) return false;
-  // e4m3 x e4m3 in either mode; any pair with an e2m1 operand in the scaled mode
-  const bool any4 = a.a_fp4 || a.w_fp4, both4 = a.a_fp4 && a.w_fp4;
-  if (any4 && mode != 1) return false;
-  if (a.K % (both4 ? 128 : 64) != 0 || a.lda_s % 4 != 0 || ((uintptr_t)a.ea & 3) != 0) return false;
+  // any pair of e4m3 / e2m1 operands in either mode; stages of 64 K, of 128 K
+  // for e2m1 x e2m1 in the scaled mode
+  const int kps = a.a_fp4 && a.w_fp4 && mode == 1 ? 128 : 64;
+  if (a.K % kps != 0 || a.lda_s % 4 != 0 || ((uintptr_t)a.ea & 3) != 0) return false;
   // one 256-row band of A (codes and scales) and of W in 32-bit byte offsets
   const int64_t rows = a.M < 256 ? a.M : 256;
   return (rows - 1) * a.lda + a.K < (int64_t(1) << 31) && (rows - 1) * a.lda_s + a.K / 32 + 4 < (int64_t(1) << 31) &&
@@ -520,20 +548,25 @@ static hipError_t launch_mx_dma(const GemmArgs& a, hipStream_t st) {
   // 256 x 256 tiles (8 waves of 128 x 64, a 4-stage ring, one workgroup per
   // CU) when they fill every CU; otherwise 128 x 128 tiles (4 waves of
   // 64 x 64, two workgroups per CU). Stages of 64 K (rows of 64 bytes of
-  // e4m3, 32 of e2m1), or 128 K when both operands are e2m1 (64-byte rows).
-  constexpr int KPS = A4 && W4 ? 128 : 64;
+  // e4m3, 32 of e2m1), or 128 K when both operands are e2m1 in the scaled
+  // mode (64-byte rows).
+  constexpr int KPS = A4 && W4 && !EXACT ? 128 : 64;
   const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   if (big >= cu_count()) return launch_mx_dma_cfg<256, 256, KPS, 2, 4, 4, EXACT, A4, W4, GROUPED>(a, st);
   return launch_mx_dma_cfg<128, 128, KPS, 2, 2, 4, EXACT, A4, W4, GROUPED>(a, st);
 }
 
+template <bool EXACT, bool GROUPED>
+static hipError_t launch_pair(const GemmArgs& a, hipStream_t st) {
+  if (a.a_fp4 && a.w_fp4) return launch_mx_dma<EXACT, true, true, GROUPED>(a, st);
+  if (a.a_fp4) return launch_mx_dma<EXACT, true, false, GROUPED>(a, st);
+  if (a.w_fp4) return launch_mx_dma<EXACT, false, true, GROUPED>(a, st);
+  return launch_mx_dma<EXACT, false, false, GROUPED>(a, st);
+}
+
 template <bool GROUPED>
 static hipError_t launch_mode(const GemmArgs& a, int mode, hipStream_t st) {
-  if (a.a_fp4 && a.w_fp4) return launch_mx_dma<false, true, true, GROUPED>(a, st);
-  if (a.a_fp4) return launch_mx_dma<false, true, false, GROUPED>(a, st);
-  if (a.w_fp4) return launch_mx_dma<false, false, true, GROUPED>(a, st);
-  return mode == 0 ? launch_mx_dma<true, false, false, GROUPED>(a, st)
-                   : launch_mx_dma<false, false, false, GROUPED>(a, st);
+  return mode == 0 ? launch_pair<true, GROUPED>(a, st) : launch_pair<false, GROUPED>(a, st);
 }
 
 hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st) { return launch_mode<false>(a, mode, st); }

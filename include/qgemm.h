@@ -349,9 +349,10 @@ int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t
  *            lda >= K) or packed e2m1 (QGEMM_FMT_MXFP4_E2M1, lda >= K/2), as
  *            written by qgemm_quantize_rows; lda % 16 == 0, 16-byte aligned.
  *   a_e8m0   device E8M0 [M][lda_s], lda_s >= K/32. With lda_s % 4 == 0, a
- *            4-byte aligned a_e8m0 and K % 64 == 0, e4m3 x e4m3 in
- *            QGEMM_MX_SCALED_MFMA mode runs on the LDS-DMA kernel, which
- *            reads each row's scales a dword at a time (never past lda_s).
+ *            4-byte aligned a_e8m0 and K % 64 == 0 (e2m1 x e2m1 in
+ *            QGEMM_MX_SCALED_MFMA mode: K % 128 == 0), the call runs on the
+ *            LDS-DMA kernel, which reads each row's scales a dword at a time
+ *            (never past lda_s).
  *   a_fmt    QGEMM_FMT_MXFP8_E4M3 or QGEMM_FMT_MXFP4_E2M1 (else QGEMM_E_MODE).
  *   w_desc   descriptor of MXFP8_E4M3 or MXFP4_E2M1 weights with the same K
  *            (K % 32 == 0).
@@ -388,8 +389,9 @@ int qgemm_run_mx(const uint8_t* a_codes, int64_t lda, const uint8_t* a_e8m0, int
  *
  *   a_codes, lda, a_e8m0, lda_s, a_fmt, out, ldo, mode: as qgemm_run_mx,
  *            for M_total rows; in addition lda_s % 4 == 0 and a_e8m0 4-byte
- *            aligned (QGEMM_E_ALIGN), and K % 64 == 0 for e4m3, K % 128 == 0
- *            for e2m1 (QGEMM_E_SHAPE). e2m1 runs in QGEMM_MX_SCALED_MFMA only.
+ *            aligned (QGEMM_E_ALIGN), and K % 64 == 0, or K % 128 == 0 for
+ *            e2m1 x e2m1 in QGEMM_MX_SCALED_MFMA mode (QGEMM_E_SHAPE). Any
+ *            pair of the two formats runs in either mode.
  *   M_total  rows of A and out, >= 0 (0: nothing is launched).
  *   offsets  device int64 [E + 1], non-decreasing, offsets[0] = 0 and
  *            offsets[E] = M_total, 8-byte aligned. It stays on the device (a

@@ -200,10 +200,12 @@ def test_run_mx_grouped_validation(lib):
     assert _grouped(lib, d=_wdesc()) == E_DESC                 # an int8 descriptor
     assert _grouped(lib, mode=2) == E_MODE
     assert _grouped(lib, af=INT8) == E_MODE
-    assert _grouped(lib, af=MX4) == E_MODE                     # an e2m1 operand runs scaled only
-    assert _grouped(lib, af=MX4, lda=160, mode=1, M=0, a=None, e=None, off=None, out=None) == OK  # mixed pair
+    # any e4m3 / e2m1 pair in either mode (M = 0: validation only)
+    assert _grouped(lib, af=MX4, lda=160, mode=1, M=0, a=None, e=None, off=None, out=None) == OK
+    assert _grouped(lib, af=MX4, lda=160, mode=0, M=0, a=None, e=None, off=None, out=None) == OK
     d4 = _mxdesc(K=384, fmt=MX4)
-    assert _grouped(lib, d=d4, af=MX4, lda=192, ldas=12, mode=0) == E_MODE   # e2m1 runs scaled only
+    assert _grouped(lib, d=d4, af=MX4, lda=192, ldas=12, mode=0, M=0, a=None, e=None, off=None, out=None) == OK
+    assert _grouped(lib, d=d4, af=MX4, lda=192, ldas=12, mode=2) == E_MODE
     assert _grouped(lib, E=0) == E_SHAPE
     assert _grouped(lib, E=4097) == E_SHAPE
     assert _grouped(lib, M=-1) == E_SHAPE

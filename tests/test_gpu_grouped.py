@@ -105,17 +105,20 @@ def test_grouped_mxfp4_scaled(ops):
     _check(got, ref, S, MX_STOL)
 
 
-@pytest.mark.parametrize("fa,fw", [(E4M3, E2M1), (E2M1, E4M3)])
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("fa,fw", [(E4M3, E2M1), (E2M1, E4M3), (E2M1, E2M1)])
 @pytest.mark.parametrize("sizes,N,K", [([40, 300, 0, 129], 150, 384), ([700, 0, 1, 1023, 256, 513, 900, 710], 4320, 128)])
-def test_grouped_mx_mixed_pairs(ops, sizes, N, K, fa, fw):
-    """e4m3 x e2m1 either way on the block-scaled matrix cores, each operand
-    in its own layout and format code (the second case on 256 x 256 tiles),
-    within the scaled mode's e4m3 bound."""
-    print_case("grouped mx mixed", sizes, N, K, fa, fw)
+def test_grouped_mx_e2m1_pairs(ops, sizes, N, K, fa, fw, mode):
+    """Pairs with an e2m1 operand: the exact mode (e2m1 codes converted to
+    bf16 after the fragment read) within 1e-5 * S, the block-scaled matrix
+    cores (each operand in its own layout and format code) within the scaled
+    mode's e4m3 bound, 1e-5 * S for e2m1 x e2m1; the second case on 256 x 256
+    tiles."""
+    print_case("grouped mx e2m1 pairs", sizes, N, K, fa, fw, "mode", mode)
     A, W, off, a, w = _setup(ops, sizes, N, K, fmt=fa, wfmt=fw, seed=17 + K)
-    got = host(ops.qgemm_run_mx_grouped(a, w, dev(off), mode=1))
+    got = host(ops.qgemm_run_mx_grouped(a, w, dev(off), mode=mode))
     ref, S = _ref(A, W, off, fmt=fa, wfmt=fw)
-    _check(got, ref, S, MX_SCALED_STOL)
+    _check(got, ref, S, MX_SCALED_STOL if mode == 1 and (fa, fw) != (E2M1, E2M1) else MX_STOL)
 
 
 @pytest.mark.parametrize("fmt,mode", [(E4M3, 0), (E4M3, 1), (E2M1, 1)])
