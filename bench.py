@@ -55,7 +55,29 @@ DESCRIPTION = {
 }
 
 
-def algorithmic(name, M, K, N, w4a8=False, fp4=False):
+MX_PAIRS = ["e4m3", "e2m1", "e4m3xe2m1", "e2m1xe4m3"]
+MX_NAMES = {"e4m3": "fp8-e4m3", "e2m1": "fp4-e2m1"}
+
+
+def mx_pair(arg):
+    """--mx-format: one element format for A and W, or 'AxW'. Returns
+    (A is e2m1, W is e2m1)."""
+    fa, _, fw = arg.partition("x")
+    return fa == "e2m1", (fw or fa) == "e2m1"
+
+
+def mx_tags(arg):
+    """dtype string, workload note and profile-name suffix of an MX format pair."""
+    fa, _, fw = arg.partition("x")
+    fw = fw or fa
+    dtype = MX_NAMES[fa] if fa == fw else f"{MX_NAMES[fa]} x {MX_NAMES[fw]}"
+    note = "" if arg == "e4m3" else (" -- MXFP4: e2m1 A and W, E8M0 per 32" if arg == "e2m1"
+                                     else f" -- {fa} A x {fw} W, E8M0 per 32")
+    suffix = "" if arg == "e4m3" else ("_fp4" if arg == "e2m1" else "_" + arg)
+    return dtype, note, suffix
+
+
+def algorithmic(name, M, K, N, w4a8=False, fp4=False, wfp4=None):
     """Ops and algorithmic bytes: whole step, and the GEMM kernel alone.
 
     Whole step: float32 A read once, W codes + per-channel scales/column sums
@@ -70,9 +92,10 @@ def algorithmic(name, M, K, N, w4a8=False, fp4=False):
         w = N * K / 2 + 4 * N * math.ceil(K / 64)
         a_codes = M * K + 4 * M
     elif act == "mxfp8":
-        cb = 0.5 if fp4 else 1.0  # code bytes per element: e2m1 packs two per byte
-        w = cb * N * K + N * (K // 32)
-        a_codes = cb * M * K + M * (K // 32)
+        cb_a = 0.5 if fp4 else 1.0  # code bytes per element: e2m1 packs two per byte
+        cb_w = 0.5 if (fp4 if wfp4 is None else wfp4) else 1.0
+        w = cb_w * N * K + N * (K // 32)
+        a_codes = cb_a * M * K + M * (K // 32)
     else:
         w = N * K + 8 * N
         a_codes = M * K + 8 * M
@@ -115,7 +138,7 @@ def measured_traffic(name):
     return float(t["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False, fp4=False):
+def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False, fp4=False, wfp4=None):
     """The oracle, untuned, on a bounded sample of the same workload.
     fused: (gamma, eps, bias) to time the RMSNorm-fused step with a bias;
     w4a8: int4 per-group-64 weights and the per-group GEMM."""
@@ -131,10 +154,11 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False, fp4=False):
     N = W.shape[0]
     if act == "mxfp8":
         rows = min(M, 64)
+        wfp4 = fp4 if wfp4 is None else wfp4
         quant = O.quantize_mxfp4 if fp4 else O.quantize_mx
         fmt = "e2m1" if fp4 else "e4m3"
-        Wq, We = quant(W)                             # offline weight preparation, untimed
-        Wd = O.mx_dequantize(Wq, We, fmt)
+        Wq, We = (O.quantize_mxfp4 if wfp4 else O.quantize_mx)(W)   # offline weight preparation, untimed
+        Wd = O.mx_dequantize(Wq, We, "e2m1" if wfp4 else "e4m3")
         sample = f"{rows} of {M} rows of A against all of W (W prepared outside the timing)"
     elif w4a8:
         rows = min(M, 256)
@@ -176,7 +200,7 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False, fp4=False):
     ops = 2.0 * rows * K * N * reps
     unit = "GB/s" if WORKLOADS[name][4] == "GB/s" else WORKLOADS[name][4]
     if unit == "GB/s":
-        _, step_bytes, _ = algorithmic(name, rows, K, N, w4a8, fp4)
+        _, step_bytes, _ = algorithmic(name, rows, K, N, w4a8, fp4, wfp4)
         value = step_bytes * reps / el / 1e9
     else:
         value = ops / el / 1e12
@@ -221,7 +245,7 @@ def calibration_copy(mib, dev):
     torch.cuda.synchronize()
 
 
-def cpu_baseline_grouped(A, W, sizes, fp4, budget_s=10.0):
+def cpu_baseline_grouped(A, W, sizes, fp4, budget_s=10.0, wfp4=None):
     """The oracle's grouped reference, untuned, on a bounded sample: up to 16
     rows of every expert against the first 1024 output columns of its weights
     (prepared outside the timing)."""
@@ -232,11 +256,13 @@ def cpu_baseline_grouped(A, W, sizes, fp4, budget_s=10.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = 1
+    wfp4 = fp4 if wfp4 is None else wfp4
     quant = O.quantize_mxfp4 if fp4 else O.quantize_mx
     f = "e2m1" if fp4 else "e4m3"
+    fw = "e2m1" if wfp4 else "e4m3"
     W = np.ascontiguousarray(W[:, :1024])
     E, N, K = W.shape
-    qw, Ew = quant(W.reshape(E * N, K))
+    qw, Ew = (O.quantize_mxfp4 if wfp4 else O.quantize_mx)(W.reshape(E * N, K))
     qw, Ew = qw.reshape(E, N, K), Ew.reshape(E, N, K // 32)
     off = np.concatenate([[0], np.cumsum(sizes)])
     take = [np.arange(off[e], off[e] + min(16, sizes[e])) for e in range(E)]
@@ -245,7 +271,7 @@ def cpu_baseline_grouped(A, W, sizes, fp4, budget_s=10.0):
     reps, t0 = 0, time.perf_counter()
     while True:
         qa, Ea = quant(As)
-        O.mx_grouped_gemm_ref(qa, Ea, offs, qw, Ew, f, f)
+        O.mx_grouped_gemm_ref(qa, Ea, offs, qw, Ew, f, fw)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 1000:
@@ -264,16 +290,14 @@ def main_grouped(args):
     from block_scaled_quantized_qgemm_amd.inputs import make_moe_inputs
 
     name = args.workload
-    fp4 = args.mx_format == "e2m1"
+    fp4, wfp4 = mx_pair(args.mx_format)
+    dtype, note, suffix = mx_tags(args.mx_format)
     mx_mode = ops.MX_EXACT if args.mx_mode == "exact" else ops.MX_SCALED_MFMA
-    if fp4 and mx_mode == ops.MX_EXACT:
-        print("bench.py: the grouped GEMM runs e2m1 on the block-scaled matrix cores only "
-              "(--mx-mode scaled-mfma)", file=sys.stderr)
-        sys.exit(2)
     if args.fused or args.w4a8:
         print("bench.py: --fused and --w4a8 do not apply to the grouped workload", file=sys.stderr)
         sys.exit(2)
     fmt = ops.FMT_MXFP4_E2M1 if fp4 else ops.FMT_MXFP8_E4M3
+    wfmt = ops.FMT_MXFP4_E2M1 if wfp4 else ops.FMT_MXFP8_E4M3
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     A_np, W_np, sizes = make_moe_inputs(name)
@@ -281,13 +305,13 @@ def main_grouped(args):
     M = A_np.shape[0]
     A0 = torch.from_numpy(A_np).to(dev)
     W0 = torch.from_numpy(W_np).to(dev)
-    w0 = ops.qgemm_prepack_experts(W0, fmt)
+    w0 = ops.qgemm_prepack_experts(W0, wfmt)
     del W0
     offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)).to(dev)
     torch.cuda.synchronize()
 
     ops_count = 2.0 * M * N * K
-    cb = 0.5 if fp4 else 1.0
+    cb = 0.5 if wfp4 else 1.0
     w_bytes = E * (cb * N * K + N * (K // 32))
     step_bytes = 4.0 * M * K + w_bytes + 4.0 * M * N
     set_bytes = A0.numel() * 4 + w0.packed.numel() + M * N * 4 + M * K
@@ -318,17 +342,17 @@ def main_grouped(args):
     torch.cuda.synchronize()
     ms_per_step, wall = timed(step, args.steps, args.eager)
     gemm_ms, _ = timed(gemm, args.steps, args.eager)
-    peak = PEAK_BF16_TFLOPS if mx_mode == ops.MX_EXACT else (PEAK_FP4_TFLOPS if fp4 else PEAK_FP8_TFLOPS)
+    # a pair with an e4m3 operand issues at the fp8 rate
+    peak = PEAK_BF16_TFLOPS if mx_mode == ops.MX_EXACT else (PEAK_FP4_TFLOPS if fp4 and wfp4 else PEAK_FP8_TFLOPS)
     roof = {"bound": "mfma", "achieved": ops_count / (gemm_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(name + ("_fp4" if fp4 else "") + ("_scaled" if mx_mode != ops.MX_EXACT else ""))
+    roof["traffic"] = measured_traffic(name + suffix + ("_scaled" if mx_mode != ops.MX_EXACT else ""))
     line = {
         "metric": METRIC, "value": ops_count / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp4-e2m1" if fp4 else "fp8-e4m3",
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic (seeded generator with the workload's shapes and distributions)",
-        "config": {"workload": f"{name}: {DESCRIPTION[name]} ({args.mx_mode} mode)"
-                               + (" -- MXFP4: e2m1 A and W, E8M0 per 32" if fp4 else ""),
+        "config": {"workload": f"{name}: {DESCRIPTION[name]} ({args.mx_mode} mode)" + note,
                    "experts": E, "M_total": M, "K": K, "N": N, "rows_per_expert": [int(x) for x in sizes],
                    "rotating_buffer_sets": nsets, "gemm_ms": gemm_ms,
                    "launch": "eager" if args.eager else "hip graph (K steps captured, replayed once)",
@@ -340,7 +364,7 @@ def main_grouped(args):
     print(f"[bench] {name}: {ms_per_step * 1e3:.2f} us/step, gemm {gemm_ms * 1e3:.2f} us, "
           f"wall {wall:.3f} s for {args.steps} steps", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_grouped(A_np, W_np, sizes, fp4, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline_grouped(A_np, W_np, sizes, fp4, args.cpu_budget, wfp4)
     print(json.dumps(line), flush=True)
 
 
@@ -364,8 +388,9 @@ def main():
     ap.add_argument("--w4a8", action="store_true",
                     help="symmetric int8 workloads: int4 weights with a float32 scale per group of 64 K "
                          "(qgemm_run_w4a8)")
-    ap.add_argument("--mx-format", default="e4m3", choices=["e4m3", "e2m1"],
-                    help="MX workload: element format of activations and weights (e2m1: MXFP4)")
+    ap.add_argument("--mx-format", default="e4m3", choices=MX_PAIRS,
+                    help="MX workloads: element format of activations and weights (e2m1: MXFP4), or a "
+                         "pair 'AxW' (e4m3xe2m1: e4m3 activations, e2m1 weights)")
     ap.add_argument("--mx-mode", default="exact", choices=["exact", "scaled-mfma"],
                     help="MX workload: exact products (bf16 matrix cores) or block-scaled fp8 matrix cores")
     args = ap.parse_args()
@@ -390,9 +415,10 @@ def main():
     if args.w4a8 and act != "int8_sym":
         print("bench.py: --w4a8 applies to the symmetric int8 workloads", file=sys.stderr)
         sys.exit(2)
-    fp4 = args.mx_format == "e2m1"
-    if fp4 and act != "mxfp8":
-        print("bench.py: --mx-format e2m1 applies to the MX workload", file=sys.stderr)
+    fp4, wfp4 = mx_pair(args.mx_format)
+    mx_dtype, mx_note, mx_suffix = mx_tags(args.mx_format)
+    if args.mx_format != "e4m3" and act != "mxfp8":
+        print("bench.py: --mx-format applies to the MX workloads", file=sys.stderr)
         sys.exit(2)
     M, K, N, _, _ = SHAPES[name]
     dev = torch.device("cuda:0")
@@ -409,12 +435,13 @@ def main():
     mx_mode = ops.MX_EXACT if args.mx_mode == "exact" else ops.MX_SCALED_MFMA
     A0 = torch.from_numpy(A_np).to(dev)
     W0 = torch.from_numpy(W_np).to(dev)
-    wfmt = fmt if act == "mxfp8" else ops.FMT_INT8_SYM   # weights are symmetric
+    wfmt = ((ops.FMT_MXFP4_E2M1 if wfp4 else ops.FMT_MXFP8_E4M3) if act == "mxfp8"
+            else ops.FMT_INT8_SYM)   # int8 weights are symmetric
     if args.w4a8:
         wfmt, wgr = ops.FMT_INT4_SYM, ops.GRAN_GROUP64
     w0 = ops.qgemm_prepack_weights(W0, wfmt, wgr)
     torch.cuda.synchronize()
-    ops_count, step_bytes, gemm_bytes = algorithmic(name, M, K, N, args.w4a8, fp4)
+    ops_count, step_bytes, gemm_bytes = algorithmic(name, M, K, N, args.w4a8, fp4, wfp4)
     if args.fused:  # the norm weight and the bias are read once more
         step_bytes += 4 * K + 4 * N
         gemm_bytes += 4 * N
@@ -486,12 +513,13 @@ def main():
         value = ops_count / (ms_per_step * 1e-3) / 1e12
         gemm_achieved = ops_count / (gemm_ms * 1e-3) / 1e12
         if act == "mxfp8":
-            peak = PEAK_BF16_TFLOPS if mx_mode == ops.MX_EXACT else (PEAK_FP4_TFLOPS if fp4 else PEAK_FP8_TFLOPS)
+            # a pair with an e4m3 operand issues at the fp8 rate
+            peak = PEAK_BF16_TFLOPS if mx_mode == ops.MX_EXACT else (PEAK_FP4_TFLOPS if fp4 and wfp4 else PEAK_FP8_TFLOPS)
         else:
             peak = PEAK_INT8_TOPS
         roof = {"bound": "mfma", "achieved": gemm_achieved, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(name + ("_w4a8" if args.w4a8 else "") + ("_fp4" if fp4 else "")
+    roof["traffic"] = measured_traffic(name + ("_w4a8" if args.w4a8 else "") + mx_suffix
                                        + ("_scaled" if act == "mxfp8" and mx_mode != ops.MX_EXACT else ""))
 
     line = {
@@ -505,11 +533,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp4-e2m1" if fp4 else "fp8-e4m3") if act == "mxfp8" else ("i8 x i4" if args.w4a8 else "i8"),
+        "dtype": mx_dtype if act == "mxfp8" else ("i8 x i4" if args.w4a8 else "i8"),
         "data": "synthetic (seeded generator with the workload's shapes and distributions)",
         "config": {"workload": f"{name}: {DESCRIPTION[name]}"
                    + (f" ({args.mx_mode} mode)" if act == "mxfp8" else "")
-                   + (" -- MXFP4: e2m1 A and W, E8M0 per 32" if fp4 else "")
+                   + (mx_note if act == "mxfp8" else "")
                    + (" with RMSNorm fused into the quantizer and a float32 bias" if args.fused else "")
                    + (" -- W4A8: int4 W with a float32 scale per group of 64 K" if args.w4a8 else ""),
                    "M": M, "K": K, "N": N,
@@ -525,7 +553,7 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(name, A_np, W_np, args.cpu_budget,
                                             (gamma.cpu().numpy(), eps, bias.cpu().numpy()) if args.fused else None,
-                                            args.w4a8, fp4)
+                                            args.w4a8, fp4, wfp4)
     print(json.dumps(line), flush=True)
 
 
