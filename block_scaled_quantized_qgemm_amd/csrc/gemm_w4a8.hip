@@ -297,28 +297,41 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_w4a8_tiled_kernel(GemmArgs p
 #pragma unroll
     for (int j = 0; j < FN; ++j) y[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // group g of a stage; the loads of stage ks after MFMA `slot` when first
+  // group g of a stage; the loads of stage ks after MFMA `slot` when first.
+  // Software-pipelined: the scaling of MFMA k's exact sum is issued after
+  // MFMA k + PD, so the conversions and FMAs run while the matrix cores work
+  // instead of waiting for each result in turn (the sums are the same, each
+  // scaled and added to its own accumulator in the same order).
   auto group = [&](const Frag& f, int g, bool first, int ks, int sl, bool live) {
     const v4i zero = {0, 0, 0, 0};
+    constexpr int NM = FN * FM, PD = 4;
+    v4i wg[FN];
+    float sc[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const v4i w = f.w[j];
-      const v4i wg = g == 0 ? v4i{(w.x << 4) & kHi, w.x & kHi, (w.y << 4) & kHi, w.y & kHi}
-                            : v4i{(w.z << 4) & kHi, w.z & kHi, (w.w << 4) & kHi, w.w & kHi};
-      const float sc = g == 0 ? f.s[j].x : f.s[j].y;
+      wg[j] = g == 0 ? v4i{(w.x << 4) & kHi, w.x & kHi, (w.y << 4) & kHi, w.y & kHi}
+                     : v4i{(w.z << 4) & kHi, w.z & kHi, (w.w << 4) & kHi, w.w & kHi};
+      sc[j] = g == 0 ? f.s[j].x : f.s[j].y;
+    }
+    v4i c[NM];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[g][i], wg, zero, 0, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[i][j][e] = __builtin_fmaf(sc, (float)c[e], y[i][j][e]);
+    for (int k = 0; k < NM + PD; ++k) {
+      if (k < NM) {
+        const int j = k / FM, i = k % FM;
+        c[k] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[g][i], wg[j], zero, 0, 0, 0);
         if (first) {
-          const int slot = j * FM + i;
 #pragma unroll
           for (int d = 0; d < IPW; ++d)
-            if ((d * SLOTS) / IPW == slot) dma(ks, sl, d, live);
+            if ((d * SLOTS) / IPW == k) dma(ks, sl, d, live);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      if (k >= PD) {
+        const int q = k - PD, j = q / FM, i = q % FM;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[i][j][e] = __builtin_fmaf(sc[j], (float)c[q][e], y[i][j][e]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
