@@ -1,5 +1,5 @@
-// MX GEMM (e4m3 x e4m3, one E8M0 scale per 32 K of each row of A and W,
-// float32 output) on an LDS-DMA ring, for gfx950.
+// MX GEMM (e4m3 or e2m1 activations and weights, one E8M0 scale per 32 K of
+// each row of A and W, float32 output) on an LDS-DMA ring, for gfx950.
 //
 // The block-scaled product ("TileLang tutorial, chapter 27", sections 4.1 and
 // 4.3): out[m][n] = sum over 32-blocks b of 2^(Ea[m][b]-127) 2^(Ew[n][b]-127)

@@ -72,12 +72,13 @@ struct GemmArgs {
 
 // qgemm_run: int8 GEMM + epilogue. out_type: 0 f32, 1 bf16, 2 i32 (no bias).
 hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_t st);
-// qgemm_run_mx: block-scaled e4m3 GEMM, float32 output. mode 0: exact products
-// (bf16 matrix cores on dequantized values), mode 1: block-scaled fp8 matrix cores.
+// qgemm_run_mx: block-scaled GEMM of any e4m3 / e2m1 pair, float32 output.
+// mode 0: exact products (bf16 matrix cores on dequantized values), mode 1:
+// block-scaled fp8 / fp4 matrix cores.
 hipError_t launch_gemm_mx(const GemmArgs& a, int mode, hipStream_t st);
-// The e4m3 x e4m3 block-scaled GEMM on an LDS-DMA ring (gemm_mx_dma.hip), in
-// either mode: whether it takes these arguments (K % 64 == 0, dword-aligned
-// activation scale rows), and its launcher.
+// The block-scaled GEMM on an LDS-DMA ring (gemm_mx_dma.hip), any pair in
+// either mode: whether it takes these arguments (K % 64 == 0, e2m1 x e2m1 in
+// mode 1: K % 128 == 0; dword-aligned activation scale rows), and its launcher.
 bool mx_dma_eligible(const GemmArgs& a, int mode);
 hipError_t launch_gemm_mx_dma(const GemmArgs& a, int mode, hipStream_t st);
 // qgemm_run_mx_grouped: the same kernel over E experts' row groups (a.M is
