@@ -15,21 +15,36 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
-// Wave-wide reductions (64 lanes) over a value every lane holds.
+// Wave-wide reductions (64 lanes) over a value every lane holds, by DPP moves
+// inside the VALU instead of round trips through the LDS unit: two quad
+// swaps, the half-row and row mirrors (each lane then holds its row of 16),
+// the broadcast of lane 15 into rows 1 and 3 and of lane 31 into rows 2 and 3
+// (lanes of the other rows take `id`, the operation's identity), so lane 63
+// holds the whole wave's result, which is then read out to every lane. Max,
+// min and integer sums do not depend on the order, so the result is exactly
+// that of any other reduction order.
+template <typename Op>
+__device__ inline int wave_reduce_dpp(int v, int id, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
+}
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return __int_as_float(wave_reduce_dpp(__float_as_int(v), __float_as_int(-INFINITY), [](int x, int y) {
+    return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y)));
+  }));
 }
 __device__ inline float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return __int_as_float(wave_reduce_dpp(__float_as_int(v), __float_as_int(INFINITY), [](int x, int y) {
+    return __float_as_int(fminf(__int_as_float(x), __int_as_float(y)));
+  }));
 }
 __device__ inline int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce_dpp(v, 0, [](int x, int y) { return x + y; });
 }
 
 // dword 3 of a raw buffer descriptor: 32-bit data format, no swizzle
