@@ -409,9 +409,11 @@ __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __re
     v = make_float4(xr[0], xr[1], xr[2], xr[3]);
   if (!valid) v = make_float4(0.f, 0.f, 0.f, 0.f);
   float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  a = fmaxf(a, __shfl_xor(a, 1, kWave));
-  a = fmaxf(a, __shfl_xor(a, 2, kWave));
-  a = fmaxf(a, __shfl_xor(a, 4, kWave));
+  // the block's eight lanes by DPP moves (quad swaps, then the half-row
+  // mirror), not through the LDS unit; a >= 0, so lanes read as 0 are harmless
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x141, 0xF, 0xF, false)));
   a = fmaxf(a, 1e-4f);
   const int E = ceil_to_ue8m0(a / (FP4 ? 6.0f : 448.0f));
   const float inv = e8m0_inverse(E);
