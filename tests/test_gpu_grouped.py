@@ -82,11 +82,12 @@ def test_grouped_mx_parity(ops, sizes, N, K, mode):
 
 
 @pytest.mark.parametrize("mode", [0, 1])
-def test_grouped_mx_large_tiles_uneven_experts(ops, mode):
-    """Enough rows for the 256x256 tiles; 8 experts of uneven sizes (one
-    empty, several ragged), so tile-rows of one expert never take rows of the
-    next."""
-    sizes = [700, 0, 1, 1023, 256, 513, 900, 710]
+@pytest.mark.parametrize("sizes", [[700, 0, 1, 1023, 256, 513, 900, 710], [2100, 2571]])
+def test_grouped_mx_large_tiles_uneven_experts(ops, sizes, mode):
+    """Enough rows for the 256x256 tiles; experts of uneven sizes (one empty,
+    several ragged), so tile-rows of one expert never take rows of the next.
+    The exact mode takes the 128x128 tiles when the average expert has under
+    2048 rows (the first layout) and the 256x256 ones otherwise."""
     N, K = 4352 - 32, 256
     print_case("grouped mx large", sizes, N, K, "mode", mode)
     A, W, off, a, w = _setup(ops, sizes, N, K, seed=11 + mode)
