@@ -8,8 +8,11 @@ on the pages) and every input is resident in HBM before the timed region.
 Activation / weight / output buffers rotate over enough copies that the
 256 MB Infinity Cache cannot hold the working set.
 
-Prints one JSON line. Default workload: 512 tokens x K=4096 x N=4096,
-per-token int8 activations, per-channel int8 weights, float32 output.
+Prints one JSON line. Default workload: the large-M GEMM, 2048 tokens x
+K=4096 x N=11008 with per-token asymmetric uint8 activations (zero point),
+per-channel int8 weights and bfloat16 output; the same line carries, under
+"secondary", the decode-shaped GEMM (8 x 4096 x 14336, HBM GB/s) and the
+MXFP8 GEMM (8192^3) in both MX modes, each with its own roofline.
 """
 from __future__ import annotations
 
@@ -33,6 +36,13 @@ PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X (the exact MX mode runs on 
 PEAK_FP4_TFLOPS = 10100.0  # dense fp4 / fp6 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0     # HBM3E
 MALL_BYTES = 256 << 20
+
+
+def mx_peak(fp4, wfp4):
+    """Dense matrix-core peak of an MX contraction: MXFP4 x MXFP4 runs at the
+    fp4 rate, any pair with an e4m3 operand at the fp8 rate. Both MX modes are
+    priced against it (the exact mode's bf16 matrix cores reach half of it)."""
+    return PEAK_FP4_TFLOPS if fp4 and wfp4 else PEAK_FP8_TFLOPS
 MOE = ("c6_moe_mxfp8",)   # grouped (MoE) workloads: bench.main_grouped
 
 # name -> (activation format, granularity, weight granularity, output type, headline unit)
@@ -138,6 +148,20 @@ def measured_traffic(name):
     return float(t["hbm_bytes_per_launch"])
 
 
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo) and its logical CPU count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_logical_cpus": os.cpu_count()}
+
+
 def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False, fp4=False, wfp4=None):
     """The oracle, untuned, on a bounded sample of the same workload.
     fused: (gamma, eps, bias) to time the RMSNorm-fused step with a bias;
@@ -205,7 +229,8 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False, fp4=False, w
     else:
         value = ops / el / 1e12
     return {"value": value, "unit": unit, "cores": int(cores), "kind": "oracle",
-            "sample": f"{sample}; {reps} passes in {el:.1f} s"}
+            "sample": f"{sample}; {reps} passes in {el:.1f} s", **host_cpu(),
+            "threads": "cores = the BLAS thread pool the oracle's matrix products ran on"}
 
 
 def timed(fn, steps, eager):
@@ -278,7 +303,8 @@ def cpu_baseline_grouped(A, W, sizes, fp4, budget_s=10.0, wfp4=None):
             break
     return {"value": 2.0 * len(As) * N * K * reps / el / 1e12, "unit": "TFLOPS", "cores": int(cores),
             "kind": "oracle", "sample": f"up to 16 rows of each expert ({len(As)} rows) against {N} columns of its weights "
-                                        f"(weights prepared outside the timing); {reps} passes in {el:.1f} s"}
+                                        f"(weights prepared outside the timing); {reps} passes in {el:.1f} s",
+            **host_cpu(), "threads": "cores = the BLAS thread pool the oracle's matrix products ran on"}
 
 
 def main_grouped(args):
@@ -342,10 +368,13 @@ def main_grouped(args):
     torch.cuda.synchronize()
     ms_per_step, wall = timed(step, args.steps, args.eager)
     gemm_ms, _ = timed(gemm, args.steps, args.eager)
-    # a pair with an e4m3 operand issues at the fp8 rate
-    peak = PEAK_BF16_TFLOPS if mx_mode == ops.MX_EXACT else (PEAK_FP4_TFLOPS if fp4 and wfp4 else PEAK_FP8_TFLOPS)
+    peak = mx_peak(fp4, wfp4)
     roof = {"bound": "mfma", "achieved": ops_count / (gemm_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["step_frac"] = ops_count / (ms_per_step * 1e-3) / 1e12 / peak
+    if mx_mode == ops.MX_EXACT:
+        roof["exact_mode_ceiling_frac"] = PEAK_BF16_TFLOPS / peak
+        roof["frac_of_bf16_cores"] = roof["achieved"] / PEAK_BF16_TFLOPS
     roof["traffic"] = measured_traffic(name + suffix + ("_scaled" if mx_mode != ops.MX_EXACT else ""))
     line = {
         "metric": METRIC, "value": ops_count / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOPS", "n_gpus": 1,
@@ -373,7 +402,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2_per_token", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c3_asym_uint8", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="measure the chosen workload only (by default the large-M headline also carries the "
+                         "decode-shaped and the MXFP8 workloads under 'secondary')")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough to exceed the MALL 3x)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -402,12 +434,31 @@ def main():
     if args.workload in MOE:
         return main_grouped(args)
 
+    line = measure(args, args.workload, args.mx_mode, not args.no_cpu_baseline)
+    if (not args.no_secondary and args.workload == "c3_asym_uint8" and not (args.fused or args.w4a8)):
+        import torch
+        sec = {}
+        for key, wl, mode in (("c4_decode", "c4_decode", "exact"),
+                              ("c5_mxfp8_exact", "c5_mxfp8", "exact"),
+                              ("c5_mxfp8_scaled", "c5_mxfp8", "scaled-mfma")):
+            torch.cuda.empty_cache()
+            sub = argparse.Namespace(**{**vars(args), "mx_format": "e4m3", "rotate": 0, "calibration_copy": 0})
+            l2 = measure(sub, wl, mode, False)
+            sec[key] = {"workload": l2["config"]["workload"], "value": l2["value"], "unit": l2["unit"],
+                        "ms_per_step": l2["ms_per_step"], "gemm_ms": l2["config"]["gemm_ms"],
+                        "dtype": l2["dtype"], "roofline": l2["roofline"]}
+        line["secondary"] = sec
+    print(json.dumps(line), flush=True)
+
+
+def measure(args, name, mx_mode_arg, with_cpu):
+    """Time one workload (K whole steps, then K GEMM launches) and return its
+    JSON line (without printing it)."""
     import numpy as np
     import torch
     from block_scaled_quantized_qgemm_amd import ops
     from block_scaled_quantized_qgemm_amd.inputs import make_inputs, WORKLOADS as SHAPES
 
-    name = args.workload
     act, gran, wgran, out, unit = WORKLOADS[name]
     if args.fused and (act == "mxfp8" or gran != "row"):
         print("bench.py: --fused applies to the per-token int8 / uint8 workloads", file=sys.stderr)
@@ -432,7 +483,7 @@ def main():
     otype = {"f32": ops.OUT_F32, "bf16": ops.OUT_BF16}[out]
     odt = {"f32": torch.float32, "bf16": torch.bfloat16}[out]
 
-    mx_mode = ops.MX_EXACT if args.mx_mode == "exact" else ops.MX_SCALED_MFMA
+    mx_mode = ops.MX_EXACT if mx_mode_arg == "exact" else ops.MX_SCALED_MFMA
     A0 = torch.from_numpy(A_np).to(dev)
     W0 = torch.from_numpy(W_np).to(dev)
     wfmt = ((ops.FMT_MXFP4_E2M1 if wfp4 else ops.FMT_MXFP8_E4M3) if act == "mxfp8"
@@ -512,13 +563,15 @@ def main():
     else:
         value = ops_count / (ms_per_step * 1e-3) / 1e12
         gemm_achieved = ops_count / (gemm_ms * 1e-3) / 1e12
-        if act == "mxfp8":
-            # a pair with an e4m3 operand issues at the fp8 rate
-            peak = PEAK_BF16_TFLOPS if mx_mode == ops.MX_EXACT else (PEAK_FP4_TFLOPS if fp4 and wfp4 else PEAK_FP8_TFLOPS)
-        else:
-            peak = PEAK_INT8_TOPS
+        peak = mx_peak(fp4, wfp4) if act == "mxfp8" else PEAK_INT8_TOPS
         roof = {"bound": "mfma", "achieved": gemm_achieved, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # the whole step (quantize + GEMM + epilogue) against the same peak
+    roof["step_frac"] = value / roof["peak"]
+    if act == "mxfp8" and mx_mode == ops.MX_EXACT:
+        # exact products run on the bf16 matrix cores: at most half the MXFP8 peak
+        roof["exact_mode_ceiling_frac"] = PEAK_BF16_TFLOPS / roof["peak"]
+        roof["frac_of_bf16_cores"] = roof["achieved"] / PEAK_BF16_TFLOPS
     roof["traffic"] = measured_traffic(name + ("_w4a8" if args.w4a8 else "") + mx_suffix
                                        + ("_scaled" if act == "mxfp8" and mx_mode != ops.MX_EXACT else ""))
 
@@ -536,7 +589,7 @@ def main():
         "dtype": mx_dtype if act == "mxfp8" else ("i8 x i4" if args.w4a8 else "i8"),
         "data": "synthetic (seeded generator with the workload's shapes and distributions)",
         "config": {"workload": f"{name}: {DESCRIPTION[name]}"
-                   + (f" ({args.mx_mode} mode)" if act == "mxfp8" else "")
+                   + (f" ({mx_mode_arg} mode)" if act == "mxfp8" else "")
                    + (mx_note if act == "mxfp8" else "")
                    + (" with RMSNorm fused into the quantizer and a float32 bias" if args.fused else "")
                    + (" -- W4A8: int4 W with a float32 scale per group of 64 K" if args.w4a8 else ""),
@@ -550,11 +603,11 @@ def main():
         calibration_copy(args.calibration_copy, dev)
     print(f"[bench] {name}: {ms_per_step * 1e3:.2f} us/step, gemm {gemm_ms * 1e3:.2f} us, "
           f"wall {wall:.3f} s for {K_steps} steps", file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
+    if with_cpu:
         line["cpu_baseline"] = cpu_baseline(name, A_np, W_np, args.cpu_budget,
                                             (gamma.cpu().numpy(), eps, bias.cpu().numpy()) if args.fused else None,
                                             args.w4a8, fp4, wfp4)
-    print(json.dumps(line), flush=True)
+    return line
 
 
 if __name__ == "__main__":

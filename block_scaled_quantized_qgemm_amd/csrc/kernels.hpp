@@ -15,7 +15,8 @@ void launch_quantize_int(const float* x, int64_t rows, int64_t K, int64_t ldx, b
                          uint8_t* q, int64_t ldq, int64_t kblocks, float* scales, int32_t* zeros, int32_t* colsum,
                          float* ws, hipStream_t st);
 
-// RMSNorm (float64 sum of squares, float32 normalized row (x * r) * gamma)
+// RMSNorm (double-double sum of squares, float32 rms, normalized row
+// (x / rms) * gamma in float32)
 // fused with per-row symmetric int8 / asymmetric uint8 quantization.
 void launch_rmsnorm_quantize(const float* x, int64_t rows, int64_t K, int64_t ldx, const float* gamma, float eps,
                              bool asym, uint8_t* q, int64_t ldq, float* scales, int32_t* zeros, hipStream_t st);

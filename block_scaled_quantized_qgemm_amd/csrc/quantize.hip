@@ -66,31 +66,58 @@ __device__ inline int block_sum_int(int v, int* red) {
   return s;
 }
 
-__device__ inline double block_sum_double(double v, double* red) {
+// Sum of squares of a row as a double-double (hi + lo): every square of a
+// float32 is exact in float64 (48 significant bits), each addition is an
+// error-free TwoSum whose rounding error is kept in lo, and the partial sums of
+// the threads are combined the same way. The terms are non-negative, so the
+// pair carries the exact sum to a relative error of about K * 2^-104; rounding
+// hi + lo once gives the correctly rounded float64 sum unless the exact sum lies
+// within that distance of the midpoint between two doubles.
+struct DD {
+  double hi, lo;
+};
+
+__device__ inline DD dd_add(DD a, double b) {
+  const double s = a.hi + b;
+  const double bb = s - a.hi;
+  const double e = (a.hi - (s - bb)) + (b - bb);
+  return DD{s, a.lo + e};
+}
+
+__device__ inline DD dd_add(DD a, DD b) {
+  DD r = dd_add(a, b.hi);
+  r.lo += b.lo;
+  return r;
+}
+
+__device__ inline double block_sum_sq_dd(DD v, double* red) {
   const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  if (lane == 0) red[wid] = v;
+  for (int o = 32; o >= 1; o >>= 1) v = dd_add(v, DD{__shfl_xor(v.hi, o, kWave), __shfl_xor(v.lo, o, kWave)});
+  if (lane == 0) {
+    red[2 * wid] = v.hi;
+    red[2 * wid + 1] = v.lo;
+  }
   __syncthreads();
-  double s = 0.0;
+  DD s{red[0], red[1]};
 #pragma unroll
-  for (int w = 0; w < kRowThreads / kWave; ++w) s += red[w];
-  return s;
+  for (int w = 1; w < kRowThreads / kWave; ++w) s = dd_add(s, DD{red[2 * w], red[2 * w + 1]});
+  return s.hi + s.lo;
 }
 
 // RMSNorm in front of the quantizer ("Activation Quantization Architecture,
 // in depth", section "Fusion: making quantization nearly free": the norm
 // kernel already holds the row, so it also finds the amax and writes codes
-// and the scale). The normalized row is y_k = (x_k * r) * gamma_k in float32
-// with r = 1 / sqrt(sum_k x_k^2 / K + eps) taken in float64 (every square is
-// exact there) and rounded once to float32.
+// and the scale). rms = sqrt(sum_k x_k^2 / K + eps) from the float64 sum of
+// squares, in float64, rounded once to float32; the normalized row is
+// y_k = (x_k / rms) * gamma_k in float32, the division correctly rounded.
 struct RowNorm {
   const float* gamma;  // [K]; null: no normalization
   float eps;
 };
 
-__device__ inline float rms_factor(double sumsq, int64_t K, float eps) {
-  return (float)(1.0 / sqrt(sumsq / (double)K + (double)eps));
+__device__ inline float rms_of(double sumsq, int64_t K, float eps) {
+  return (float)sqrt(sumsq / (double)K + (double)eps);
 }
 
 // Scale (and zero point) from the row statistics, in float32 exactly as the
@@ -169,7 +196,7 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     float* __restrict__ scales, int32_t* __restrict__ zeros, int32_t* __restrict__ colsum, RowNorm nm) {
   __shared__ float red[16];
   __shared__ int redi[8];
-  __shared__ double redd[8];
+  __shared__ double redd[16];
   const int64_t row = blockIdx.x;
   const float* xr = x + row * ldx;
   const int t = threadIdx.x;
@@ -209,18 +236,19 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     }
   }
   if constexpr (NORM) {
-    double ss = 0.0;
+    DD ss{0.0, 0.0};
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      ss = fma((double)v[u].x, (double)v[u].x, ss);
-      ss = fma((double)v[u].y, (double)v[u].y, ss);
-      ss = fma((double)v[u].z, (double)v[u].z, ss);
-      ss = fma((double)v[u].w, (double)v[u].w, ss);
+      ss = dd_add(ss, (double)v[u].x * (double)v[u].x);
+      ss = dd_add(ss, (double)v[u].y * (double)v[u].y);
+      ss = dd_add(ss, (double)v[u].z * (double)v[u].z);
+      ss = dd_add(ss, (double)v[u].w * (double)v[u].w);
     }
-    const float r = rms_factor(block_sum_double(ss, redd), K, nm.eps);
+    const float rms = rms_of(block_sum_sq_dd(ss, redd), K, nm.eps);
 #pragma unroll
     for (int u = 0; u < VPT; ++u)
-      v[u] = make_float4((v[u].x * r) * g[u].x, (v[u].y * r) * g[u].y, (v[u].z * r) * g[u].z, (v[u].w * r) * g[u].w);
+      v[u] = make_float4((v[u].x / rms) * g[u].x, (v[u].y / rms) * g[u].y, (v[u].z / rms) * g[u].z,
+                         (v[u].w / rms) * g[u].w);
   }
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
@@ -286,18 +314,18 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_long_kernel(
     float* __restrict__ scales, int32_t* __restrict__ zeros, int32_t* __restrict__ colsum, RowNorm nm) {
   __shared__ float red[16];
   __shared__ int redi[8];
-  __shared__ double redd[8];
+  __shared__ double redd[16];
   const int64_t row = blockIdx.x;
   const float* xr = x + row * ldx;
   const int t = threadIdx.x;
-  float r = 1.0f;
+  float rms = 1.0f;
   if constexpr (NORM) {
-    double ss = 0.0;
-    for (int64_t k = t; k < K; k += kRowThreads) ss = fma((double)xr[k], (double)xr[k], ss);
-    r = rms_factor(block_sum_double(ss, redd), K, nm.eps);
+    DD ss{0.0, 0.0};
+    for (int64_t k = t; k < K; k += kRowThreads) ss = dd_add(ss, (double)xr[k] * (double)xr[k]);
+    rms = rms_of(block_sum_sq_dd(ss, redd), K, nm.eps);
   }
-  // element k of the row as quantized: x, or the normalized (x * r) * gamma
-  auto val = [&](int64_t k) { return NORM ? (xr[k] * r) * nm.gamma[k] : xr[k]; };
+  // element k of the row as quantized: x, or the normalized (x / rms) * gamma
+  auto val = [&](int64_t k) { return NORM ? (xr[k] / rms) * nm.gamma[k] : xr[k]; };
   float s;
   int z;
   if (PRECOMP) {

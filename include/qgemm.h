@@ -241,9 +241,11 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx,
  * kernel already holds each row, so it finds the row's amax and writes the
  * codes and one scale per token without another read of the activations).
  *
- *   r      = 1 / sqrt(sum_k x[m,k]^2 / K + eps)   float64 (every square is
- *            exact there), rounded once to float32
- *   y[m,k] = (x[m,k] * r) * gamma[k]              two float32 multiplies
+ *   rms    = sqrt(sum_k x[m,k]^2 / K + eps)   float64 (every square is exact
+ *            there, the sum is carried as a double-double and rounded once),
+ *            then rounded once to float32
+ *   y[m,k] = (x[m,k] / rms) * gamma[k]       the page's order: a correctly
+ *            rounded float32 division, then a float32 multiply
  *   then exactly qgemm_quantize_rows on y with gran = ROW: INT8_SYM
  *   (s = max(amax / 127, 1e-8), q = clamp(rint(y / s), -127, 127)) or
  *   UINT8_ASYM (s, z from the row's min and max).
@@ -254,9 +256,10 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx,
  *   fmt      QGEMM_FMT_INT8_SYM or QGEMM_FMT_UINT8_ASYM; gran QGEMM_GRAN_ROW
  *            (any other combination: QGEMM_E_MODE).
  *   q, ldq, scales, zero_points as in qgemm_quantize_rows (ROW granularity).
- *   The order of the float64 sum of squares is the kernel's; it can move r
- *   by one float32 ulp only when the float64 value lies within about
- *   K * 2^-53 (relative) of a float32 rounding boundary.
+ *   The double-double sum of squares equals the correctly rounded float64
+ *   sum unless the exact sum lies within about K * 2^-104 (relative) of the
+ *   midpoint between two doubles, so rms is the same float32 value as the
+ *   plain definition computed with an exact sum.
  */
 int qgemm_rmsnorm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx,
                                 const float* gamma, float eps,

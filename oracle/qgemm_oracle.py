@@ -328,14 +328,17 @@ def quantized_linear(x, w, act: str = "sym_row", wgt: str = "channel", bias=None
 # ----------------------------------------------------------------------------
 # RMSNorm in front of the per-token quantizer
 # ----------------------------------------------------------------------------
-def rms_factor(x, eps):
-    """r[m] = 1 / sqrt(mean_k x[m, k]^2 + eps) per row, as float32.
+def rms_value(x, eps):
+    """rms[m] = sqrt(mean_k x[m, k]^2 + eps) per row, as float32.
 
     [AQ] "Fusion: making quantization nearly free" (the fused norm-and-quantize
-    pseudocode: rms = sqrt(mean(x * x) + eps)). Readings: every square is
-    exact in float64 and the sum of a row is rounded once (math.fsum); the
-    mean, the square root and the reciprocal are float64; the factor is
-    rounded once to float32.
+    pseudocode loads the row as float32 and forms rms = sqrt(mean(x * x) +
+    eps)). The page fixes the formula, not the arithmetic. Reading: every
+    square is exact in float64 (a float32 significand squared has 48 bits),
+    the row's sum of squares is rounded once (math.fsum, the correctly
+    rounded float64 sum), the mean, the sum with eps and the square root are
+    float64 operations, and rms is rounded once to float32, the precision of
+    the row it divides.
     """
     import math
     x = np.asarray(x, np.float32)
@@ -344,27 +347,27 @@ def rms_factor(x, eps):
     for m in range(x.shape[0]):
         row = x[m].astype(np.float64)
         ss = math.fsum((row * row).tolist())
-        r[m] = np.float32(1.0 / math.sqrt(ss / K + float(np.float32(eps))))
+        r[m] = np.float32(math.sqrt(ss / K + float(np.float32(eps))))
     return r
 
 
-def rmsnorm(x, gamma, eps, r=None):
+def rmsnorm(x, gamma, eps, rms=None):
     """y[m, k] = x[m, k] / rms[m] * gamma[k] ([AQ] "Fusion: making
     quantization nearly free", the RMSNorm line of the pseudocode).
 
-    Reading: the division by rms is a multiplication by the float32 factor
-    ``rms_factor`` (the usual reciprocal form of the norm), and the two
-    products are float32 roundings in the pseudocode's order: (x * r) * gamma.
-    ``r`` may be passed in (a per-row float32 factor) to evaluate the same
-    formula with a neighbouring factor.
+    Evaluated in the pseudocode's order on float32 values: the correctly
+    rounded float32 quotient x / rms (an IEEE division by the float32
+    ``rms_value``, not a multiplication by a reciprocal, which rounds twice),
+    then its float32 product with gamma. ``rms`` may be passed in (a float32
+    value per row) to evaluate the same formula with another rms.
     """
     x = np.asarray(x, np.float32)
     g = np.asarray(gamma, np.float32)
-    r = rms_factor(x, eps) if r is None else np.asarray(r, np.float32)
-    return ((x * r[:, None]).astype(np.float32) * g[None, :]).astype(np.float32)
+    rms = rms_value(x, eps) if rms is None else np.asarray(rms, np.float32)
+    return ((x / rms[:, None]).astype(np.float32) * g[None, :]).astype(np.float32)
 
 
-def rmsnorm_quantize(x, gamma, eps, act: str = "sym_row", r=None):
+def rmsnorm_quantize(x, gamma, eps, act: str = "sym_row", rms=None):
     """The fused norm-and-quantize step: ``rmsnorm`` then the per-token
     quantizer on its float32 output ([AQ] "Fusion: making quantization nearly
     free": amax of the normalized row, s = amax / 127, codes and one scale per
@@ -372,7 +375,7 @@ def rmsnorm_quantize(x, gamma, eps, act: str = "sym_row", r=None):
     ``quantize_asym_uint8`` per row (s floored at 1e-8 after the division, as
     everywhere else), so the fused step equals the two steps composed.
     Returns (q, s) or (q, s, z)."""
-    y = rmsnorm(x, gamma, eps, r)
+    y = rmsnorm(x, gamma, eps, rms)
     if act == "sym_row":
         return quantize_sym_int8(y, per_row=True)
     if act == "asym_row":

@@ -453,6 +453,8 @@ def test_gemm_mx_modes_on_an_8_group_with_a_wide_exponent_spread(ops, K):
     mfma = host(ops.qgemm_run_mx(a, pw, mode=1))[0, 0]
     assert exact == ref[0, 0]
     assert mfma == 448.0 and abs(mfma - ref[0, 0]) <= MX_SCALED_STOL * S[0, 0]
+    print(f"[measured] wide-exponent group, K={K}: scaled-mode err/S = {abs(mfma - ref[0, 0]) / S[0, 0]:.3e} "
+          f"(bound 2^-10 = {2.0 ** -10:.3e}); exact-mode err/S = {abs(exact - ref[0, 0]) / S[0, 0]:.3e}", flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -501,29 +503,16 @@ def test_gemm_mx_bias(ops, M, N, K):
     assert (np.abs(got - ref) <= MX_STOL * S + F32_RTOL * np.abs(ref)).all()
 
 
-def _rms_candidates(x, eps):
-    """Per row: the oracle's float32 factor, its float32 neighbour on the
-    side of the float64 value, and whether that value lies so close to the
-    rounding boundary between them (relative 1e-11, above the float64 sum's
-    order-dependent error for these K) that either is a valid result."""
-    r = O.rms_factor(x, eps)
-    r64 = np.array([1.0 / math.sqrt(math.fsum((row.astype(np.float64) ** 2).tolist()) / x.shape[1]
-                                    + float(np.float32(eps))) for row in x])
-    up = r64 > r.astype(np.float64)
-    alt = np.where(up, np.nextafter(r, np.float32(np.inf)), np.nextafter(r, np.float32(-np.inf))).astype(np.float32)
-    boundary = (r.astype(np.float64) + alt.astype(np.float64)) / 2.0
-    ambiguous = np.abs(r64 - boundary) <= 1e-11 * np.abs(r64)
-    return r, alt, ambiguous
-
-
 @pytest.mark.parametrize("act", ["sym_row", "asym_row"])
 @pytest.mark.parametrize("M,K,misaligned", [(1, 1, False), (3, 5, False), (7, 17, False), (64, 256, False),
                                             (33, 1000, False), (5, 4097, False), (512, 4096, False),
                                             (9, 8192, False), (2, 9000, False), (6, 260, True)])
 def test_rmsnorm_quantize_parity(ops, act, M, K, misaligned):
     """Codes, scales and zero points of the fused step equal the oracle's bit
-    for bit, except on rows whose float64 norm factor sits at a float32
-    rounding boundary, where the neighbouring factor is accepted too."""
+    for bit on every row. The kernel divides by the float32 rms as the page
+    writes (x / rms * gamma); its double-double sum of squares rounds to the
+    same float64 value as the oracle's exact sum (it could differ only for an
+    exact sum within about K * 2^-104 of the midpoint between two doubles)."""
     print_case("rmsnorm quantize", act, M, K, misaligned)
     A, _ = make_inputs("c2_per_token", M=M, K=K, N=1, seed=M * 17 + K)
     if M >= 8:
@@ -535,16 +524,8 @@ def test_rmsnorm_quantize_parity(ops, act, M, K, misaligned):
     fmt = ACT[act][0]
     gd = dev(np.concatenate([np.zeros(1, np.float32), g]))[1:] if misaligned else dev(g)
     r = ops.qgemm_rmsnorm_quantize_rows(dev(A), gd, eps, fmt)
-    q_gpu = host(r.codes()).view(np.uint8)
-    s_gpu = host(r.scales).view(np.uint32)
-    z_gpu = host(r.zero_points) if fmt == 1 else None
-    r32, alt, amb = _rms_candidates(A, eps)
-    assert amb.sum() <= max(1, M // 64)
-    for cand in (r32, np.where(amb, alt, r32)):
-        out = O.rmsnorm_quantize(A, g, eps, act=act, r=cand)
-        ok = (q_gpu == out[0].view(np.uint8)).all(axis=1) & (s_gpu == out[1].view(np.uint32))
-        if fmt == 1:
-            ok &= z_gpu == out[2]
-        if cand is r32:
-            first = ok
-    assert (first | (amb & ok)).all(), np.argwhere(~(first | (amb & ok)))[:5]
+    out = O.rmsnorm_quantize(A, g, eps, act=act)
+    assert np.array_equal(host(r.codes()).view(np.uint8), out[0].view(np.uint8))
+    assert np.array_equal(host(r.scales).view(np.uint32), out[1].view(np.uint32))
+    if fmt == 1:
+        assert np.array_equal(host(r.zero_points), out[2])

@@ -503,7 +503,7 @@ def test_rmsnorm_constant_rows():
         y = O.rmsnorm(np.full((1, 4), c, np.float32), g, 0.0)
         assert np.array_equal(y[0], np.sign(c) * g)
     y = O.rmsnorm(np.full((1, 4), 3.0, np.float32), np.ones(4, np.float32), 0.0)
-    assert np.all(y == 1.0)                          # 3 * RN(1/3) rounds back to 1
+    assert np.all(y == 1.0)                          # rms = 3 exactly, 3 / 3 = 1
 
 
 def test_rmsnorm_power_of_two_scale_invariance():
