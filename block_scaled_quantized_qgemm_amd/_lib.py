@@ -37,6 +37,8 @@ SIGNATURES = {
     "qgemm_workspace_bytes": (c_size, [c_i64, c_i64, c_int, c_int]),
     "qgemm_quantize_rows": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_i64,
                                     c_vp, c_vp, c_vp, c_i64, c_vp, c_size, c_vp]),
+    "qgemm_quantize_rows_noalloc": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_i64,
+                                            c_vp, c_vp, c_vp, c_i64, c_vp]),
     "qgemm_prepack_weights": (c_int, [c_vp, c_i64, c_i64, c_i64, c_int, c_int, c_vp, c_size,
                                       ctypes.POINTER(WDesc), c_vp, c_size, c_vp]),
     "qgemm_rmsnorm_quantize_rows": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_float, c_int, c_int,

@@ -132,9 +132,15 @@ size_t qgemm_workspace_bytes(int64_t rows, int64_t K, int fmt, int gran) {
   return 0;
 }
 
-int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int fmt, int gran, void* q,
-                        int64_t ldq, float* scales, int32_t* zero_points, uint8_t* mx_scales, int64_t ld_mx,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the two quantize entry points (everything but the
+// workspace); QGEMM_OK with *empty set when M == 0.
+int check_quantize_args(const float* x, int64_t M, int64_t K, int64_t ldx, int fmt, int gran, void* q, int64_t ldq,
+                        float* scales, int32_t* zero_points, uint8_t* mx_scales, int64_t ld_mx, bool* empty) {
+  *empty = false;
   const bool mx = is_mx_fmt(fmt);
   if (mx) {
     if (gran != QGEMM_GRAN_BLOCK32) return QGEMM_E_MODE;
@@ -143,7 +149,10 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int f
   }
   if (M < 0 || M > kMaxRows || K < 1 || K > ((int64_t)1 << 30)) return QGEMM_E_SHAPE;
   if (mx && K % 32 != 0) return QGEMM_E_SHAPE;
-  if (M == 0) return QGEMM_OK;
+  if (M == 0) {
+    *empty = true;
+    return QGEMM_OK;
+  }
   if (!x || !q) return QGEMM_E_NULL;
   if (ldx < K || ldq < code_bytes(fmt, K)) return QGEMM_E_SHAPE;
   if (!aligned(x, 4) || ldq % 16 != 0 || !aligned(q, 16)) return QGEMM_E_ALIGN;
@@ -155,19 +164,53 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int f
     if (fmt == QGEMM_FMT_UINT8_ASYM && !zero_points) return QGEMM_E_NULL;
     if (!aligned(scales, 4) || (zero_points && !aligned(zero_points, 4))) return QGEMM_E_ALIGN;
   }
+  return QGEMM_OK;
+}
+
+void launch_quantize(const float* x, int64_t M, int64_t K, int64_t ldx, int fmt, int gran, void* q, int64_t ldq,
+                     float* scales, int32_t* zero_points, uint8_t* mx_scales, int64_t ld_mx, float* ws,
+                     hipStream_t st) {
+  if (is_mx_fmt(fmt)) {
+    qg::launch_quantize_mx(x, M, K, ldx, fmt == QGEMM_FMT_MXFP4_E2M1, (uint8_t*)q, ldq, mx_scales, ld_mx, st);
+  } else {
+    qg::launch_quantize_int(x, M, K, ldx, fmt == QGEMM_FMT_UINT8_ASYM, gran == QGEMM_GRAN_TENSOR, (uint8_t*)q, ldq,
+                            0, scales, zero_points, nullptr, ws, st);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx, int fmt, int gran, void* q,
+                        int64_t ldq, float* scales, int32_t* zero_points, uint8_t* mx_scales, int64_t ld_mx,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_quantize_args(x, M, K, ldx, fmt, gran, q, ldq, scales, zero_points, mx_scales, ld_mx, &empty);
+  if (rc != QGEMM_OK || empty) return rc;
   const size_t need = qgemm_workspace_bytes(M, K, fmt, gran);
   if (need > 0 && (!workspace || workspace_bytes < need)) return QGEMM_E_WORKSPACE;
   if (need > 0 && !aligned(workspace, 4)) return QGEMM_E_ALIGN;
   int dc = check_device();
   if (dc != QGEMM_OK) return dc;
+  launch_quantize(x, M, K, ldx, fmt, gran, q, ldq, scales, zero_points, mx_scales, ld_mx, (float*)workspace,
+                  as_stream(stream));
+  return launch_status();
+}
 
-  hipStream_t st = as_stream(stream);
-  if (mx) {
-    qg::launch_quantize_mx(x, M, K, ldx, fmt == QGEMM_FMT_MXFP4_E2M1, (uint8_t*)q, ldq, mx_scales, ld_mx, st);
-  } else {
-    qg::launch_quantize_int(x, M, K, ldx, fmt == QGEMM_FMT_UINT8_ASYM, gran == QGEMM_GRAN_TENSOR,
-                            (uint8_t*)q, ldq, 0, scales, zero_points, nullptr, (float*)workspace, st);
-  }
+int qgemm_quantize_rows_noalloc(const float* x, int64_t M, int64_t K, int64_t ldx, int fmt, int gran, void* q,
+                                int64_t ldq, float* scales, int32_t* zero_points, uint8_t* mx_scales, int64_t ld_mx,
+                                void* stream) {
+  bool empty = false;
+  int rc = check_quantize_args(x, M, K, ldx, fmt, gran, q, ldq, scales, zero_points, mx_scales, ld_mx, &empty);
+  if (rc != QGEMM_OK || empty) return rc;
+  const size_t need = qgemm_workspace_bytes(M, K, fmt, gran);
+  if (need > (size_t)qg::kScratchFloats * sizeof(float)) return QGEMM_E_WORKSPACE;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+  float* ws = nullptr;
+  if (need > 0 && qg::scratch_buffer(&ws) != hipSuccess) return QGEMM_E_HIP;
+  launch_quantize(x, M, K, ldx, fmt, gran, q, ldq, scales, zero_points, mx_scales, ld_mx, ws, as_stream(stream));
   return launch_status();
 }
 

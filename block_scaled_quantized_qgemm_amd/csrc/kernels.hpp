@@ -15,6 +15,13 @@ void launch_quantize_int(const float* x, int64_t rows, int64_t K, int64_t ldx, b
                          uint8_t* q, int64_t ldq, int64_t kblocks, float* scales, int32_t* zeros, int32_t* colsum,
                          float* ws, hipStream_t st);
 
+// The library's static scratch array for the allocation-free quantize entry
+// point: kScratchFloats floats on each device. scratch_buffer() returns the
+// current device's copy (looked up once per device, no allocation).
+constexpr int64_t kScratchFloats = int64_t(1) << 18;  // 1 MiB
+constexpr int kMaxScratchDevices = 64;
+hipError_t scratch_buffer(float** ptr);
+
 // RMSNorm (double-double sum of squares, float32 rms, normalized row
 // (x / rms) * gamma in float32)
 // fused with per-row symmetric int8 / asymmetric uint8 quantization.

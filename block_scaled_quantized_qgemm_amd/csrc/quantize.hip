@@ -13,6 +13,8 @@
 // block amax is a three-step shuffle; e4m3 codes are converted two at a time
 // with the hardware conversion (round to nearest even, OCP e4m3fn on gfx950),
 // e2m1 codes by comparisons with the midpoints of the fp4 grid.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -500,6 +502,36 @@ __global__ __launch_bounds__(kRowThreads) void quant_int4_groups_kernel(const fl
   if ((lane & 4) == 0)
     codes[(blk << 10) + ((16 * c + (n & 15)) << 4) + 8 * (g & 1) + 4 * (kk >> 3) + (kk & 3)] = (uint8_t)(nib | (up << 4));
   if (lane == 0) scales[((n >> 4) * (K_pad >> 8) + (g >> 2)) * 64 + 4 * (n & 15) + (g & 3)] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch memory for the allocation-free quantize entry point: the per-row
+// statistics of the per-tensor quantizer (one float per row, two for the
+// asymmetric format). Each GPU holds its own copy of the array; host code
+// must use the address looked up for that device, never the array's name.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxScratchDevices];  // per device: its copy of `scratch`, once looked up
+}  // namespace
+
+hipError_t scratch_buffer(float** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

@@ -177,6 +177,42 @@ def qgemm_packed_weight_bytes(N: int, K: int, fmt: int, gran: int) -> int:
     return int(L.load().qgemm_packed_weight_bytes(N, K, fmt, gran))
 
 
+def _quantized_rows_out(x: torch.Tensor, fmt: int, gran: int) -> QuantizedRows:
+    """Output buffers of a row quantization of the float32 [M, K] matrix x."""
+    M, K = x.shape
+    dev = x.device
+    ld = _round_up(max(K // 2 if fmt == FMT_MXFP4_E2M1 else K, 1), 16)
+    q = torch.empty((M, ld), dtype=torch.int8 if fmt == FMT_INT8_SYM else torch.uint8, device=dev)
+    scales = zeros = mx = None
+    if fmt in _MX_FMTS:
+        # E8M0 rows padded to a multiple of 4 bytes: the GEMM's DMA path
+        # fetches them a dword at a time
+        mx = torch.empty((M, _round_up(max(K // 32, 1), 4)), dtype=torch.uint8, device=dev)
+    else:
+        scales = torch.empty((1 if gran == GRAN_TENSOR else M,), dtype=torch.float32, device=dev)
+        if fmt == FMT_UINT8_ASYM:
+            zeros = torch.empty_like(scales, dtype=torch.int32)
+    return QuantizedRows(q, K, fmt, gran, scales, zeros, mx)
+
+
+def qgemm_quantize_rows_noalloc(x: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = GRAN_ROW,
+                                out: Optional[QuantizedRows] = None, stream=None) -> QuantizedRows:
+    """qgemm_quantize_rows without a workspace: the library keeps per-tensor
+    statistics in its own static device array (see qgemm.h). With ``out``
+    given, nothing is allocated on the device."""
+    lib = L.load()
+    assert x.dtype == torch.float32 and x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    if out is None:
+        out = _quantized_rows_out(x, fmt, gran)
+    st = lib.qgemm_quantize_rows_noalloc(
+        _ptr(x), M, K, x.stride(0), fmt, gran, _ptr(out.q), out.q.stride(0),
+        _ptr(out.scales), _ptr(out.zero_points), _ptr(out.mx_scales),
+        0 if out.mx_scales is None else out.mx_scales.stride(0), ctypes.c_void_p(_stream(x.device, stream)))
+    _check("qgemm_quantize_rows_noalloc", st)
+    return out
+
+
 def qgemm_quantize_rows(x: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = GRAN_ROW,
                         out: Optional[QuantizedRows] = None, workspace: Optional[torch.Tensor] = None,
                         stream=None) -> QuantizedRows:
@@ -186,18 +222,7 @@ def qgemm_quantize_rows(x: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = GR
     M, K = x.shape
     dev = x.device
     if out is None:
-        ld = _round_up(max(K // 2 if fmt == FMT_MXFP4_E2M1 else K, 1), 16)
-        q = torch.empty((M, ld), dtype=torch.int8 if fmt == FMT_INT8_SYM else torch.uint8, device=dev)
-        scales = zeros = mx = None
-        if fmt in _MX_FMTS:
-            # E8M0 rows padded to a multiple of 4 bytes: the GEMM's DMA path
-            # fetches them a dword at a time
-            mx = torch.empty((M, _round_up(max(K // 32, 1), 4)), dtype=torch.uint8, device=dev)
-        else:
-            scales = torch.empty((1 if gran == GRAN_TENSOR else M,), dtype=torch.float32, device=dev)
-            if fmt == FMT_UINT8_ASYM:
-                zeros = torch.empty_like(scales, dtype=torch.int32)
-        out = QuantizedRows(q, K, fmt, gran, scales, zeros, mx)
+        out = _quantized_rows_out(x, fmt, gran)
     need = qgemm_workspace_bytes(M, K, fmt, gran)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define QGEMM_ABI_VERSION 6
+#define QGEMM_ABI_VERSION 7
 #define QGEMM_WDESC_MAGIC 0x51474d57u /* "WMGQ" */
 
 /* Status codes. Every entry point returns one of these. */
@@ -234,6 +234,33 @@ int qgemm_quantize_rows(const float* x, int64_t M, int64_t K, int64_t ldx,
                         uint8_t* mx_scales, int64_t ld_mx,
                         void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * qgemm_quantize_rows_noalloc -- qgemm_quantize_rows without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ *   Same formats, granularities, arguments (minus the workspace), results and
+ *   errors as qgemm_quantize_rows. The per-tensor granularity keeps its row
+ *   statistics in a static device array of the library (1 MiB on each GPU it
+ *   runs on, held until the process ends) instead of a workspace: up to
+ *   262,144 rows for INT8_SYM and 131,072 for UINT8_ASYM, beyond which the
+ *   call returns QGEMM_E_WORKSPACE before launching anything. The ROW and
+ *   BLOCK32 granularities use no scratch memory.
+ *   The call allocates nothing: no hipMalloc, no hipFree, no allocating
+ *   library routine (its first call on a device looks up that device's copy
+ *   of the array once). Every slot it reads was written by the same call, so
+ *   nothing needs clearing between calls.
+ *   All calls on one GPU share its array: per-tensor calls that overlap on
+ *   that GPU (concurrent streams, or threads) race and may return wrong
+ *   scales; serialize them.
+ */
+int qgemm_quantize_rows_noalloc(const float* x, int64_t M, int64_t K, int64_t ldx,
+                                int fmt, int gran,
+                                void* q, int64_t ldq,
+                                float* scales, int32_t* zero_points,
+                                uint8_t* mx_scales, int64_t ld_mx,
+                                void* stream);
 
 /*
  * qgemm_rmsnorm_quantize_rows -- RMSNorm and per-row quantization in one pass

@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "qgemm.h")
 OK, E_NULL, E_SHAPE, E_MODE, E_ALIGN, E_OVERFLOW, E_DEVICE, E_DESC, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8
 INT8, UINT8, MX, INT4, MX4 = 0, 1, 2, 3, 4
 TENSOR, ROW, BLK, G64 = 0, 1, 2, 3
-ABI = 6
+ABI = 7
 
 
 @pytest.fixture(scope="module")
@@ -102,6 +102,29 @@ def test_quantize_rows_validation(lib):
     assert _q(lib, fmt=MX4, gran=ROW) == E_MODE
     assert _q(lib, fmt=MX4, gran=BLK, s=None, mx=FAKE, ldmx=2, ldq=16) == E_SHAPE   # K / 2 = 32 bytes
     assert _q(lib, fmt=MX4, gran=BLK, s=None, mx=FAKE, ldmx=2, ldq=40) == E_ALIGN
+
+
+def _qn(lib, x=FAKE, M=4, K=64, ldx=64, fmt=INT8, gran=ROW, q=FAKE, ldq=64, s=FAKE, z=None, mx=None, ldmx=0):
+    return lib.qgemm_quantize_rows_noalloc(x, M, K, ldx, fmt, gran, q, ldq, s, z, mx, ldmx, None)
+
+
+def test_quantize_rows_noalloc_validation(lib):
+    """The allocation-free entry point validates like qgemm_quantize_rows
+    (before any device call) and refuses per-tensor sizes beyond its 1 MiB
+    static array: 2^18 rows of int8 statistics, 2^17 of uint8."""
+    assert _qn(lib, fmt=7) == E_MODE
+    assert _qn(lib, fmt=MX, gran=ROW) == E_MODE
+    assert _qn(lib, K=0) == E_SHAPE
+    assert _qn(lib, M=0, x=None, q=None, s=None) == OK
+    assert _qn(lib, x=None) == E_NULL
+    assert _qn(lib, fmt=UINT8, z=None) == E_NULL
+    assert _qn(lib, ldq=63) == E_SHAPE
+    assert _qn(lib, q=FAKE + 4) == E_ALIGN
+    assert _qn(lib, fmt=MX, gran=BLK, s=None, mx=FAKE, ldmx=1) == E_SHAPE
+    assert _qn(lib, gran=TENSOR, M=(1 << 18) + 1) == E_WS
+    assert _qn(lib, gran=TENSOR, fmt=UINT8, z=FAKE, M=(1 << 17) + 1) == E_WS
+    assert lib.qgemm_workspace_bytes(1 << 18, 64, INT8, TENSOR) == 1 << 20
+    assert lib.qgemm_workspace_bytes(1 << 17, 64, UINT8, TENSOR) == 1 << 20
 
 
 def _wdesc(**kw):
