@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqgemm.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemm_mx_dma.hip", "gemm_w4a8.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemm_i8_wide.hip", "gemm_mx_dma.hip", "gemm_w4a8.hip"]
+OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -35,15 +36,39 @@ def hipcc() -> str:
 
 
 def build_library(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the shared
+    library; every call compiles everything again."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(OBJDIR, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f not in ("-shared",) and not f.startswith("-Wl,")]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+        jobs.append((obj, [hipcc(), *compile_flags, "-c", "-I", os.path.join(ROOT, "include"),
+                           os.path.join(CSRC, src), "-o", obj]))
+
+    def run(job):
+        obj, cmd = job
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(workers) as ex:
+        results = list(ex.map(run, jobs))
+    failed = [(o, r) for o, r in results if r.returncode != 0]
+    for _, r in failed:
+        sys.stderr.write(r.stdout + r.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed compiling " + ", ".join(os.path.basename(o) for o, _ in failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    link = [hipcc(), *HIPCC_FLAGS, *[o for o, _ in results], "-o", tmp]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+        print(" ".join(link), flush=True)
+    r = subprocess.run(link, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libqgemm.so")
+        raise RuntimeError("hipcc failed linking libqgemm.so")
     os.replace(tmp, LIB)
     return LIB
 

@@ -838,6 +838,7 @@ static hipError_t launch_i8(const GemmArgs& a, hipStream_t st) {
   // grain fills the last round and whose barriers overlap each other's
   // matrix-core work.
   const int64_t cus = cu_count();
+  if (const int fn = wide_tile_fn(a.M, a.N, cus)) return launch_gemm_i8_wide<ASYM, OUT>(a, fn, st);
   auto tiles = [&](int64_t bm, int64_t bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   if (tiles(256, 256) >= cus) {
     if (tiles(256, 256) % cus == 0) return launch_dma<256, 256, 64, 2, 4, 5, ASYM, OUT>(a, st);

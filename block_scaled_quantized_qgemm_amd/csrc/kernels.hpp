@@ -78,6 +78,13 @@ struct GemmArgs {
   int64_t w_stride;
 };
 
+// The large-M int8 GEMM (gemm_i8_wide.hip): the W-block count FN of its
+// 256 x 32 FN tiles for this shape on `cus` compute units, or 0 when the shape
+// is better served by the tilings of gemm.hip; and its launcher.
+int wide_tile_fn(int64_t M, int64_t N, int64_t cus);
+template <bool ASYM, int OUT>
+hipError_t launch_gemm_i8_wide(const GemmArgs& a, int fn, hipStream_t st);
+
 // qgemm_run: int8 GEMM + epilogue. out_type: 0 f32, 1 bf16, 2 i32 (no bias).
 hipError_t launch_gemm_i8(const GemmArgs& a, bool asym, int out_type, hipStream_t st);
 // qgemm_run_mx: block-scaled GEMM of any e4m3 / e2m1 pair, float32 output.

@@ -253,6 +253,31 @@ def test_gemm_large_tile_configs(ops, M, N, K, act):
     _check_out(host(ops.qgemm_run(a, pw, 0)), ref["y"], 0)
 
 
+WIDE_CASES = [(M, N, K, act) for M, N, K in [(2000, 11000, 320), (4000, 4090, 300)]
+              for act in ("sym_row", "asym_row", "sym_tensor")] + [(2048, 11008, 4096, "asym_row")]
+
+
+@pytest.mark.parametrize("out_type", [0, 1])
+@pytest.mark.parametrize("M,N,K,act", WIDE_CASES)
+def test_gemm_wide_tiles(ops, M, N, K, act, out_type):
+    """Shapes the one-tile-per-CU kernel takes on a 256-CU device: 2000 x 11000
+    as 8 row bands x 32 strips of 352 columns (ragged in M and N, and in the
+    last strip), 4000 x 4090 as 16 x 16 tiles of 256 x 256, and the full
+    2048 x 11008 x 4096 shape; int32 sums exact (every output), float32 /
+    bf16 epilogue in tolerance."""
+    print_case("gemm wide tiles", M, N, K, act, out_type)
+    A, W = make_inputs("c3_asym_uint8" if act == "asym_row" else "c2_per_token", M=M, K=K, N=N,
+                       seed=M + 7 * N + K)
+    if act == "asym_row":
+        A = A - np.float32(0.3)     # both signs: zero points strictly inside (0, 255)
+    ref = O.quantized_linear(A, W, act=ACT[act][2], wgt="channel")
+    fmt, gran, _ = ACT[act]
+    a = ops.qgemm_quantize_rows(dev(A), fmt, gran)
+    pw = ops.qgemm_prepack_weights(dev(W), 0, 1)
+    _check_out(host(ops.qgemm_run(a, pw, 2)), None, 2, ref["C"])
+    _check_out(host(ops.qgemm_run(a, pw, out_type)), ref["y"], out_type)
+
+
 @pytest.mark.parametrize("asym", [False, True])
 @pytest.mark.parametrize("M", [8, 17, 300])
 def test_gemm_int32_at_the_k_limit(ops, M, asym):
@@ -280,9 +305,10 @@ def test_gemm_int32_at_the_k_limit(ops, M, asym):
 
 
 @pytest.mark.parametrize("M,N,asym", [(1100, 3900, False), (4100, 4100, False), (4000, 4090, False),
-                                      (4000, 4090, True)])
+                                      (4000, 4090, True), (2000, 11000, False), (2000, 11000, True)])
 def test_gemm_int32_at_the_k_limit_large_tiles(ops, M, N, asym):
-    """The 128x128, 128x256 (two per CU) and 256x256 tile configurations at
+    """The 128x128, 128x256 (two per CU) and one-tile-per-CU (256 x 256 and
+    256 x 352) tile configurations at
     the largest K, on inputs whose exact sums have a closed form: every
     activation code at its extreme and weight rows of alternating +127 and
     -127 codes give C[m][n] = +-127 * 127 * K (uint8: +-255 * 127 * (K - 1),
