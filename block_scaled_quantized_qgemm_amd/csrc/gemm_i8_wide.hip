@@ -223,7 +223,11 @@ __global__ __launch_bounds__(512) void gemm_i8_wide_kernel(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  // ---- epilogue
+  // ---- epilogue. The tile's row scales / zero points and column scales /
+  // column sums / bias go to LDS once; then each wave stages one 16-row block
+  // of its int32 sums at a time in its own slab and finishes it in passes of
+  // 64 four-column groups: one 16-byte read of the sums and 16-byte reads of
+  // the four columns' parameters per lane, all issued before the arithmetic.
   float* rsa = reinterpret_cast<float*>(smem + C::EPI_ROWS);
   int* rza = reinterpret_cast<int*>(smem + C::EPI_ROWS + BM * 4);
   float* csw = reinterpret_cast<float*>(smem + C::EPI_COLS);
@@ -239,8 +243,15 @@ __global__ __launch_bounds__(512) void gemm_i8_wide_kernel(GemmArgs p) {
     const bool in = n < p.N;
     csw[c] = in ? (p.w_per_tensor ? p.sw[0] : p.sw[n]) : 0.0f;
     ccs[c] = (ASYM && in) ? p.colsum[n] : 0;
-    cbs[c] = (p.bias && in) ? p.bias[n] : 0.0f;
+    cbs[c] = (p.bias && in) ? p.bias[n] : 0.0f;  // a missing bias adds +0, which changes no result
   }
+  // The parameters are read by every wave: one barrier, waiting for LDS only
+  // (a __syncthreads would also wait for this wave's earlier global stores).
+  // After it each wave works in its own slab: a wave's LDS operations complete
+  // in order, so its staging writes and reads need no further barrier, and the
+  // output stores of a block drain while the next block is staged.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & ~(15 << 8));
+  __builtin_amdgcn_s_barrier();
   int* slab = reinterpret_cast<int*>(smem + wid * C::EPI_W);
   constexpr int GPR = TN / 4;  // four-column groups per slab row
 #pragma unroll
@@ -250,29 +261,39 @@ __global__ __launch_bounds__(512) void gemm_i8_wide_kernel(GemmArgs p) {
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int t = 0; t < 4; ++t) slab[(4 * (lane >> 4) + t) * C::RS + 16 * j + (lane & 15)] = acc[i][j][t];
-    __syncthreads();
 #pragma unroll
     for (int pass = 0; pass < FN; ++pass) {
       const int gq = pass * 64 + lane;
       const int r = gq / GPR, cg = gq % GPR;
       const int lr = wm * 64 + i * 16 + r;   // row inside the tile
       const int lc = wn * TN + 4 * cg;       // column inside the tile
-      const int64_t m = m0 + lr, n = n0 + lc;
       const v4i raw = *reinterpret_cast<const v4i*>(slab + r * C::RS + 4 * cg);
-      if (m < p.M && n < p.N) {
-        const float sam = rsa[lr];
-        const int zm = rza[lr];
-        float y[4];
-        int ci[4];
+      const v4f sw4 = *reinterpret_cast<const v4f*>(csw + lc);
+      const v4f bs4 = *reinterpret_cast<const v4f*>(cbs + lc);
+      const float sam = rsa[lr];
+      v4i cs4 = v4i{0, 0, 0, 0};
+      int nz = 0;
+      if (ASYM) {
+        cs4 = *reinterpret_cast<const v4i*>(ccs + lc);
+        nz = 128 - rza[lr];  // C = raw + (128 - z) * colsum
+      }
+      float y[4];
+      int ci[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          int c = raw[t];
-          // wrap-around int32 arithmetic: the true C fits, so the result is exact
-          if (ASYM) c = (int)((uint32_t)c - (uint32_t)(zm - 128) * (uint32_t)ccs[lc + t]);
-          ci[t] = c;
-          y[t] = (float)c * (sam * csw[lc + t]);
-          if (p.bias) y[t] = y[t] + cbs[lc + t];  // the bias after the scales, in float32
+      for (int t = 0; t < 4; ++t) {
+        int c = raw[t];
+        if (ASYM) {
+          // exact (128 - z) * colsum with 24-bit multiplies: |128 - z| <= 128 and
+          // colsum = 4096 hi + lo with lo in [0, 4095] and |hi| < 2^12
+          const int lo = cs4[t] & 4095, hi = cs4[t] >> 12;
+          c = (int)((uint32_t)c + (uint32_t)__mul24(nz, lo));   // wrap-around int32: the true C fits
+          c = (int)((uint32_t)c + ((uint32_t)__mul24(nz, hi) << 12));
         }
+        ci[t] = c;
+        y[t] = (float)c * (sam * sw4[t]) + bs4[t];  // the bias after the scales, in float32
+      }
+      const int64_t m = m0 + lr, n = n0 + lc;
+      if (m < p.M && n < p.N) {
         const bool full = n + 3 < p.N;
         if constexpr (OUT == 2) {
           int32_t* o = reinterpret_cast<int32_t*>(p.out) + m * p.ldo + n;
@@ -288,21 +309,19 @@ __global__ __launch_bounds__(512) void gemm_i8_wide_kernel(GemmArgs p) {
             for (int t = 0; t < 4 && n + t < p.N; ++t) o[t] = y[t];
         } else {
           uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + m * p.ldo + n;
-          uint16_t h[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) h[t] = f32_to_bf16_rne(y[t]);
+          // round to nearest even (v_cvt_pk_bf16_f32; the outputs are never denormal)
+          const __bf16 h0 = (__bf16)y[0], h1 = (__bf16)y[1], h2 = (__bf16)y[2], h3 = (__bf16)y[3];
+          const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
           if (full) {
-            uint2 v;
-            v.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-            v.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-            *reinterpret_cast<uint2*>(o) = v;
+            *reinterpret_cast<uint2*>(o) = make_uint2(w0, w1);
           } else {
-            for (int t = 0; t < 4 && n + t < p.N; ++t) o[t] = h[t];
+            const uint16_t hv[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1, (uint16_t)(w1 >> 16)};
+            for (int t = 0; t < 4 && n + t < p.N; ++t) o[t] = hv[t];
           }
         }
       }
     }
-    __syncthreads();
   }
 }
 
