@@ -9,7 +9,7 @@
 // of GPU -- Day 98", section "The program, and the gate that has to be per
 // column"): C = sum_k (q_a - z_a) q_w exactly in int32, then
 // out = float(C) * (s_a * s_w) (+ bias) once per output; uint8 codes enter the
-// signed matrix cores as q - 128 and the epilogue subtracts (z - 128) * colsum.
+// signed matrix cores as q - 128, and (128 - z) * colsum restores C.
 //
 // Structure:
 //  * 8 waves as 4 (rows) x 2 (columns); wave tiles of 64 x 16 FN, computed as
@@ -26,15 +26,20 @@
 //    next stage's A fragments and first three W fragments are read after it
 //    while the stage's last four block columns of MFMAs run, so the barrier
 //    and the fragment latency are covered by matrix-core work.
-//  * Epilogue through LDS: per wave and 16-row block, the int32 block is staged,
-//    then each lane finishes four consecutive columns of a row with the tile's
-//    row scales / zero points and column scales / sums / bias staged in LDS.
+//  * The MFMAs take the W fragment as their first operand, so a lane's four
+//    accumulators of a block are four consecutive columns of one output row.
+//    For asymmetric A they start at (128 - z) colsum, so they end at C; the
+//    epilogue finishes them in registers with the row and column scales and
+//    the bias that the prologue put in LDS and stores each lane's four
+//    outputs with one instruction.
 #include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace qg {
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // A stage rows are 64 bytes (four 16-byte K chunks); chunk c of row r sits at
 // 64 r + 16 (c ^ a_swz(r)). A fragment read has lanes 0-15 on rows r0 .. r0+15
@@ -55,19 +60,18 @@ struct WideCfg {
   static constexpr int IPW = (LOADS + NW - 1) / NW;
   static constexpr bool SPARE = LOADS % NW != 0;  // some waves issue an empty load per stage
   static constexpr int LDS_MAX = 160 * 1024;
-  static constexpr int NS_FIT = (LDS_MAX - (SPARE ? 1024 : 0)) / STAGE;
+  // the epilogue's parameters, written once in the prologue past the ring:
+  // row scales (BM), column scales and bias (BN each)
+  static constexpr int PAR = BM * 4 + BN * 8;
+  static constexpr int NS_FIT = (LDS_MAX - (SPARE ? 1024 : 0) - PAR) / STAGE;
   static constexpr int NS = NS_FIT > 5 ? 5 : NS_FIT;
   static constexpr int RING = NS * STAGE;
   static constexpr int SPARE_OFF = RING;         // the spare 1 KB for empty loads
-  // epilogue: per wave a 16-row int32 slab, rows RS words apart (RS % 16 == 4:
-  // the four row groups a 16x16 block writes at once fall on distinct banks)
-  static constexpr int RS = TN + 4;
-  static constexpr int EPI_W = 16 * RS * 4;
-  static constexpr int EPI_ROWS = NW * EPI_W;    // row params after the slabs
-  static constexpr int EPI_COLS = EPI_ROWS + BM * 8;
-  static constexpr int EPI_END = EPI_COLS + BN * 12;
-  static constexpr int LDS = (RING + (SPARE ? 1024 : 0)) > EPI_END ? (RING + (SPARE ? 1024 : 0)) : EPI_END;
+  static constexpr int PAR_ROWS = RING + (SPARE ? 1024 : 0);
+  static constexpr int PAR_COLS = PAR_ROWS + BM * 4;
+  static constexpr int LDS = PAR_ROWS + PAR;
   static_assert(FN >= 5 && NS >= 3, "ring");
+  static_assert(BM <= NT && BN <= NT, "one parameter per thread");
   static_assert(LDS <= LDS_MAX, "LDS");
   static_assert((NS - 2) * IPW < 64, "vmcnt range");
   static constexpr int PD = 3;                   // W fragments are read PD block columns ahead
@@ -145,10 +149,6 @@ __global__ __launch_bounds__(512) void gemm_i8_wide_kernel(GemmArgs p) {
   };
 
   v4i acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
   // fragment reads: A block i of this wave (16 rows, lane l: row l % 16, K
   // chunk l / 16 of the stage), W block j (the packed 1 KB in lane order)
@@ -160,12 +160,85 @@ __global__ __launch_bounds__(512) void gemm_i8_wide_kernel(GemmArgs p) {
     return *reinterpret_cast<const v4i*>(smem + s * STAGE + C::A_BYTES + ((wn * FN + j) << 10) + lane * 16);
   };
 
+  // The epilogue's parameters go to LDS in the prologue, loaded before the
+  // stage loads (so the first stage's wait covers them): thread t < BM loads
+  // row t's scale, thread t < BN column t's scale and bias. Rows past M are
+  // clamped to M - 1 and columns past N get zeros; neither is stored. A
+  // missing bias is never read.
+  float par_f = 0.0f, par_sw = 0.0f, par_b = 0.0f;
+  if (tid < BM) par_f = p.a_per_tensor ? p.sa[0] : p.sa[min(m0 + tid, p.M - 1)];
+  if (tid < BN && n0 + tid < p.N) {
+    par_sw = p.w_per_tensor ? p.sw[0] : p.sw[n0 + tid];
+    if (p.bias) par_b = p.bias[n0 + tid];
+  }
+  float* const rsa = reinterpret_cast<float*>(smem + C::PAR_ROWS);
+  float* const csw = reinterpret_cast<float*>(smem + C::PAR_COLS);
+  float* const cbs = reinterpret_cast<float*>(smem + C::PAR_COLS + BN * 4);
+  // Accumulator block (i, j) holds, in lane l, row 16 i + l % 16 of the wave's
+  // rows and columns 16 j + 4 (l / 16) .. + 3 of its columns (the MFMAs take
+  // the W fragment as their first operand, so they compute W times A^T).
+  const int64_t nw0 = n0 + wn * TN;               // the wave's first column (uniform)
+  const int lc0 = wn * TN + 4 * (lane >> 4);      // the lane's first column in the tile
+  // Asymmetric A: the accumulators start at (128 - z) colsum and so end at C
+  // itself. Each partial sum is then the sum over the K columns done of
+  // (q - z) w plus (128 - z) times the sum of the remaining w, every term at
+  // most 255 * 127 in magnitude, so the K limit keeps all of them in int32.
+  int zrow[FM];
+  v4i cs_j[FN];
+  if constexpr (ASYM) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = min(m0 + wm * 64 + 16 * i + (lane & 15), p.M - 1);
+      zrow[i] = p.a_per_tensor ? p.za[0] : p.za[m];
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = nw0 + 16 * j + 4 * (lane >> 4);  // colsum has N_pad >= n + 4 entries
+      cs_j[j] = n < p.N ? *reinterpret_cast<const v4i*>(p.colsum + n) : v4i{0, 0, 0, 0};
+    }
+  }
+
   // prologue: stages 0 .. NS-2 in flight, then stage 0's first fragments
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
 #pragma unroll
     for (int i = 0; i < IPW; ++i) dma(s, s, i, s < nkt);
+  if constexpr (ASYM) {
+    // 128 - z in [-127, 128]; |colsum| <= 127 K_pad, below 2^23 up to K_pad = 65536:
+    // one exact 24-bit multiply per accumulator, else a 32-bit one
+    int nz[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) nz[i] = ((128 - zrow[i]) << 20) >> 20;
+    if (p.K_pad <= 65536) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int cs = (cs_j[j][t] << 8) >> 8;
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j][t] = nz[i] * cs;
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j][t] = nz[i] * cs_j[j][t];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+  }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW));
+  // (visible to every wave after the first stage barrier, which waits for LDS)
+  if (tid < BM) rsa[tid] = par_f;
+  if (tid < BN) {
+    csw[tid] = par_sw;
+    cbs[tid] = par_b;
+  }
   __builtin_amdgcn_s_barrier();
   constexpr int PD = C::PD, NB = PD + 1;
   v4i af[2][FM], wf[NB], nw[PD];
@@ -203,7 +276,7 @@ __global__ __launch_bounds__(512) void gemm_i8_wide_kernel(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[PB][i], wf[j % NB], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[j % NB], af[PB][i], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (j < IPW) dma(ks, sl, j, live);
@@ -221,107 +294,87 @@ __global__ __launch_bounds__(512) void gemm_i8_wide_kernel(GemmArgs p) {
   }
   // the empty loads past the last stage may still be in flight
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
 
-  // ---- epilogue. The tile's row scales / zero points and column scales /
-  // column sums / bias go to LDS once; then each wave stages one 16-row block
-  // of its int32 sums at a time in its own slab and finishes it in passes of
-  // 64 four-column groups: one 16-byte read of the sums and 16-byte reads of
-  // the four columns' parameters per lane, all issued before the arithmetic.
-  float* rsa = reinterpret_cast<float*>(smem + C::EPI_ROWS);
-  int* rza = reinterpret_cast<int*>(smem + C::EPI_ROWS + BM * 4);
-  float* csw = reinterpret_cast<float*>(smem + C::EPI_COLS);
-  int* ccs = reinterpret_cast<int*>(smem + C::EPI_COLS + BN * 4);
-  float* cbs = reinterpret_cast<float*>(smem + C::EPI_COLS + BN * 8);
-  for (int r = tid; r < BM; r += C::NT) {
-    const int64_t m = min(m0 + r, p.M - 1);
-    rsa[r] = p.a_per_tensor ? p.sa[0] : p.sa[m];
-    rza[r] = ASYM ? (p.a_per_tensor ? p.za[0] : p.za[m]) : 0;
-  }
-  for (int c = tid; c < BN; c += C::NT) {
-    const int64_t n = n0 + c;
-    const bool in = n < p.N;
-    csw[c] = in ? (p.w_per_tensor ? p.sw[0] : p.sw[n]) : 0.0f;
-    ccs[c] = (ASYM && in) ? p.colsum[n] : 0;
-    cbs[c] = (p.bias && in) ? p.bias[n] : 0.0f;  // a missing bias adds +0, which changes no result
-  }
-  // The parameters are read by every wave: one barrier, waiting for LDS only
-  // (a __syncthreads would also wait for this wave's earlier global stores).
-  // After it each wave works in its own slab: a wave's LDS operations complete
-  // in order, so its staging writes and reads need no further barrier, and the
-  // output stores of a block drain while the next block is staged.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & ~(15 << 8));
-  __builtin_amdgcn_s_barrier();
-  int* slab = reinterpret_cast<int*>(smem + wid * C::EPI_W);
-  constexpr int GPR = TN / 4;  // four-column groups per slab row
+  // ---- epilogue, from registers and without a barrier (the parameters were
+  // written in the prologue, the ring is not touched): each lane finishes the
+  // four consecutive outputs of one row that each accumulator block holds and
+  // stores them with one instruction.
+  float sam[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) sam[i] = rsa[wm * 64 + 16 * i + (lane & 15)];
+  // per 16-row block: is the lane's row inside M, and where its block 0 outputs go
+  using OutT = std::conditional_t<OUT == 2, int32_t, std::conditional_t<OUT == 0, float, uint16_t>>;
+  bool rok[FM];
+  OutT* orow[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    // block (i, j): lane l, item t is row 4 (l / 16) + t, column 16 j + l % 16
+    const int64_t m = m0 + wm * 64 + 16 * i + (lane & 15);
+    rok[i] = m < p.M;
+    orow[i] = reinterpret_cast<OutT*>(p.out) + (rok[i] ? m : 0) * p.ldo + n0 + lc0;
+  }
+
+  // EDGE: the wave's outputs reach past M or N (checks per block and lane)
+  auto finish = [&](auto has_bias, auto edge) {
+    constexpr bool BIAS = decltype(has_bias)::value, EDGE = decltype(edge)::value;
+    // block column j's parameters; those of j + 1 are read while j is finished
+    v4f sw4 = *reinterpret_cast<const v4f*>(csw + lc0), bs4{}, sw_n{}, bs_n{};
+    if (BIAS) bs4 = *reinterpret_cast<const v4f*>(cbs + lc0);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) slab[(4 * (lane >> 4) + t) * C::RS + 16 * j + (lane & 15)] = acc[i][j][t];
-#pragma unroll
-    for (int pass = 0; pass < FN; ++pass) {
-      const int gq = pass * 64 + lane;
-      const int r = gq / GPR, cg = gq % GPR;
-      const int lr = wm * 64 + i * 16 + r;   // row inside the tile
-      const int lc = wn * TN + 4 * cg;       // column inside the tile
-      const v4i raw = *reinterpret_cast<const v4i*>(slab + r * C::RS + 4 * cg);
-      const v4f sw4 = *reinterpret_cast<const v4f*>(csw + lc);
-      const v4f bs4 = *reinterpret_cast<const v4f*>(cbs + lc);
-      const float sam = rsa[lr];
-      v4i cs4 = v4i{0, 0, 0, 0};
-      int nz = 0;
-      if (ASYM) {
-        cs4 = *reinterpret_cast<const v4i*>(ccs + lc);
-        nz = 128 - rza[lr];  // C = raw + (128 - z) * colsum
+    for (int j = 0; j < FN; ++j) {
+      if (EDGE && nw0 + 16 * j >= p.N) break;  // this and later block columns are past N
+      if (j + 1 < FN) {
+        sw_n = *reinterpret_cast<const v4f*>(csw + lc0 + 16 * (j + 1));
+        if (BIAS) bs_n = *reinterpret_cast<const v4f*>(cbs + lc0 + 16 * (j + 1));
       }
-      float y[4];
-      int ci[4];
+      const int64_t n = nw0 + 16 * j + 4 * (lane >> 4);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        int c = raw[t];
-        if (ASYM) {
-          // exact (128 - z) * colsum with 24-bit multiplies: |128 - z| <= 128 and
-          // colsum = 4096 hi + lo with lo in [0, 4095] and |hi| < 2^12
-          const int lo = cs4[t] & 4095, hi = cs4[t] >> 12;
-          c = (int)((uint32_t)c + (uint32_t)__mul24(nz, lo));   // wrap-around int32: the true C fits
-          c = (int)((uint32_t)c + ((uint32_t)__mul24(nz, hi) << 12));
+      for (int i = 0; i < FM; ++i) {
+        const v4i ci = acc[i][j];
+        v4f y;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          y[t] = (float)ci[t] * (sam[i] * sw4[t]);
+          if (BIAS) y[t] = y[t] + bs4[t];  // the bias after the scales, in float32
         }
-        ci[t] = c;
-        y[t] = (float)c * (sam * sw4[t]) + bs4[t];  // the bias after the scales, in float32
-      }
-      const int64_t m = m0 + lr, n = n0 + lc;
-      if (m < p.M && n < p.N) {
-        const bool full = n + 3 < p.N;
+        OutT* const o = orow[i] + 16 * j;
+        const bool full = !EDGE || (rok[i] && n + 3 < p.N);
         if constexpr (OUT == 2) {
-          int32_t* o = reinterpret_cast<int32_t*>(p.out) + m * p.ldo + n;
           if (full)
-            *reinterpret_cast<v4i*>(o) = v4i{ci[0], ci[1], ci[2], ci[3]};
-          else
+            *reinterpret_cast<v4i*>(o) = ci;
+          else if (rok[i])
             for (int t = 0; t < 4 && n + t < p.N; ++t) o[t] = ci[t];
         } else if constexpr (OUT == 0) {
-          float* o = reinterpret_cast<float*>(p.out) + m * p.ldo + n;
           if (full)
-            *reinterpret_cast<v4f*>(o) = v4f{y[0], y[1], y[2], y[3]};
-          else
+            *reinterpret_cast<v4f*>(o) = y;
+          else if (rok[i])
             for (int t = 0; t < 4 && n + t < p.N; ++t) o[t] = y[t];
         } else {
-          uint16_t* o = reinterpret_cast<uint16_t*>(p.out) + m * p.ldo + n;
           // round to nearest even (v_cvt_pk_bf16_f32; the outputs are never denormal)
-          const __bf16 h0 = (__bf16)y[0], h1 = (__bf16)y[1], h2 = (__bf16)y[2], h3 = (__bf16)y[3];
-          const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-          const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+          const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{y[0], y[1]}, v2bf));
+          const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{y[2], y[3]}, v2bf));
           if (full) {
             *reinterpret_cast<uint2*>(o) = make_uint2(w0, w1);
-          } else {
+          } else if (rok[i]) {
             const uint16_t hv[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1, (uint16_t)(w1 >> 16)};
             for (int t = 0; t < 4 && n + t < p.N; ++t) o[t] = hv[t];
           }
         }
       }
+      sw4 = sw_n;
+      bs4 = bs_n;
     }
+  };
+  const bool interior = m0 + wm * 64 + 64 <= p.M && nw0 + TN <= p.N;  // uniform
+  if (p.bias) {
+    if (interior)
+      finish(std::true_type{}, std::false_type{});
+    else
+      finish(std::true_type{}, std::true_type{});
+  } else {
+    if (interior)
+      finish(std::false_type{}, std::false_type{});
+    else
+      finish(std::false_type{}, std::true_type{});
   }
 }
 
