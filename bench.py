@@ -114,13 +114,18 @@ def algorithmic(name, M, K, N, w4a8=False, fp4=False, wfp4=None):
     return ops, step_bytes, gemm_bytes
 
 
-def source_digest(w4a8=False):
-    """Digest of the code of the GEMM kernel a workload times: its sources
-    with comments and whitespace removed, so only a code change makes the
-    stored counter figures stale."""
+def source_digest(name):
+    """Digest of the code of the GEMM kernels a workload's name selects (int4
+    weights, MX, or int8): their sources with comments and whitespace
+    removed, so only a code change makes the stored counter figures stale."""
     import re
     h = hashlib.sha256()
-    srcs = ("gemm_w4a8.hip",) if w4a8 else ("gemm.hip", "gemm_mx_dma.hip")
+    if name.endswith("_w4a8"):
+        srcs = ("gemm_w4a8.hip",)
+    elif "mxfp" in name:
+        srcs = ("gemm_mx_dma.hip",)
+    else:
+        srcs = ("gemm.hip", "gemm_i8_wide.hip")
     for f in srcs + ("common.hpp", "kernels.hpp"):
         with open(os.path.join(ROOT, "block_scaled_quantized_qgemm_amd", "csrc", f)) as fh:
             code = fh.read()
@@ -143,7 +148,7 @@ def measured_traffic(name):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("source_digest") != source_digest(name.endswith("_w4a8")):
+    if t.get("source_digest") != source_digest(name):
         return None
     return float(t["hbm_bytes_per_launch"])
 

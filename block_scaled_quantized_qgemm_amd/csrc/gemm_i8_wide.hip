@@ -292,43 +292,51 @@ __global__ __launch_bounds__(512) void gemm_i8_wide_kernel(GemmArgs p) {
     stage(kt, std::integral_constant<int, 0>{});
     stage(kt + 1, std::integral_constant<int, 1>{});
   }
-  // the empty loads past the last stage may still be in flight
+  // The ring becomes the epilogue's staging area once every wave is past its
+  // last fragment read and its loads (the empty ones past the last stage
+  // included) have landed.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
 
-  // ---- epilogue, from registers and without a barrier (the parameters were
-  // written in the prologue, the ring is not touched): each lane finishes the
-  // four consecutive outputs of one row that each accumulator block holds and
-  // stores them with one instruction.
+  // ---- epilogue. Each lane finishes, in registers, the four consecutive
+  // outputs of one row that an accumulator block holds (the parameters were
+  // written to LDS in the prologue). A 16-row block of the wave's outputs is
+  // then staged in the wave's own LDS slab, row-major, and leaves as 16-byte
+  // chunks, each row's TN columns contiguous, so every output line is written
+  // whole by one wave (16-byte row pieces from the lanes alone would leave
+  // half-written lines to be merged, or not, in L2). A wave's LDS operations
+  // complete in order, so the slab needs no barrier between its uses.
+  using OutT = std::conditional_t<OUT == 2, int32_t, std::conditional_t<OUT == 0, float, uint16_t>>;
+  constexpr int OB = sizeof(OutT);
+  constexpr int SROW = TN * OB + 16;        // slab row pitch: 4 banks of skew per row
+  constexpr int CPR = TN * OB / 16;         // 16-byte chunks per slab row
+  constexpr int EPR = 16 / OB;              // outputs per chunk
+  constexpr int PASSES = (16 * CPR + 63) / 64;
+  static_assert(C::NW * 16 * SROW <= C::RING, "slabs fit in the ring");
+  static_assert((TN * OB) % 16 == 0, "whole chunks");
+  uint8_t* const slab = smem + wid * 16 * SROW;
   float sam[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) sam[i] = rsa[wm * 64 + 16 * i + (lane & 15)];
-  // per 16-row block: is the lane's row inside M, and where its block 0 outputs go
-  using OutT = std::conditional_t<OUT == 2, int32_t, std::conditional_t<OUT == 0, float, uint16_t>>;
-  bool rok[FM];
-  OutT* orow[FM];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int64_t m = m0 + wm * 64 + 16 * i + (lane & 15);
-    rok[i] = m < p.M;
-    orow[i] = reinterpret_cast<OutT*>(p.out) + (rok[i] ? m : 0) * p.ldo + n0 + lc0;
-  }
+  const int64_t mw0 = m0 + wm * 64;  // the wave's first row (uniform)
+  // rows start 16-byte aligned (out is; the tile and wave column offsets are
+  // multiples of 16 bytes) unless a bf16 ldo is 4 mod 8
+  const bool a16 = OB == 4 || p.ldo % 8 == 0;
 
-  // EDGE: the wave's outputs reach past M or N (checks per block and lane)
+  // EDGE: the wave's outputs reach past M or N (checks per chunk and lane)
   auto finish = [&](auto has_bias, auto edge) {
     constexpr bool BIAS = decltype(has_bias)::value, EDGE = decltype(edge)::value;
-    // block column j's parameters; those of j + 1 are read while j is finished
-    v4f sw4 = *reinterpret_cast<const v4f*>(csw + lc0), bs4{}, sw_n{}, bs_n{};
-    if (BIAS) bs4 = *reinterpret_cast<const v4f*>(cbs + lc0);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if (EDGE && nw0 + 16 * j >= p.N) break;  // this and later block columns are past N
-      if (j + 1 < FN) {
-        sw_n = *reinterpret_cast<const v4f*>(csw + lc0 + 16 * (j + 1));
-        if (BIAS) bs_n = *reinterpret_cast<const v4f*>(cbs + lc0 + 16 * (j + 1));
-      }
-      const int64_t n = nw0 + 16 * j + 4 * (lane >> 4);
+    for (int i = 0; i < FM; ++i) {
+      // block column j's parameters; those of j + 1 are read while j is finished
+      v4f sw4 = *reinterpret_cast<const v4f*>(csw + lc0), bs4{}, sw_n{}, bs_n{};
+      if (BIAS) bs4 = *reinterpret_cast<const v4f*>(cbs + lc0);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int j = 0; j < FN; ++j) {
+        if (j + 1 < FN) {
+          sw_n = *reinterpret_cast<const v4f*>(csw + lc0 + 16 * (j + 1));
+          if (BIAS) bs_n = *reinterpret_cast<const v4f*>(cbs + lc0 + 16 * (j + 1));
+        }
         const v4i ci = acc[i][j];
         v4f y;
 #pragma unroll
@@ -336,35 +344,44 @@ __global__ __launch_bounds__(512) void gemm_i8_wide_kernel(GemmArgs p) {
           y[t] = (float)ci[t] * (sam[i] * sw4[t]);
           if (BIAS) y[t] = y[t] + bs4[t];  // the bias after the scales, in float32
         }
-        OutT* const o = orow[i] + 16 * j;
-        const bool full = !EDGE || (rok[i] && n + 3 < p.N);
+        uint8_t* const dst = slab + (lane & 15) * SROW + (16 * j + 4 * (lane >> 4)) * OB;
         if constexpr (OUT == 2) {
-          if (full)
-            *reinterpret_cast<v4i*>(o) = ci;
-          else if (rok[i])
-            for (int t = 0; t < 4 && n + t < p.N; ++t) o[t] = ci[t];
+          *reinterpret_cast<v4i*>(dst) = ci;
         } else if constexpr (OUT == 0) {
-          if (full)
-            *reinterpret_cast<v4f*>(o) = y;
-          else if (rok[i])
-            for (int t = 0; t < 4 && n + t < p.N; ++t) o[t] = y[t];
+          *reinterpret_cast<v4f*>(dst) = y;
         } else {
           // round to nearest even (v_cvt_pk_bf16_f32; the outputs are never denormal)
           const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{y[0], y[1]}, v2bf));
           const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{y[2], y[3]}, v2bf));
-          if (full) {
-            *reinterpret_cast<uint2*>(o) = make_uint2(w0, w1);
-          } else if (rok[i]) {
-            const uint16_t hv[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1, (uint16_t)(w1 >> 16)};
-            for (int t = 0; t < 4 && n + t < p.N; ++t) o[t] = hv[t];
+          *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+        }
+        sw4 = sw_n;
+        bs4 = bs_n;
+      }
+      // the block's 16 rows x TN columns, 16 bytes per lane and pass
+#pragma unroll
+      for (int pass = 0; pass < PASSES; ++pass) {
+        const int q = pass * 64 + lane;
+        if (16 * CPR % 64 != 0 && q >= 16 * CPR) break;
+        const int r = q / CPR, c = q % CPR;
+        const v4i v = *reinterpret_cast<const v4i*>(slab + r * SROW + 16 * c);
+        const int64_t m = mw0 + 16 * i + r, n = nw0 + c * EPR;
+        OutT* const o = reinterpret_cast<OutT*>(p.out) + m * p.ldo + n;
+        if (!EDGE || (m < p.M && n + EPR <= p.N)) {
+          if (a16) {
+            *reinterpret_cast<v4i*>(o) = v;
+          } else {  // bf16 rows that start 8 bytes into a 16-byte unit
+            reinterpret_cast<uint2*>(o)[0] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+            reinterpret_cast<uint2*>(o)[1] = make_uint2((uint32_t)v[2], (uint32_t)v[3]);
           }
+        } else if (m < p.M) {
+          const OutT* e = reinterpret_cast<const OutT*>(&v);
+          for (int t = 0; t < EPR && n + t < p.N; ++t) o[t] = e[t];
         }
       }
-      sw4 = sw_n;
-      bs4 = bs_n;
     }
   };
-  const bool interior = m0 + wm * 64 + 64 <= p.M && nw0 + TN <= p.N;  // uniform
+  const bool interior = mw0 + 64 <= p.M && nw0 + TN <= p.N;  // uniform
   if (p.bias) {
     if (interior)
       finish(std::true_type{}, std::false_type{});

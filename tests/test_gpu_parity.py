@@ -278,6 +278,30 @@ def test_gemm_wide_tiles(ops, M, N, K, act, out_type):
     _check_out(host(ops.qgemm_run(a, pw, out_type)), ref["y"], out_type)
 
 
+@pytest.mark.parametrize("out_type", [0, 1, 2])
+def test_gemm_wide_tiles_into_a_padded_output(ops, out_type):
+    """The one-tile-per-CU kernel writing into a caller's [M, 11004] buffer:
+    bf16 rows then start 8 bytes into a 16-byte unit every other row (ldo is
+    4 mod 8), float32 / int32 rows 16-byte aligned. Outputs as in
+    test_gemm_wide_tiles; the padding columns past N keep their sentinel."""
+    M, N, K = 2000, 11000, 320
+    print_case("gemm wide padded out", M, N, K, out_type)
+    A, W = make_inputs("c3_asym_uint8", M=M, K=K, N=N, seed=11)
+    A = A - np.float32(0.3)
+    ref = O.quantized_linear(A, W, act="asym_row", wgt="channel")
+    a = ops.qgemm_quantize_rows(dev(A), 1, 1)
+    pw = ops.qgemm_prepack_weights(dev(W), 0, 1)
+    import torch
+    dt = {0: torch.float32, 1: torch.bfloat16, 2: torch.int32}[out_type]
+    buf = torch.full((M, 11004), 7, dtype=dt, device="cuda")
+    ops.qgemm_run(a, pw, out_type, out=buf)
+    got = buf.cpu()
+    assert (got[:, N:] == 7).all()
+    if out_type == 1:
+        got = got.view(torch.int16)
+    _check_out(got[:, :N].numpy(), ref["y"], out_type, ref["C"])
+
+
 @pytest.mark.parametrize("asym", [False, True])
 @pytest.mark.parametrize("M", [8, 17, 300])
 def test_gemm_int32_at_the_k_limit(ops, M, asym):
