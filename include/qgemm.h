@@ -4,8 +4,10 @@
  * One hot path: dynamic per-token activation quantization, an int8 x int8
  * GEMM accumulated exactly in int32, and a dequantization epilogue that
  * applies s_a * s_w once per output and subtracts z_a * colsum(W_q) for
- * asymmetric activations; plus the MX variant (e4m3 data, one E8M0 scale per
- * 32 K-elements) on the block-scaled fp8 matrix cores.
+ * asymmetric activations; plus the MX variant (e4m3 or e2m1 data, one E8M0
+ * scale per 32 K-elements), by default in an exact mode on the bf16 matrix
+ * cores (every product and block scale exact, float32 sums), optionally on
+ * the block-scaled fp8/fp4 matrix cores (faster, looser; see qgemm_run_mx).
  *
  * Pages the operations follow (titles as they appear on the pages):
  *   [D98]  "100 Days of GPU -- Day 98: Quantization and sparsity"
@@ -18,7 +20,9 @@
  * - Pointers named "device" are HIP device allocations on the current
  *   device; the caller allocates and owns every buffer, including the
  *   workspace. The library allocates no device memory and keeps no state
- *   beyond a per-device cache of "is this a gfx950".
+ *   beyond a per-device cache of "is this a gfx950" and of its compute-unit
+ *   count, and a 1 MiB static device array per GPU that only
+ *   qgemm_quantize_rows_noalloc uses.
  * - Matrices are row-major with an explicit leading dimension in ELEMENTS.
  *   Activations are [M, K] (one row per token); weights are [N, K] (one row
  *   per output channel, K contiguous); outputs are [M, N].
@@ -57,6 +61,7 @@ typedef enum {
   QGEMM_E_ALIGN = -4,     /* a pointer or leading dimension is not aligned as documented   */
   QGEMM_E_OVERFLOW = -5,  /* K too large for an exact int32 accumulator                    */
   QGEMM_E_DEVICE = -6,    /* the current device is not a gfx950                            */
+  QGEMM_E_UNSUPPORTED_DEVICE = QGEMM_E_DEVICE, /* the same code under its longer name        */
   QGEMM_E_DESC = -7,      /* the weight descriptor is invalid or does not fit the call     */
   QGEMM_E_WORKSPACE = -8, /* workspace missing or smaller than qgemm_workspace_bytes()     */
   QGEMM_E_HIP = -9        /* a HIP runtime call or a kernel launch failed                  */
