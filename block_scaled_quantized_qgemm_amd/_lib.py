@@ -43,6 +43,8 @@ SIGNATURES = {
                                       ctypes.POINTER(WDesc), c_vp, c_size, c_vp]),
     "qgemm_rmsnorm_quantize_rows": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_float, c_int, c_int,
                                             c_vp, c_i64, c_vp, c_vp, c_vp]),
+    "qgemm_unpack_weights": (c_int, [ctypes.POINTER(WDesc), c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64,
+                                     c_vp]),
     "qgemm_run": (c_int, [c_vp, c_i64, c_vp, c_vp, c_int, c_int, c_i64, ctypes.POINTER(WDesc), c_vp,
                           c_vp, c_i64, c_int, c_vp, c_vp, c_size, c_vp]),
     "qgemm_run_mx": (c_int, [c_vp, c_i64, c_vp, c_i64, c_int, c_i64, ctypes.POINTER(WDesc), c_vp,

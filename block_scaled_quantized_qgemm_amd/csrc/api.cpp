@@ -284,6 +284,51 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int
   return QGEMM_OK;
 }
 
+int qgemm_unpack_weights(const qgemm_wdesc* desc, const void* packed, void* codes_out, int64_t ld_codes,
+                         float* scales_out, int64_t ld_scales, int32_t* colsums_out, uint8_t* mx_scales_out,
+                         int64_t ld_mx, void* stream) {
+  if (!desc || !packed) return QGEMM_E_NULL;
+  int rc = check_desc(desc, desc->fmt);
+  if (rc != QGEMM_OK) return rc;
+  const int fmt = desc->fmt;
+  const bool i8 = fmt == QGEMM_FMT_INT8_SYM, i4 = fmt == QGEMM_FMT_INT4_SYM, mx = is_mx_fmt(fmt);
+  const int64_t N = desc->N, K = desc->K;
+  // what the format holds
+  if ((scales_out && mx) || (colsums_out && !i8) || (mx_scales_out && !mx)) return QGEMM_E_MODE;
+  const int64_t code_row = fmt == QGEMM_FMT_MXFP4_E2M1 ? K / 2 : K;  // bytes of a plain code row
+  const int64_t groups = (K + 63) / 64;
+  if (codes_out && ld_codes < code_row) return QGEMM_E_SHAPE;
+  if (scales_out && i4 && ld_scales < groups) return QGEMM_E_SHAPE;
+  if (mx_scales_out && ld_mx < K / 32) return QGEMM_E_SHAPE;
+  if (!aligned(packed, 256) || (scales_out && !aligned(scales_out, 4)) || (colsums_out && !aligned(colsums_out, 4)))
+    return QGEMM_E_ALIGN;
+  if (!codes_out && !scales_out && !colsums_out && !mx_scales_out) return QGEMM_OK;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+
+  hipStream_t st = as_stream(stream);
+  const uint8_t* base = static_cast<const uint8_t*>(packed);
+  const int ufmt = i8 ? qg::UNPACK_FMT_INT8 : (i4 ? qg::UNPACK_FMT_INT4 : qg::UNPACK_FMT_MX);
+  auto run = [&](int what, const uint8_t* src, int64_t src_pitch, void* out, int64_t ld, int64_t rows, int64_t cols,
+                 int64_t row_bytes) {
+    qg::UnpackArgs u{src, src_pitch, out, ld, rows, cols, row_bytes, desc->K_pad, what, ufmt};
+    return qg::launch_unpack(u, st) == hipSuccess;
+  };
+  bool ok = true;
+  if (codes_out)
+    ok = ok && run(qg::UNPACK_CODES, base + desc->codes_off, code_bytes(fmt, desc->K_pad), codes_out, ld_codes, N,
+                   (code_row + 15) / 16, code_row);
+  if (scales_out && i8)
+    ok = ok && run(qg::UNPACK_WORDS, base + desc->scales_off, 0, scales_out, 1,
+                   desc->gran == QGEMM_GRAN_TENSOR ? 1 : N, 1, 0);
+  if (scales_out && i4)
+    ok = ok && run(qg::UNPACK_INT4_SCALES, base + desc->scales_off, 0, scales_out, ld_scales, N, groups, 0);
+  if (colsums_out) ok = ok && run(qg::UNPACK_WORDS, base + desc->colsum_off, 0, colsums_out, 1, N, 1, 0);
+  if (mx_scales_out)
+    ok = ok && run(qg::UNPACK_E8M0, base + desc->scales_off, desc->K_pad / 32, mx_scales_out, ld_mx, N, K / 32, 0);
+  return ok ? launch_status() : QGEMM_E_HIP;
+}
+
 int qgemm_run(const void* a_q, int64_t lda, const float* a_scales, const int32_t* a_zero, int a_fmt, int a_gran,
               int64_t M, const qgemm_wdesc* w_desc, const void* w_packed, void* out, int64_t ldo, int out_type,
               const float* bias, void* workspace, size_t workspace_bytes, void* stream) {

@@ -41,6 +41,24 @@ void launch_quantize_int4(const float* w, int64_t rows, int64_t K, int64_t ldw, 
 // Compute units of the current device (cached per device).
 int cu_count();
 
+// One output of qgemm_unpack_weights: a plain copy of a section of a packed
+// weight buffer. Codes go one 16-byte piece of an output row per thread (int8
+// and int4 codes as one int8 per element, MX codes as stored), the other
+// outputs one element per thread.
+enum { UNPACK_CODES = 0, UNPACK_WORDS = 1, UNPACK_INT4_SCALES = 2, UNPACK_E8M0 = 3 };
+enum { UNPACK_FMT_INT8 = 0, UNPACK_FMT_INT4 = 1, UNPACK_FMT_MX = 2 };
+struct UnpackArgs {
+  const uint8_t* src;   // the section of the packed buffer the output comes from
+  int64_t src_pitch;    // bytes per source row (MX codes, E8M0)
+  void* out;
+  int64_t ld;           // output row pitch in elements (bytes for codes)
+  int64_t rows, cols;   // output rows; elements (16-byte pieces for codes) per row
+  int64_t row_bytes;    // codes: the bytes of one output row
+  int64_t K_pad;
+  int what, fmt;
+};
+hipError_t launch_unpack(const UnpackArgs& a, hipStream_t st);
+
 struct GemmArgs {
   const uint8_t* a;     // activation codes [M][lda]
   int64_t lda;

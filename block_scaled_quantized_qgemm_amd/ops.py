@@ -279,6 +279,37 @@ def qgemm_prepack_weights(w: torch.Tensor, fmt: int = FMT_INT8_SYM, gran: int = 
     return PackedWeights(packed, desc)
 
 
+def qgemm_unpack_weights(w: PackedWeights, stream=None) -> dict:
+    """Plain copies of what a prepared weight buffer holds (see qgemm.h), as a
+    dict of device tensors: 'codes' [N, K] (int8 for int8 and int4 weights,
+    uint8 bytes for MX; e2m1 two per byte, [N, K / 2]); 'scales' float32 [N]
+    or [1] (int8) or [N, ceil(K / 64)] (int4); 'colsums' int32 [N] (int8);
+    'mx_scales' uint8 [N, K / 32] (MX). Only what the format has."""
+    lib = L.load()
+    d = w.desc
+    dev = w.packed.device
+    N, K = int(d.N), int(d.K)
+    mx = d.fmt in (FMT_MXFP8_E4M3, FMT_MXFP4_E2M1)
+    out = {}
+    code_cols = K // 2 if d.fmt == FMT_MXFP4_E2M1 else K
+    out["codes"] = torch.empty((N, code_cols), dtype=torch.uint8 if mx else torch.int8, device=dev)
+    if d.fmt == FMT_INT8_SYM:
+        out["scales"] = torch.empty((1 if d.gran == GRAN_TENSOR else N,), dtype=torch.float32, device=dev)
+        out["colsums"] = torch.empty((N,), dtype=torch.int32, device=dev)
+    elif d.fmt == FMT_INT4_SYM:
+        out["scales"] = torch.empty((N, (K + 63) // 64), dtype=torch.float32, device=dev)
+    else:
+        out["mx_scales"] = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    sc = out.get("scales")
+    mxs = out.get("mx_scales")
+    st = lib.qgemm_unpack_weights(ctypes.byref(d), _ptr(w.packed), _ptr(out["codes"]), out["codes"].stride(0),
+                                  _ptr(sc), sc.stride(0) if sc is not None and sc.dim() == 2 else 1,
+                                  _ptr(out.get("colsums")), _ptr(mxs), mxs.stride(0) if mxs is not None else 0,
+                                  ctypes.c_void_p(_stream(dev, stream)))
+    _check("qgemm_unpack_weights", st)
+    return out
+
+
 def qgemm_prepack_experts(w: torch.Tensor, fmt: int = FMT_MXFP8_E4M3, stream=None) -> PackedExperts:
     """Prepare E experts' float32 [E, N, K] MX weights into one buffer for
     qgemm_run_mx_grouped (one qgemm_prepack_weights call per expert slice)."""

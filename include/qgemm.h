@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define QGEMM_ABI_VERSION 7
+#define QGEMM_ABI_VERSION 8
 #define QGEMM_WDESC_MAGIC 0x51474d57u /* "WMGQ" */
 
 /* Status codes. Every entry point returns one of these. */
@@ -327,6 +327,38 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw,
                           void* packed, size_t packed_bytes, qgemm_wdesc* desc,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * qgemm_unpack_weights -- plain copies of what a prepared weight buffer holds:
+ * the codes, scales, column sums and E8M0 scales that qgemm_prepack_weights
+ * computed ([AQ] quantize_per_channel; [D98] the column sums; [TL27] 2.3 and
+ * 2.4 for the MX and int4 scales), read out of the packed layout into plain
+ * row-major arrays, for inspection, checkpoints and tests.
+ *
+ *   desc, packed  a descriptor and its packed device buffer (any format).
+ *   Every output is optional (NULL: not written); all are device memory:
+ *   codes_out     [N][ld_codes] bytes: int8 codes (INT8_SYM; INT4_SYM as one
+ *                 sign-extended int8 per element), e4m3 codes (MXFP8), or e2m1
+ *                 codes two per byte as stored (MXFP4, K / 2 bytes per row);
+ *                 ld_codes >= the row's bytes.
+ *   scales_out    float32 scales: INT8_SYM [N] (ROW) or [1] (TENSOR), ld_scales
+ *                 ignored; INT4_SYM [N][ld_scales], ld_scales >= ceil(K / 64),
+ *                 one per group of 64 K. Not for MX formats (QGEMM_E_MODE).
+ *   colsums_out   int32 [N] column sums (INT8_SYM only, else QGEMM_E_MODE).
+ *   mx_scales_out E8M0 bytes [N][ld_mx], ld_mx >= K / 32 (MX formats only,
+ *                 else QGEMM_E_MODE).
+ * Errors: QGEMM_E_NULL (desc or packed), QGEMM_E_DESC, QGEMM_E_MODE,
+ * QGEMM_E_SHAPE (a leading dimension too small), QGEMM_E_ALIGN (packed not
+ * 256-byte aligned, scales_out / colsums_out not 4-byte aligned),
+ * QGEMM_E_DEVICE, QGEMM_E_HIP. Launches one small kernel per output
+ * requested, on `stream`; allocates nothing and records no memset.
+ */
+int qgemm_unpack_weights(const qgemm_wdesc* desc, const void* packed,
+                         void* codes_out, int64_t ld_codes,
+                         float* scales_out, int64_t ld_scales,
+                         int32_t* colsums_out,
+                         uint8_t* mx_scales_out, int64_t ld_mx,
+                         void* stream);
 
 /*
  * qgemm_run -- int8 GEMM with the fused dequantization epilogue (steps G, E).

@@ -133,6 +133,16 @@ expect("run W4A8", rw(DEV[9], 256, DEV[10], ROW, 4, ctypes.byref(d4), DEV[8], DE
 expect("run W4A8 int32 out", rw(DEV[9], 256, DEV[10], ROW, 4, ctypes.byref(d4), DEV[8], DEV[11], 64, 2, None, None, 0,
                                 None), E_MODE, 0)
 
+un = lib.qgemm_unpack_weights
+expect("unpack int8: codes, scales, column sums",
+       un(ctypes.byref(d8), DEV[8], DEV[14], 256, DEV[15], 0, DEV[13], None, 0, None), OK, 3)
+expect("unpack int4: codes, scales", un(ctypes.byref(d4), DEV[8], DEV[14], 256, DEV[15], 4, None, None, 0, None),
+       OK, 2)
+expect("unpack MX: codes, E8M0", un(ctypes.byref(dmx), DEV[8], DEV[14], 256, None, 0, None, DEV[15], 8, None), OK, 2)
+expect("unpack nothing requested", un(ctypes.byref(d8), DEV[8], None, 0, None, 0, None, None, 0, None), OK, 0)
+expect("unpack MX with float scales", un(ctypes.byref(dmx), DEV[8], None, 0, DEV[15], 0, None, None, 0, None),
+       E_MODE, 0)
+
 if failures:
     print("\n".join(failures))
     sys.exit(1)

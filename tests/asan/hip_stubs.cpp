@@ -104,6 +104,12 @@ hipError_t launch_gemm_mx_grouped(const GemmArgs& a, int, hipStream_t) {
   ++qg_stub_launches;
   return hipSuccess;
 }
+hipError_t launch_unpack(const UnpackArgs& a, hipStream_t) {
+  require(a.src != nullptr && a.out != nullptr && a.rows >= 1 && a.cols >= 1 && a.ld >= 1 && a.K_pad % 256 == 0,
+          "unpack args");
+  ++qg_stub_launches;
+  return hipSuccess;
+}
 hipError_t launch_gemm_w4a8(const GemmArgs& a, int, hipStream_t) {
   check_gemm(a);
   ++qg_stub_launches;

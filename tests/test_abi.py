@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "qgemm.h")
 OK, E_NULL, E_SHAPE, E_MODE, E_ALIGN, E_OVERFLOW, E_DEVICE, E_DESC, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8
 INT8, UINT8, MX, INT4, MX4 = 0, 1, 2, 3, 4
 TENSOR, ROW, BLK, G64 = 0, 1, 2, 3
-ABI = 7
+ABI = 8
 
 
 @pytest.fixture(scope="module")
@@ -299,6 +299,51 @@ def _w4desc(**kw):
 
 def _run4(lib, d, a=FAKE, lda=304, s=FAKE, gran=ROW, M=8, w=FAKE, out=FAKE, ldo=100, ot=0, bias=None):
     return lib.qgemm_run_w4a8(a, lda, s, gran, M, ctypes.byref(d), w, out, ldo, ot, bias, None, 0, None)
+
+
+def test_unpack_weights_validation(lib):
+    """qgemm_unpack_weights rejects bad arguments before any launch: a missing
+    descriptor or buffer, a damaged descriptor, an output the format does not
+    have, a leading dimension too small, a misaligned buffer."""
+    d = L.WDesc()
+    dev = 0x10000000
+    un = lib.qgemm_unpack_weights
+    assert un(None, dev, dev, 64, None, 0, None, None, 0, None) == E_NULL
+    assert un(ctypes.byref(d), None, dev, 64, None, 0, None, None, 0, None) == E_NULL
+    assert un(ctypes.byref(d), dev, dev, 64, None, 0, None, None, 0, None) == E_DESC  # zero descriptor
+    # a descriptor as qgemm_prepack_weights fills it, for checks that come before the device
+    def desc(N, K, fmt, gran, colsum=True):
+        nb = lib.qgemm_packed_weight_bytes(N, K, fmt, gran)
+        assert nb > 0
+        x = L.WDesc()
+        x.magic, x.version, x.fmt, x.gran, x.N, x.K = 0x51474D57, ABI, fmt, gran, N, K
+        x.N_pad, x.K_pad = (N + 255) // 256 * 256, (K + 255) // 256 * 256
+        x.codes_off = 0
+        if fmt == INT4:
+            x.scales_off = (x.N_pad * x.K_pad // 2 + 255) // 256 * 256
+            x.colsum_off = -1
+        elif fmt == INT8:
+            x.scales_off = (x.N_pad * x.K_pad + 255) // 256 * 256
+            x.colsum_off = (x.scales_off + 4 * x.N_pad + 255) // 256 * 256
+        else:
+            cb = x.K_pad // 2 if fmt == MX4 else x.K_pad
+            x.scales_off = (x.N_pad * cb + 255) // 256 * 256
+            x.colsum_off = -1
+        x.bytes = nb
+        return x
+    d8, d4, dmx = desc(64, 256, INT8, ROW), desc(64, 256, INT4, G64), desc(64, 256, MX, BLK)
+    assert un(ctypes.byref(d8), dev, None, 0, None, 0, None, dev, 8, None) == E_MODE     # no E8M0 in int8
+    assert un(ctypes.byref(dmx), dev, None, 0, dev, 0, None, None, 0, None) == E_MODE   # no float scales in MX
+    assert un(ctypes.byref(d4), dev, None, 0, None, 0, dev, None, 0, None) == E_MODE    # no column sums in int4
+    assert un(ctypes.byref(d8), dev, dev, 255, None, 0, None, None, 0, None) == E_SHAPE   # ld_codes < K
+    assert un(ctypes.byref(d4), dev, None, 0, dev, 3, None, None, 0, None) == E_SHAPE     # ld_scales < 4 groups
+    assert un(ctypes.byref(dmx), dev, None, 0, None, 0, None, dev, 7, None) == E_SHAPE    # ld_mx < K / 32
+    assert un(ctypes.byref(d8), dev + 16, dev, 256, None, 0, None, None, 0, None) == E_ALIGN
+    assert un(ctypes.byref(d8), dev, None, 0, dev + 2, 0, None, None, 0, None) == E_ALIGN
+    assert un(ctypes.byref(d8), dev, None, 0, None, 0, None, None, 0, None) == OK        # nothing requested
+    bad = L.WDesc.from_buffer_copy(d8)
+    bad.bytes += 256
+    assert un(ctypes.byref(bad), dev, dev, 256, None, 0, None, None, 0, None) == E_DESC
 
 
 def test_run_w4a8_validation(lib):
