@@ -122,6 +122,32 @@ __device__ inline float rms_of(double sumsq, int64_t K, float eps) {
   return (float)sqrt(sumsq / (double)K + (double)eps);
 }
 
+// Block sum of float64 values, plain float64 additions.
+__device__ inline double block_sum_d(double v, double* red) {
+  const int lane = threadIdx.x % kWave, wid = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  double s = red[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / kWave; ++w) s += red[w];
+  return s;
+}
+
+// Whether the float32 rounding of r, a float64 rms whose relative error is at
+// most (K + 16) 2^-53 (a sum of K exact squares in float64, then a division by
+// K, the addition of eps and the square root, each rounded once), could differ
+// from the rounding of the exact value: r lies within that error of the
+// midpoint between (float)r and its neighbour on r's side.
+__device__ inline bool rms_rounding_unsure(double r, int64_t K) {
+  const float f = (float)r;
+  const double fd = (double)f;
+  const float g = r >= fd ? nextafterf(f, INFINITY) : nextafterf(f, -INFINITY);
+  const double mid = 0.5 * (fd + (double)g);
+  return fabs(r - mid) <= r * (double)(K + 16) * 0x1p-53;
+}
+
 // Scale (and zero point) from the row statistics, in float32 exactly as the
 // formulas read: s = max(amax / 127, 1e-8); asymmetric s = max((max - min) /
 // 255, 1e-8), z = clamp(rint(-min / s), 0, 255).
@@ -238,15 +264,33 @@ __global__ __launch_bounds__(kRowThreads) void quant_rows_kernel(
     }
   }
   if constexpr (NORM) {
-    DD ss{0.0, 0.0};
+    // The sum of squares in float64 (every square is exact there); it decides
+    // the float32 rms unless the float64 rms is within its error bound of a
+    // float32 rounding midpoint, and then (about once in 10^5 rows, the same
+    // for every thread of the block) the row is summed again exactly, as a
+    // double-double.
+    double ssd = 0.0;
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      ss = dd_add(ss, (double)v[u].x * (double)v[u].x);
-      ss = dd_add(ss, (double)v[u].y * (double)v[u].y);
-      ss = dd_add(ss, (double)v[u].z * (double)v[u].z);
-      ss = dd_add(ss, (double)v[u].w * (double)v[u].w);
+      ssd = __builtin_fma((double)v[u].x, (double)v[u].x, ssd);
+      ssd = __builtin_fma((double)v[u].y, (double)v[u].y, ssd);
+      ssd = __builtin_fma((double)v[u].z, (double)v[u].z, ssd);
+      ssd = __builtin_fma((double)v[u].w, (double)v[u].w, ssd);
     }
-    const float rms = rms_of(block_sum_sq_dd(ss, redd), K, nm.eps);
+    const double r = sqrt(block_sum_d(ssd, redd) / (double)K + (double)nm.eps);
+    float rms = (float)r;
+    if (rms_rounding_unsure(r, K)) {
+      __syncthreads();  // every thread has read the float64 partial sums
+      DD ss{0.0, 0.0};
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        ss = dd_add(ss, (double)v[u].x * (double)v[u].x);
+        ss = dd_add(ss, (double)v[u].y * (double)v[u].y);
+        ss = dd_add(ss, (double)v[u].z * (double)v[u].z);
+        ss = dd_add(ss, (double)v[u].w * (double)v[u].w);
+      }
+      rms = rms_of(block_sum_sq_dd(ss, redd), K, nm.eps);
+    }
 #pragma unroll
     for (int u = 0; u < VPT; ++u)
       v[u] = make_float4((v[u].x / rms) * g[u].x, (v[u].y / rms) * g[u].y, (v[u].z / rms) * g[u].z,

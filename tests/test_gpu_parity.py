@@ -554,15 +554,37 @@ def test_gemm_mx_bias(ops, M, N, K):
 
 
 @pytest.mark.parametrize("act", ["sym_row", "asym_row"])
+def test_rmsnorm_rms_on_a_float32_midpoint(ops, act):
+    """Rows whose float64 rms lies exactly on the midpoint between two float32
+    values: x = (1 + 2^-23, 1, 1, 1) with eps = 2^-24 gives mean(x^2) + eps =
+    (1 + 2^-24)^2 exactly, so rms is the midpoint between 1 and 1 + 2^-23 and
+    rounds to the even 1.0; the kernel's float64 sum cannot decide such a row
+    by itself and sums it again exactly. Codes and scales equal the oracle's;
+    a second row, scaled by 3, is an ordinary one."""
+    print_case("rmsnorm rms on a midpoint", act)
+    A = np.array([[1 + 2.0 ** -23, 1, 1, 1], [3 * (1 + 2.0 ** -23), 3, 3, 3]], np.float32)
+    g = np.array([0.5, -1.0, 2.0, 1.0], np.float32)
+    eps = np.float32(2.0 ** -24)
+    assert O.rms_value(A[:1], eps)[0] == np.float32(1.0)  # the tie went to even
+    fmt = ACT[act][0]
+    r = ops.qgemm_rmsnorm_quantize_rows(dev(A), dev(g), float(eps), fmt)
+    out = O.rmsnorm_quantize(A, g, eps, act=act)
+    assert np.array_equal(host(r.codes()).view(np.uint8), out[0].view(np.uint8))
+    assert np.array_equal(host(r.scales).view(np.uint32), out[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("act", ["sym_row", "asym_row"])
 @pytest.mark.parametrize("M,K,misaligned", [(1, 1, False), (3, 5, False), (7, 17, False), (64, 256, False),
                                             (33, 1000, False), (5, 4097, False), (512, 4096, False),
                                             (9, 8192, False), (2, 9000, False), (6, 260, True)])
 def test_rmsnorm_quantize_parity(ops, act, M, K, misaligned):
     """Codes, scales and zero points of the fused step equal the oracle's bit
     for bit on every row. The kernel divides by the float32 rms as the page
-    writes (x / rms * gamma); its double-double sum of squares rounds to the
-    same float64 value as the oracle's exact sum (it could differ only for an
-    exact sum within about K * 2^-104 of the midpoint between two doubles)."""
+    writes (x / rms * gamma). Its float64 sum of squares decides the float32
+    rms unless the float64 rms is within the sum's error bound of a float32
+    rounding midpoint; such rows are summed again as a double-double, which
+    rounds to the oracle's exact sum (it could differ only for an exact sum
+    within about K * 2^-104 of the midpoint between two doubles)."""
     print_case("rmsnorm quantize", act, M, K, misaligned)
     A, _ = make_inputs("c2_per_token", M=M, K=K, N=1, seed=M * 17 + K)
     if M >= 8:
