@@ -336,6 +336,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
     // e4m3: chunks 4 kk + h and 4 kk + h + 2 (K 16h .. and 32 + 16h ..);
     // e2m1: chunk 2 kk + h (K 32h .. 32h + 31)
     const int ca = A4 ? 2 * kk + h : 4 * kk + h, cw = W4 ? 2 * kk + h : 4 * kk + h;
+    // the scale dwords of the wave's row blocks first, from one base each:
+    // rows 32 apart are 512 bytes apart, so the compiler pairs them into
+    // two-address LDS reads
+    const int* pa = ssa + 4 * (wm * TM + (lane & 31));
+    const int* pb = ssb + 4 * (wn * TN + (lane & 31));
+    int wa[FM], wb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) wa[i] = pa[128 * i];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) wb[j] = pb[128 * j];
     // exact mode, e2m1: the 8-byte halves h of chunks 2 kk and 2 kk + 1 (K
     // 16h .. 16h + 15 and 32 + 16h ..), one dword per 16-deep chunk t
 #pragma unroll
@@ -350,7 +360,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
         const v4i hi = A4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sa + lds_off<RBA>(r, ca + 2));
         f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      f.sa[i] = (ssa[4 * r] >> sh) & mask;
+      f.sa[i] = (wa[i] >> sh) & mask;
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
         const v4i hi = W4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sb + lds_off<RBW>(r, cw + 2));
         f.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      f.sb[j] = (ssb[4 * r] >> sh) & mask;
+      f.sb[j] = (wb[j] >> sh) & mask;
     }
   };
 
