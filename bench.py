@@ -275,6 +275,97 @@ def calibration_copy(mib, dev):
     torch.cuda.synchronize()
 
 
+def _ceiling_bytes(t, n):
+    """The first n bytes of a device tensor (repeated when it is shorter)."""
+    import torch
+    b = t.reshape(-1).view(torch.uint8)
+    if b.numel() < n:
+        b = b.repeat((n + b.numel() - 1) // b.numel())
+    return b[:n].contiguous()
+
+
+def mfma_ceiling(kind, a_src, b_src, waves_per_simd=2, target_ms=4.0, reps=5):
+    """Measured issue rate of a GEMM kernel's matrix-core instruction
+    (qgemm_ceiling_mfma): one workgroup per CU with waves_per_simd waves on
+    every SIMD, the workload's own code bytes as operands (the part is
+    power-limited and its clock depends on the operand bits), nothing else in
+    the loop. Launches of about target_ms, after about 20 ms of warm-up so the
+    clock settles. Returns the rate in T(FL)OP/s and the shader clock (GHz)
+    the part held, from the probe's own cycle and real-time counters."""
+    import torch
+    from block_scaled_quantized_qgemm_amd import ops
+    a = _ceiling_bytes(a_src, ops.CEILING_A_BYTES)
+    b = _ceiling_bytes(b_src, ops.CEILING_B_BYTES)
+    sink = torch.zeros(1, dtype=torch.int32, device=a.device)
+    trips = 256
+    wg, _ = ops.qgemm_ceiling_mfma_shape(kind, waves_per_simd, trips)
+    clocks = torch.zeros(2 * wg, dtype=torch.int64, device=a.device)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(t, n):
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(n):
+            ops.qgemm_ceiling_mfma(kind, waves_per_simd, t, a, b, sink, clocks)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / n
+
+    ms = run(trips, 2)
+    trips = max(1, min(1 << 24, int(trips * target_ms / max(ms, 1e-3))))
+    run(trips, 5)
+    ms = run(trips, reps)
+    _, n_ops = ops.qgemm_ceiling_mfma_shape(kind, waves_per_simd, trips)
+    c = clocks.view(-1, 2).double().cpu()
+    ghz = float((c[:, 0] / (c[:, 1] / 1e8)).mean() / 1e9)
+    return n_ops / (ms * 1e-3) / 1e12, ghz
+
+
+CEILING_NAMES = {0: "v_mfma_i32_16x16x64_i8", 1: "v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3)",
+                 2: "v_mfma_scale_f32_32x32x64_f8f6f4 (e2m1)", 3: "v_mfma_f32_32x32x16_bf16"}
+
+
+def add_mfma_ceiling(roof, kind, a_src, b_src):
+    """Put the measured matrix-core ceiling of the GEMM's instruction next to
+    the published peak in a roofline."""
+    rate, ghz = mfma_ceiling(kind, a_src, b_src)
+    roof["measured_ceiling"] = {
+        "value": rate, "unit": roof["unit"], "clock_ghz": ghz,
+        "probe": f"qgemm_ceiling_mfma: {CEILING_NAMES[kind]} back to back, 8 independent accumulators, "
+                 "2 waves per SIMD, one workgroup per CU, operands from this workload's codes"}
+    roof["frac_of_measured_ceiling"] = roof["achieved"] / rate
+
+
+def add_stream_ceiling(roof, bufs, steps):
+    """Put the measured HBM read rate of a plain stream over the same rotating
+    weight buffers (qgemm_ceiling_stream, best of four block sizes) next to
+    the published peak in a roofline."""
+    import torch
+    from block_scaled_quantized_qgemm_amd import ops
+    nbytes = min(b.numel() for b in bufs) // 16 * 16
+    sink = torch.zeros(1, dtype=torch.int32, device=bufs[0].device)
+    best = None
+    for bb in (32768, 65536, 131072, 262144):
+        ms, _ = timed(lambda i: ops.qgemm_ceiling_stream(bufs[i % len(bufs)], nbytes, bb, sink), steps, False)
+        rate = nbytes / (ms * 1e-3) / 1e9
+        if best is None or rate > best[0]:
+            best = (rate, bb)
+    roof["measured_ceiling"] = {
+        "value": best[0], "unit": "GB/s",
+        "probe": f"qgemm_ceiling_stream: one plain read of the {nbytes / 1e6:.1f} MB prepared weight buffer per "
+                 f"launch, {best[1] // 1024} KB per workgroup, over the same rotating buffers"}
+    roof["frac_of_measured_ceiling"] = roof["achieved"] / best[0]
+
+
+def ceiling_kind(ops, act, mx_mode, fp4, wfp4):
+    """The matrix-core instruction a workload's GEMM kernel issues."""
+    if act != "mxfp8":
+        return ops.CEIL_I8
+    if mx_mode == ops.MX_EXACT:
+        return ops.CEIL_BF16
+    return ops.CEIL_F4_SCALED if fp4 and wfp4 else ops.CEIL_F8_SCALED
+
+
 def cpu_baseline_grouped(A, W, sizes, fp4, budget_s=10.0, wfp4=None):
     """The oracle's grouped reference, untuned, on a bounded sample: up to 16
     rows of every expert against the first 1024 output columns of its weights
@@ -381,6 +472,8 @@ def main_grouped(args):
         roof["exact_mode_ceiling_frac"] = PEAK_BF16_TFLOPS / peak
         roof["frac_of_bf16_cores"] = roof["achieved"] / PEAK_BF16_TFLOPS
     roof["traffic"] = measured_traffic(name + suffix + ("_scaled" if mx_mode != ops.MX_EXACT else ""))
+    if not args.no_ceiling:
+        add_mfma_ceiling(roof, ceiling_kind(ops, "mxfp8", mx_mode, fp4, wfp4), sets[0][2].q, w0.packed)
     line = {
         "metric": METRIC, "value": ops_count / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
@@ -413,6 +506,9 @@ def main():
                          "decode-shaped and the MXFP8 workloads under 'secondary')")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough to exceed the MALL 3x)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the measured ceilings (matrix-core issue rate of the GEMM's instruction on the "
+                         "workload's codes, or a plain HBM stream over the same weight buffers)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB device-to-device: a plain copy of known size "
@@ -579,6 +675,11 @@ def measure(args, name, mx_mode_arg, with_cpu):
         roof["frac_of_bf16_cores"] = roof["achieved"] / PEAK_BF16_TFLOPS
     roof["traffic"] = measured_traffic(name + ("_w4a8" if args.w4a8 else "") + mx_suffix
                                        + ("_scaled" if act == "mxfp8" and mx_mode != ops.MX_EXACT else ""))
+    if not args.no_ceiling:
+        if unit == "GB/s":
+            add_stream_ceiling(roof, [st[1].packed for st in sets], K_steps)
+        else:
+            add_mfma_ceiling(roof, ceiling_kind(ops, act, mx_mode, fp4, wfp4), sets[0][2].q, w0.packed)
 
     line = {
         "metric": METRIC,

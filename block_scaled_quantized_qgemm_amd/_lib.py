@@ -1,4 +1,5 @@
-"""ctypes loader for libqgemm.so (the C ABI declared in include/qgemm.h).
+"""ctypes loader for libqgemm.so (the C ABI declared in include/qgemm.h, and
+the measured-ceiling calls of include/qgemm_ceiling.h).
 
 torch is imported first on purpose: the library then binds to the HIP runtime
 torch already loaded (same soname), so torch's streams and allocations are
@@ -29,7 +30,7 @@ class WDesc(ctypes.Structure):
     ]
 
 
-# every symbol include/qgemm.h declares, with its C signature
+# every symbol include/*.h declares, with its C signature
 SIGNATURES = {
     "qgemm_abi_version": (c_int, []),
     "qgemm_status_string": (ctypes.c_char_p, [c_int]),
@@ -53,6 +54,10 @@ SIGNATURES = {
                                      ctypes.POINTER(WDesc), c_vp, c_vp, c_i64, c_int, c_vp, c_vp, c_size, c_vp]),
     "qgemm_run_w4a8": (c_int, [c_vp, c_i64, c_vp, c_int, c_i64, ctypes.POINTER(WDesc), c_vp,
                                c_vp, c_i64, c_int, c_vp, c_vp, c_size, c_vp]),
+    # include/qgemm_ceiling.h
+    "qgemm_ceiling_mfma_shape": (c_int, [c_int, c_int, c_i64, ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double)]),
+    "qgemm_ceiling_mfma": (c_int, [c_int, c_int, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "qgemm_ceiling_stream": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp]),
 }
 
 _lib = None

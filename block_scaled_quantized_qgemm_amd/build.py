@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqgemm.so")
 
 SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemm_i8_wide.hip", "gemm_mx_dma.hip", "gemm_w4a8.hip",
-           "unpack.hip"]
+           "unpack.hip", "ceiling.hip"]
 OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC_FLAGS = [

@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "../../include/qgemm.h"
+#include "../../include/qgemm_ceiling.h"
 #include "kernels.hpp"
 
 namespace {
@@ -510,6 +511,60 @@ int qgemm_run_w4a8(const int8_t* a_q, int64_t lda, const float* a_scales, int a_
   g.ldo = ldo;
   g.bias = bias;
   hipError_t e = qg::launch_gemm_w4a8(g, out_type, as_stream(stream));
+  return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
+}
+
+// ---- measured ceilings (not part of the GEMM path; qgemm_ceiling.h) ----
+
+namespace {
+constexpr int64_t kCeilMaxTrips = int64_t(1) << 24;
+int check_ceiling(int kind, int waves_per_simd, int64_t trips) {
+  if (kind < QGEMM_CEIL_I8 || kind > QGEMM_CEIL_BF16) return QGEMM_E_MODE;
+  if (waves_per_simd < 1 || waves_per_simd > 2 || trips < 1 || trips > kCeilMaxTrips) return QGEMM_E_SHAPE;
+  return QGEMM_OK;
+}
+}  // namespace
+
+int qgemm_ceiling_mfma_shape(int kind, int waves_per_simd, int64_t trips, int64_t* workgroups, double* ops) {
+  if (!workgroups || !ops) return QGEMM_E_NULL;
+  int rc = check_ceiling(kind, waves_per_simd, trips);
+  if (rc != QGEMM_OK) return rc;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+  // 2 * M * N * K of one instruction
+  const double per = kind == QGEMM_CEIL_I8 ? 2.0 * 16 * 16 * 64 : kind == QGEMM_CEIL_BF16 ? 2.0 * 32 * 32 * 16
+                                                                                       : 2.0 * 32 * 32 * 64;
+  const int64_t wg = qg::cu_count();
+  *workgroups = wg;
+  *ops = per * (double)qg::kCeilSets * (double)trips * 4.0 * waves_per_simd * (double)wg;
+  return QGEMM_OK;
+}
+
+int qgemm_ceiling_mfma(int kind, int waves_per_simd, int64_t trips, const void* a_ops, const void* b_ops,
+                       int32_t* sink, int64_t* clocks, void* stream) {
+  if (!a_ops || !b_ops || !sink) return QGEMM_E_NULL;
+  int rc = check_ceiling(kind, waves_per_simd, trips);
+  if (rc != QGEMM_OK) return rc;
+  if (!aligned(a_ops, 32) || !aligned(b_ops, 32) || !aligned(sink, 4) || (clocks && !aligned(clocks, 8)))
+    return QGEMM_E_ALIGN;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+  hipError_t e = qg::launch_ceiling_mfma(kind, waves_per_simd, trips, static_cast<const uint8_t*>(a_ops),
+                                         static_cast<const uint8_t*>(b_ops), sink, clocks, as_stream(stream));
+  return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
+}
+
+int qgemm_ceiling_stream(const void* src, int64_t bytes, int64_t block_bytes, int32_t* sink, void* stream) {
+  if (!src || !sink) return QGEMM_E_NULL;
+  if (bytes < 0 || bytes % 16 != 0 || bytes > (int64_t(1) << 40)) return QGEMM_E_SHAPE;
+  if (block_bytes < 16384 || block_bytes > (int64_t(1) << 20) || block_bytes % 16384 != 0) return QGEMM_E_SHAPE;
+  if ((bytes + block_bytes - 1) / block_bytes > 0x7fffffff) return QGEMM_E_SHAPE;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return QGEMM_E_ALIGN;
+  if (bytes == 0) return QGEMM_OK;
+  int dc = check_device();
+  if (dc != QGEMM_OK) return dc;
+  hipError_t e = qg::launch_ceiling_stream(static_cast<const uint8_t*>(src), bytes, block_bytes, sink,
+                                           as_stream(stream));
   return e == hipSuccess ? QGEMM_OK : QGEMM_E_HIP;
 }
 

@@ -59,6 +59,23 @@ struct UnpackArgs {
 };
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t st);
 
+// Measured ceilings (qgemm_ceiling_mfma, qgemm_ceiling_stream; not part of
+// the GEMM path). Matrix cores: one workgroup per CU, 256 * waves_per_simd
+// threads; lane l of every wave takes kCeilSets 32-byte operand sets from
+// a_ops + 32 * (kCeilSets * l + q) and one from b_ops + 32 * l, then issues
+// trips * kCeilSets instructions of the kind. `clocks` (may be null) gets,
+// per workgroup, the shader-clock and 100 MHz real-time ticks of its loop.
+// Stream: one workgroup of 256 threads per block_bytes (a multiple of 16 KB)
+// of src, 16-byte loads clamped to the last 16 bytes.
+enum { CEIL_I8 = 0, CEIL_F8_SCALED = 1, CEIL_F4_SCALED = 2, CEIL_BF16 = 3 };
+constexpr int kCeilSets = 8;
+constexpr int kCeilHoldWords = 24 * 1024;  // 96 KB of LDS: one workgroup per CU
+constexpr int kCeilSinkMagic = 0x5eed5eed;
+hipError_t launch_ceiling_mfma(int kind, int waves_per_simd, int64_t trips, const uint8_t* a_ops,
+                               const uint8_t* b_ops, int32_t* sink, int64_t* clocks, hipStream_t st);
+hipError_t launch_ceiling_stream(const uint8_t* src, int64_t bytes, int64_t block_bytes, int32_t* sink,
+                                 hipStream_t st);
+
 struct GemmArgs {
   const uint8_t* a;     // activation codes [M][lda]
   int64_t lda;

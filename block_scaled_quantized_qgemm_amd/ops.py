@@ -19,6 +19,9 @@ _MX_FMTS = (FMT_MXFP8_E4M3, FMT_MXFP4_E2M1)
 GRAN_TENSOR, GRAN_ROW, GRAN_BLOCK32, GRAN_GROUP64 = 0, 1, 2, 3
 OUT_F32, OUT_BF16, OUT_I32 = 0, 1, 2
 MX_EXACT, MX_SCALED_MFMA = 0, 1
+# include/qgemm_ceiling.h: the matrix-core instruction a ceiling measurement issues
+CEIL_I8, CEIL_F8_SCALED, CEIL_F4_SCALED, CEIL_BF16 = 0, 1, 2, 3
+CEILING_A_BYTES, CEILING_B_BYTES = 16384, 2048
 
 _OUT_DTYPES = {OUT_F32: torch.float32, OUT_BF16: torch.bfloat16, OUT_I32: torch.int32}
 
@@ -411,3 +414,42 @@ def qgemm_run_w4a8(a: QuantizedRows, w: PackedWeights, out_type: int = OUT_F32,
                             _bias_ptr(bias, N), None, 0, ctypes.c_void_p(_stream(dev, stream)))
     _check("qgemm_run_w4a8", st)
     return out[:, :N]
+
+
+# ---- measured ceilings (include/qgemm_ceiling.h; not part of the GEMM path) ----
+
+def qgemm_ceiling_mfma_shape(kind: int, waves_per_simd: int, trips: int):
+    """(workgroups, operations) of one qgemm_ceiling_mfma launch on the current device."""
+    lib = L.load()
+    wg, ops_ = ctypes.c_int64(0), ctypes.c_double(0.0)
+    st = lib.qgemm_ceiling_mfma_shape(kind, waves_per_simd, trips, ctypes.byref(wg), ctypes.byref(ops_))
+    _check("qgemm_ceiling_mfma_shape", st)
+    return int(wg.value), float(ops_.value)
+
+
+def qgemm_ceiling_mfma(kind: int, waves_per_simd: int, trips: int, a_ops: torch.Tensor, b_ops: torch.Tensor,
+                       sink: torch.Tensor, clocks: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Issue trips * 8 matrix-core instructions of `kind` per wave on every CU
+    (see qgemm_ceiling.h). a_ops / b_ops: device byte tensors of at least
+    CEILING_A_BYTES / CEILING_B_BYTES; sink: int32 [1]; clocks: int64
+    [2 * workgroups] or None."""
+    lib = L.load()
+    assert a_ops.is_contiguous() and a_ops.numel() * a_ops.element_size() >= CEILING_A_BYTES
+    assert b_ops.is_contiguous() and b_ops.numel() * b_ops.element_size() >= CEILING_B_BYTES
+    assert sink.dtype == torch.int32 and sink.numel() >= 1
+    if clocks is not None:
+        wg, _ = qgemm_ceiling_mfma_shape(kind, waves_per_simd, trips)
+        assert clocks.dtype == torch.int64 and clocks.is_contiguous() and clocks.numel() >= 2 * wg
+    st = lib.qgemm_ceiling_mfma(kind, waves_per_simd, trips, _ptr(a_ops), _ptr(b_ops), _ptr(sink), _ptr(clocks),
+                                ctypes.c_void_p(_stream(a_ops.device, stream)))
+    _check("qgemm_ceiling_mfma", st)
+
+
+def qgemm_ceiling_stream(src: torch.Tensor, nbytes: int, block_bytes: int, sink: torch.Tensor, stream=None) -> None:
+    """Read the first nbytes of the device tensor src once, one workgroup per
+    block_bytes (see qgemm_ceiling.h)."""
+    lib = L.load()
+    assert src.is_contiguous() and nbytes <= src.numel() * src.element_size()
+    assert sink.dtype == torch.int32 and sink.numel() >= 1
+    st = lib.qgemm_ceiling_stream(_ptr(src), nbytes, block_bytes, _ptr(sink), ctypes.c_void_p(_stream(src.device, stream)))
+    _check("qgemm_ceiling_stream", st)

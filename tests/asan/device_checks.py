@@ -143,6 +143,18 @@ expect("unpack nothing requested", un(ctypes.byref(d8), DEV[8], None, 0, None, 0
 expect("unpack MX with float scales", un(ctypes.byref(dmx), DEV[8], None, 0, DEV[15], 0, None, None, 0, None),
        E_MODE, 0)
 
+# measured ceilings: one launch each; the shape call launches nothing and
+# reports one workgroup per CU (the stub has 256) and the operation count
+wg, ops_ = ctypes.c_int64(0), ctypes.c_double(0.0)
+expect("ceiling shape", lib.qgemm_ceiling_mfma_shape(0, 2, 100, ctypes.byref(wg), ctypes.byref(ops_)),
+       OK if MODE == "gfx950" else E_DEVICE, 0)
+if MODE == "gfx950" and (wg.value != 256 or ops_.value != 2.0 * 16 * 16 * 64 * 8 * 100 * 4 * 2 * 256):
+    failures.append(f"ceiling shape: {wg.value} workgroups, {ops_.value} operations")
+expect("ceiling mfma", lib.qgemm_ceiling_mfma(1, 2, 100, DEV[0], DEV[1], DEV[2], DEV[3], None), OK, 1)
+expect("ceiling mfma, bad kind", lib.qgemm_ceiling_mfma(7, 2, 100, DEV[0], DEV[1], DEV[2], None, None), E_MODE, 0)
+expect("ceiling stream", lib.qgemm_ceiling_stream(DEV[0], 1 << 20, 1 << 16, DEV[2], None), OK, 1)
+expect("ceiling stream, empty", lib.qgemm_ceiling_stream(DEV[0], 0, 1 << 16, DEV[2], None), OK, 0)
+
 if failures:
     print("\n".join(failures))
     sys.exit(1)

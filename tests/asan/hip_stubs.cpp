@@ -110,6 +110,19 @@ hipError_t launch_unpack(const UnpackArgs& a, hipStream_t) {
   ++qg_stub_launches;
   return hipSuccess;
 }
+hipError_t launch_ceiling_mfma(int kind, int waves_per_simd, int64_t trips, const uint8_t* a_ops,
+                               const uint8_t* b_ops, int32_t* sink, int64_t*, hipStream_t) {
+  require(kind >= 0 && kind <= 3 && (waves_per_simd == 1 || waves_per_simd == 2) && trips >= 1 && a_ops && b_ops &&
+              sink,
+          "ceiling mfma args");
+  ++qg_stub_launches;
+  return hipSuccess;
+}
+hipError_t launch_ceiling_stream(const uint8_t* src, int64_t bytes, int64_t block_bytes, int32_t* sink, hipStream_t) {
+  require(src && sink && bytes >= 16 && bytes % 16 == 0 && block_bytes % 16384 == 0, "ceiling stream args");
+  ++qg_stub_launches;
+  return hipSuccess;
+}
 hipError_t launch_gemm_w4a8(const GemmArgs& a, int, hipStream_t) {
   check_gemm(a);
   ++qg_stub_launches;

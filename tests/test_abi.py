@@ -13,6 +13,7 @@ torch = pytest.importorskip("torch")
 from block_scaled_quantized_qgemm_amd import _lib as L  # noqa: E402
 
 HEADER = os.path.join(ROOT, "include", "qgemm.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 OK, E_NULL, E_SHAPE, E_MODE, E_ALIGN, E_OVERFLOW, E_DEVICE, E_DESC, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8
 INT8, UINT8, MX, INT4, MX4 = 0, 1, 2, 3, 4
@@ -28,7 +29,7 @@ def lib():
 
 
 def _declared_functions():
-    src = open(HEADER).read()
+    src = "".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return set(re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(qgemm_\w+)\s*\(", src, flags=re.M))
 
@@ -374,6 +375,42 @@ def test_run_w4a8_validation(lib):
     assert _run4(lib, huge, lda=kp, M=1) == E_SHAPE
 
 
+def test_ceiling_validation(lib):
+    """The measured-ceiling calls (qgemm_ceiling.h) reject bad arguments before
+    any launch: missing buffers, an unknown instruction kind, waves per SIMD
+    or trips out of range, misaligned buffers, stream sizes that are not whole
+    16-byte loads or whole 16 KB blocks."""
+    dev = 0x10000000
+    wg, ops_ = ctypes.c_int64(0), ctypes.c_double(0.0)
+    shape = lib.qgemm_ceiling_mfma_shape
+    assert shape(0, 2, 16, None, ctypes.byref(ops_)) == E_NULL
+    assert shape(4, 2, 16, ctypes.byref(wg), ctypes.byref(ops_)) == E_MODE
+    assert shape(-1, 2, 16, ctypes.byref(wg), ctypes.byref(ops_)) == E_MODE
+    assert shape(0, 3, 16, ctypes.byref(wg), ctypes.byref(ops_)) == E_SHAPE
+    assert shape(0, 0, 16, ctypes.byref(wg), ctypes.byref(ops_)) == E_SHAPE
+    assert shape(0, 2, 0, ctypes.byref(wg), ctypes.byref(ops_)) == E_SHAPE
+    assert shape(0, 2, (1 << 24) + 1, ctypes.byref(wg), ctypes.byref(ops_)) == E_SHAPE
+    mf = lib.qgemm_ceiling_mfma
+    assert mf(0, 2, 16, None, dev, dev, None, None) == E_NULL
+    assert mf(0, 2, 16, dev, dev, None, None, None) == E_NULL
+    assert mf(5, 2, 16, dev, dev, dev, None, None) == E_MODE
+    assert mf(1, 2, 0, dev, dev, dev, None, None) == E_SHAPE
+    assert mf(1, 2, 16, dev + 16, dev, dev, None, None) == E_ALIGN
+    assert mf(1, 2, 16, dev, dev + 8, dev, None, None) == E_ALIGN
+    assert mf(1, 2, 16, dev, dev, dev + 2, None, None) == E_ALIGN
+    assert mf(1, 2, 16, dev, dev, dev, dev + 4, None) == E_ALIGN
+    st = lib.qgemm_ceiling_stream
+    assert st(None, 1024, 16384, dev, None) == E_NULL
+    assert st(dev, 1024, 16384, None, None) == E_NULL
+    assert st(dev, 1000, 16384, dev, None) == E_SHAPE      # not whole 16-byte loads
+    assert st(dev, -16, 16384, dev, None) == E_SHAPE
+    assert st(dev, 1024, 8192, dev, None) == E_SHAPE       # block under 16 KB
+    assert st(dev, 1024, 20000, dev, None) == E_SHAPE      # not whole 16 KB
+    assert st(dev, 1024, (1 << 20) + 16384, dev, None) == E_SHAPE
+    assert st(dev + 8, 1024, 16384, dev, None) == E_ALIGN
+    assert st(dev, 0, 16384, dev, None) == OK                # nothing to read
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
 def test_no_device_is_an_error_not_a_fallback(lib):
     # fully valid arguments: the only thing missing is a gfx950
@@ -383,6 +420,10 @@ def test_no_device_is_an_error_not_a_fallback(lib):
     assert _grouped(lib) == E_DEVICE
     assert lib.qgemm_rmsnorm_quantize_rows(FAKE, 4, 64, 64, FAKE, 1e-6, INT8, ROW, FAKE, 64, FAKE, None,
                                            None) == E_DEVICE
+    wg, ops_ = ctypes.c_int64(0), ctypes.c_double(0.0)
+    assert lib.qgemm_ceiling_mfma_shape(0, 2, 16, ctypes.byref(wg), ctypes.byref(ops_)) == E_DEVICE
+    assert lib.qgemm_ceiling_mfma(0, 2, 16, FAKE, FAKE, FAKE, None, None) == E_DEVICE
+    assert lib.qgemm_ceiling_stream(FAKE, 1024, 16384, FAKE, None) == E_DEVICE
 
 
 def test_packed_int8_block_layout_round_trip():
