@@ -705,20 +705,25 @@ static hipError_t launch_dma(const GemmArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Decode-shaped GEMM (M <= 16 rows): the time is the stream of W out of HBM,
 // so every byte of W is read once, straight into registers, and the matrix
-// cores only need to keep up. A workgroup owns one block of 16 weight rows
-// (a v_mfma_i32_16x16x64_i8 column block) over all of K; its eight waves
+// cores only need to keep up. A workgroup owns kDecCols blocks of 16 weight
+// rows (v_mfma_i32_16x16x64_i8 column blocks) over all of K; its eight waves
 // take contiguous ranges of K. A wave works through its range in batches of
-// eight 64-deep steps: each step is one contiguous 1 KB load of W (a 16 x 64
-// weight block already in the operand's lane order) and one 16-byte load per
-// lane of the activation rows. Every load of a batch is issued before any is
-// used (16 loads in flight per wave, three workgroups per CU). The activation
-// rows ride in the other operand. Rows >= M, steps at or past K_pad and
-// columns past the last 16-byte chunk holding column K - 1 come back as zeros
-// from the range-checked buffer loads. The eight partial int32 tiles are
-// summed through LDS before the epilogue, so the result is exact.
+// eight 64-deep steps: each step is one contiguous 1 KB load of W per block
+// (a 16 x 64 weight block already in the operand's lane order) and one
+// 16-byte load per lane of the activation rows, which then feeds every
+// block's instruction. Weight loads are non-temporal (each byte is used
+// once). Every load of a batch is issued before any is used (24 loads in
+// flight per wave, two workgroups per CU). The activation rows ride in the
+// other operand. Rows >= M, steps at or past K_pad (each block has its own
+// buffer range) and columns past the last 16-byte chunk holding column K - 1
+// come back as zeros from the range-checked buffer loads. The eight partial
+// int32 tiles are summed through LDS before the epilogue, so the result is
+// exact.
 // ---------------------------------------------------------------------------
 constexpr int kDecWaves = 8;  // waves per workgroup, each on its own K range
 constexpr int kDecBatch = 8;  // 64-deep steps per load batch
+constexpr int kDecCols = 2;   // 16-row weight blocks per workgroup
+constexpr int kDecWAux = 2;   // non-temporal weight loads
 
 // ONE: K_pad <= 512 * kDecWaves, one batch per wave (no loop).
 // MLE8 (M <= 8): rows 8-15 of the 16-row activation operand only feed output
@@ -731,10 +736,10 @@ template <bool ASYM, int OUT, bool ONE, bool MLE8>
 __global__ __launch_bounds__(kDecWaves * 64) void gemm_i8_decode_kernel(GemmArgs p) {
   constexpr int U = kDecBatch;
   constexpr int UA = MLE8 ? U / 2 : U;  // activation loads per batch
-  __shared__ v4i red[kDecWaves][64];
+  __shared__ v4i red[kDecWaves][kDecCols][64];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * kDecCols;
   const int steps = (int)(p.K_pad / 64);
   // steps of each wave: a whole number of batches. Steps at or past K_pad
   // fall outside the block's W range and read as zeros, so no load is tested;
@@ -749,21 +754,30 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_i8_decode_kernel(GemmArgs
   const int arow = MLE8 ? (lane & 7) : (lane & 15);
   const int akin = (MLE8 ? ((lane >> 3) & 1) * 64 : 0) + (lane >> 4) * 16;
   constexpr uint32_t kOff = 0x80000000u;
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.w + n0 * p.K_pad), (short)0, (int)(16 * p.K_pad), kRawBufferWord3);
+  // one range per 16-row block, so its steps past K_pad read zeros (the
+  // packed rows are padded to a multiple of 256, so every block exists)
+  __amdgpu_buffer_rsrc_t wrs[kDecCols];
+#pragma unroll
+  for (int c = 0; c < kDecCols; ++c)
+    wrs[c] = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w + (n0 + 16 * c) * p.K_pad), (short)0, (int)(16 * p.K_pad),
+                                               kRawBufferWord3);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.a, (short)0, (int)((p.M - 1) * p.lda + ((p.K + 15) & ~(int64_t)15)), kRawBufferWord3);
   const uint32_t woff = (uint32_t)sbeg * 1024u + (uint32_t)(lane * 16);  // 16 x 64 blocks, lane order
   const uint32_t aoff = arow < p.M ? (uint32_t)(arow * p.lda + sbeg * 64 + akin) : kOff;
 
   // one batch at a time: its loads are all issued before the first MFMA
-  v4i acc = {0, 0, 0, 0};
+  v4i acc[kDecCols];
+#pragma unroll
+  for (int c = 0; c < kDecCols; ++c) acc[c] = v4i{0, 0, 0, 0};
   for (int b = 0; b < (ONE ? U : per); b += U) {
-    v4i av[UA], wv[U];
+    v4i av[UA], wv[kDecCols][U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      wv[u] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)(woff + (uint32_t)((b + u) * 1024)), 0, 0));
+#pragma unroll
+      for (int c = 0; c < kDecCols; ++c)
+        wv[c][u] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs[c], (int)(woff + (uint32_t)((b + u) * 1024)), 0, kDecWAux));
 #pragma unroll
     for (int u = 0; u < UA; ++u)
       av[u] = __builtin_bit_cast(
@@ -780,22 +794,25 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_i8_decode_kernel(GemmArgs
         a = av[MLE8 ? u / 2 : u];
       }
       if (ASYM) a ^= (int)0x80808080u;  // uint8 codes enter as q - 128 (a dead step still meets zero weights)
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wv[u], acc, 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < kDecCols; ++c) acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wv[c][u], acc[c], 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  red[wid][lane] = acc;
+#pragma unroll
+  for (int c = 0; c < kDecCols; ++c) red[wid][c][lane] = acc[c];
   __syncthreads();
 
-  // thread t < 256 finishes item t / 64 of lane t % 64: row 4 * (l / 16) + item, column l % 16
-  for (int t = threadIdx.x; t < 256; t += kDecWaves * 64) {
-    const int l = t & 63, item = t >> 6;
+  // thread t < 256 kDecCols finishes item (t / 64) % 4 of lane t % 64 of block
+  // t / 256: row 4 * (l / 16) + item, column 16 * block + l % 16
+  for (int t = threadIdx.x; t < 256 * kDecCols; t += kDecWaves * 64) {
+    const int cb = t >> 8, l = t & 63, item = (t >> 6) & 3;
     const int m = 4 * (l >> 4) + item;
-    const int64_t n = n0 + (l & 15);
+    const int64_t n = n0 + 16 * cb + (l & 15);
     if (m < p.M && n < p.N) {
       int c = 0;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) c += red[w][l][item];
+      for (int w = 0; w < kDecWaves; ++w) c += red[w][cb][l][item];
       const float sa = p.a_per_tensor ? p.sa[0] : p.sa[m];
       const int z = ASYM ? (p.a_per_tensor ? p.za[0] : p.za[m]) : 0;
       if (ASYM) c = (int)((uint32_t)c - (uint32_t)(z - 128) * (uint32_t)p.colsum[n]);
@@ -809,7 +826,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void gemm_i8_decode_kernel(GemmArgs
 
 template <bool ASYM, int OUT, bool MLE8>
 static void launch_decode_rows(const GemmArgs& a, hipStream_t st) {
-  const int64_t groups = (a.N + 15) / 16;
+  const int64_t groups = (a.N + 16 * kDecCols - 1) / (16 * kDecCols);
   if (a.K_pad <= 64 * kDecBatch * kDecWaves)
     hipLaunchKernelGGL((gemm_i8_decode_kernel<ASYM, OUT, true, MLE8>), dim3((unsigned)groups), dim3(kDecWaves * 64),
                        0, st, a);
