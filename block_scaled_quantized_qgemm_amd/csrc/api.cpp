@@ -172,7 +172,7 @@ void launch_quantize(const float* x, int64_t M, int64_t K, int64_t ldx, int fmt,
                      float* scales, int32_t* zero_points, uint8_t* mx_scales, int64_t ld_mx, float* ws,
                      hipStream_t st) {
   if (is_mx_fmt(fmt)) {
-    qg::launch_quantize_mx(x, M, K, ldx, fmt == QGEMM_FMT_MXFP4_E2M1, (uint8_t*)q, ldq, mx_scales, ld_mx, st);
+    qg::launch_quantize_mx(x, M, K, ldx, fmt == QGEMM_FMT_MXFP4_E2M1, (uint8_t*)q, ldq, mx_scales, ld_mx, 0, st);
   } else {
     qg::launch_quantize_int(x, M, K, ldx, fmt == QGEMM_FMT_UINT8_ASYM, gran == QGEMM_GRAN_TENSOR, (uint8_t*)q, ldq,
                             0, scales, zero_points, nullptr, ws, st);
@@ -265,8 +265,9 @@ int qgemm_prepack_weights(const float* w, int64_t N, int64_t K, int64_t ldw, int
   } else {
     if (hipMemsetAsync(base + L.scales_off, 127, (size_t)(L.N_pad * (L.K_pad / 32)), st) != hipSuccess)
       return QGEMM_E_HIP;
+    // e4m3 codes in 1 KB blocks of 16 rows x 64 K, e2m1 codes row-major
     qg::launch_quantize_mx(w, N, K, ldw, fmt == QGEMM_FMT_MXFP4_E2M1, base + L.codes_off, code_bytes(fmt, L.K_pad),
-                           base + L.scales_off, L.K_pad / 32, st);
+                           base + L.scales_off, L.K_pad / 32, L.K_pad, st);
   }
   int rc = launch_status();
   if (rc != QGEMM_OK) return rc;
@@ -309,7 +310,9 @@ int qgemm_unpack_weights(const qgemm_wdesc* desc, const void* packed, void* code
 
   hipStream_t st = as_stream(stream);
   const uint8_t* base = static_cast<const uint8_t*>(packed);
-  const int ufmt = i8 ? qg::UNPACK_FMT_INT8 : (i4 ? qg::UNPACK_FMT_INT4 : qg::UNPACK_FMT_MX);
+  const int ufmt = i8 ? qg::UNPACK_FMT_INT8
+                       : i4 ? qg::UNPACK_FMT_INT4
+                            : (fmt == QGEMM_FMT_MXFP8_E4M3 ? qg::UNPACK_FMT_MX8 : qg::UNPACK_FMT_MX);
   auto run = [&](int what, const uint8_t* src, int64_t src_pitch, void* out, int64_t ld, int64_t rows, int64_t cols,
                  int64_t row_bytes) {
     qg::UnpackArgs u{src, src_pitch, out, ld, rows, cols, row_bytes, desc->K_pad, what, ufmt};

@@ -84,6 +84,14 @@ __device__ inline int lds_off(int row, int chunk) {
   return row * RB + ((chunk ^ ((row / RPL) % CPR)) << 4);
 }
 
+// Byte offset of e4m3 weight code (n, k) in a prepared MX buffer: 1 KB
+// blocks of 16 rows x 64 K in block-row-major order, row n % 16 of a block at
+// byte 64 (n % 16), its 64 codes in K order (so the 16 rows x 64 K a GEMM
+// stage takes from one block are a single contiguous 1 KB load).
+__host__ __device__ inline int64_t mx8_code_off(int64_t n, int64_t k, int64_t K_pad) {
+  return ((((n >> 4) * (K_pad >> 6)) + (k >> 6)) << 10) + ((n & 15) << 6) + (k & 63);
+}
+
 // E8M0 code E as the float32 2^(E-127) (E in [1, 254]).
 __device__ inline float e8m0_to_f32(int E) { return __uint_as_float((uint32_t)E << 23); }
 

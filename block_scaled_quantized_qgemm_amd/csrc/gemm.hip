@@ -215,7 +215,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_kernel(GemmArgs p) {
         const uint2 h_ = *reinterpret_cast<const uint2*>(p.w + n * (p.K_pad >> 1) + (k >> 1));  \
         RB_[i] = v4i{(int)h_.x, (int)h_.y, 0, 0};                                               \
       } else {                                                                                  \
-        RB_[i] = *reinterpret_cast<const v4i*>(p.w + n * p.K_pad + k);                          \
+        RB_[i] = *reinterpret_cast<const v4i*>(p.w + mx8_code_off(n, k, p.K_pad));              \
       }                                                                                         \
       if constexpr (MODE == MXB) EB[i] = (int)p.ew[n * wblocks + (k >> 5)];                     \
     }                                                                                           \

@@ -114,6 +114,7 @@ struct MxDmaCfg {
   static constexpr int SINK = SCALES + 2 * SUPER;   // 1 KB that the empty scale loads target
   static constexpr int LDS = SINK + 1024 > EPI ? SINK + 1024 : EPI;
   static_assert(KPS == 64 || KPS == 128, "stage depth");
+  static_assert(W4 || RBW == 64, "e4m3 weight stages are one 64-K block column");
   static_assert(!(EXACT && KPS != 64), "exact-mode stages are 64 deep");
   static_assert(DATA % (1024 * NW) == 0 && (BM * RBA) % 1024 == 0 && (BM + BN) % 64 == 0 && BM % 64 == 0,
                 "loads per wave");
@@ -270,7 +271,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
       const int P = (j - C::IA) * 1024 + lane * 16;
       const int r = P / RBW;
       const int c = ((P % RBW) >> 4) ^ ((r / (256 / RBW)) % (RBW / 16));
-      voff[i] = (uint32_t)(r * ldw) + (uint32_t)(c * 16);
+      // e2m1 weights are row-major; e4m3 weights come in 1 KB blocks of 16
+      // rows x 64 K (mx8_code_off), so this load, rows 16 (j - IA) .. + 15 of
+      // the tile, reads one whole block (the stage's K offset: kt KB)
+      voff[i] = W4 ? (uint32_t)(r * ldw) + (uint32_t)(c * 16)
+                   : (uint32_t)((r >> 4) * 16 * ldw) + (uint32_t)((r & 15) * 64 + c * 16);
     }
   }
 #pragma unroll
@@ -286,7 +291,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(ja ? abase : wbase), (short)0, live ? (int)(ja ? nrec_a : nrec_w) : 0, kRawBufferWord3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, QG_LDSP(smem + s * STAGE + j * 1024), 16, (int)voff[i],
-                                               kt * (ja ? RBA : RBW), 0, 0);
+                                               kt * (ja ? RBA : (W4 ? RBW : 1024)), 0, 0);
     } else {
       const int js = wid * IPS + (i - IPD);
       const bool ja = js * 64 < BM, real = js < C::NSL && kt % C::SS == 0;

@@ -30,8 +30,11 @@ void launch_rmsnorm_quantize(const float* x, int64_t rows, int64_t K, int64_t ld
 
 // MXFP8 (e4m3 codes) or, fp4, MXFP4 (e2m1 codes, two per byte, element 2i
 // in the low nibble) row quantization with E8M0 per 32 K-elements; K % 32 == 0.
+// Codes go row-major with stride ldq, except e4m3 weights being prepared
+// (wblk_kpad = their K_pad > 0): those go to the blocked layout of
+// mx8_code_off.
 void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, bool fp4, uint8_t* q, int64_t ldq,
-                        uint8_t* e8, int64_t lde, hipStream_t st);
+                        uint8_t* e8, int64_t lde, int64_t wblk_kpad, hipStream_t st);
 
 // int4 weights, symmetric, one scale per group of 64 K of each row, into the
 // packed layout of GemmArgs::w (INT4). The buffer must be zero beforehand.
@@ -46,7 +49,7 @@ int cu_count();
 // and int4 codes as one int8 per element, MX codes as stored), the other
 // outputs one element per thread.
 enum { UNPACK_CODES = 0, UNPACK_WORDS = 1, UNPACK_INT4_SCALES = 2, UNPACK_E8M0 = 3 };
-enum { UNPACK_FMT_INT8 = 0, UNPACK_FMT_INT4 = 1, UNPACK_FMT_MX = 2 };
+enum { UNPACK_FMT_INT8 = 0, UNPACK_FMT_INT4 = 1, UNPACK_FMT_MX = 2, UNPACK_FMT_MX8 = 3 };
 struct UnpackArgs {
   const uint8_t* src;   // the section of the packed buffer the output comes from
   int64_t src_pitch;    // bytes per source row (MX codes, E8M0)
@@ -87,7 +90,10 @@ struct GemmArgs {
   // packed codes, N_pad x K_pad. int8: 1 KB blocks of 16 rows x 64 K, block
   // (n / 16, k / 64) at byte ((n / 16) * (K_pad / 64) + k / 64) * 1024, and in
   // it the 16 bytes k % 64 in [16c, 16c + 16) of row n % 16 at 256 c + 16 (n % 16)
-  // (one v_mfma_i32_16x16x64_i8 B operand in lane order). MX: row-major.
+  // (one v_mfma_i32_16x16x64_i8 B operand in lane order). MX e4m3: 1 KB
+  // blocks of 16 rows x 64 K in the same block order, row n % 16 at byte
+  // 64 (n % 16) in K order (mx8_code_off). MX e2m1: row-major, K_pad / 2
+  // bytes per row.
   // INT4: N_pad x K_pad / 2 bytes in 1 KB blocks of 16 rows x 128 K, block
   // (n / 16, k / 128) at ((n / 16) * (K_pad / 128) + k / 128) * 1024; lane
   // l = 16 c + n % 16 owns the 16 bytes at 16 l: bytes 0-7 hold k % 128 in

@@ -471,15 +471,17 @@ __device__ inline uint32_t e2m1_code(float v) {
 template <bool VEC, bool FP4>
 __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __restrict__ x, int64_t ldx,
                                                                int64_t K, uint8_t* __restrict__ q, int64_t ldq,
-                                                               uint8_t* __restrict__ e8, int64_t lde) {
+                                                               uint8_t* __restrict__ e8, int64_t lde,
+                                                               int64_t wblk_kpad) {
   const int64_t row = blockIdx.x;
   const int64_t k = (int64_t)blockIdx.y * (4 * kRowThreads) + 4 * threadIdx.x;
   const bool valid = k < K;  // K % 32 == 0: a block's eight lanes agree
   const float* xr = x + row * ldx + (valid ? k : 0);
   float4 v;
-  if (VEC)
-    v = *reinterpret_cast<const float4*>(xr);
-  else
+  if (VEC) {  // each activation is read once: non-temporal loads
+    const v4f t4 = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(xr));
+    v = make_float4(t4[0], t4[1], t4[2], t4[3]);
+  } else
     v = make_float4(xr[0], xr[1], xr[2], xr[3]);
   if (!valid) v = make_float4(0.f, 0.f, 0.f, 0.f);
   float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
@@ -507,7 +509,9 @@ __global__ __launch_bounds__(kRowThreads) void quant_mx_kernel(const float* __re
   }
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(v.x * inv, v.y * inv, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(v.z * inv, v.w * inv, w, true);
-  uint8_t* qr = q + row * ldq + k;
+  // activations row-major; e4m3 weights (wblk_kpad = K_pad) in the blocked
+  // layout of mx8_code_off (four codes of one row segment of a block)
+  uint8_t* qr = q + (wblk_kpad ? mx8_code_off(row, k, wblk_kpad) : row * ldq + k);
   if (VEC) {
     *reinterpret_cast<uint32_t*>(qr) = (uint32_t)w;
   } else {
@@ -646,19 +650,20 @@ void launch_quantize_int4(const float* w, int64_t rows, int64_t K, int64_t ldw, 
 }
 
 void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, bool fp4, uint8_t* q, int64_t ldq,
-                        uint8_t* e8, int64_t lde, hipStream_t st) {
+                        uint8_t* e8, int64_t lde, int64_t wblk_kpad, hipStream_t st) {
   if (rows == 0) return;
   dim3 grid((unsigned)rows, (unsigned)((K + 4 * kRowThreads - 1) / (4 * kRowThreads))), block(kRowThreads);
   const bool vec = ldx % 4 == 0 && ((uintptr_t)x % 16) == 0 && ldq % 4 == 0 && ((uintptr_t)q % 4) == 0;
+  const int64_t wb = fp4 ? 0 : wblk_kpad;
   if (fp4) {
     if (vec)
-      quant_mx_kernel<true, true><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+      quant_mx_kernel<true, true><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde, wb);
     else
-      quant_mx_kernel<false, true><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+      quant_mx_kernel<false, true><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde, wb);
   } else if (vec) {
-    quant_mx_kernel<true, false><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+    quant_mx_kernel<true, false><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde, wb);
   } else {
-    quant_mx_kernel<false, false><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde);
+    quant_mx_kernel<false, false><<<grid, block, 0, st>>>(x, ldx, K, q, ldq, e8, lde, wb);
   }
 }
 

@@ -40,7 +40,9 @@ __global__ __launch_bounds__(256) void unpack_kernel(UnpackArgs a) {
             v = a.src[((n / 16) * (a.K_pad / 64) + b / 64) * 1024 + 256 * ((b % 64) / 16) + 16 * (n % 16) + b % 16];
           else if (a.fmt == UNPACK_FMT_INT4)
             v = (uint8_t)int4_code(a.src, n, b, a.K_pad);
-          else  // MX: row-major, K_pad (e4m3) or K_pad / 2 (e2m1) bytes per row
+          else if (a.fmt == UNPACK_FMT_MX8)  // e4m3: 1 KB blocks of 16 rows x 64 K
+            v = a.src[mx8_code_off(n, b, a.K_pad)];
+          else  // e2m1: row-major, K_pad / 2 bytes per row
             v = a.src[n * a.src_pitch + b];
           dst[i] = v;
         }

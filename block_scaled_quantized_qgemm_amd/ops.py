@@ -95,6 +95,14 @@ def unblock_int8_codes(raw: torch.Tensor, n_pad: int, k_pad: int) -> torch.Tenso
     return b.permute(0, 3, 1, 2, 4).reshape(n_pad, k_pad)     # [rb, r, kb, c, j]
 
 
+def unblock_mx8_codes(raw: torch.Tensor, n_pad: int, k_pad: int) -> torch.Tensor:
+    """Row-major [n_pad, k_pad] copy of packed e4m3 weight codes stored as 1 KB
+    blocks of 16 rows x 64 K in block-row-major order, row n % 16 of a block
+    at 64 (n % 16) with its 64 codes in K order."""
+    b = raw.reshape(n_pad // 16, k_pad // 64, 16, 64)        # [rb, kb, r, j]
+    return b.permute(0, 2, 1, 3).reshape(n_pad, k_pad)        # [rb, r, kb, j]
+
+
 def unblock_int4_codes(raw: torch.Tensor, n_pad: int, k_pad: int) -> torch.Tensor:
     """Row-major int8 [n_pad, k_pad] codes from the packed int4 layout: 1 KB
     blocks of 16 rows x 128 K; lane 16 c + r of a block owns 16 bytes, 8 per
@@ -125,8 +133,9 @@ class PackedWeights:
         return int(self.desc.K)
 
     def codes(self) -> torch.Tensor:
-        """Codes as [N_pad, K_pad], row-major. The int8 buffer stores 1 KB blocks
-        of 16 rows x 64 K (see qgemm_wdesc); those come back as a row-major copy."""
+        """Codes as [N_pad, K_pad], row-major. The int8 and e4m3 buffers store
+        1 KB blocks of 16 rows x 64 K (see qgemm_wdesc); those come back as a
+        row-major copy."""
         d = self.desc
         if d.fmt == FMT_INT4_SYM:
             raw = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad // 2]
@@ -135,8 +144,8 @@ class PackedWeights:
             raw = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad // 2]
             return unpack_fp4_codes(raw.view(d.N_pad, d.K_pad // 2), d.K_pad)
         raw = self.packed[d.codes_off: d.codes_off + d.N_pad * d.K_pad]
-        if d.fmt != FMT_INT8_SYM:
-            return raw.view(d.N_pad, d.K_pad)
+        if d.fmt == FMT_MXFP8_E4M3:
+            return unblock_mx8_codes(raw, d.N_pad, d.K_pad)
         return unblock_int8_codes(raw, d.N_pad, d.K_pad).view(torch.int8)
 
     def scales(self) -> torch.Tensor:

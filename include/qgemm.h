@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define QGEMM_ABI_VERSION 8
+#define QGEMM_ABI_VERSION 9
 #define QGEMM_WDESC_MAGIC 0x51474d57u /* "WMGQ" */
 
 /* Status codes. Every entry point returns one of these. */
@@ -138,7 +138,12 @@ typedef enum {
  *           holds, at 256*c + 16*(n%16), the 16 codes of row n with k%64 in
  *           [16c, 16c+16) (so each block is one 16x16x64 int8 matrix-core
  *           operand in lane order and a streamed 1 KB load).
- *           QGEMM_FMT_MXFP8_E4M3: e4m3 codes [N_pad][K_pad], row-major.
+ *           QGEMM_FMT_MXFP8_E4M3: 1 KB blocks of 16 rows x 64 K in the same
+ *           block order as INT8; code (n, k) at byte
+ *           ((n/16)*(K_pad/64) + k/64) * 1024 + 64*(n%16) + k%64 (each block
+ *           holds its 16 rows' 64 codes in K order, so the 16 rows x 64 K a
+ *           GEMM stage takes is one contiguous 1 KB load; ABI version 9 and
+ *           later).
  *           QGEMM_FMT_MXFP4_E2M1: e2m1 codes [N_pad][K_pad/2] bytes, row-major,
  *           two per byte (element 2i in the low nibble).
  *           QGEMM_FMT_INT4_SYM: N_pad x K_pad / 2 bytes in 1 KB blocks of 16

@@ -73,8 +73,9 @@ void launch_rmsnorm_quantize(const float* x, int64_t rows, int64_t K, int64_t ld
   ++qg_stub_launches;
 }
 void launch_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ldx, bool, uint8_t* q, int64_t ldq,
-                        uint8_t* e8, int64_t lde, hipStream_t) {
+                        uint8_t* e8, int64_t lde, int64_t wblk_kpad, hipStream_t) {
   require(x && q && e8 && rows >= 0 && K % 32 == 0 && ldx >= K && lde >= K / 32, "quantize_mx args");
+  require(wblk_kpad == 0 || (wblk_kpad >= K && wblk_kpad % 256 == 0), "quantize_mx blocked weights");
   (void)ldq;
   ++qg_stub_launches;
 }

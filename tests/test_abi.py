@@ -18,7 +18,7 @@ HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.jo
 OK, E_NULL, E_SHAPE, E_MODE, E_ALIGN, E_OVERFLOW, E_DEVICE, E_DESC, E_WS = 0, -1, -2, -3, -4, -5, -6, -7, -8
 INT8, UINT8, MX, INT4, MX4 = 0, 1, 2, 3, 4
 TENSOR, ROW, BLK, G64 = 0, 1, 2, 3
-ABI = 8
+ABI = 9
 
 
 @pytest.fixture(scope="module")
@@ -441,6 +441,22 @@ def test_packed_int8_block_layout_round_trip():
             off = ((n // 16) * kb + k // 64) * 1024 + 256 * ((k % 64) // 16) + 16 * (n % 16) + k % 16
             raw[off] = ref[n, k]
     assert torch.equal(unblock_int8_codes(raw, n_pad, k_pad), ref)
+
+
+def test_packed_mx8_block_layout_round_trip():
+    """The Python view of packed e4m3 weight codes inverts the documented block
+    layout: code (n, k) at ((n // 16) * (K_pad // 64) + k // 64) KB + 64 * (n % 16)
+    + k % 64."""
+    import torch
+    from block_scaled_quantized_qgemm_amd.ops import unblock_mx8_codes
+    n_pad, k_pad = 48, 256
+    ref = torch.randint(0, 256, (n_pad, k_pad), dtype=torch.int32).to(torch.uint8)
+    raw = torch.zeros(n_pad * k_pad, dtype=torch.uint8)
+    kb = k_pad // 64
+    for n in range(n_pad):
+        for k in range(k_pad):
+            raw[((n // 16) * kb + k // 64) * 1024 + 64 * (n % 16) + k % 64] = ref[n, k]
+    assert torch.equal(unblock_mx8_codes(raw, n_pad, k_pad), ref)
 
 
 def test_packed_int4_block_layout_round_trip():
