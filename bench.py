@@ -238,10 +238,13 @@ def cpu_baseline(name, A, W, budget_s=10.0, fused=None, w4a8=False, fp4=False, w
             "threads": "cores = the BLAS thread pool the oracle's matrix products ran on"}
 
 
-def timed(fn, steps, eager):
+def timed(fn, steps, eager, repeats=None):
     """Milliseconds per call of fn(i), i = 0 .. steps-1, on the current stream,
     and the host wall time. The calls are captured once into a HIP graph and
-    replayed (eager: launched from Python), bracketed by events on the stream."""
+    replayed (eager: launched from Python), bracketed by events on the stream.
+    With a list `repeats`, four further passes are each timed the same way
+    afterwards, and every pass's ms per call (the measurement first) is put in
+    it: the others only describe the measurement's spread."""
     import torch
     if eager:
         run = lambda: [fn(i) for i in range(steps)]  # noqa: E731
@@ -260,7 +263,22 @@ def timed(fn, steps, eager):
     run()
     stop.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps, time.perf_counter() - t0
+    ms, wall = start.elapsed_time(stop) / steps, time.perf_counter() - t0
+    if repeats is not None:
+        repeats.append(ms)
+        for _ in range(4):
+            start.record()
+            run()
+            stop.record()
+            torch.cuda.synchronize()
+            repeats.append(start.elapsed_time(stop) / steps)
+    return ms, wall
+
+
+def spread(ms_list):
+    """min / median / mean of per-pass ms per step."""
+    v = sorted(ms_list)
+    return {"passes": len(v), "min_ms": v[0], "median_ms": v[len(v) // 2], "mean_ms": sum(v) / len(v)}
 
 
 def calibration_copy(mib, dev):
@@ -547,7 +565,8 @@ def main():
             l2 = measure(sub, wl, mode, False)
             sec[key] = {"workload": l2["config"]["workload"], "value": l2["value"], "unit": l2["unit"],
                         "ms_per_step": l2["ms_per_step"], "gemm_ms": l2["config"]["gemm_ms"],
-                        "dtype": l2["dtype"], "roofline": l2["roofline"]}
+                        "step_spread": l2["config"]["step_spread"], "quantize": l2["config"]["quantize"],
+                        "prepack_ms": l2["config"]["prepack_ms"], "dtype": l2["dtype"], "roofline": l2["roofline"]}
         line["secondary"] = sec
     print(json.dumps(line), flush=True)
 
@@ -593,6 +612,13 @@ def measure(args, name, mx_mode_arg, with_cpu):
         wfmt, wgr = ops.FMT_INT4_SYM, ops.GRAN_GROUP64
     w0 = ops.qgemm_prepack_weights(W0, wfmt, wgr)
     torch.cuda.synchronize()
+    # weight preparation is offline; one warm call timed with events, reported apart
+    pstart, pstop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pstart.record()
+    ops.qgemm_prepack_weights(W0, wfmt, wgr)
+    pstop.record()
+    torch.cuda.synchronize()
+    prepack_ms = pstart.elapsed_time(pstop)
     ops_count, step_bytes, gemm_bytes = algorithmic(name, M, K, N, args.w4a8, fp4, wfp4)
     if args.fused:  # the norm weight and the bias are read once more
         step_bytes += 4 * K + 4 * N
@@ -651,11 +677,23 @@ def measure(args, name, mx_mode_arg, with_cpu):
     K_steps = args.steps
 
     # Timed region 1: K whole steps (quantize + GEMM + epilogue) back to back.
-    ms_per_step, wall = timed(step, K_steps, args.eager)
+    # Four more passes afterwards describe the spread (not the value).
+    passes = []
+    ms_per_step, wall = timed(step, K_steps, args.eager, passes)
     # Timed region 2: the GEMM kernel alone, K launches over the same rotating
     # buffer sets, bracketed by events on the stream it runs on; the average
     # launch duration feeds the roofline.
     gemm_ms, _ = timed(gemm, K_steps, args.eager)
+    # The quantizer alone over the same rotation: its bytes (float32 A read,
+    # codes and per-row scales / zero points or E8M0 bytes written; the norm
+    # weight when fused) against HBM.
+    quant_ms, _ = timed(quantize, K_steps, args.eager)
+    if act == "mxfp8":
+        q_bytes = 4.0 * M * K + (0.5 if fp4 else 1.0) * M * K + M * (K // 32)
+    else:
+        q_bytes = 4.0 * M * K + M * K + 8.0 * M + (4.0 * K if args.fused else 0.0)
+    quant = {"ms": quant_ms, "gbps": q_bytes / (quant_ms * 1e-3) / 1e9, "bytes": q_bytes,
+             "frac_of_hbm": q_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
     if unit == "GB/s":
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -702,7 +740,8 @@ def measure(args, name, mx_mode_arg, with_cpu):
                    "M": M, "K": K, "N": N,
                    "rotating_buffer_sets": nsets, "gemm_ms": gemm_ms,
                    "launch": "eager" if args.eager else "hip graph (K steps captured, replayed once)",
-                   "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9},
+                   "step_hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+                   "step_spread": spread(passes), "quantize": quant, "prepack_ms": prepack_ms},
         "roofline": roof,
     }
     if args.calibration_copy:
