@@ -575,7 +575,7 @@ static hipError_t launch_mx_dma(const GemmArgs& a, hipStream_t st) {
   // 128 x 128 instead (one wave per SIMD, its 256 accumulators in AGPRs): one
   // wave with that many independent bf16 matrix-core instructions keeps its
   // SIMD's matrix core busy, and per SIMD it reads half the fragments and
-  // converts a third fewer codes (C5: 834-837 us against 840-853 us).
+  // converts a third fewer codes (8192^3 e4m3: 834-837 us against 840-853 us).
   constexpr int KPS = A4 && W4 && !EXACT ? 128 : 64;
   const bool small_groups = GROUPED && EXACT && a.M < 2048 * (int64_t)a.num_groups;
   const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
