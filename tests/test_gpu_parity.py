@@ -485,6 +485,28 @@ def test_gemm_mx_dma_bias(ops, fmt, mode):
     assert (np.abs(got - ref) <= tol * S + F32_RTOL * np.abs(ref)).all()
 
 
+def test_gemm_mx_exact_large_tiles_bias_and_padded_output(ops):
+    """The exact mode's 256x256 tiles as 4 waves of 128x128 (at least one tile
+    per CU): ragged M and N, several stages of K, a float32 bias, and an output
+    whose leading dimension is past N (the padding keeps its sentinel)."""
+    M, N, K, ldo = 4000, 4312, 512, 4400
+    print_case("gemm mx exact large tiles bias", M, N, K, "ldo", ldo)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=5151)
+    b = rng_for(N + 7).normal(0.0, 10.0, size=N).astype(np.float32)
+    a = ops.qgemm_quantize_rows(dev(A), 2, 2)
+    pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
+    out = torch.full((M, ldo), -3.0, dtype=torch.float32, device="cuda")
+    ops.qgemm_run_mx(a, pw, mode=0, bias=dev(b), out=out[:, :N])
+    o = host(out)
+    assert (o[:, N:] == -3.0).all()
+    got = o[:, :N].astype(np.float64)
+    qa, Ea = O.quantize_mx(A)
+    qw, Ew = O.quantize_mx(W)
+    ref, S = O.mx_gemm_ref(qa, Ea, qw, Ew)
+    ref = ref + b.astype(np.float64)[None, :]
+    assert (np.abs(got - ref) <= MX_STOL * S + F32_RTOL * np.abs(ref)).all()
+
+
 @pytest.mark.parametrize("K", [32, 64])
 def test_gemm_mx_modes_on_an_8_group_with_a_wide_exponent_spread(ops, K):
     """448 and 2^-6 in one group of 8 K: exact mode keeps the small product;
