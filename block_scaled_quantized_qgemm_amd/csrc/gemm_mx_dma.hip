@@ -106,9 +106,12 @@ struct MxDmaCfg {
   static constexpr int IPS = (NSL + NW - 1) / NW;    // ... per wave and stage (see the loads)
   static constexpr int IPW = IPD + IPS;
   static constexpr int MPS = (EXACT ? 4 : 1) * FM * FN;  // matrix-core instructions per 64-deep step
-  // instructions the stage's loads are spread over: the first half of the
-  // only step (KPS 64), or every step before the last (KPS 128)
-  static constexpr int SLOTS = NKK == 1 ? MPS / 2 : (NKK - 1) * MPS;
+  // instructions the stage's loads are spread over: all of the only step
+  // (KPS 64), or every step before the last (KPS 128)
+  static constexpr int SLOTS = NKK == 1 ? MPS : (NKK - 1) * MPS;
+  // stages the prologue puts in flight: with one step per stage the ring is
+  // refilled after the stage's barrier, so all NS slots start full
+  static constexpr int PRO = NKK == 1 ? NS : NS - 1;
   static constexpr int RS = TN + 8;                  // epilogue staging row stride (words)
   static constexpr int EPI = NW * 32 * RS * 4;
   static constexpr int SINK = SCALES + 2 * SUPER;   // 1 KB that the empty scale loads target
@@ -118,10 +121,10 @@ struct MxDmaCfg {
   static_assert(!(EXACT && KPS != 64), "exact-mode stages are 64 deep");
   static_assert(DATA % (1024 * NW) == 0 && (BM * RBA) % 1024 == 0 && (BM + BN) % 64 == 0 && BM % 64 == 0,
                 "loads per wave");
-  static_assert(FM % 2 == 0 && FN >= 1, "two halves of a step's MFMAs");
-  static_assert(NS >= 2 && (NS - 2) * IPW < 64, "vmcnt range");
-  // a scale slot is refilled NS - 1 stages before its first stage, after the
-  // last stage of its previous contents
+  static_assert(FM >= 1 && FN >= 1, "fragments");
+  static_assert(NS >= 2 && (PRO - 1) * IPW < 64, "vmcnt range");
+  // a scale slot is refilled NS (KPS 64) or NS - 1 (KPS 128) stages before
+  // its first stage, after every read of its previous contents
   static_assert(NS <= SS + 1, "scale slot reuse");
   static_assert(TN % 4 == 0 && (TN / 4) <= 64 && 64 % (TN / 4) == 0, "epilogue lane map");
 };
@@ -323,12 +326,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
 
   // Fragments and scale bytes of one 64-deep step kk of stage kt. The step's
   // block h sits in byte 2 kk + h of dword (kt % SS) * SPS / 4 of the row's 16
-  // scale bytes, shifted by b0 = (kt % SS) * SPS % 4 bytes. The scaled mode
-  // keeps the lane's block in the low byte; the exact mode keeps both blocks
-  // of the step (low byte: K 0-31 of the step, next byte: K 32-63).
+  // scale bytes, shifted by b0 = (kt % SS) * SPS % 4 bytes. load_frags keeps
+  // the dwords as read and their shift `sh`; unpack() then leaves the lane's
+  // block in the low byte (scaled mode) or both blocks of the step (exact
+  // mode; low byte: K 0-31 of the step, next byte: K 32-63). The shift is
+  // done apart from the reads so that it can wait where the fragments are
+  // waited for anyway, not between the reads and the next MFMAs.
   struct Frag {
     v8i a[FM], b[FN];
     int sa[FM], sb[FN];
+    int sh;
   };
   auto load_frags = [&](int kt, int kk, Frag& f) {
     const uint8_t* sa = smem + (kt % NS) * STAGE;
@@ -337,7 +344,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
     const int* ssa = reinterpret_cast<const int*>(smem + C::SCALES + ((kt / C::SS) & 1) * C::SUPER) + q * C::SPS / 4;
     const int* ssb = ssa + 4 * BM;
     const int sh = 8 * (q * C::SPS % 4 + 2 * kk) + (EXACT ? 0 : 8 * h);
-    constexpr int mask = EXACT ? 0xffff : 0xff;
     // e4m3: chunks 4 kk + h and 4 kk + h + 2 (K 16h .. and 32 + 16h ..);
     // e2m1: chunk 2 kk + h (K 32h .. 32h + 31)
     const int ca = A4 ? 2 * kk + h : 4 * kk + h, cw = W4 ? 2 * kk + h : 4 * kk + h;
@@ -365,7 +371,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
         const v4i hi = A4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sa + lds_off<RBA>(r, ca + 2));
         f.a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      f.sa[i] = (wa[i] >> sh) & mask;
+      f.sa[i] = wa[i];
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -379,8 +385,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
         const v4i hi = W4 ? v4i{0, 0, 0, 0} : *reinterpret_cast<const v4i*>(sb + lds_off<RBW>(r, cw + 2));
         f.b[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-      f.sb[j] = (wb[j] >> sh) & mask;
+      f.sb[j] = wb[j];
     }
+    f.sh = sh;
+  };
+  auto unpack = [&](Frag& f) {
+    constexpr int mask = EXACT ? 0xffff : 0xff;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) f.sa[i] = (f.sa[i] >> f.sh) & mask;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) f.sb[j] = (f.sb[j] >> f.sh) & mask;
   };
 
   // The matrix-core instructions m0_ .. m1_ - 1 of one 64-deep step (index
@@ -434,44 +448,57 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_mx_dma_kernel(GemmArgs p) {
     __builtin_amdgcn_s_barrier();
   };
 
-  // One stage kt: `f0` holds its first step's fragments; on return `f0`
-  // holds the next stage's. Stage kt + NS - 1 refills the slot every wave
-  // finished reading before the previous barrier; its loads go between the
-  // instructions before this stage's barrier.
+  // One stage kt: `fa` holds the fragments of its first step (unpacked).
+  //
+  // One step per stage (KPS 64): the barrier comes first. After it, stage
+  // kt + 1 has landed and every wave has finished reading slot kt % NS (its
+  // fragments were read during stage kt - 1), so the stage reads stage
+  // kt + 1's fragments into `fb` and refills slot kt % NS with stage kt + NS,
+  // both under all of its MFMAs; the stage ends by unpacking fb's scale
+  // bytes. The matrix cores thus never wait on the barrier's fragment reads,
+  // and NS - 1 stages stay in flight.
+  //
+  // Two steps per stage (KPS 128): step 0 (fragments in fa) with the loads of
+  // stage kt + NS - 1 (into the slot every wave finished reading before the
+  // previous barrier) while step 1's fragments are read into fb; barrier;
+  // step 1 while the next stage's step 0 is read into fa.
   Frag f0, f1;
   auto stage = [&](int kt, Frag& fa, Frag& fb) {
-    const int ks = kt + NS - 1;
-    const bool live = ks < nkt;
-    const int sl = ks % NS;
     if constexpr (NKK == 1) {
-      // first half with the loads, barrier, the next stage's fragment reads
-      // under the second half
-      mfmas(fa, 0, MPS / 2, 0, ks, sl, live);
+      const int ks = kt + NS;
       stage_barrier();
       load_frags(kt + 1, 0, fb);
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(fa, MPS / 2, MPS, -1, ks, sl, live);
+      mfmas(fa, 0, MPS, 0, ks, kt % NS, ks < nkt);
+      __builtin_amdgcn_sched_barrier(0);
+      unpack(fb);
     } else {
-      // step 0 (fragments in fa) with the loads while step 1's are read into
-      // fb; barrier; step 1 while the next stage's step 0 is read into fa
+      const int ks = kt + NS - 1;
+      const bool live = ks < nkt;
+      const int sl = ks % NS;
       load_frags(kt, 1, fb);
       __builtin_amdgcn_sched_barrier(0);
       mfmas(fa, 0, MPS, 0, ks, sl, live);
       stage_barrier();
+      unpack(fb);
+      __builtin_amdgcn_sched_barrier(0);
       load_frags(kt + 1, 0, fa);
       __builtin_amdgcn_sched_barrier(0);
       mfmas(fb, 0, MPS, -1, ks, sl, live);
+      __builtin_amdgcn_sched_barrier(0);
+      unpack(fa);
     }
   };
 
-  // prologue: stages 0 .. NS-2 in flight
+  // prologue: stages 0 .. PRO - 1 in flight
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
+  for (int s = 0; s < C::PRO; ++s)
 #pragma unroll
     for (int i = 0; i < IPW; ++i) dma(s, s, i, s < nkt);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPW));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((C::PRO - 1) * IPW));
   __builtin_amdgcn_s_barrier();
   load_frags(0, 0, f0);
+  unpack(f0);
 
   if constexpr (NKK == 1) {
     // two stages per trip so the fragment sets alternate without copies
@@ -560,29 +587,34 @@ bool mx_dma_eligible(const GemmArgs& a, int mode) {
 
 template <bool EXACT, bool A4, bool W4, bool GROUPED>
 static hipError_t launch_mx_dma(const GemmArgs& a, hipStream_t st) {
-  // 256 x 256 tiles (8 waves of 128 x 64, a 4-stage ring, one workgroup per
-  // CU) when they fill every CU; otherwise 128 x 128 tiles (4 waves of
-  // 64 x 64, two workgroups per CU). Stages of 64 K (rows of 64 bytes of
-  // e4m3, 32 of e2m1), or 128 K when both operands are e2m1 in the scaled
-  // mode (64-byte rows).
+  // 256 x 256 tiles (one workgroup per CU, a 4-stage ring) when they fill
+  // every CU; otherwise 128 x 128 tiles (4 waves of 64 x 64, two workgroups
+  // per CU). Stages of 64 K (rows of 64 bytes of e4m3, 32 of e2m1), or 128 K
+  // when both operands are e2m1 in the scaled mode (64-byte rows).
+  // On the 256 x 256 tiles the exact mode with e4m3 x e4m3 runs 4 waves of
+  // 128 x 128 (one wave per SIMD, its 256 accumulators in AGPRs): one wave
+  // with that many independent bf16 matrix-core instructions keeps its SIMD's
+  // matrix core busy, and per SIMD it reads half the fragments and converts a
+  // third fewer codes (8192^3: 834-837 us against 840-853 us on 8 waves, in
+  // alternating runs). With an e2m1 operand the 4 waves were 4-6% slower; in
+  // the scaled mode they matched the 8 waves with operands streamed from HBM
+  // (8192^3: 517-519 us against 517-518 us) and were 5% slower on the grouped
+  // MoE shape, so those keep 8 waves of 128 x 64.
   // The grouped exact mode keeps the 128 x 128 tiles when the average expert
   // has under 2048 rows: its partial last tile-rows then waste a large share
   // of 256-row tiles, and the exact mode, bound by its matrix cores and
   // conversions, gains from the finer grain (8 experts of about 1024 rows:
   // 299 us against 321 us; the scaled fp8 mode, bound by data movement,
   // keeps the larger tiles).
-  // The exact mode with e4m3 operands on the 256 x 256 tiles takes 4 waves of
-  // 128 x 128 instead (one wave per SIMD, its 256 accumulators in AGPRs): one
-  // wave with that many independent bf16 matrix-core instructions keeps its
-  // SIMD's matrix core busy, and per SIMD it reads half the fragments and
-  // converts a third fewer codes (8192^3 e4m3: 834-837 us against 840-853 us).
   constexpr int KPS = A4 && W4 && !EXACT ? 128 : 64;
   const bool small_groups = GROUPED && EXACT && a.M < 2048 * (int64_t)a.num_groups;
   const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (EXACT && !A4 && !W4 && !GROUPED && big >= cu_count())
-    return launch_mx_dma_cfg<256, 256, KPS, 2, 2, 4, EXACT, A4, W4, GROUPED>(a, st);
-  if (big >= cu_count() && !small_groups)
-    return launch_mx_dma_cfg<256, 256, KPS, 2, 4, 4, EXACT, A4, W4, GROUPED>(a, st);
+  if (big >= cu_count() && !small_groups) {
+    if constexpr (EXACT && !A4 && !W4)
+      return launch_mx_dma_cfg<256, 256, KPS, 2, 2, 4, EXACT, A4, W4, GROUPED>(a, st);
+    else
+      return launch_mx_dma_cfg<256, 256, KPS, 2, 4, 4, EXACT, A4, W4, GROUPED>(a, st);
+  }
   return launch_mx_dma_cfg<128, 128, KPS, 2, 2, 4, EXACT, A4, W4, GROUPED>(a, st);
 }
 
