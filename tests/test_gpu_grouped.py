@@ -82,13 +82,15 @@ def test_grouped_mx_parity(ops, sizes, N, K, mode):
 
 
 @pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("K", [64, 256])
 @pytest.mark.parametrize("sizes", [[700, 0, 1, 1023, 256, 513, 900, 710], [2100, 2571]])
-def test_grouped_mx_large_tiles_uneven_experts(ops, sizes, mode):
+def test_grouped_mx_large_tiles_uneven_experts(ops, sizes, K, mode):
     """Enough rows for the 256x256 tiles; experts of uneven sizes (one empty,
     several ragged), so tile-rows of one expert never take rows of the next.
     The exact mode takes the 128x128 tiles when the average expert has under
-    2048 rows (the first layout) and the 256x256 ones otherwise."""
-    N, K = 4352 - 32, 256
+    2048 rows (the first layout) and the 256x256 ones otherwise. K = 64 is a
+    single stage, fewer than the 4-stage ring the prologue fills."""
+    N = 4352 - 32
     print_case("grouped mx large", sizes, N, K, "mode", mode)
     A, W, off, a, w = _setup(ops, sizes, N, K, seed=11 + mode)
     got = host(ops.qgemm_run_mx_grouped(a, w, dev(off), mode=mode))

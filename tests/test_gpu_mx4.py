@@ -136,6 +136,20 @@ def test_gemm_mxfp4_large_tiles(ops, fa, fw):
     assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-6
 
 
+@pytest.mark.parametrize("fa,fw,mode,K", [("e2m1", "e2m1", 1, 128), ("e2m1", "e2m1", 1, 256),
+                                          ("e2m1", "e2m1", 0, 64), ("e4m3", "e2m1", 0, 128),
+                                          ("e2m1", "e4m3", 1, 64), ("e4m3", "e2m1", 1, 192)])
+def test_gemm_mxfp4_large_tiles_fewer_stages_than_the_ring(ops, fa, fw, mode, K):
+    """The 256x256 tiles with an e2m1 operand and one to three stages (128 K
+    deep for e2m1 x e2m1 in the scaled mode, else 64), fewer than the 4-stage
+    ring: both modes on ragged M and N."""
+    M, N = 4000, 4312
+    print_case("gemm mxfp4 large tiles short K", M, N, K, fa, fw, "mode", mode)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=7 * K + mode)
+    stol = MX_STOL if (mode == 0 or (fa, fw) == ("e2m1", "e2m1")) else MX_SCALED_STOL
+    _gemm_check(ops, A, W, fa, fw, mode=mode, stol=stol)
+
+
 def test_gemm_mxfp4_bias(ops):
     print_case("gemm mxfp4 bias")
     A, W = make_inputs("c5_mxfp8", M=40, K=160, N=70, seed=5)

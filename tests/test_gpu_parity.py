@@ -406,6 +406,21 @@ def test_gemm_mx_large_tiles_ragged(ops, mode):
 
 
 @pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("K", [64, 128, 192])
+def test_gemm_mx_large_tiles_fewer_stages_than_the_ring(ops, K, mode):
+    """The 256x256 tile configurations (4 waves in the exact mode, 8 in the
+    scaled one) with one to three 64-deep stages, fewer than the 4-stage ring
+    their prologue fills: the loads of the stages past K take an empty range,
+    and every stage's wait must still cover its own loads. Ragged M and N."""
+    M, N = 4000, 4312
+    print_case("gemm mx large tiles short K", M, N, K, "mode", mode)
+    A, W = make_inputs("c5_mxfp8", M=M, K=K, N=N, seed=77 + K)
+    a = ops.qgemm_quantize_rows(dev(A), 2, 2)
+    pw = ops.qgemm_prepack_weights(dev(W), 2, 2)
+    _mx_check(host(ops.qgemm_run_mx(a, pw, mode=mode)), A, W, MX_STOL if mode == 0 else MX_SCALED_STOL)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("M,N,K", [(130, 260, 320), (600, 700, 1088)])
 def test_gemm_mx_both_scale_pitches(ops, M, N, K, mode):
     """K % 64 == 0: the LDS-DMA kernel (E8M0 rows padded to a dword) and the
