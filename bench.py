@@ -547,7 +547,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; multi-GPU runs are not part of it "
+        print("bench.py: the benchmark measures one GPU; the library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
     if args.workload in MOE:
