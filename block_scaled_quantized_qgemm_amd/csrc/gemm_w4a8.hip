@@ -6,15 +6,22 @@
 namespace qg {
 
 constexpr int kW4Waves = 8;  // waves per workgroup, each on its own K range
+constexpr int kW4Cols = 2;   // 16-row weight blocks per workgroup (row kernel)
 
 // ---------------------------------------------------------------------------
 // W4A8: int8 activations x int4 weights with one float32 scale per group of
 // 64 K ("TileLang tutorial, chapter 27", sections 3.3(c) and 5.1), for 16-row
 // bands of A: the decode kernel's stream over W at half the bytes. A
-// workgroup owns 16 weight rows over all of K; its eight waves take
-// contiguous ranges of 128-deep steps (two groups). Per step a lane loads 16
-// bytes of codes (its 16-K chunk of both groups) and its activation chunks;
-// per two steps, the four group scales of its weight row (16 bytes).
+// workgroup owns kW4Cols blocks of 16 weight rows over all of K; its eight
+// waves take contiguous ranges of 128-deep steps (two groups). Per step a
+// lane loads its activation chunks once for all blocks and, per block, 16
+// bytes of codes (its 16-K chunk of both groups); per two steps, the four
+// group scales of its weight row in each block (16 bytes). Each block has its
+// own buffer ranges, so a block's steps past K_pad read zeros, never the next
+// block's codes. Two blocks per workgroup share each activation load between
+// twice the weight bytes: the activation loads, identical in every
+// workgroup, were 40% of a wave's loads with one block (8 x 4096 x 14336:
+// 8.9 -> 8.0 us; four blocks, 224 workgroups: 8.4 us).
 //
 // With at most 8 activation rows, rows 8-15 of the 16-row operand only feed
 // output rows that are never stored, so one 16-byte load per lane carries
@@ -39,10 +46,11 @@ template <int OUT, bool ONE, bool MLE8>
 __global__ __launch_bounds__(kW4Waves * 64) void gemm_w4a8_kernel(GemmArgs p) {
   constexpr int U = kW4Batch;
   constexpr int kHi = (int)0xF0F0F0F0u;
-  __shared__ v4f red[kW4Waves][64];
+  constexpr int NC = kW4Cols;
+  __shared__ v4f red[kW4Waves][NC][64];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * NC;
   const int64_t m0 = (int64_t)blockIdx.y * 16;
   const int64_t mrows = p.M - m0 < 16 ? p.M - m0 : 16;
   const int pairs = (int)(p.K_pad / 128);
@@ -53,10 +61,14 @@ __global__ __launch_bounds__(kW4Waves * 64) void gemm_w4a8_kernel(GemmArgs p) {
   const int row = lane & 15;
   constexpr uint32_t kOff = 0x80000000u;
   const int64_t blk0 = (n0 >> 4) * pairs;  // first code block of the workgroup's rows
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.w + blk0 * 1024), (short)0, (int)(pairs * 1024), kRawBufferWord3);
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.sw + blk0 * 32), (short)0, (int)(pairs * 128), kRawBufferWord3);
+  __amdgpu_buffer_rsrc_t wrs[NC], srs[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    wrs[c] = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w + (blk0 + c * pairs) * 1024), (short)0, (int)(pairs * 1024),
+                                               kRawBufferWord3);
+    srs[c] = __builtin_amdgcn_make_buffer_rsrc((void*)(p.sw + (blk0 + c * pairs) * 32), (short)0, (int)(pairs * 128),
+                                               kRawBufferWord3);
+  }
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.a + m0 * p.lda), (short)0, (int)((mrows - 1) * p.lda + ((p.K + 15) & ~(int64_t)15)),
       kRawBufferWord3);
@@ -66,10 +78,12 @@ __global__ __launch_bounds__(kW4Waves * 64) void gemm_w4a8_kernel(GemmArgs p) {
   const int akin = (MLE8 ? ((lane >> 3) & 1) * 64 : 0) + (lane >> 4) * 16;
   const uint32_t aoff = arow < mrows ? (uint32_t)(arow * p.lda + pbeg * 128 + akin) : kOff;
 
-  v4f y = {0.f, 0.f, 0.f, 0.f};
+  v4f y[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) y[c] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int b = 0; b < (ONE ? U : per); b += U) {
-    v4i wv[U], a0[U], a1[MLE8 ? 1 : U];
-    v4f sv[U / 2];
+    v4i wv[NC][U], a0[U], a1[MLE8 ? 1 : U];
+    v4f sv[NC][U / 2];
     // per step: activations, codes, and every second step the scales
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -78,11 +92,14 @@ __global__ __launch_bounds__(kW4Waves * 64) void gemm_w4a8_kernel(GemmArgs p) {
       if (!MLE8)
         a1[u] = __builtin_bit_cast(
             v4i, __builtin_amdgcn_raw_buffer_load_b128(ars, (int)(aoff + st * 128u + 64u), 0, 0));
-      wv[u] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)(woff + st * 1024u), 0, kStreamLoad));
-      if (u % 2 == 0)
-        sv[u / 2] = __builtin_bit_cast(
-            v4f, __builtin_amdgcn_raw_buffer_load_b128(srs, (int)(soff + st * 128u), 0, kStreamLoad));
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        wv[c][u] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs[c], (int)(woff + st * 1024u), 0, kStreamLoad));
+        if (u % 2 == 0)
+          sv[c][u / 2] = __builtin_bit_cast(
+              v4f, __builtin_amdgcn_raw_buffer_load_b128(srs[c], (int)(soff + st * 128u), 0, kStreamLoad));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -94,33 +111,38 @@ __global__ __launch_bounds__(kW4Waves * 64) void gemm_w4a8_kernel(GemmArgs p) {
       } else {
         x1 = a1[MLE8 ? 0 : u];
       }
-      const v4i w = wv[u];
-      const v4i w0 = {(w.x << 4) & kHi, w.x & kHi, (w.y << 4) & kHi, w.y & kHi};
-      const v4i w1 = {(w.z << 4) & kHi, w.z & kHi, (w.w << 4) & kHi, w.w & kHi};
-      const v4i zero = {0, 0, 0, 0};
-      const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[u], w0, zero, 0, 0, 0);
-      const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, w1, zero, 0, 0, 0);
-      const float s0 = (u & 1) ? sv[u / 2].z : sv[u / 2].x;
-      const float s1 = (u & 1) ? sv[u / 2].w : sv[u / 2].y;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = __builtin_fmaf(s0, (float)c0[i], y[i]);
+      for (int c = 0; c < NC; ++c) {
+        const v4i w = wv[c][u];
+        const v4i w0 = {(w.x << 4) & kHi, w.x & kHi, (w.y << 4) & kHi, w.y & kHi};
+        const v4i w1 = {(w.z << 4) & kHi, w.z & kHi, (w.w << 4) & kHi, w.w & kHi};
+        const v4i zero = {0, 0, 0, 0};
+        const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[u], w0, zero, 0, 0, 0);
+        const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, w1, zero, 0, 0, 0);
+        const float s0 = (u & 1) ? sv[c][u / 2].z : sv[c][u / 2].x;
+        const float s1 = (u & 1) ? sv[c][u / 2].w : sv[c][u / 2].y;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = __builtin_fmaf(s1, (float)c1[i], y[i]);
+        for (int i = 0; i < 4; ++i) y[c][i] = __builtin_fmaf(s0, (float)c0[i], y[c][i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[c][i] = __builtin_fmaf(s1, (float)c1[i], y[c][i]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  red[wid][lane] = y;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) red[wid][c][lane] = y[c];
   __syncthreads();
 
-  // thread t < 256 finishes item t / 64 of lane t % 64: row 4 * (l / 16) + item, column l % 16
-  for (int t = threadIdx.x; t < 256; t += kW4Waves * 64) {
-    const int l = t & 63, item = t >> 6;
+  // thread t < 256 NC finishes item (t % 256) / 64 of lane t % 64 of block t / 256:
+  // row 4 * (l / 16) + item, column 16 * block + l % 16
+  for (int t = threadIdx.x; t < 256 * NC; t += kW4Waves * 64) {
+    const int l = t & 63, item = (t >> 6) & 3, cb = t >> 8;
     const int64_t m = m0 + 4 * (l >> 4) + item;
-    const int64_t n = n0 + (l & 15);
+    const int64_t n = n0 + 16 * cb + (l & 15);
     if (m < p.M && n < p.N) {
-      float acc = red[0][l][item];
+      float acc = red[0][cb][l][item];
 #pragma unroll
-      for (int w = 1; w < kW4Waves; ++w) acc += red[w][l][item];
+      for (int w = 1; w < kW4Waves; ++w) acc += red[w][cb][l][item];
       const float sa = p.a_per_tensor ? p.sa[0] : p.sa[m];
       float yv = acc * (sa * 0.0625f);  // the codes entered as 16 q
       if (p.bias) yv = yv + p.bias[n];
@@ -411,7 +433,7 @@ static hipError_t launch_w4a8(const GemmArgs& a, hipStream_t st) {
     if (big >= cu_count()) return launch_w4a8_tiled<128, 128, 2, 4, 4, OUT>(a, st);
     return launch_w4a8_tiled<64, 128, 2, 4, 6, OUT>(a, st);
   }
-  const dim3 grid((unsigned)((a.N + 15) / 16), (unsigned)((a.M + 15) / 16));
+  const dim3 grid((unsigned)((a.N + 16 * kW4Cols - 1) / (16 * kW4Cols)), (unsigned)((a.M + 15) / 16));
   if (a.M <= 8)
     launch_w4a8_rows<OUT, true>(a, grid, st);
   else
